@@ -1,0 +1,451 @@
+"""Pins of the fp64 oracle against facts fixed outside itself.
+
+Each test names what it pins and where the fact comes from: a value the pages
+print (tests/golden/pages_figures.json), a published test vector, a textbook
+table, a library routine, a closed form, or brute force.  CPU only.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.linalg
+import scipy.stats
+
+import oracle as O
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+@pytest.fixture(scope="module")
+def cb128_4():
+    return O.build_codebook(128, 4)
+
+
+@pytest.fixture(scope="module")
+def cb128_2():
+    return O.build_codebook(128, 2)
+
+
+@pytest.fixture(scope="module")
+def cb128_3():
+    return O.build_codebook(128, 3)
+
+
+# --------------------------------------------------------------------- PRNG --
+def test_splitmix64_published_vectors():
+    g = golden("splitmix64.json")
+    out = O.splitmix64(g["state0"]["state"], 3)
+    assert [f"{int(x):016x}" for x in out] == g["state0"]["outputs_hex"]
+    out = O.splitmix64(g["state1234567"]["state"], 5)
+    assert [str(int(x)) for x in out] == g["state1234567"]["outputs"]
+    # counter form: starting later in the stream gives the same draws
+    assert np.array_equal(O.splitmix64(99, 4, start=3), O.splitmix64(99, 7)[3:])
+
+
+def test_gaussians_are_standard_normal():
+    g = O.gaussians(7, O.TAG_MC, 400_000)
+    assert abs(g.mean()) < 5 / math.sqrt(g.size)
+    assert abs(g.var() - 1.0) < 5 * math.sqrt(2.0 / g.size)
+    assert scipy.stats.kstest(g, "norm").pvalue > 1e-4
+    u = O.uniforms(7, O.TAG_SIGNS, 100_000)
+    assert u.min() >= 0.0 and u.max() < 1.0
+    assert scipy.stats.kstest(u, "uniform").pvalue > 1e-4
+
+
+# ---------------------------------------------------------------------- WHT --
+@pytest.mark.parametrize("d", [2, 8, 64, 128])
+def test_sylvester_matches_scipy_and_is_orthogonal(d):
+    H = O.sylvester(d)
+    assert np.array_equal(H, scipy.linalg.hadamard(d))
+    assert np.array_equal(H @ H.T, d * np.eye(d, dtype=np.int64))
+
+
+@pytest.mark.parametrize("d", [64, 128])
+def test_signed_wht_is_orthogonal_rotation(d):
+    R = O.rotation(d, seed=3)
+    s = O.wht_signs(d, 3)
+    assert set(np.unique(s)) == {-1.0, 1.0}
+    assert np.allclose(R, scipy.linalg.hadamard(d) @ np.diag(s) / math.sqrt(d), atol=0, rtol=0)
+    assert np.max(np.abs(R @ R.T - np.eye(d))) < 1e-12
+    # signs really differ between seeds and come from the low bit of each draw
+    assert not np.array_equal(O.wht_signs(d, 3), O.wht_signs(d, 4))
+    raw = O.stream(3, O.TAG_SIGNS, d)
+    assert np.array_equal(s < 0, (raw & np.uint64(1)) == 1)
+
+
+# --------------------------------------------------------------- octahedral --
+def test_octahedral_golden_points():
+    for p in golden("octahedral_points.json")["points"]:
+        n = np.array([p["n"]], dtype=np.float64)
+        xi, eta = O.octa_encode(n)
+        assert abs(xi[0] - p["xi_eta"][0]) < 1e-15 and abs(eta[0] - p["xi_eta"][1]) < 1e-15, p
+        back = O.octa_decode(np.array(p["xi_eta"][:1], float), np.array(p["xi_eta"][1:], float))
+        assert np.max(np.abs(back[0] - n[0] / np.linalg.norm(n[0]))) < 1e-15, p
+
+
+def test_octahedral_round_trip_1e6():
+    rng = np.random.default_rng(11)
+    g = rng.standard_normal((1_000_000, 3))
+    n = g / np.linalg.norm(g, axis=1, keepdims=True)
+    xi, eta = O.octa_encode(n)
+    assert np.all(np.abs(xi) <= 1) and np.all(np.abs(eta) <= 1)
+    # upper hemisphere <=> inside the diamond
+    inside = np.abs(xi) + np.abs(eta) <= 1
+    near_equator = np.abs(n[:, 2]) < 1e-12
+    assert np.array_equal(inside[~near_equator], n[~near_equator, 2] >= 0)
+    back = O.octa_decode(xi, eta)
+    assert np.max(np.abs(back - n)) < 1e-12
+
+
+def test_octahedral_density_bounded():
+    """The map is only roughly equal-area per face ([YL] 八面体折叠):
+    the density of (xi, eta) for uniform directions stays within a bounded
+    factor of uniform.  The exact ratio for a radial projection onto the
+    octahedron is 3*sqrt(3) (face centre vs vertex)."""
+    rng = np.random.default_rng(5)
+    g = rng.standard_normal((2_000_000, 3))
+    xi, eta = O.octa_encode(g / np.linalg.norm(g, axis=1, keepdims=True))
+    h, _, _ = np.histogram2d(xi, eta, bins=8, range=[[-1, 1], [-1, 1]])
+    ratio = h.max() / h.min()
+    assert 1.5 < ratio < 3 * math.sqrt(3)
+
+
+# ----------------------------------------------------------------- triplets --
+@pytest.mark.parametrize("d", [64, 128])
+def test_triplet_norms_lemma(d):
+    """Sum rho_i^2 = 1; rho_i^2 ~ Beta(3/2, (d-3)/2) for full triplets so that
+    rho concentrates near sqrt(3/d) ([YL] 三元组分解, Lemma 3.1)."""
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((20_000, d))
+    R = O.rotation(d, 1)
+    u = k / np.linalg.norm(k, axis=1, keepdims=True)
+    t = O.split_triplets(u @ R.T)
+    rho, _ = O.triplet_polar(t.reshape(-1, 3))
+    rho = rho.reshape(-1, O.n_triplets(d))
+    assert np.max(np.abs(np.sum(rho ** 2, axis=1) - 1)) < 1e-12
+    full = rho[:, :-1].ravel() ** 2
+    assert abs(full.mean() - 3 / d) < 5 * full.std() / math.sqrt(full.size)
+    assert scipy.stats.kstest(full[:50_000], scipy.stats.beta(1.5, (d - 3) / 2).cdf).pvalue > 1e-4
+    last_real = d - 3 * (O.n_triplets(d) - 1)
+    last = rho[:, -1] ** 2
+    assert scipy.stats.kstest(last, scipy.stats.beta(last_real / 2, (d - last_real) / 2).cdf).pvalue > 1e-4
+    # sqrt(3/d) is the RMS of rho; its mean is slightly below
+    assert abs(math.sqrt(np.mean(full)) - math.sqrt(3 / d)) < 2e-3
+    assert rho[:, :-1].mean() < math.sqrt(3 / d)
+
+
+def test_zero_triplet_direction():
+    rho, n = O.triplet_polar(np.zeros((2, 3)))
+    assert np.all(rho == 0) and np.array_equal(n, [[0, 0, 1], [0, 0, 1]])
+
+
+# ---------------------------------------------------------------- Lloyd-Max --
+def test_lloyd_max_reproduces_max_1960_gaussian_table():
+    g = golden("max1960_gaussian.json")
+    x = np.random.default_rng(0).standard_normal(2_000_000)
+    for L, mse_ref in zip(g["levels"], g["mse"]):
+        c = O.lloyd_max(x, L)
+        mse = np.mean((x - c[O.quantize(x, c)]) ** 2)
+        assert abs(mse / mse_ref - 1) < 0.01, (L, mse, mse_ref)
+    c = O.lloyd_max(x, 2)
+    assert np.allclose(c, [-math.sqrt(2 / math.pi), math.sqrt(2 / math.pi)], atol=3e-3)
+
+
+def test_lloyd_max_fixed_point(cb128_3):
+    rho, dirs = O.mc_samples(128, 0)
+    for c, samples in ((cb128_3.c_rho, rho), (O.lloyd_max(dirs, 16), dirs)):
+        idx = O.quantize(samples, c)
+        for k in range(c.size):
+            cell = samples[idx == k]
+            assert cell.size > 0
+            assert abs(cell.mean() - c[k]) < 1e-12 * max(1.0, abs(c[k])) + 1e-13
+
+
+def test_direction_codebook_antisymmetric(cb128_4):
+    c = cb128_4.c_xi
+    assert np.array_equal(c, -c[::-1])
+    assert np.all(np.diff(c) > 0) and np.all(np.diff(cb128_4.c_rho) > 0)
+    assert O.midpoints(c)[c.size // 2 - 1] == 0.0
+
+
+def _lloyd_weighted(x, w, L, iters=20000, symmetric=False):
+    """Lloyd-Max on a weighted quadrature grid (test helper)."""
+    c = np.interp((np.arange(L) + 0.5) / L, np.cumsum(w) / w.sum(), x)
+    if symmetric:
+        c = 0.5 * (c - c[::-1])
+    for _ in range(iters):
+        m = 0.5 * (c[:-1] + c[1:])
+        idx = np.searchsorted(m, x, side="left")
+        s = np.bincount(idx, w * x, L)
+        n = np.bincount(idx, w, L)
+        new = s / n
+        if np.max(np.abs(new - c)) < 1e-14:
+            break
+        c = new
+    return c
+
+
+def test_rho_codebook_matches_quadrature_lloyd_max(cb128_4):
+    """MC codebook for rho vs Lloyd-Max solved by quadrature on the exact
+    pooled density: 42 full triplets with rho^2 ~ Beta(3/2, 125/2) and one
+    2-coordinate triplet with rho^2 ~ Beta(1, 63) at d=128."""
+    x = np.linspace(1e-6, 0.8, 400_001)
+    dens = lambda a, b: scipy.stats.beta(a, b).pdf(x * x) * 2 * x  # noqa: E731
+    w = (42 * dens(1.5, 62.5) + dens(1.0, 63.0)) / 43
+    c = _lloyd_weighted(x, w, cb128_4.c_rho.size)
+    # Monte-Carlo spread of the lowest centroid over codebook seeds is about
+    # 2e-3 relative (65536 vectors); the others are tighter.
+    assert np.max(np.abs(c / cb128_4.c_rho - 1)) < 6e-3
+    assert np.max(np.abs(c[1:] / cb128_4.c_rho[1:] - 1)) < 2e-3
+
+
+def test_direction_codebook_matches_quadrature_lloyd_max(cb128_2, cb128_3):
+    """MC xi/eta codebook vs Lloyd-Max by quadrature on the exact density of
+    the octahedral coordinate.  For a uniform direction the pair (xi, eta) has
+    density proportional to 1/|v|^3 on the square (v the unnormalised decode
+    vector: radial projection onto the octahedron, and the fold has unit
+    Jacobian); the 2-coordinate last triplet of d=128 gives
+    xi = cos t/(|cos t| + |sin t|) for uniform t.  Pooled 42:1."""
+    n, m = 20000, 2000
+    g = (np.arange(n) + 0.5) / n * 2 - 1
+    e = (np.arange(m) + 0.5) / m * 2 - 1
+    w_full = np.zeros(n)
+    for s in range(0, n, 1000):
+        XI, ETA = g[s:s + 1000, None], e[None, :]
+        r = 1 - np.abs(XI) - np.abs(ETA)
+        lower = r < 0
+        X = np.where(lower, (1 - np.abs(ETA)) * np.sign(XI), XI)
+        Y = np.where(lower, (1 - np.abs(XI)) * np.sign(ETA), ETA)
+        w_full[s:s + 1000] = (1.0 / np.sqrt(X * X + Y * Y + r * r) ** 3).sum(axis=1)
+    w_full /= w_full.sum()
+    th = (np.arange(20_000_000) + 0.5) / 20_000_000 * 2 * math.pi
+    h_last, _ = np.histogram(np.cos(th) / (np.abs(np.cos(th)) + np.abs(np.sin(th))), bins=n, range=(-1, 1))
+    w = 42 * w_full + h_last / h_last.sum()
+    w = 0.5 * (w + w[::-1])
+    for cb in (cb128_2, cb128_3):
+        c = _lloyd_weighted(g, w, cb.c_xi.size, symmetric=True)
+        # the Lloyd fixed point of a near-flat density is ill-conditioned, so
+        # the Monte-Carlo codebook sits within ~1e-3 of the quadrature one
+        assert np.max(np.abs(c - cb.c_xi)) < 1.5e-3
+
+
+def test_nearest_centroid_brute_force():
+    rng = np.random.default_rng(4)
+    for L in (2, 4, 8, 32):
+        c = np.sort(rng.standard_normal(L))
+        x = rng.standard_normal(5000) * 2
+        brute = np.argmin(np.abs(x[:, None] - c[None, :]), axis=1)
+        assert np.array_equal(O.quantize(x, c), brute)
+    c = np.array([-1.0, 1.0])
+    assert O.quantize(np.array([0.0, 1e-300, -1e-300]), c).tolist() == [0, 1, 0]
+
+
+# --------------------------------------------------------------------- bits --
+def test_bits_per_triplet():
+    for b in (2, 3, 4):
+        assert sum(O.default_alloc(b)) == 3 * b + 1
+        assert sum((b, b, b)) == 3 * b
+        lay = O.layout(128, O.default_alloc(b))
+        assert lay["n_triplets"] == 43 and lay["pad_dim"] == 129
+        assert lay["words_per_key"] == math.ceil(43 * (3 * b + 1) / 32)
+    assert O.layout(64, (4, 4, 2))["n_triplets"] == 22
+    assert O.layout(128, (4, 4, 2))["words_per_key"] == 14
+    assert O.layout(128, (5, 5, 3))["words_per_key"] == 18
+    assert O.layout(128, (3, 3, 1))["words_per_key"] == 10
+    assert O.layout(64, (4, 4, 2))["words_per_key"] == 7
+
+
+def test_pack_golden_and_bijection():
+    g = golden("packing_example.json")
+    codes = np.array([g["codes"]], dtype=np.int64)
+    w = O.pack_codes(codes, g["alloc"])
+    assert w.tolist() == [g["words"]]
+    assert np.array_equal(O.unpack_codes(w, 5, g["alloc"]), codes)
+    rng = np.random.default_rng(9)
+    for alloc in ((3, 3, 1), (4, 4, 2), (5, 5, 3), (3, 3, 3), (4, 3, 2)):
+        for T in (22, 43):
+            c = np.stack([rng.integers(0, 1 << a, (100, T)) for a in alloc], axis=-1)
+            w = O.pack_codes(c, alloc)
+            assert np.array_equal(O.unpack_codes(w, T, alloc), c)
+            used = T * sum(alloc)
+            if used % 32:
+                assert np.all((w[:, -1].astype(np.uint64) >> np.uint64(used % 32)) == 0)
+    tiles = O.to_tiles(w.reshape(1, 100, -1), 128)
+    assert tiles.shape == (1, 2, w.shape[1], 64)
+    assert tiles[0, 1, 3, 5] == w[64 + 5, 3]
+    assert np.array_equal(O.from_tiles(tiles, 100)[0], w)
+
+
+def test_sign_packing():
+    rng = np.random.default_rng(1)
+    s = np.where(rng.standard_normal((10, 128)) >= 0, 1.0, -1.0)
+    w = O.pack_signs(s)
+    assert w.shape == (10, 4)
+    assert np.array_equal(O.unpack_signs(w, 128), s)
+    one = np.full((1, 64), -1.0)
+    one[0, 33] = 1.0
+    assert O.pack_signs(one).tolist() == [[0, 2]]
+
+
+# --------------------------------------------------------------- end to end --
+@pytest.mark.parametrize("d", [64, 128])
+def test_unquantised_chain_is_exact(d):
+    """With the quantiser replaced by the identity the rotation, triplet split,
+    octahedral map and their inverses give back the key to 1e-12."""
+    cb = O.build_codebook(d, 3)
+    rng = np.random.default_rng(3)
+    k = rng.standard_normal((500, d)) * rng.lognormal(0, 1, (500, 1))
+    k[7] = 0.0
+    e = O.encode(k, cb, identity=True)
+    uh = O.reconstruct_rotated(e.values, d)
+    assert np.max(np.abs(uh - e.rotated)) < 1e-12
+    gamma = np.linalg.norm(k, axis=1)
+    back = gamma[:, None] * (uh @ cb.R)
+    assert np.max(np.abs(back - k) / np.maximum(gamma, 1)[:, None]) < 1e-12
+
+
+def _mse(cb, n_keys=65536, seed=123):
+    k = np.random.default_rng(seed).standard_normal((n_keys, cb.d))
+    e = O.encode(k, cb)
+    g = np.linalg.norm(k, axis=1)
+    kh = O.decode(e.codes, g, cb)
+    return float(np.mean(np.sum((k - kh) ** 2, axis=1) / g ** 2))
+
+
+def test_printed_mse_b4(cb128_4):
+    """[YL] 实验结果: normalised MSE 0.0071 at 4 bits, below TurboQuant-MSE."""
+    g = golden("pages_figures.json")
+    mse = _mse(cb128_4)
+    assert abs(mse / g["octopus_mse_b4"] - 1) < 0.03
+    assert mse < g["turboquant_mse_b4"]
+
+
+def test_printed_mse_b2(cb128_2):
+    g = golden("pages_figures.json")
+    mse = _mse(cb128_2)
+    assert abs(mse / g["octopus_mse_b2"] - 1) < 0.03
+    assert mse < g["polarquant_mse_b2"]
+
+
+def test_allocation_sweep_prefers_direction_plus_one():
+    """[YL] 非均匀比特分配: delta=+1 beats uniform, delta=-1 is far worse.
+    Scalar rounding here, so only the ordering is pinned (the printed
+    percentages belong to the page's rounding rule)."""
+    g = golden("pages_figures.json")
+    res = {}
+    for delta in (-1, 0, 1):
+        cb = O.build_codebook(128, 3, alloc=(3 + delta, 3 + delta, 3 - delta), M=16384)
+        res[delta] = _mse(cb, n_keys=8192)
+    assert res[1] < res[0] < res[-1]
+    assert res[-1] / res[0] - 1 > g["delta_minus1_loss_min"]
+    assert g["delta_plus1_gain_range"][0] - 0.05 < 1 - res[1] / res[0] < g["delta_plus1_gain_range"][1] + 0.05
+
+
+def test_zero_key_encodes_and_decodes_to_zero(cb128_3):
+    k = np.zeros((1, 128))
+    e = O.encode(k, cb128_3)
+    assert e.gamma[0] == 0
+    L = cb128_3.c_xi.size
+    assert np.all(e.codes[0, :, 0] == L // 2 - 1) and np.all(e.codes[0, :, 2] == 0)
+    assert np.all(O.decode(e.codes, e.gamma, cb128_3) == 0)
+
+
+def test_logits_two_ways(cb128_3):
+    rng = np.random.default_rng(8)
+    k = rng.standard_normal((300, 128))
+    q = rng.standard_normal((5, 128))
+    e = O.encode(k, cb128_3)
+    kh = O.decode(e.codes, e.gamma, cb128_3)
+    uh = O.decode_rotated(e.codes, cb128_3)
+    l1 = O.logits(q, kh)
+    l2 = O.logits_rotated(q, uh, e.gamma, cb128_3)
+    assert np.max(np.abs(l1 - l2)) < 1e-12 * np.max(np.abs(l1))
+
+
+def test_attention_matches_torch_sdpa(cb128_3):
+    torch = pytest.importorskip("torch")
+    rng = np.random.default_rng(6)
+    B, Hq, Hkv, n, nq, d = 2, 8, 2, 200, 3, 128
+    k = rng.standard_normal((B, Hkv, n, d))
+    v = rng.standard_normal((B, Hkv, n, d))
+    q = rng.standard_normal((B, Hq, nq, d))
+    e = O.encode(k.reshape(-1, d), cb128_3)
+    kh = O.decode(e.codes, e.gamma, cb128_3).reshape(B, Hkv, n, d)
+    out = O.gqa_attention(q, kh, v)
+    G = Hq // Hkv
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(kh).repeat_interleave(G, 1),
+        torch.from_numpy(v).repeat_interleave(G, 1)).numpy()
+    assert np.max(np.abs(out - ref)) < 1e-12
+    # and with exact (unquantised) keys the chain reproduces textbook attention
+    ref2 = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(q), torch.from_numpy(k).repeat_interleave(G, 1),
+        torch.from_numpy(v).repeat_interleave(G, 1)).numpy()
+    e2 = O.encode(k.reshape(-1, d), cb128_3, identity=True)
+    gam = np.linalg.norm(k.reshape(-1, d), axis=1)
+    k2 = (gam[:, None] * (O.reconstruct_rotated(e2.values, d) @ cb128_3.R)).reshape(B, Hkv, n, d)
+    assert np.max(np.abs(O.gqa_attention(q, k2, v) - ref2)) < 1e-12
+
+
+# ---------------------------------------------------------------------- QJL --
+def test_qjl_sign_expectation_closed_form():
+    """E[sgn(<S_j, r>) <S_j, q>] = sqrt(2/pi) <q, r>/|r| for Gaussian rows
+    ([TQ] 四 QJL estimator), averaged over rows of many seeded S."""
+    d = 32
+    rng = np.random.default_rng(0)
+    q, r = rng.standard_normal(d), rng.standard_normal(d)
+    vals = []
+    for seed in range(400):
+        S = O.qjl_matrix(d, seed)
+        vals.append(np.sign(S @ r + 0.0) * (S @ q))
+    vals = np.concatenate(vals)
+    target = math.sqrt(2 / math.pi) * q @ r / np.linalg.norm(r)
+    assert abs(vals.mean() - target) < 4 * vals.std() / math.sqrt(vals.size)
+
+
+def test_qjl_logits_unbiased_over_seeds(cb128_3):
+    """Seed-averaged OCTOPUS-QJL logit -> <q, k> ([AR] OCTOPUS-QJL)."""
+    import dataclasses
+    d = 128
+    rng = np.random.default_rng(1)
+    k = rng.standard_normal((4, d))
+    q = rng.standard_normal(d)
+    exact = k @ q
+    est, plain = [], []
+    for seed in range(192):
+        cb = dataclasses.replace(cb128_3, seed=seed, signs=O.wht_signs(d, seed), R=O.rotation(d, seed))
+        e = O.encode(k, cb)
+        uh = O.decode_rotated(e.codes, cb)
+        S = O.qjl_matrix(d, seed)
+        qe = O.qjl_encode(e.rotated, uh, S)
+        est.append(O.qjl_logits(q, uh, e.gamma, qe, S, cb))
+        plain.append(O.logits_rotated(q, uh, e.gamma, cb))
+    est, plain = np.array(est), np.array(plain)
+    se = est.std(axis=0) / math.sqrt(est.shape[0])
+    assert np.all(np.abs(est.mean(axis=0) - exact) < 4.5 * se + 1e-6 * np.abs(exact))
+    # QJL leaves the reconstruction alone: its base term is the plain logit
+    assert np.array_equal(O.qjl_logits(q, uh, e.gamma, dataclasses.replace(qe, nu=qe.nu * 0), S, cb), plain[-1])
+
+
+# ------------------------------------------------------------ joint rounding --
+def test_joint_rounding_3x3_vs_exhaustive_and_better_than_scalar(cb128_2):
+    """[YL] 联合取整: the 3x3 neighbourhood of the scalar indices finds the
+    exhaustive optimum for (nearly) all triplets and lowers the error."""
+    rng = np.random.default_rng(2)
+    k = rng.standard_normal((100, 128))
+    e = O.encode(k, cb128_2)
+    t = O.split_triplets(e.rotated).reshape(-1, 3)
+    j3 = O.joint_round(t, cb128_2)
+    jx = O.joint_round(t, cb128_2, exhaustive=True)
+    assert np.mean(np.all(j3 == jx, axis=1)) > 0.995
+    err = lambda c: np.sum((O.dequantize(c.reshape(-1, 1, 3), cb128_2)[:, 0, 2:3]  # noqa: E731
+                            * O.octa_decode(cb128_2.c_xi[c[:, 0]], cb128_2.c_eta[c[:, 1]]) - t) ** 2)
+    assert err(jx) <= err(j3) + 1e-12
+    assert err(j3) < err(e.codes.reshape(-1, 3))
