@@ -1,0 +1,276 @@
+"""Python binding of liboctox.so, the OCTOPUS key-codec library for MI355X.
+
+Argument marshalling only: every step of the codec runs in the HIP kernels
+behind the C ABI declared in include/octo.h.  The functions below carry the
+same names as the C entry points; torch tensors are used only as device
+memory and torch's current stream as the launch stream.  The library must be
+built first (``python -m rotation_preconditioned_quantization_amd.build``);
+importing works without it, but every call then raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import math
+import os
+from dataclasses import dataclass
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "liboctox.so")
+
+OCTO_OK, OCTO_ERR_INVALID_ARG, OCTO_ERR_UNSUPPORTED, OCTO_ERR_HIP, OCTO_ERR_NOMEM, OCTO_ERR_WORKSPACE = range(6)
+OCTO_F32, OCTO_BF16, OCTO_F16 = 0, 1, 2
+STAGE_ROTATE, STAGE_MAIN, STAGE_COMBINE, STAGE_ALL = 1, 2, 4, 7
+TILE = 64
+
+
+class OctoError(RuntimeError):
+    def __init__(self, status: int, what: str, msg: str):
+        super().__init__(f"{what}: status {status} ({msg})")
+        self.status = status
+
+
+class octo_params(ctypes.Structure):
+    _fields_ = [("d", ctypes.c_int), ("b", ctypes.c_int), ("seed", ctypes.c_uint64),
+                ("cb_seed", ctypes.c_uint64), ("b_xi", ctypes.c_int), ("b_eta", ctypes.c_int),
+                ("b_rho", ctypes.c_int), ("qjl", ctypes.c_int), ("mc_vectors", ctypes.c_int),
+                ("device", ctypes.c_int)]
+
+
+class octo_layout(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int) for n in (
+        "d", "n_triplets", "pad_dim", "b_xi", "b_eta", "b_rho", "bits_per_triplet",
+        "bits_per_key", "words_per_key", "tile_keys", "qjl", "qjl_words_per_key")] + \
+        [("packed_bytes_per_key_alloc", ctypes.c_size_t)]
+
+
+_lib = None
+
+_P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
+_SIGS = {
+    "octo_codebook_build": (_I, [ctypes.POINTER(octo_params), ctypes.POINTER(_P)]),
+    "octo_codebook_free": (_I, [_P]),
+    "octo_codebook_layout": (_I, [_P, ctypes.POINTER(octo_layout)]),
+    "octo_codebook_export": (_I, [_P, _P, _P, _P, _P, _P]),
+    "octo_packed_bytes": (_SZ, [_P, _I64, _I64]),
+    "octo_qjl_bits_bytes": (_SZ, [_P, _I64, _I64]),
+    "octo_encode": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "octo_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I64]),
+    "octo_decode_logits": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
+    "octo_decode_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64, _F,
+                              _P, _P, _SZ, _P]),
+    "octo_decode_logits_stages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ,
+                                       _P, _I]),
+    "octo_decode_attn_stages": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64,
+                                     _F, _P, _P, _SZ, _P, _I]),
+    "octo_debug_reconstruct": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "octo_status_str": (ctypes.c_char_p, [_I]),
+    "octo_last_error": (ctypes.c_char_p, []),
+}
+
+
+def lib():
+    """The loaded library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is not built: run "
+                               "`python -m rotation_preconditioned_quantization_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = L
+    return _lib
+
+
+def exported_symbols():
+    return sorted(_SIGS)
+
+
+def _check(status: int, what: str):
+    if status != OCTO_OK:
+        raise OctoError(status, what, lib().octo_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(t):
+    import torch
+    return {torch.float32: OCTO_F32, torch.bfloat16: OCTO_BF16, torch.float16: OCTO_F16}[t.dtype]
+
+
+def _stream(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclass
+class Layout:
+    d: int
+    n_triplets: int
+    pad_dim: int
+    b_xi: int
+    b_eta: int
+    b_rho: int
+    bits_per_triplet: int
+    bits_per_key: int
+    words_per_key: int
+    tile_keys: int
+    qjl: int
+    qjl_words_per_key: int
+
+
+class Codebook:
+    """Owns an octo_codebook handle (octo_codebook_build / octo_codebook_free)."""
+
+    def __init__(self, d: int, b: int, seed: int = 0, cb_seed: int = 0, alloc=None,
+                 qjl: bool = False, mc_vectors: int = 0, device: int | None = 0):
+        p = octo_params()
+        p.d, p.b, p.seed, p.cb_seed = d, b, seed, cb_seed
+        p.b_xi, p.b_eta, p.b_rho = alloc if alloc is not None else (-1, -1, -1)
+        p.qjl, p.mc_vectors = int(bool(qjl)), mc_vectors
+        p.device = -1 if device is None else device
+        h = ctypes.c_void_p()
+        _check(lib().octo_codebook_build(ctypes.byref(p), ctypes.byref(h)), "octo_codebook_build")
+        self.handle = h
+        lay = octo_layout()
+        _check(lib().octo_codebook_layout(h, ctypes.byref(lay)), "octo_codebook_layout")
+        self.layout = Layout(*[getattr(lay, f) for f, _ in octo_layout._fields_[:-1]])
+        self.d, self.b, self.seed, self.cb_seed, self.qjl = d, b, seed, cb_seed, bool(qjl)
+
+    def close(self):
+        if getattr(self, "handle", None) is not None:
+            lib().octo_codebook_free(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+    def export(self):
+        """Host copies of the tables: (c_xi, c_eta, c_rho, signs, S or None) as numpy."""
+        import numpy as np
+        lay = self.layout
+        cx = np.zeros(1 << lay.b_xi)
+        ce = np.zeros(1 << lay.b_eta)
+        cr = np.zeros(1 << lay.b_rho)
+        sg = np.zeros(self.d, dtype=np.int8)
+        S = np.zeros((self.d, self.d), dtype=np.float32) if self.qjl else None
+        _check(lib().octo_codebook_export(self.handle, cx.ctypes.data, ce.ctypes.data, cr.ctypes.data,
+                                          sg.ctypes.data, S.ctypes.data if S is not None else None),
+               "octo_codebook_export")
+        return cx, ce, cr, sg, S
+
+    # sizes ---------------------------------------------------------------
+    def packed_words(self, n_seq: int, cap: int) -> int:
+        return lib().octo_packed_bytes(self.handle, n_seq, cap) // 4
+
+    def qjl_words(self, n_seq: int, cap: int) -> int:
+        return lib().octo_qjl_bits_bytes(self.handle, n_seq, cap) // 4
+
+    def workspace_bytes(self, mode: int, B: int, Hq: int, Hkv: int, n_q: int, n_keys: int) -> int:
+        return lib().octo_decode_workspace_bytes(self.handle, mode, B, Hq, Hkv, n_q, n_keys)
+
+
+class Cache:
+    """Caller-owned device buffers of one compressed K cache (torch tensors)."""
+
+    def __init__(self, cb: Codebook, n_seq: int, cap: int, device="cuda", qjl: bool | None = None):
+        import torch
+        if cap % TILE:
+            raise ValueError("cap must be a multiple of 64")
+        self.cb, self.n_seq, self.cap = cb, n_seq, cap
+        self.packed = torch.zeros(cb.packed_words(n_seq, cap), dtype=torch.int32, device=device)
+        self.gamma = torch.zeros(n_seq * cap, dtype=torch.float32, device=device)
+        use_qjl = cb.qjl if qjl is None else qjl
+        self.qjl_bits = (torch.zeros(cb.qjl_words(n_seq, cap), dtype=torch.int32, device=device)
+                         if use_qjl else None)
+        self.qjl_norm = (torch.zeros(n_seq * cap, dtype=torch.int16, device=device)
+                         if use_qjl else None)
+
+
+def octo_encode(cb: Codebook, keys, cache: Cache, pos0: int = 0, stream=None):
+    """keys: device tensor [n_seq, n_new, d] (f32/bf16/f16, last dim contiguous)."""
+    n_seq, n_new, d = keys.shape
+    if d != cb.d or keys.stride(2) != 1:
+        raise ValueError("keys must be [n_seq, n_new, d] with a contiguous last dim")
+    _check(lib().octo_encode(cb.handle, _ptr(keys), _dtype_code(keys), n_seq, n_new, keys.stride(0),
+                             keys.stride(1), pos0, cache.cap, _ptr(cache.packed), _ptr(cache.gamma),
+                             _ptr(cache.qjl_bits), _ptr(cache.qjl_norm), _stream(stream)),
+           "octo_encode")
+
+
+def _workspace(cb, mode, B, Hq, Hkv, n_q, n_keys, workspace, device):
+    import torch
+    need = cb.workspace_bytes(mode, B, Hq, Hkv, n_q, n_keys)
+    if workspace is None:
+        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+    return workspace, need
+
+
+def octo_decode_logits(cb: Codebook, q, cache: Cache, n_keys: int, Hkv: int, logits=None,
+                       workspace=None, use_qjl: bool | None = None, stream=None,
+                       stages: int = STAGE_ALL):
+    """q: [B, Hq, d]; returns fp32 logits [B, Hq, n_keys] (raw <q, k^>)."""
+    import torch
+    B, Hq, d = q.shape
+    if logits is None:
+        logits = torch.empty((B, Hq, n_keys), dtype=torch.float32, device=q.device)
+    workspace, _ = _workspace(cb, 0, B, Hq, Hkv, 1, n_keys, workspace, q.device)
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _check(lib().octo_decode_logits_stages(cb.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv,
+                                           _ptr(cache.packed), _ptr(cache.gamma),
+                                           _ptr(cache.qjl_bits) if qjl else None,
+                                           _ptr(cache.qjl_norm) if qjl else None, n_keys, cache.cap,
+                                           _ptr(logits), _ptr(workspace), workspace.numel(),
+                                           _stream(stream), stages),
+           "octo_decode_logits")
+    return logits
+
+
+def octo_decode_attn(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, out=None,
+                     scale: float = 0.0, workspace=None, use_qjl: bool | None = None, stream=None,
+                     stages: int = STAGE_ALL):
+    """q: [B, Hq, n_q, d]; v: [B*Hkv, cap, d] bf16; returns fp32 [B, Hq, n_q, d].
+
+    ``stages`` selects a subset of the launches (octo_decode_attn_stages)."""
+    import torch
+    B, Hq, n_q, d = q.shape
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q.device)
+    workspace, _ = _workspace(cb, 1, B, Hq, Hkv, n_q, n_keys, workspace, q.device)
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _check(lib().octo_decode_attn_stages(cb.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, n_q,
+                                         _ptr(cache.packed), _ptr(cache.gamma),
+                                         _ptr(cache.qjl_bits) if qjl else None,
+                                         _ptr(cache.qjl_norm) if qjl else None, _ptr(v),
+                                         _dtype_code(v), n_keys, cache.cap, scale, _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream), stages),
+           "octo_decode_attn")
+    return out
+
+
+def octo_debug_reconstruct(cb: Codebook, cache: Cache, n_keys: int, out=None, stream=None):
+    import torch
+    if out is None:
+        out = torch.empty((cache.n_seq, n_keys, cb.d), dtype=torch.float32, device=cache.packed.device)
+    _check(lib().octo_debug_reconstruct(cb.handle, _ptr(cache.packed), _ptr(cache.gamma), cache.n_seq,
+                                        n_keys, cache.cap, _ptr(out), _stream(stream)),
+           "octo_debug_reconstruct")
+    return out
+
+
+def default_scale(d: int) -> float:
+    return 1.0 / math.sqrt(d)

@@ -1,0 +1,138 @@
+// Device-side helpers shared by the OCTOPUS HIP kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+#include "octo_internal.hpp"
+
+namespace octo {
+
+enum { DT_F32 = 0, DT_BF16 = 1, DT_F16 = 2 };
+
+template <int D, int B>
+struct Codec {
+  static constexpr int T = (D + 2) / 3;          // triplets, zero padded
+  static constexpr int BX = B + 1;               // bits of xi   ([YL] 非均匀比特分配:
+  static constexpr int BE = B + 1;               // bits of eta    direction b+1,
+  static constexpr int BR = B - 1;               // bits of rho    length b-1)
+  static constexpr int BT = BX + BE + BR;        // bits per triplet (3b+1)
+  static constexpr int W = (T * BT + 31) / 32;   // u32 words per key
+  static constexpr int LX = 1 << BX, LE = 1 << BE, LR = 1 << BR;
+  static constexpr int NDIR = 1 << (BX + BE);
+  static constexpr uint32_t DIR_MASK = NDIR - 1;
+};
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float f16_lo(uint32_t w) {
+  return __half2float(__ushort_as_half((unsigned short)(w & 0xffffu)));
+}
+__device__ __forceinline__ float f16_hi(uint32_t w) {
+  return __half2float(__ushort_as_half((unsigned short)(w >> 16)));
+}
+
+// Convert one 16-byte chunk of dtype DT to floats (8 for 16-bit types, 4 for f32).
+template <int DT>
+__device__ __forceinline__ void cvt_chunk(const uint4& c, float* out) {
+  if constexpr (DT == DT_F32) {
+    out[0] = __uint_as_float(c.x); out[1] = __uint_as_float(c.y);
+    out[2] = __uint_as_float(c.z); out[3] = __uint_as_float(c.w);
+  } else if constexpr (DT == DT_BF16) {
+    out[0] = bf16_lo(c.x); out[1] = bf16_hi(c.x); out[2] = bf16_lo(c.y); out[3] = bf16_hi(c.y);
+    out[4] = bf16_lo(c.z); out[5] = bf16_hi(c.z); out[6] = bf16_lo(c.w); out[7] = bf16_hi(c.w);
+  } else {
+    out[0] = f16_lo(c.x); out[1] = f16_hi(c.x); out[2] = f16_lo(c.y); out[3] = f16_hi(c.y);
+    out[4] = f16_lo(c.z); out[5] = f16_hi(c.z); out[6] = f16_lo(c.w); out[7] = f16_hi(c.w);
+  }
+}
+
+template <int DT> struct DtSize { static constexpr int v = DT == DT_F32 ? 4 : 2; };
+
+// Unnormalised Walsh-Hadamard transform y = H_D x in registers, Sylvester
+// order (H_2m = [[H_m, H_m], [H_m, -H_m]]): in-place butterflies of stride
+// 1, 2, 4, ...  ([YL] 旋转魔法 / 工程实现: O(d log d) butterflies).
+template <int D>
+__device__ __forceinline__ void wht_regs(float (&v)[D]) {
+#pragma unroll
+  for (int h = 1; h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+// s .* v where bit j of the mask means s_j = -1 (flip the IEEE sign bit).
+template <int D>
+__device__ __forceinline__ void apply_signs(float (&v)[D], const uint32_t (&bits)[4]) {
+#pragma unroll
+  for (int j = 0; j < D; ++j) {
+    const uint32_t m = ((bits[j >> 5] >> (j & 31)) & 1u) << 31;
+    v[j] = __uint_as_float(__float_as_uint(v[j]) ^ m);
+  }
+}
+
+// Nearest centroid by the midpoint rule i = #{k : x > m_k}, from LDS tables.
+__device__ __forceinline__ int quant_lookup(float x, const uint8_t* lut, const float* mid, float lo,
+                                            float inv_w, float nbm1) {
+  float f = (x - lo) * inv_w;
+  f = __builtin_fminf(__builtin_fmaxf(f, 0.0f), nbm1);
+  const int base = lut[(int)f];
+  return base + (x > mid[base] ? 1 : 0) + (x > mid[base + 1] ? 1 : 0);
+}
+
+// Bit field [pos, pos+bits) of a little-endian u32 stream held in registers.
+// Called from fully unrolled loops, so pos and bits fold to constants and the
+// word array stays in registers (one v_bfe or v_alignbit + v_and).
+template <int W>
+__device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[W], int pos, int bits) {
+  const int wi = pos >> 5, off = pos & 31;
+  const uint32_t lo = w[wi];
+  const uint32_t hi = (wi + 1 < W) ? w[wi + 1] : 0u;
+  const uint32_t v = (off + bits <= 32) ? (lo >> off) : __builtin_amdgcn_alignbit(hi, lo, off);
+  return v & ((1u << bits) - 1u);
+}
+
+// Pointer into the constant address space: uniform loads through it become
+// scalar loads (s_load) whose results feed VALU ops as SGPR operands.
+typedef const __attribute__((address_space(4))) float cfloat;
+
+// An SGPR zero the compiler cannot see through.  Adding it to a loop's
+// constant-memory indices keeps those loads inside the loop (reloaded from
+// the scalar cache) instead of being hoisted into hundreds of VGPRs.
+__device__ __forceinline__ int opaque_zero() {
+  int z = 0;
+  asm volatile("" : "+s"(z));
+  return z;
+}
+
+// Wave64 all-reduce with DPP: xor 1, xor 2 (quad_perm), half-row mirror,
+// row mirror give every lane its 16-lane row result; the four rows are then
+// combined through lanes 0, 16, 32, 48.
+template <typename Op>
+__device__ __forceinline__ float wave_allreduce(float x, Op op) {
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0xB1, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x4E, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x141, 0xF, 0xF, false)));
+  x = op(x, __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(x), 0x140, 0xF, 0xF, false)));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 48));
+  return op(op(r0, r1), op(r2, r3));
+}
+
+struct OpMax { __device__ float operator()(float a, float b) const { return fmaxf(a, b); } };
+struct OpAdd { __device__ float operator()(float a, float b) const { return a + b; } };
+
+__device__ __forceinline__ float wave_max(float x) { return wave_allreduce(x, OpMax()); }
+__device__ __forceinline__ float wave_sum(float x) { return wave_allreduce(x, OpAdd()); }
+
+}  // namespace octo

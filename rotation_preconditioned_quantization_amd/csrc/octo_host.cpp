@@ -1,0 +1,761 @@
+// Host side of the OCTOPUS library: C ABI, codebook builder, argument checks
+// and kernel dispatch.  The codebook builder runs on the host in fp64; the
+// kernels live in k_*.hip.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "../../include/octo.h"
+#include "octo_internal.hpp"
+
+using namespace octo;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+octo_status fail(octo_status s, const std::string& msg) {
+  g_last_error = msg;
+  return s;
+}
+
+// ---------------------------------------------------------------------------
+// Seeded randomness ([AB]: deterministic given a seed).  SplitMix64 (Steele,
+// Lea & Flood 2014) started at seed ^ tag; uniforms (x >> 11) * 2^-53;
+// Box-Muller pairs g_2p = r cos(2 pi u2), g_2p+1 = r sin(2 pi u2),
+// r = sqrt(-2 ln(1 - u1)).
+// ---------------------------------------------------------------------------
+constexpr uint64_t kGamma = 0x9E3779B97F4A7C15ull;
+constexpr uint64_t kTagSigns = 0x4F43544F5349474Eull;  // "OCTOSIGN"
+constexpr uint64_t kTagMC = 0x4F43544F4D43534Dull;     // "OCTOMCSM"
+constexpr uint64_t kTagQJL = 0x4F43544F514A4C53ull;    // "OCTOQJLS"
+
+inline uint64_t splitmix_out(uint64_t state0, uint64_t i) {
+  uint64_t z = state0 + (i + 1) * kGamma;
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
+
+inline double uniform_at(uint64_t state0, uint64_t i) {
+  return (double)(splitmix_out(state0, i) >> 11) * (1.0 / 9007199254740992.0);
+}
+
+void gaussians(uint64_t seed, uint64_t tag, size_t n, double* out) {
+  const uint64_t s0 = seed ^ tag;
+  const double two_pi = 6.283185307179586;
+  for (size_t p = 0; 2 * p < n; ++p) {
+    const double u1 = uniform_at(s0, 2 * p), u2 = uniform_at(s0, 2 * p + 1);
+    const double r = std::sqrt(-2.0 * std::log(1.0 - u1));
+    const double th = two_pi * u2;
+    out[2 * p] = r * std::cos(th);
+    if (2 * p + 1 < n) out[2 * p + 1] = r * std::sin(th);
+  }
+}
+
+// Octahedral encode of a unit (or zero-guarded) direction ([YL] 八面体折叠);
+// sgn(0) = +1, z = 0 is the upper hemisphere.
+inline void octa_encode(double x, double y, double z, double* xi, double* eta) {
+  const double l1 = std::fabs(x) + std::fabs(y) + std::fabs(z);
+  const double px = x / l1, py = y / l1;
+  if (z < 0) {
+    *xi = (1.0 - std::fabs(py)) * (px >= 0 ? 1.0 : -1.0);
+    *eta = (1.0 - std::fabs(px)) * (py >= 0 ? 1.0 : -1.0);
+  } else {
+    *xi = px;
+    *eta = py;
+  }
+}
+
+inline void octa_decode(double xi, double eta, double* v) {
+  const double r = 1.0 - std::fabs(xi) - std::fabs(eta);
+  double x = xi, y = eta;
+  if (r < 0) {
+    x = (1.0 - std::fabs(eta)) * (xi >= 0 ? 1.0 : -1.0);
+    y = (1.0 - std::fabs(xi)) * (eta >= 0 ? 1.0 : -1.0);
+  }
+  const double n = std::sqrt(x * x + y * y + r * r);
+  v[0] = x / n;
+  v[1] = y / n;
+  v[2] = r / n;
+}
+
+// Lloyd-Max on samples ([YL] 三元组分解; [AB]): start at the sample quantiles
+// (k + 1/2)/L, then c_k <- mean of the samples with m_{k-1} < x <= m_k (an
+// empty cell keeps its centroid) until max |dc| <= 1e-12 or 2000 rounds.
+// `x` must be sorted; cell sums come from prefix sums.
+std::vector<double> lloyd_max_sorted(const std::vector<double>& x, int L) {
+  const size_t N = x.size();
+  std::vector<double> c(L);
+  if (L == 1) {
+    double s = 0;
+    for (double v : x) s += v;
+    c[0] = s / (double)N;
+    return c;
+  }
+  std::vector<double> prefix(N + 1);
+  prefix[0] = 0.0;
+  for (size_t i = 0; i < N; ++i) prefix[i + 1] = prefix[i] + x[i];
+  for (int k = 0; k < L; ++k) c[k] = x[(size_t)std::floor((k + 0.5) * (double)N / (double)L)];
+  std::vector<size_t> edges(L - 1);
+  for (int it = 0; it < 2000; ++it) {
+    for (int k = 0; k + 1 < L; ++k) {
+      const double m = 0.5 * (c[k] + c[k + 1]);
+      edges[k] = (size_t)(std::upper_bound(x.begin(), x.end(), m) - x.begin());
+    }
+    double dmax = 0.0;
+    for (int k = 0; k < L; ++k) {
+      const size_t lo = k == 0 ? 0 : edges[k - 1];
+      const size_t hi = k == L - 1 ? N : edges[k];
+      double nc = c[k];
+      if (hi > lo) nc = (prefix[hi] - prefix[lo]) / (double)(hi - lo);
+      dmax = std::max(dmax, std::fabs(nc - c[k]));
+      c[k] = nc;
+    }
+    if (dmax <= 1e-12) break;
+  }
+  return c;
+}
+
+std::vector<double> antisymmetrize(const std::vector<double>& c) {
+  const size_t L = c.size();
+  std::vector<double> o(L);
+  for (size_t k = 0; k < L; ++k) o[k] = 0.5 * (c[k] - c[L - 1 - k]);
+  return o;
+}
+
+// Bucketed nearest-centroid table (see QuantTable).  Returns false if no
+// bucket count up to kMaxLut keeps <= 2 midpoints per widened bucket.
+struct HostQuant {
+  std::vector<float> mid;     // nmid + 2 sentinels
+  std::vector<uint8_t> lut;
+  float lo = 0, inv_w = 0;
+  int nb = 0, nmid = 0;
+};
+
+bool build_quant(const std::vector<double>& mids, double lo, double hi, HostQuant* q) {
+  const int nmid = (int)mids.size();
+  std::vector<float> mf(nmid);
+  for (int k = 0; k < nmid; ++k) mf[k] = (float)mids[k];
+  for (int nb = 256; nb <= kMaxLut; nb *= 2) {
+    const double w = (hi - lo) / nb;
+    const double margin = 0.01 * w;
+    std::vector<uint8_t> lut(nb);
+    bool ok = true;
+    for (int b = 0; b < nb && ok; ++b) {
+      const double L = b == 0 ? -INFINITY : lo + b * w - margin;
+      const double U = b == nb - 1 ? INFINITY : lo + (b + 1) * w + margin;
+      int below = 0, inside = 0;
+      for (int k = 0; k < nmid; ++k) {
+        if ((double)mf[k] < L) ++below;
+        else if ((double)mf[k] < U) ++inside;
+      }
+      if (inside > 2 || below > 255) ok = false;
+      lut[b] = (uint8_t)below;
+    }
+    if (!ok) continue;
+    q->mid = mf;
+    q->mid.push_back(INFINITY);
+    q->mid.push_back(INFINITY);
+    q->lut = lut;
+    q->lo = (float)lo;
+    q->inv_w = (float)(nb / (hi - lo));
+    q->nb = nb;
+    q->nmid = nmid;
+    return true;
+  }
+  return false;
+}
+
+std::vector<double> midpoints(const std::vector<double>& c) {
+  std::vector<double> m(c.size() - 1);
+  for (size_t k = 0; k + 1 < c.size(); ++k) m[k] = 0.5 * (c[k] + c[k + 1]);
+  return m;
+}
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+}  // namespace
+
+struct octo_codebook {
+  int d = 0, b = 0, bx = 0, be = 0, br = 0, T = 0, bt = 0, W = 0;
+  uint64_t seed = 0, cb_seed = 0;
+  int qjl = 0, mc = 0, device = -1;
+  bool kernels = false;  // a compiled kernel exists for (d, allocation)
+  std::vector<double> c_xi, c_eta, c_rho;
+  std::vector<int8_t> signs;
+  std::vector<float> S;
+  uint32_t sign_bits[4] = {0, 0, 0, 0};
+  void* dev = nullptr;
+  DevTables tables{};
+};
+
+namespace {
+
+octo_status build_device_tables(octo_codebook* cb) {
+  HostQuant qx, qe, qr2;
+  if (!build_quant(midpoints(cb->c_xi), -1.0, 1.0, &qx) ||
+      !build_quant(midpoints(cb->c_eta), -1.0, 1.0, &qe))
+    return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the xi/eta midpoints");
+  std::vector<double> m2 = midpoints(cb->c_rho);
+  for (double& m : m2) m = m * m;
+  const double hi = m2.empty() ? 1.0 : std::min(1.0, 1.25 * m2.back() + 1e-3);
+  if (!build_quant(m2, 0.0, hi, &qr2))
+    return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
+
+  const int ndir = 1 << (cb->bx + cb->be);
+  std::vector<float> dir(4 * (size_t)ndir);
+  for (int ie = 0; ie < (1 << cb->be); ++ie)
+    for (int ix = 0; ix < (1 << cb->bx); ++ix) {
+      double v[3];
+      octa_decode(cb->c_xi[ix], cb->c_eta[ie], v);
+      const size_t o = 4 * (size_t)(ix | (ie << cb->bx));
+      dir[o] = (float)v[0];
+      dir[o + 1] = (float)v[1];
+      dir[o + 2] = (float)v[2];
+      dir[o + 3] = 0.f;
+    }
+  std::vector<float> rho(cb->c_rho.begin(), cb->c_rho.end());
+
+  // One device allocation, 256-byte aligned regions.
+  struct Region { const void* src; size_t bytes; size_t off; };
+  std::vector<Region> reg = {
+      {dir.data(), dir.size() * 4, 0},           {rho.data(), rho.size() * 4, 0},
+      {qx.mid.data(), qx.mid.size() * 4, 0},     {qe.mid.data(), qe.mid.size() * 4, 0},
+      {qr2.mid.data(), qr2.mid.size() * 4, 0},   {qx.lut.data(), qx.lut.size(), 0},
+      {qe.lut.data(), qe.lut.size(), 0},         {qr2.lut.data(), qr2.lut.size(), 0},
+      {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0}};
+  size_t total = 0;
+  for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
+  int prev = 0;
+  if (hipGetDevice(&prev) != hipSuccess) return fail(OCTO_ERR_HIP, "hipGetDevice failed");
+  if (hipSetDevice(cb->device) != hipSuccess)
+    return fail(OCTO_ERR_HIP, "hipSetDevice(" + std::to_string(cb->device) + ") failed");
+  void* dev = nullptr;
+  hipError_t e = hipMalloc(&dev, total);
+  if (e != hipSuccess) {
+    hipSetDevice(prev);
+    return fail(OCTO_ERR_NOMEM, std::string("hipMalloc of codebook tables: ") + hipGetErrorString(e));
+  }
+  for (auto& r : reg) {
+    if (r.bytes == 0) continue;
+    e = hipMemcpy((char*)dev + r.off, r.src, r.bytes, hipMemcpyHostToDevice);
+    if (e != hipSuccess) break;
+  }
+  hipSetDevice(prev);
+  if (e != hipSuccess) {
+    hipFree(dev);
+    return fail(OCTO_ERR_HIP, std::string("upload of codebook tables: ") + hipGetErrorString(e));
+  }
+  cb->dev = dev;
+  char* base = (char*)dev;
+  DevTables& t = cb->tables;
+  t.dirtab = (const float4*)(base + reg[0].off);
+  t.rho_tab = (const float*)(base + reg[1].off);
+  auto qt = [&](const HostQuant& h, int mid_r, int lut_r) {
+    QuantTable q;
+    q.mid = (const float*)(base + reg[mid_r].off);
+    q.lut = (const uint8_t*)(base + reg[lut_r].off);
+    q.lo = h.lo;
+    q.inv_w = h.inv_w;
+    q.nb = h.nb;
+    q.nmid = h.nmid;
+    return q;
+  };
+  t.qx = qt(qx, 2, 5);
+  t.qe = qt(qe, 3, 6);
+  t.qr2 = qt(qr2, 4, 7);
+  t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[8].off);
+  for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
+  return OCTO_OK;
+}
+
+int dtype_size(octo_dtype t) { return t == OCTO_F32 ? 4 : 2; }
+bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+octo_status check_cb(const octo_codebook* cb) {
+  if (!cb) return fail(OCTO_ERR_INVALID_ARG, "codebook is NULL");
+  if (cb->device < 0 || !cb->dev)
+    return fail(OCTO_ERR_INVALID_ARG, "host-only codebook: build it with device >= 0");
+  if (!cb->kernels) return fail(OCTO_ERR_UNSUPPORTED, "no kernel for this d / allocation");
+  int cur = -1;
+  if (hipGetDevice(&cur) != hipSuccess) return fail(OCTO_ERR_HIP, "hipGetDevice failed");
+  if (cur != cb->device)
+    return fail(OCTO_ERR_INVALID_ARG, "current HIP device " + std::to_string(cur) +
+                                          " differs from the codebook's device " +
+                                          std::to_string(cb->device));
+  return OCTO_OK;
+}
+
+octo_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return OCTO_OK;
+  return fail(OCTO_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+int heads_per_pass(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+
+struct Split { int n_split, tiles_per_split; };
+
+Split attn_split(int64_t n_keys, int64_t n_seq, int passes) {
+  const int64_t ntile = std::max<int64_t>(1, (n_keys + kTile - 1) / kTile);
+  const int64_t rows = std::max<int64_t>(1, n_seq * passes);
+  int64_t ns = (1024 + rows - 1) / rows;
+  ns = std::min<int64_t>(ns, (ntile + 7) / 8);
+  ns = std::max<int64_t>(ns, 1);
+  const int64_t tps = (ntile + ns - 1) / ns;
+  ns = (ntile + tps - 1) / tps;
+  return {(int)ns, (int)tps};
+}
+
+struct WsLayout { size_t qrot, qp, part, total; };
+
+WsLayout ws_layout(const octo_codebook* cb, int mode, int B, int Hq, int Hkv, int n_q,
+                   int64_t n_keys) {
+  WsLayout w{};
+  const size_t rows = (size_t)B * Hq * n_q;
+  w.qrot = 0;
+  size_t off = align256(rows * 3 * cb->T * sizeof(float));
+  w.qp = off;
+  if (cb->qjl) off += align256(rows * cb->d * sizeof(float));
+  w.part = off;
+  if (mode == 1) {
+    const int G = Hkv > 0 ? Hq / Hkv : 1;
+    const int hp = heads_per_pass(std::max(G, 1));
+    const Split sp = attn_split(n_keys, (int64_t)B * Hkv, std::max(G, 1) / hp);
+    off += align256(rows * (size_t)sp.n_split * (cb->d + 2) * sizeof(float));
+  }
+  w.total = off;
+  return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* octo_status_str(octo_status s) {
+  switch (s) {
+    case OCTO_OK: return "OCTO_OK";
+    case OCTO_ERR_INVALID_ARG: return "OCTO_ERR_INVALID_ARG";
+    case OCTO_ERR_UNSUPPORTED: return "OCTO_ERR_UNSUPPORTED";
+    case OCTO_ERR_HIP: return "OCTO_ERR_HIP";
+    case OCTO_ERR_NOMEM: return "OCTO_ERR_NOMEM";
+    case OCTO_ERR_WORKSPACE: return "OCTO_ERR_WORKSPACE";
+  }
+  return "OCTO_ERR_UNKNOWN";
+}
+
+const char* octo_last_error(void) { return g_last_error.c_str(); }
+
+octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
+  if (!p || !out) return fail(OCTO_ERR_INVALID_ARG, "params/out is NULL");
+  *out = nullptr;
+  const int d = p->d, b = p->b;
+  if (d < 4 || d > 1024 || (d & (d - 1)))
+    return fail(OCTO_ERR_INVALID_ARG, "d must be a power of two in [4, 1024]");
+  const bool dflt = p->b_xi < 0 || p->b_eta < 0 || p->b_rho < 0;
+  const int bx = dflt ? b + 1 : p->b_xi, be = dflt ? b + 1 : p->b_eta, br = dflt ? b - 1 : p->b_rho;
+  if (b < 1 || b > 8 || bx < 1 || bx > 8 || be < 1 || be > 8 || br < 0 || br > 8)
+    return fail(OCTO_ERR_INVALID_ARG, "bit allocation out of range");
+  if (p->mc_vectors < 0) return fail(OCTO_ERR_INVALID_ARG, "mc_vectors < 0");
+  const bool kernels = (d == 64 || d == 128) && (b >= 2 && b <= 4) && bx == b + 1 && be == b + 1 &&
+                       br == b - 1;
+  if (p->device >= 0 && !kernels)
+    return fail(OCTO_ERR_UNSUPPORTED,
+                "kernels exist for d in {64,128}, b in {2,3,4} and the (b+1,b+1,b-1) allocation; "
+                "build with device = -1 for host-only tables");
+  octo_codebook* cb = new (std::nothrow) octo_codebook();
+  if (!cb) return fail(OCTO_ERR_NOMEM, "host allocation failed");
+  cb->d = d;
+  cb->b = b;
+  cb->bx = bx;
+  cb->be = be;
+  cb->br = br;
+  cb->T = (d + 2) / 3;
+  cb->bt = bx + be + br;
+  cb->W = (cb->T * cb->bt + 31) / 32;
+  cb->seed = p->seed;
+  cb->cb_seed = p->cb_seed;
+  cb->qjl = p->qjl ? 1 : 0;
+  cb->mc = p->mc_vectors ? p->mc_vectors : 65536;
+  cb->device = p->device;
+  cb->kernels = kernels;
+
+  try {
+    // WHT signs: s_j = +1 if the low bit of draw j is 0 ([YL] 旋转魔法).
+    cb->signs.resize(d);
+    for (int j = 0; j < d; ++j) {
+      const bool neg = splitmix_out(p->seed ^ kTagSigns, (uint64_t)j) & 1ull;
+      cb->signs[j] = neg ? -1 : 1;
+      if (neg && j < 128) cb->sign_bits[j >> 5] |= 1u << (j & 31);
+    }
+    // Monte-Carlo samples of the rotated triplet marginals: normalised
+    // Gaussian vectors are uniform on the sphere, so their rotation is too.
+    const int T = cb->T, M = cb->mc;
+    std::vector<double> g((size_t)d);
+    std::vector<double> rho;
+    std::vector<double> dirs;
+    rho.reserve((size_t)M * T);
+    dirs.reserve((size_t)M * T * 4);
+    std::vector<double> xs((size_t)M * T), es((size_t)M * T);
+    std::vector<double> all((size_t)M * d);
+    gaussians(p->cb_seed, kTagMC, (size_t)M * d, all.data());
+    size_t n = 0;
+    for (int v = 0; v < M; ++v) {
+      const double* gv = &all[(size_t)v * d];
+      double ss = 0.0;
+      for (int j = 0; j < d; ++j) ss += gv[j] * gv[j];
+      const double nrm = std::sqrt(ss);
+      for (int i = 0; i < T; ++i) {
+        double t[3];
+        for (int c = 0; c < 3; ++c) t[c] = (3 * i + c < d) ? gv[3 * i + c] / nrm : 0.0;
+        const double r = std::sqrt(t[0] * t[0] + t[1] * t[1] + t[2] * t[2]);
+        double nx = 0, ny = 0, nz = 1;
+        if (r > 0) { nx = t[0] / r; ny = t[1] / r; nz = t[2] / r; }
+        double xi, eta;
+        octa_encode(nx, ny, nz, &xi, &eta);
+        rho.push_back(r);
+        xs[n] = xi;
+        es[n] = eta;
+        ++n;
+      }
+    }
+    // xi and eta pooled and symmetrised.
+    dirs.insert(dirs.end(), xs.begin(), xs.end());
+    dirs.insert(dirs.end(), es.begin(), es.end());
+    const size_t half = dirs.size();
+    for (size_t i = 0; i < half; ++i) dirs.push_back(-dirs[i]);
+    std::vector<double>().swap(all);
+    std::sort(rho.begin(), rho.end());
+    std::sort(dirs.begin(), dirs.end());
+    cb->c_xi = antisymmetrize(lloyd_max_sorted(dirs, 1 << bx));
+    cb->c_eta = (be == bx) ? cb->c_xi : antisymmetrize(lloyd_max_sorted(dirs, 1 << be));
+    cb->c_rho = lloyd_max_sorted(rho, 1 << br);
+    if (cb->qjl) {
+      std::vector<double> s((size_t)d * d);
+      gaussians(p->seed, kTagQJL, s.size(), s.data());
+      cb->S.assign(s.begin(), s.end());
+    }
+  } catch (const std::bad_alloc&) {
+    delete cb;
+    return fail(OCTO_ERR_NOMEM, "host allocation failed during codebook build");
+  }
+  if (cb->device >= 0) {
+    const octo_status st = build_device_tables(cb);
+    if (st != OCTO_OK) {
+      delete cb;
+      return st;
+    }
+  }
+  *out = cb;
+  return OCTO_OK;
+}
+
+octo_status octo_codebook_free(octo_codebook* cb) {
+  if (!cb) return OCTO_OK;
+  if (cb->dev) {
+    int prev = 0;
+    hipGetDevice(&prev);
+    hipSetDevice(cb->device);
+    hipFree(cb->dev);
+    hipSetDevice(prev);
+  }
+  delete cb;
+  return OCTO_OK;
+}
+
+octo_status octo_codebook_layout(const octo_codebook* cb, octo_layout* o) {
+  if (!cb || !o) return fail(OCTO_ERR_INVALID_ARG, "NULL argument");
+  o->d = cb->d;
+  o->n_triplets = cb->T;
+  o->pad_dim = 3 * cb->T;
+  o->b_xi = cb->bx;
+  o->b_eta = cb->be;
+  o->b_rho = cb->br;
+  o->bits_per_triplet = cb->bt;
+  o->bits_per_key = cb->T * cb->bt;
+  o->words_per_key = cb->W;
+  o->tile_keys = kTile;
+  o->qjl = cb->qjl;
+  o->qjl_words_per_key = cb->qjl ? cb->d / 32 : 0;
+  o->packed_bytes_per_key_alloc = (size_t)cb->W * 4;
+  return OCTO_OK;
+}
+
+octo_status octo_codebook_export(const octo_codebook* cb, double* c_xi, double* c_eta,
+                                 double* c_rho, int8_t* signs, float* qjl_S) {
+  if (!cb) return fail(OCTO_ERR_INVALID_ARG, "codebook is NULL");
+  if (c_xi) std::memcpy(c_xi, cb->c_xi.data(), cb->c_xi.size() * sizeof(double));
+  if (c_eta) std::memcpy(c_eta, cb->c_eta.data(), cb->c_eta.size() * sizeof(double));
+  if (c_rho) std::memcpy(c_rho, cb->c_rho.data(), cb->c_rho.size() * sizeof(double));
+  if (signs) std::memcpy(signs, cb->signs.data(), cb->signs.size());
+  if (qjl_S) {
+    if (cb->S.empty()) return fail(OCTO_ERR_INVALID_ARG, "codebook has no QJL matrix");
+    std::memcpy(qjl_S, cb->S.data(), cb->S.size() * sizeof(float));
+  }
+  return OCTO_OK;
+}
+
+size_t octo_packed_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap) {
+  if (!cb || n_seq < 0 || cap < 0) return 0;
+  return (size_t)n_seq * (size_t)((cap + kTile - 1) / kTile) * kTile * cb->W * 4;
+}
+
+size_t octo_qjl_bits_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap) {
+  if (!cb || n_seq < 0 || cap < 0 || !cb->qjl) return 0;
+  return (size_t)n_seq * (size_t)((cap + kTile - 1) / kTile) * kTile * (cb->d / 32) * 4;
+}
+
+octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kdt, int64_t n_seq,
+                        int64_t n_new, int64_t seq_stride, int64_t key_stride, int64_t pos0,
+                        int64_t cap, void* packed, float* gamma, void* qjl_bits,
+                        uint16_t* qjl_norm, void* stream) {
+  octo_status st = check_cb(cb);
+  if (st != OCTO_OK) return st;
+  if (kdt != OCTO_F32 && kdt != OCTO_BF16 && kdt != OCTO_F16)
+    return fail(OCTO_ERR_INVALID_ARG, "unknown key dtype");
+  if (n_seq < 0 || n_new < 0 || pos0 < 0 || cap <= 0 || cap % kTile)
+    return fail(OCTO_ERR_INVALID_ARG, "need n_seq, n_new, pos0 >= 0 and cap a positive multiple of 64");
+  if (pos0 + n_new > cap) return fail(OCTO_ERR_INVALID_ARG, "pos0 + n_new exceeds cap");
+  if (n_seq > 65535) return fail(OCTO_ERR_INVALID_ARG, "n_seq > 65535");
+  if (n_seq == 0 || n_new == 0) return OCTO_OK;
+  const int es = dtype_size(kdt);
+  if (!keys || !packed || !gamma) return fail(OCTO_ERR_INVALID_ARG, "NULL keys/packed/gamma");
+  if (key_stride < cb->d || (n_seq > 1 && seq_stride < 0))
+    return fail(OCTO_ERR_INVALID_ARG, "key_stride < d or seq_stride < 0");
+  if (!aligned(keys, 16) || (key_stride * es) % 16 || (seq_stride * es) % 16)
+    return fail(OCTO_ERR_INVALID_ARG, "key rows must be 16-byte aligned");
+  if (!aligned(packed, 4) || !aligned(gamma, 4))
+    return fail(OCTO_ERR_INVALID_ARG, "packed/gamma must be 4-byte aligned");
+  if ((qjl_bits == nullptr) != (qjl_norm == nullptr))
+    return fail(OCTO_ERR_INVALID_ARG, "pass both QJL buffers or neither");
+  if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
+  if (qjl_bits && (!aligned(qjl_bits, 4) || !aligned(qjl_norm, 2)))
+    return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
+  EncodeArgs a{};
+  a.t = cb->tables;
+  a.keys = keys;
+  a.seq_stride = seq_stride;
+  a.key_stride = key_stride;
+  a.n_new = n_new;
+  a.pos0 = pos0;
+  a.cap = cap;
+  a.packed = (uint32_t*)packed;
+  a.gamma = gamma;
+  a.qjl_bits = (uint32_t*)qjl_bits;
+  a.qjl_norm = qjl_norm;
+  return hip_status(launch_encode(cb->d, cb->b, (int)kdt, qjl_bits != nullptr, a, n_seq,
+                                  (hipStream_t)stream),
+                    "encode launch");
+}
+
+size_t octo_decode_workspace_bytes(const octo_codebook* cb, int mode, int B, int Hq, int Hkv,
+                                   int n_q, int64_t n_keys) {
+  if (!cb || B < 0 || Hq < 0 || Hkv <= 0 || n_q < 0 || n_keys < 0) return 0;
+  return ws_layout(cb, mode, B, Hq, Hkv, n_q, n_keys).total;
+}
+
+static octo_status check_decode_common(const octo_codebook* cb, const void* q, octo_dtype qdt,
+                                       int B, int Hq, int Hkv, const void* packed,
+                                       const float* gamma, const void* qjl_bits,
+                                       const uint16_t* qjl_norm, int64_t n_keys, int64_t cap,
+                                       void* workspace) {
+  octo_status st = check_cb(cb);
+  if (st != OCTO_OK) return st;
+  if (qdt != OCTO_F32 && qdt != OCTO_BF16 && qdt != OCTO_F16)
+    return fail(OCTO_ERR_INVALID_ARG, "unknown query dtype");
+  if (B < 0 || Hq < 0 || Hkv <= 0 || (Hq % Hkv))
+    return fail(OCTO_ERR_INVALID_ARG, "need B >= 0, Hkv > 0 and Hq a multiple of Hkv");
+  if ((int64_t)B * Hkv > 65535) return fail(OCTO_ERR_INVALID_ARG, "B * Hkv > 65535");
+  if (n_keys < 0 || cap <= 0 || cap % kTile || n_keys > cap)
+    return fail(OCTO_ERR_INVALID_ARG, "need 0 <= n_keys <= cap and cap a positive multiple of 64");
+  if (!q || !packed || !gamma) return fail(OCTO_ERR_INVALID_ARG, "NULL q/packed/gamma");
+  if (!aligned(q, 4) || !aligned(packed, 4) || !aligned(gamma, 4))
+    return fail(OCTO_ERR_INVALID_ARG, "q/packed/gamma misaligned");
+  if ((qjl_bits == nullptr) != (qjl_norm == nullptr))
+    return fail(OCTO_ERR_INVALID_ARG, "pass both QJL buffers or neither");
+  if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
+  if (!workspace || !aligned(workspace, 256))
+    return fail(OCTO_ERR_WORKSPACE, "workspace missing or not 256-byte aligned");
+  return OCTO_OK;
+}
+
+octo_status octo_decode_logits(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                               int Hq, int Hkv, const void* packed, const float* gamma,
+                               const void* qjl_bits, const uint16_t* qjl_norm, int64_t n_keys,
+                               int64_t cap, float* logits, void* workspace,
+                               size_t workspace_bytes, void* stream) {
+  return octo_decode_logits_stages(cb, q, qdt, B, Hq, Hkv, packed, gamma, qjl_bits, qjl_norm,
+                                   n_keys, cap, logits, workspace, workspace_bytes, stream,
+                                   OCTO_STAGE_ALL);
+}
+
+octo_status octo_decode_logits_stages(const octo_codebook* cb, const void* q, octo_dtype qdt,
+                                      int B, int Hq, int Hkv, const void* packed,
+                                      const float* gamma, const void* qjl_bits,
+                                      const uint16_t* qjl_norm, int64_t n_keys, int64_t cap,
+                                      float* logits, void* workspace, size_t workspace_bytes,
+                                      void* stream, int stages) {
+  octo_status st = check_decode_common(cb, q, qdt, B, Hq, Hkv, packed, gamma, qjl_bits, qjl_norm,
+                                       n_keys, cap, workspace);
+  if (st != OCTO_OK) return st;
+  if (!logits || !aligned(logits, 4)) return fail(OCTO_ERR_INVALID_ARG, "logits NULL/misaligned");
+  const WsLayout wl = ws_layout(cb, 0, B, Hq, Hkv, 1, n_keys);
+  if (workspace_bytes < wl.total) return fail(OCTO_ERR_WORKSPACE, "workspace too small");
+  if (B == 0 || Hq == 0 || n_keys == 0) return OCTO_OK;
+  hipStream_t s = (hipStream_t)stream;
+  const bool qjl = qjl_bits != nullptr;
+  RotateArgs r{};
+  r.t = cb->tables;
+  r.q = q;
+  r.qdt = (int)qdt;
+  r.B = B;
+  r.Hq = Hq;
+  r.Hkv = Hkv;
+  r.n_q = 1;
+  r.mult = 1.0f;
+  r.qrot = (float*)((char*)workspace + wl.qrot);
+  r.qp = qjl ? (float*)((char*)workspace + wl.qp) : nullptr;
+  if (stages & OCTO_STAGE_ROTATE) {
+    st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
+    if (st != OCTO_OK) return st;
+  }
+  if (!(stages & OCTO_STAGE_MAIN)) return OCTO_OK;
+  const int G = Hq / Hkv, hp = heads_per_pass(G);
+  DecodeArgs a{};
+  a.t = cb->tables;
+  a.qrot = r.qrot;
+  a.qp = r.qp;
+  a.packed = (const uint32_t*)packed;
+  a.gamma = gamma;
+  a.qjl_bits = (const uint32_t*)qjl_bits;
+  a.qjl_norm = qjl_norm;
+  a.n_keys = n_keys;
+  a.cap = cap;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.logits = logits;
+  const int64_t n_seq = (int64_t)B * Hkv;
+  const int64_t ntile = (n_keys + kTile - 1) / kTile;
+  const int64_t rows = n_seq * (G / hp);
+  int64_t nbx = (2048 + rows - 1) / rows;
+  nbx = std::max<int64_t>(1, std::min<int64_t>(nbx, (ntile + 3) / 4));
+  return hip_status(launch_logits(cb->d, cb->b, hp, qjl, a, n_seq, (int)nbx, s), "logits launch");
+}
+
+octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                             int Hq, int Hkv, int n_q, const void* packed, const float* gamma,
+                             const void* qjl_bits, const uint16_t* qjl_norm, const void* v,
+                             octo_dtype vdt, int64_t n_keys, int64_t cap, float scale, float* out,
+                             void* workspace, size_t workspace_bytes, void* stream) {
+  return octo_decode_attn_stages(cb, q, qdt, B, Hq, Hkv, n_q, packed, gamma, qjl_bits, qjl_norm, v,
+                                 vdt, n_keys, cap, scale, out, workspace, workspace_bytes, stream,
+                                 OCTO_STAGE_ALL);
+}
+
+octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, int n_q, const void* packed,
+                                    const float* gamma, const void* qjl_bits,
+                                    const uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int stages) {
+  octo_status st = check_decode_common(cb, q, qdt, B, Hq, Hkv, packed, gamma, qjl_bits, qjl_norm,
+                                       n_keys, cap, workspace);
+  if (st != OCTO_OK) return st;
+  if (n_q < 1) return fail(OCTO_ERR_INVALID_ARG, "n_q < 1");
+  if (vdt != OCTO_BF16) return fail(OCTO_ERR_UNSUPPORTED, "V must be bf16");
+  if (!v || !aligned(v, 16)) return fail(OCTO_ERR_INVALID_ARG, "v NULL or not 16-byte aligned");
+  if (!out || !aligned(out, 4)) return fail(OCTO_ERR_INVALID_ARG, "out NULL/misaligned");
+  const WsLayout wl = ws_layout(cb, 1, B, Hq, Hkv, n_q, n_keys);
+  if (workspace_bytes < wl.total) return fail(OCTO_ERR_WORKSPACE, "workspace too small");
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t out_elems = (int64_t)B * Hq * n_q * cb->d;
+  if (out_elems == 0) return OCTO_OK;
+  if (n_keys == 0) {
+    if (!(stages & OCTO_STAGE_COMBINE)) return OCTO_OK;
+    return hip_status(launch_fill_zero(out, out_elems, s), "fill launch");
+  }
+  const float sc = scale > 0.f ? scale : 1.0f / std::sqrt((float)cb->d);
+  const bool qjl = qjl_bits != nullptr;
+  RotateArgs r{};
+  r.t = cb->tables;
+  r.q = q;
+  r.qdt = (int)qdt;
+  r.B = B;
+  r.Hq = Hq;
+  r.Hkv = Hkv;
+  r.n_q = n_q;
+  r.mult = sc * 1.4426950408889634f;  // logits in log2 units for exp2
+  r.qrot = (float*)((char*)workspace + wl.qrot);
+  r.qp = qjl ? (float*)((char*)workspace + wl.qp) : nullptr;
+  if (stages & OCTO_STAGE_ROTATE) {
+    st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
+    if (st != OCTO_OK) return st;
+  }
+  const int G = Hq / Hkv;
+  if (n_q > 1) {
+    if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
+    return fail(OCTO_ERR_UNSUPPORTED, "multi-query path not built yet");
+  }
+  const int hp = heads_per_pass(G);
+  const int64_t n_seq = (int64_t)B * Hkv;
+  const Split sp = attn_split(n_keys, n_seq, G / hp);
+  DecodeArgs a{};
+  a.t = cb->tables;
+  a.qrot = r.qrot;
+  a.qp = r.qp;
+  a.packed = (const uint32_t*)packed;
+  a.gamma = gamma;
+  a.qjl_bits = (const uint32_t*)qjl_bits;
+  a.qjl_norm = qjl_norm;
+  a.v = v;
+  a.n_keys = n_keys;
+  a.cap = cap;
+  a.Hq = Hq;
+  a.Hkv = Hkv;
+  a.G = G;
+  a.tiles_per_split = sp.tiles_per_split;
+  a.n_split = sp.n_split;
+  a.part = (float*)((char*)workspace + wl.part);
+  if (stages & OCTO_STAGE_MAIN) {
+    st = hip_status(launch_attn(cb->d, cb->b, hp, qjl, a, n_seq, s), "attention launch");
+    if (st != OCTO_OK) return st;
+  }
+  if (!(stages & OCTO_STAGE_COMBINE)) return OCTO_OK;
+  CombineArgs c{};
+  c.part = a.part;
+  c.out = out;
+  c.rows = B * Hq;
+  c.n_split = sp.n_split;
+  c.d = cb->d;
+  return hip_status(launch_combine(c, s), "combine launch");
+}
+
+octo_status octo_debug_reconstruct(const octo_codebook* cb, const void* packed, const float* gamma,
+                                   int64_t n_seq, int64_t n_keys, int64_t cap, float* keys_out,
+                                   void* stream) {
+  octo_status st = check_cb(cb);
+  if (st != OCTO_OK) return st;
+  if (n_seq < 0 || n_keys < 0 || cap <= 0 || cap % kTile || n_keys > cap || n_seq > 65535)
+    return fail(OCTO_ERR_INVALID_ARG, "bad n_seq/n_keys/cap");
+  if (!packed || !gamma || !keys_out) return fail(OCTO_ERR_INVALID_ARG, "NULL pointer");
+  ReconArgs a{};
+  a.t = cb->tables;
+  a.packed = (const uint32_t*)packed;
+  a.gamma = gamma;
+  a.n_keys = n_keys;
+  a.cap = cap;
+  a.out = keys_out;
+  return hip_status(launch_reconstruct(cb->d, cb->b, a, n_seq, (hipStream_t)stream),
+                    "reconstruct launch");
+}
+
+}  // extern "C"

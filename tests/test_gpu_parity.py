@@ -1,0 +1,374 @@
+"""GPU parity: the HIP path (through the C ABI) against the fp64 oracle.
+
+Every test draws seeded synthetic inputs (workloads), runs the library on
+cuda:0 and compares with the oracle under the rules in tests/parity.py.
+Sizes span several 64-key tiles with ragged tails; the full-size configs
+compare sampled sequences.  Marked gpu: needs an MI355X and the built library.
+"""
+import functools
+import math
+import sys
+
+import numpy as np
+import pytest
+
+torch = pytest.importorskip("torch")
+
+import oracle as O  # noqa: E402
+import workloads as WL  # noqa: E402
+from parity import (assert_codes_match, compare_codes, logit_err, rel_err_rows,  # noqa: E402
+                    unpack_device_codes, unpack_device_signs)
+
+pytestmark = pytest.mark.gpu
+
+
+def _octo():
+    import rotation_preconditioned_quantization_amd as octo
+    return octo
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _need_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    _octo().lib()  # loud failure if the HIP library is missing
+
+
+@functools.lru_cache(maxsize=None)
+def ocb(d, b, seed=0, cb_seed=0):
+    return O.build_codebook(d, b, seed=seed, cb_seed=cb_seed)
+
+
+@functools.lru_cache(maxsize=None)
+def gcb(d, b, seed=0, cb_seed=0, qjl=False):
+    return _octo().Codebook(d, b, seed=seed, cb_seed=cb_seed, qjl=qjl, device=0)
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def f64(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def encode_and_check(d, b, keys, cap, pos0=0, qjl=False, seed=0, label=""):
+    """Encode keys [n_seq, n, d] at pos0 and check codes and gamma."""
+    octo = _octo()
+    g = gcb(d, b, seed, 0, qjl)
+    n_seq, n, _ = keys.shape
+    cache = octo.Cache(g, n_seq, cap, qjl=qjl)
+    octo.octo_encode(g, keys, cache, pos0=pos0)
+    torch.cuda.synchronize()
+    cb = ocb(d, b, seed)
+    kk = f64(keys).reshape(-1, d)
+    enc = O.encode(kk, cb)
+    codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, n_seq, cap, n, start=pos0)
+    n_mis = assert_codes_match(codes, enc, cb, label)
+    gamma = cache.gamma.cpu().numpy().reshape(n_seq, cap)[:, pos0:pos0 + n].reshape(-1)
+    ref_g = np.linalg.norm(kk, axis=1)
+    assert np.all(np.abs(gamma - ref_g) <= 1e-6 * np.maximum(ref_g, 1e-30)), label
+    say(f"[{label}] encode ok: {n_seq}x{n} keys, {n_mis} excused index flips")
+    return cache, codes, enc
+
+
+# ----------------------------------------------------------------- encoder --
+def test_encode_toy_full_config1():
+    cfg = WL.CONFIGS[1]
+    keys = WL.make_keys(cfg, "cuda")
+    cache, codes, enc = encode_and_check(cfg.d, cfg.b, keys, cfg.cap, label="config1")
+    # reconstruction of the device stream
+    octo = _octo()
+    rec = f64(octo.octo_debug_reconstruct(gcb(cfg.d, cfg.b), cache, cfg.N)).reshape(-1, cfg.d)
+    gamma = cache.gamma.cpu().numpy()[: cfg.N]
+    ref = O.decode(codes.reshape(-1, O.n_triplets(cfg.d), 3), gamma, ocb(cfg.d, cfg.b))
+    assert np.max(rel_err_rows(rec, ref)) <= 1e-3
+
+
+@pytest.mark.parametrize("d,b", [(128, 2), (128, 3), (128, 4), (64, 2), (64, 3), (64, 4)])
+@pytest.mark.parametrize("kdt", ["f32", "bf16"])
+def test_encode_all_shapes_ragged(d, b, kdt):
+    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    keys = WL.make_keys(cfg, "cuda", seed=d + b, n_seq=3, n=200)
+    encode_and_check(d, b, keys, cap=256, label=f"d{d}b{b}{kdt}")
+
+
+def test_encode_f16_keys():
+    cfg = WL.CONFIGS[2].scaled(kdtype="f16", keys="gauss")
+    keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=2, n=130)
+    encode_and_check(128, 4, keys, cap=192, label="f16")
+
+
+def test_encode_online_append_matches_bulk():
+    """Encoding in pieces (one token at a time at the end) writes the same
+    words as one bulk call ([AB]: online codec)."""
+    octo = _octo()
+    cfg = WL.CONFIGS[2]
+    keys = WL.make_keys(cfg, "cuda", seed=11, n_seq=2, n=139)
+    g = gcb(128, 4)
+    bulk = octo.Cache(g, 2, 192)
+    octo.octo_encode(g, keys, bulk)
+    step = octo.Cache(g, 2, 192)
+    octo.octo_encode(g, keys[:, :100].contiguous(), step, pos0=0)
+    octo.octo_encode(g, keys[:, 100:137].contiguous(), step, pos0=100)
+    octo.octo_encode(g, keys[:, 137:138].contiguous(), step, pos0=137)
+    octo.octo_encode(g, keys[:, 138:139].contiguous(), step, pos0=138)
+    torch.cuda.synchronize()
+    assert torch.equal(bulk.packed, step.packed)
+    assert torch.equal(bulk.gamma, step.gamma)
+    # the unaligned append really wrote at the right place
+    encode_and_check(128, 4, keys[:, 100:137].contiguous(), cap=192, pos0=100, label="append")
+
+
+def test_encode_degenerate_keys():
+    d = 128
+    k = torch.zeros((1, 70, d), dtype=torch.float32)
+    k[0, 1, 5] = 3.0                     # one nonzero coordinate
+    k[0, 2, :] = 1.0                     # constant key
+    k[0, 3, ::2] = -2.0                  # alternating zeros
+    k[0, 4, :] = torch.linspace(-1, 1, d)
+    k[0, 5, 0] = 1e-30                   # tiny
+    k[0, 6] = torch.randn(d) * 1e4       # large
+    k[0, 7:] = torch.randn(63, d)
+    encode_and_check(d, 3, k.cuda(), cap=128, label="degenerate")
+
+
+def test_encode_is_deterministic():
+    octo = _octo()
+    keys = WL.make_keys(WL.CONFIGS[3], "cuda", seed=2, n_seq=4, n=300)
+    g = gcb(128, 2)
+    a = octo.Cache(g, 4, 320)
+    b = octo.Cache(g, 4, 320)
+    octo.octo_encode(g, keys, a)
+    octo.octo_encode(g, keys, b)
+    torch.cuda.synchronize()
+    assert torch.equal(a.packed, b.packed) and torch.equal(a.gamma, b.gamma)
+
+
+# ------------------------------------------------------------------ logits --
+def check_logits(cfg, B, Hkv, G, n, cap, seed=0, qjl=False, label=""):
+    octo = _octo()
+    d, b = cfg.d, cfg.b
+    Hq = Hkv * G
+    keys = WL.make_keys(cfg, "cuda", seed=seed, n_seq=B * Hkv, n=n)
+    cache, codes, enc = encode_and_check(d, b, keys, cap, qjl=qjl, label=label)
+    q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=1), "cuda", seed=seed, B=B)[:, :, 0]
+    g = gcb(d, b, 0, 0, qjl)
+    lg = f64(octo.octo_decode_logits(g, q, cache, n, Hkv))
+    cb = ocb(d, b)
+    gam = cache.gamma.cpu().numpy().reshape(B * Hkv, cap)[:, :n]
+    qq = f64(q)
+    if qjl:
+        S = O.qjl_matrix(d, 0)
+        gsign = unpack_device_signs(cache.qjl_bits.cpu().numpy(), d, B * Hkv, cap, n)
+        gnu = cache.qjl_norm.cpu().numpy().view(np.float16).reshape(B * Hkv, cap)[:, :n]
+        check_qjl_encoder(enc, codes, gsign, gnu, cb, S, label)
+    worst = 0.0
+    for s in range(B * Hkv):
+        bb, kvh = divmod(s, Hkv)
+        uh = O.decode_rotated(codes[s], cb)
+        for gg in range(G):
+            h = kvh * G + gg
+            if qjl:
+                qe = O.QJLEncoded(gsign[s], gnu[s], None, None)
+                ref = O.qjl_logits(qq[bb, h], uh, gam[s], qe, S, cb)
+            else:
+                ref = O.logits_rotated(qq[bb, h], uh, gam[s], cb)
+            worst = max(worst, logit_err(lg[bb, h], ref, np.linalg.norm(qq[bb, h]), gam[s], d))
+    say(f"[{label}] logits worst rel err {worst:.2e}")
+    assert worst <= 1e-3
+
+
+def check_qjl_encoder(enc, codes, gsign, gnu, cb, S, label):
+    d = cb.d
+    n_seq, n = gsign.shape[:2]
+    uh = O.decode_rotated(enc.codes.reshape(n_seq * n, cb.T, 3), cb)
+    qe = O.qjl_encode(enc.rotated, uh, S)
+    _, _, _, _, key_mis = compare_codes(codes, enc, cb)
+    rn = np.linalg.norm(qe.resid, axis=1, keepdims=True)
+    margin = np.abs(qe.proj) / (np.linalg.norm(S, axis=1)[None, :] * np.maximum(rn, 1e-30))
+    diff = gsign.reshape(-1, d) != qe.signs
+    unexc = diff & (margin > 1e-6) & ~key_mis[:, None]
+    assert not unexc.any(), f"{label}: {int(unexc.sum())} unexcused QJL sign flips"
+    assert diff.sum() <= 1e-4 * diff.size
+    nu_g = gnu.reshape(-1).astype(np.float64)
+    nu_o = qe.nu.astype(np.float64)
+    ok = (np.abs(nu_g - nu_o) <= np.spacing(qe.nu).astype(np.float64) * 1.01) | key_mis
+    assert ok.all(), f"{label}: residual norms differ by more than one fp16 ulp"
+
+
+def test_logits_toy_full_config1():
+    cfg = WL.CONFIGS[1]
+    check_logits(cfg, 1, 1, 1, cfg.N, cfg.cap, label="config1")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
+def test_logits_gqa_ragged(G):
+    cfg = WL.CONFIGS[2]
+    check_logits(cfg, 2, 2, G, 333, 384, seed=G, label=f"gqa{G}")
+
+
+@pytest.mark.parametrize("d,b", [(64, 3), (128, 2)])
+def test_logits_other_shapes(d, b):
+    cfg = WL.CONFIGS[3].scaled(d=d, b=b)
+    check_logits(cfg, 1, 2, 4, 700, 768, seed=5, label=f"d{d}b{b}")
+
+
+def test_logits_qjl_small_config5_recipe():
+    cfg = WL.CONFIGS[5]
+    check_logits(cfg, 2, 2, 4, 450, 512, seed=1, qjl=True, label="qjl")
+
+
+def test_logits_qjl_d64():
+    cfg = WL.CONFIGS[5].scaled(d=64)
+    check_logits(cfg, 1, 1, 2, 200, 256, seed=2, qjl=True, label="qjl-d64")
+
+
+# --------------------------------------------------------------- attention --
+def check_attention(cfg, B, Hkv, G, n, cap, seed=0, qjl=False, label="", seqs=None):
+    octo = _octo()
+    d, b = cfg.d, cfg.b
+    Hq = Hkv * G
+    n_seq = B * Hkv
+    keys = WL.make_keys(cfg, "cuda", seed=seed, n_seq=n_seq, n=n)
+    g = gcb(d, b, 0, 0, qjl)
+    cache = octo.Cache(g, n_seq, cap, qjl=qjl)
+    octo.octo_encode(g, keys, cache)
+    v = WL.make_values(cfg, "cuda", seed=seed, n_seq=n_seq, cap=cap)
+    q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=1), "cuda", seed=seed, B=B)
+    out = f64(octo.octo_decode_attn(g, q, cache, v, n, Hkv))
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    seqs = range(n_seq) if seqs is None else seqs
+    # encoder parity on the checked sequences
+    sub = torch.stack([keys[s] for s in seqs])
+    enc = O.encode(f64(sub).reshape(-1, d), cb)
+    allc = unpack_device_codes(cache.packed.cpu().numpy(), cb, n_seq, cap, n)
+    assert_codes_match(np.stack([allc[s] for s in seqs]), enc, cb, label)
+    gam = cache.gamma.cpu().numpy().reshape(n_seq, cap)[:, :n]
+    qq, vv = f64(q), f64(v)
+    S = O.qjl_matrix(d, 0) if qjl else None
+    if qjl:
+        gsign = unpack_device_signs(cache.qjl_bits.cpu().numpy(), d, n_seq, cap, n)
+        gnu = cache.qjl_norm.cpu().numpy().view(np.float16).reshape(n_seq, cap)[:, :n]
+    worst = 0.0
+    for s in seqs:
+        bb, kvh = divmod(s, Hkv)
+        uh = O.decode_rotated(allc[s], cb)
+        for gg in range(G):
+            h = kvh * G + gg
+            if qjl:
+                qe = O.QJLEncoded(gsign[s], gnu[s], None, None)
+                lg = O.qjl_logits(qq[bb, h, 0], uh, gam[s], qe, S, cb)
+            else:
+                lg = O.logits_rotated(qq[bb, h, 0], uh, gam[s], cb)
+            ref = O.softmax_attention(lg / math.sqrt(d), vv[s, :n])
+            err = np.linalg.norm(out[bb, h, 0] - ref) / np.linalg.norm(ref)
+            worst = max(worst, err)
+    say(f"[{label}] attention worst rel err {worst:.2e}")
+    assert worst <= 2e-3
+
+
+def test_attention_llm_recipe_small():
+    check_attention(WL.CONFIGS[2], 1, 2, 4, 1000, 1024, seed=1, label="llm-small")
+
+
+def test_attention_extreme_recipe_small():
+    check_attention(WL.CONFIGS[3], 2, 2, 4, 777, 832, seed=2, label="extreme-small")
+
+
+@pytest.mark.parametrize("G", [1, 2, 3, 8])
+def test_attention_gqa(G):
+    check_attention(WL.CONFIGS[2].scaled(b=3), 1, 2, G, 300, 320, seed=G, label=f"attn-gqa{G}")
+
+
+def test_attention_d64():
+    check_attention(WL.CONFIGS[3].scaled(d=64, b=3, keys="gauss"), 1, 3, 2, 500, 512, seed=4,
+                    label="attn-d64")
+
+
+def test_attention_with_qjl():
+    check_attention(WL.CONFIGS[5], 1, 2, 4, 400, 448, seed=6, qjl=True, label="attn-qjl")
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65])
+def test_attention_tiny_caches(n):
+    check_attention(WL.CONFIGS[2], 1, 1, 4, n, 128, seed=n, label=f"attn-n{n}")
+
+
+def test_attention_empty_cache_writes_zeros():
+    octo = _octo()
+    g = gcb(128, 4)
+    cache = octo.Cache(g, 2, 64)
+    v = torch.zeros((2, 64, 128), dtype=torch.bfloat16, device="cuda")
+    q = torch.randn((1, 8, 1, 128), device="cuda").bfloat16()
+    out = torch.full((1, 8, 1, 128), 7.0, device="cuda")
+    octo.octo_decode_attn(g, q, cache, v, 0, 2, out=out)
+    torch.cuda.synchronize()
+    assert torch.all(out == 0)
+
+
+def test_argument_errors_on_device():
+    octo = _octo()
+    g = gcb(128, 4)
+    cache = octo.Cache(g, 1, 128)
+    keys = torch.randn((1, 10, 128), device="cuda")
+    with pytest.raises(octo.OctoError):
+        octo.octo_encode(g, keys, cache, pos0=120)  # pos0 + n > cap
+    q = torch.randn((1, 3, 128), device="cuda")
+    with pytest.raises(octo.OctoError):
+        octo.octo_decode_logits(g, q, cache, 10, 2)  # Hq % Hkv != 0
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(octo.OctoError) as e:
+        octo.octo_decode_logits(g, torch.randn((1, 2, 128), device="cuda"), cache, 10, 1, workspace=ws)
+    assert e.value.status == octo.OCTO_ERR_WORKSPACE
+
+
+# ---------------------------------------------------------- full-size runs --
+def test_full_config2_attention():
+    cfg = WL.CONFIGS[2]
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config2-full",
+                    seqs=[0, 5])
+
+
+def test_full_config3_attention_sampled():
+    cfg = WL.CONFIGS[3]
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config3-full",
+                    seqs=[3, 30])
+
+
+def test_full_config5_qjl_logits_sampled():
+    octo = _octo()
+    cfg = WL.CONFIGS[5]
+    d, b = cfg.d, cfg.b
+    keys = WL.make_keys(cfg, "cuda")
+    g = gcb(d, b, 0, 0, True)
+    cache = octo.Cache(g, cfg.n_seq, cfg.cap, qjl=True)
+    octo.octo_encode(g, keys, cache)
+    q = WL.make_queries(cfg, "cuda")[:, :, 0]
+    lg = octo.octo_decode_logits(g, q, cache, cfg.N, cfg.Hkv)
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    S = O.qjl_matrix(d, 0)
+    qq = f64(q)
+    for s in (0, 63):
+        bb, kvh = divmod(s, cfg.Hkv)
+        kk = f64(keys[s])
+        enc = O.encode(kk, cb)
+        packed = cache.packed.view(cfg.n_seq, -1)[s].cpu().numpy()
+        codes = unpack_device_codes(packed, cb, 1, cfg.cap, cfg.N)
+        assert_codes_match(codes, enc, cb, f"config5 seq{s}")
+        gsign = unpack_device_signs(cache.qjl_bits.view(cfg.n_seq, -1)[s].cpu().numpy(), d, 1,
+                                    cfg.cap, cfg.N)
+        gnu = cache.qjl_norm.view(cfg.n_seq, -1)[s].cpu().numpy().view(np.float16)[: cfg.N]
+        check_qjl_encoder(enc, codes, gsign, gnu[None], cb, S, f"config5 seq{s}")
+        uh = O.decode_rotated(codes[0], cb)
+        gam = cache.gamma.view(cfg.n_seq, -1)[s, : cfg.N].cpu().numpy()
+        qe = O.QJLEncoded(gsign[0], gnu, None, None)
+        for gg in range(cfg.G):
+            h = kvh * cfg.G + gg
+            ref = O.qjl_logits(qq[bb, h], uh, gam, qe, S, cb)
+            err = logit_err(f64(lg[bb, h]), ref, np.linalg.norm(qq[bb, h]), gam, d)
+            assert err <= 1e-3, (s, h, err)
+    say("[config5-full] sampled sequences ok")
