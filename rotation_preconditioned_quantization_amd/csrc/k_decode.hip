@@ -17,48 +17,69 @@
 namespace octo {
 
 // ---------------------------------------------------------------------------
-// Query rotation.  Block = D threads, one query row per block.
+// Query rotation.  One wavefront per query row; lane l holds elements
+// l + 64 k.  Butterfly strides below 64 pair lanes l and l ^ h (shuffles),
+// stride 64 pairs the two values a lane holds.
 // ---------------------------------------------------------------------------
 template <int D>
-__global__ __launch_bounds__(128) void k_rotate(RotateArgs a) {
+__global__ __launch_bounds__(64) void k_rotate(RotateArgs a) {
   constexpr int T = (D + 2) / 3;
-  __shared__ float s[D];
+  constexpr int NV = D / 64;
+  __shared__ float s_q[D];
   const int r = blockIdx.x;
   const int qi = r % a.n_q;
   const int h = (r / a.n_q) % a.Hq;
   const int b = r / (a.n_q * a.Hq);
   const int G = a.Hq / a.Hkv;
   const int orow = ((b * a.Hkv + h / G) * G + (h % G)) * a.n_q + qi;
-  const int j = threadIdx.x;
-  float x;
-  if (a.qdt == DT_F32) {
-    x = ((const float*)a.q)[(int64_t)r * D + j];
-  } else {
-    const unsigned short u = ((const unsigned short*)a.q)[(int64_t)r * D + j];
-    x = a.qdt == DT_BF16 ? __uint_as_float((uint32_t)u << 16) : __half2float(__ushort_as_half(u));
+  const int l = threadIdx.x;
+  float x[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = l + 64 * k;
+    float v;
+    if (a.qdt == DT_F32) {
+      v = ((const float*)a.q)[(int64_t)r * D + j];
+    } else {
+      const unsigned short u = ((const unsigned short*)a.q)[(int64_t)r * D + j];
+      v = a.qdt == DT_BF16 ? __uint_as_float((uint32_t)u << 16) : __half2float(__ushort_as_half(u));
+    }
+    if ((a.t.sign_bits[j >> 5] >> (j & 31)) & 1u) v = -v;
+    x[k] = v;
   }
-  if ((a.t.sign_bits[j >> 5] >> (j & 31)) & 1u) x = -x;
-  s[j] = x;
-  __syncthreads();
-  for (int hh = 1; hh < D; hh <<= 1) {
-    const float o = s[j ^ hh];
-    __syncthreads();
-    x = (j & hh) ? (o - x) : (x + o);
-    s[j] = x;
-    __syncthreads();
+#pragma unroll
+  for (int hh = 1; hh < 64; hh <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const float o = __shfl_xor(x[k], hh, 64);
+      x[k] = (l & hh) ? (o - x[k]) : (x[k] + o);
+    }
   }
-  const float qv = x * (a.mult * rsqrtf((float)D));
+  if constexpr (NV == 2) {
+    const float a0 = x[0], a1 = x[1];
+    x[0] = a0 + a1;
+    x[1] = a0 - a1;
+  }
+  const float mult = a.mult * rsqrtf((float)D);
   float* out = a.qrot + (int64_t)orow * (3 * T);
-  out[j] = qv;
-  if (j < 3 * T - D) out[D + j] = 0.f;
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    x[k] *= mult;
+    out[l + 64 * k] = x[k];
+    s_q[l + 64 * k] = x[k];
+  }
+  if (l < 3 * T - D) out[D + l] = 0.f;
   if (a.qp != nullptr) {
     __syncthreads();
-    s[j] = qv;
-    __syncthreads();
-    const float* row = a.t.S + (int64_t)j * D;
-    float acc = 0.f;
-    for (int k = 0; k < D; ++k) acc = __builtin_fmaf(row[k], s[k], acc);
-    a.qp[(int64_t)orow * D + j] = acc * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = l + 64 * k;
+      const float* row = a.t.S + (int64_t)j * D;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) acc = __builtin_fmaf(row[c], s_q[c], acc);
+      a.qp[(int64_t)orow * D + j] = acc * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+    }
   }
 }
 
@@ -323,22 +344,63 @@ __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
   }
 }
 
-// out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s.
-__global__ __launch_bounds__(128) void k_combine(CombineArgs a) {
+// out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s, one block per
+// row.  The split weights are formed once in LDS; every thread then sums an
+// independent strided slice of the splits for its output column, so the
+// partial loads are issued back to back instead of one latency at a time.
+constexpr int kCombineThreads = 256;
+constexpr int kMaxSplit = 1024;
+
+__global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
+  __shared__ float s_w[kMaxSplit];
+  __shared__ float s_red[kCombineThreads];
   const int64_t row = blockIdx.x;
-  const float* p = a.part + row * a.n_split * (a.d + 2);
-  float M = -INFINITY;
-  for (int s = 0; s < a.n_split; ++s) M = fmaxf(M, p[s * (a.d + 2)]);
-  for (int c = threadIdx.x; c < a.d; c += blockDim.x) {
-    float num = 0.f, den = 0.f;
-    for (int s = 0; s < a.n_split; ++s) {
-      const float ms = p[s * (a.d + 2)];
-      if (ms == -INFINITY) continue;
-      const float w = exp2f(ms - M);
-      den = __builtin_fmaf(w, p[s * (a.d + 2) + 1], den);
-      num = __builtin_fmaf(w, p[s * (a.d + 2) + 2 + c], num);
-    }
-    a.out[row * a.d + c] = den > 0.f ? num / den : 0.f;
+  const int tid = threadIdx.x;
+  const int ns = a.n_split, stride = a.d + 2;
+  const float* p = a.part + row * ns * stride;
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += kCombineThreads) {
+    const float m = p[s * stride];
+    s_w[s] = m;
+    mloc = fmaxf(mloc, m);
+  }
+  s_red[tid] = mloc;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
+    __syncthreads();
+  }
+  const float M = s_red[0];
+  __syncthreads();
+  float lden = 0.f;
+  for (int s = tid; s < ns; s += kCombineThreads) {
+    const float m = s_w[s];
+    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
+    s_w[s] = w;
+    lden = __builtin_fmaf(w, p[s * stride + 1], lden);
+  }
+  s_red[tid] = lden;
+  __syncthreads();
+  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
+    if (tid < o) s_red[tid] += s_red[tid + o];
+    __syncthreads();
+  }
+  const float den = s_red[0];
+  __syncthreads();
+  // kCombineThreads / d threads per output column, each over a slice of splits
+  const int per_col = kCombineThreads / a.d;
+  const int c = tid % a.d, part = tid / a.d;
+  float num = 0.f;
+  if (part < per_col) {
+#pragma unroll 4
+    for (int s = part; s < ns; s += per_col) num = __builtin_fmaf(s_w[s], p[s * stride + 2 + c], num);
+  }
+  s_red[tid] = num;
+  __syncthreads();
+  if (tid < a.d) {
+    float tot = 0.f;
+    for (int k = 0; k < per_col; ++k) tot += s_red[k * a.d + tid];
+    a.out[row * a.d + tid] = den > 0.f ? tot / den : 0.f;
   }
 }
 
@@ -388,7 +450,7 @@ hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s) {
   const unsigned rows = (unsigned)(a.B * a.Hq * a.n_q);
   if (rows == 0) return hipSuccess;
   if (d == 64) hipLaunchKernelGGL(k_rotate<64>, dim3(rows), dim3(64), 0, s, a);
-  else if (d == 128) hipLaunchKernelGGL(k_rotate<128>, dim3(rows), dim3(128), 0, s, a);
+  else if (d == 128) hipLaunchKernelGGL(k_rotate<128>, dim3(rows), dim3(64), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -442,7 +504,8 @@ hipError_t launch_attn(int d, int b, int hp, bool qjl, const DecodeArgs& a, int6
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_combine, dim3(a.rows), dim3(128), 0, s, a);
+  if (a.n_split > kMaxSplit || a.d > kCombineThreads) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_combine, dim3(a.rows), dim3(kCombineThreads), 0, s, a);
   return hipGetLastError();
 }
 

@@ -1,0 +1,245 @@
+// Multi-query fused attention over the compressed cache (many query tokens
+// per head, e.g. a block of video frames attending to the cache) on gfx950
+// MFMA ([YL] 工程实现: keys rebuilt on the fly, FlashAttention tiling, online
+// softmax; the block/chunk decoding of the video workloads in 实验结果).
+//
+// Workgroup = 4 wavefronts = 128 queries of one head over one split of the
+// cache.  Per tile of KT keys:
+//   1. every wave rebuilds KT/4 keys (one per lane) from the packed stream
+//      into LDS as fp16 rotated unit directions u'^ (gamma kept in fp32);
+//   2. the bf16 V tile is stored transposed in LDS as fp16;
+//   3. each wave computes S^T = K^ Q'^T for its 32 queries with
+//      v_mfma_f32_32x32x16_f16 (fp32 accumulate), scales by gamma, runs the
+//      online softmax in the accumulator registers, and feeds P^T straight
+//      from those registers into O^T += V^T P^T (same MFMA shape).
+// Queries are the rotated q' = R q (keys are never inverse-rotated), scaled
+// per row by a power of two so fp16 holds them without overflow.
+#include "octo_device.hpp"
+
+namespace octo {
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMQQueries = 128;  // queries per workgroup (32 per wave)
+
+template <int D>
+struct MQShape {
+  static constexpr int KT = D == 64 ? 256 : 128;  // keys per tile
+  static constexpr int KPW = KT / 4;              // keys rebuilt per wave
+  static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
+  static constexpr int VP = KT * 2 + 16;          // V^T row pitch in bytes (fp16)
+};
+
+template <int D, int B>
+__global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
+  using C = Codec<D, B>;
+  using S = MQShape<D>;
+  constexpr int T = C::T, W = C::W;
+  constexpr int KT = S::KT, KPW = S::KPW, KP = S::KP, VP = S::VP;
+  constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
+  constexpr int NMB = D / 32;  // 32-row blocks of O^T
+
+  __shared__ __align__(16) unsigned char s_k[KT * KP];
+  __shared__ __align__(16) unsigned char s_vt[D * VP];
+  __shared__ float s_g[KT];
+  __shared__ float4 s_dir[C::NDIR];
+  __shared__ float s_rho[C::LR];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int g = lane >> 5, ln = lane & 31;
+  const int bh = blockIdx.z;                 // b * Hq + h
+  const int b = bh / a.H, h = bh % a.H;
+  const int kvh = h / a.G;
+  const int64_t seq = (int64_t)b * a.Hkv + kvh;
+  const int q = blockIdx.y * kMQQueries + wave * 32 + ln;
+  const bool qvalid = q < a.n_q;
+
+  for (int i = tid; i < C::NDIR; i += 256) s_dir[i] = a.t.dirtab[i];
+  if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
+
+  // Q' fragment: B[k = dim][n = query], lane (ln, g) holds dims 16j + 8g + 0..7.
+  half8 qf[NKS];
+  float qscale_inv;
+  {
+    const float* qrow = a.qrot + (((seq * a.G + h % a.G) * a.n_q) + (qvalid ? q : 0)) * (3 * T);
+    float v[NKS][8];
+    float amax = 0.f;
+#pragma unroll
+    for (int j = 0; j < NKS; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        v[j][i] = qvalid ? qrow[16 * j + 8 * g + i] : 0.f;
+        amax = fmaxf(amax, fabsf(v[j][i]));
+      }
+    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    int ex = 0;
+    __builtin_frexpf(amax, &ex);
+    const int sh = amax > 0.f ? 7 - ex : 0;   // row max into [64, 128)
+    const float sc = __builtin_ldexpf(1.0f, sh);
+    qscale_inv = __builtin_ldexpf(1.0f, -sh);
+#pragma unroll
+    for (int j = 0; j < NKS; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) qf[j][i] = (_Float16)(v[j][i] * sc);
+  }
+
+  floatx16 o[NMB];
+#pragma unroll
+  for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) o[mb][r] = 0.f;
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int64_t ntile = (a.n_keys + KT - 1) / KT;
+  const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
+  const int64_t t_end = t_begin + a.tiles_per_split < ntile ? t_begin + a.tiles_per_split : ntile;
+  const int64_t tiles64 = a.cap / kTile;
+  const unsigned short* vseq = (const unsigned short*)a.v + seq * a.cap * D;
+
+  for (int64_t t = t_begin; t < t_end; ++t) {
+    const int64_t k0 = t * KT;
+    __syncthreads();  // previous tile's LDS reads are done
+    // 1. rebuild keys
+    if (lane < KPW) {
+      const int kk = wave * KPW + lane;
+      const int64_t key = k0 + kk;
+      _Float16* row = (_Float16*)(s_k + kk * KP);
+      if (key < a.n_keys) {
+        const uint32_t* src =
+            a.packed + ((seq * tiles64 + (key >> 6)) * W) * kTile + (key & 63);
+        uint32_t words[W];
+#pragma unroll
+        for (int w = 0; w < W; ++w) words[w] = src[w * kTile];
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+          const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
+          const float4 n = s_dir[code & C::DIR_MASK];
+          const float rh = s_rho[code >> (C::BX + C::BE)];
+          row[3 * i] = (_Float16)(rh * n.x);
+          if (3 * i + 1 < D) row[3 * i + 1] = (_Float16)(rh * n.y);
+          if (3 * i + 2 < D) row[3 * i + 2] = (_Float16)(rh * n.z);
+        }
+        s_g[kk] = a.gamma[seq * a.cap + key];
+      } else {
+#pragma unroll
+        for (int j = 0; j < D; ++j) row[j] = (_Float16)0.f;
+        s_g[kk] = 0.f;
+      }
+    }
+    // 2. V tile, transposed to [dim][key] fp16
+    for (int c = tid; c < KT * (D / 8); c += 256) {
+      const int kk = c / (D / 8), part = c % (D / 8);
+      uint4 u = make_uint4(0, 0, 0, 0);
+      if (k0 + kk < a.n_keys) u = *(const uint4*)(vseq + (k0 + kk) * D + part * 8);
+      float f[8];
+      cvt_chunk<DT_BF16>(u, f);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *(_Float16*)(s_vt + (part * 8 + i) * VP + kk * 2) = (_Float16)f[i];
+    }
+    __syncthreads();
+
+    // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T
+#pragma unroll 1
+    for (int ch = 0; ch < KT / 64; ++ch) {
+      floatx16 s[2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+        const int kb = ch * 64 + sb * 32;
+        floatx16 acc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+#pragma unroll
+        for (int j = 0; j < NKS; ++j) {
+          const half8 kf = *(const half8*)(s_k + (kb + ln) * KP + (16 * j + 8 * g) * 2);
+          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], acc, 0, 0, 0);
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int kr = kb + 8 * (r >> 2) + 4 * g + (r & 3);
+          const float val = acc[r] * s_g[kr] * qscale_inv;
+          acc[r] = (k0 + kr < a.n_keys) ? val : -INFINITY;
+        }
+        s[sb] = acc;
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      float lsum = 0.f;
+      half8 pf[2][2];
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[sb][r] - m_new);
+          const _Float16 ph = (_Float16)p;
+          lsum += (float)ph;
+          pf[sb][r >> 3][r & 7] = ph;
+        }
+      l_run = __builtin_fmaf(l_run, alpha, lsum);
+      m_run = m_new;
+#pragma unroll
+      for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb) {
+#pragma unroll
+        for (int half = 0; half < 2; ++half) {
+          const int kbase = ch * 64 + sb * 32 + 16 * half + 4 * g;
+#pragma unroll
+          for (int mb = 0; mb < NMB; ++mb) {
+            const unsigned char* vrow = s_vt + (32 * mb + ln) * VP;
+            const half4 lo = *(const half4*)(vrow + kbase * 2);
+            const half4 hi = *(const half4*)(vrow + (kbase + 8) * 2);
+            const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+            o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sb][half], o[mb], 0, 0, 0);
+          }
+        }
+      }
+    }
+  }
+
+  l_run += __shfl_xor(l_run, 32, 64);
+  if (qvalid) {
+    float* dst = a.part + (((int64_t)bh * a.n_q + q) * a.n_split + blockIdx.x) * (D + 2);
+    if (g == 0) {
+      dst[0] = m_run;
+      dst[1] = l_run;
+    }
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) dst[2 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = o[mb][r];
+  }
+}
+
+template <int D, int B>
+static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
+  const dim3 grid((unsigned)a.n_split, (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries),
+                  (unsigned)(a.B * a.H));
+  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+int mq_tile_keys(int d) { return d == 64 ? MQShape<64>::KT : MQShape<128>::KT; }
+
+hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
+  switch (d * 10 + b) {
+    case 642: return mq_t<64, 2>(a, s);
+    case 643: return mq_t<64, 3>(a, s);
+    case 644: return mq_t<64, 4>(a, s);
+    case 1282: return mq_t<128, 2>(a, s);
+    case 1283: return mq_t<128, 3>(a, s);
+    case 1284: return mq_t<128, 4>(a, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace octo

@@ -314,6 +314,18 @@ Split attn_split(int64_t n_keys, int64_t n_seq, int passes) {
   return {(int)ns, (int)tps};
 }
 
+Split mq_split(int64_t n_keys, int d, int64_t rows) {
+  const int kt = mq_tile_keys(d);
+  const int64_t ntile = std::max<int64_t>(1, (n_keys + kt - 1) / kt);
+  int64_t ns = (1024 + rows - 1) / std::max<int64_t>(1, rows);
+  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ntile));
+  const int64_t tps = (ntile + ns - 1) / ns;
+  ns = (ntile + tps - 1) / tps;
+  return {(int)ns, (int)tps};
+}
+
+int64_t mq_rows(int B, int Hq, int n_q) { return (int64_t)B * Hq * ((n_q + 127) / 128); }
+
 struct WsLayout { size_t qrot, qp, part, total; };
 
 WsLayout ws_layout(const octo_codebook* cb, int mode, int B, int Hq, int Hkv, int n_q,
@@ -325,7 +337,10 @@ WsLayout ws_layout(const octo_codebook* cb, int mode, int B, int Hq, int Hkv, in
   w.qp = off;
   if (cb->qjl) off += align256(rows * cb->d * sizeof(float));
   w.part = off;
-  if (mode == 1) {
+  if (mode == 1 && n_q > 1) {
+    const Split sp = mq_split(n_keys, cb->d, mq_rows(B, Hq, n_q));
+    off += align256(rows * (size_t)sp.n_split * (cb->d + 2) * sizeof(float));
+  } else if (mode == 1) {
     const int G = Hkv > 0 ? Hq / Hkv : 1;
     const int hp = heads_per_pass(std::max(G, 1));
     const Split sp = attn_split(n_keys, (int64_t)B * Hkv, std::max(G, 1) / hp);
@@ -703,7 +718,35 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
-    return fail(OCTO_ERR_UNSUPPORTED, "multi-query path not built yet");
+    const Split sp = mq_split(n_keys, cb->d, mq_rows(B, Hq, n_q));
+    MQArgs m{};
+    m.t = cb->tables;
+    m.qrot = r.qrot;
+    m.packed = (const uint32_t*)packed;
+    m.gamma = gamma;
+    m.v = v;
+    m.n_keys = n_keys;
+    m.cap = cap;
+    m.B = B;
+    m.n_q = n_q;
+    m.H = Hq;
+    m.Hkv = Hkv;
+    m.G = G;
+    m.tiles_per_split = sp.tiles_per_split;
+    m.n_split = sp.n_split;
+    m.part = (float*)((char*)workspace + wl.part);
+    if (stages & OCTO_STAGE_MAIN) {
+      st = hip_status(launch_mq_attn(cb->d, cb->b, m, s), "multi-query attention launch");
+      if (st != OCTO_OK) return st;
+    }
+    if (!(stages & OCTO_STAGE_COMBINE)) return OCTO_OK;
+    CombineArgs c{};
+    c.part = m.part;
+    c.out = out;
+    c.rows = B * Hq * n_q;
+    c.n_split = sp.n_split;
+    c.d = cb->d;
+    return hip_status(launch_combine(c, s), "combine launch");
   }
   const int hp = heads_per_pass(G);
   const int64_t n_seq = (int64_t)B * Hkv;

@@ -94,9 +94,9 @@ struct MQArgs {
   const float* gamma;
   const void* v;
   int64_t n_keys, cap;
-  int n_q, H, Hkv, G;
+  int B, n_q, H, Hkv, G;  // H = query heads
   int tiles_per_split, n_split;
-  float* part;           // [H][n_q][n_split][d + 2]
+  float* part;           // [B*H][n_q][n_split][d + 2]
 };
 
 hipError_t launch_encode(int d, int b, int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq,
@@ -110,5 +110,6 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s);
+int mq_tile_keys(int d);  // keys per tile of the multi-query kernel
 
 }  // namespace octo

@@ -71,10 +71,13 @@ def compare_codes(gpu_codes: np.ndarray, enc: O.Encoded, cb: O.Codebook):
     return n_mis, n_exc, n_mis - n_exc, total, mism.any(axis=(1, 2))
 
 
-def assert_codes_match(gpu_codes, enc, cb, label=""):
+def assert_codes_match(gpu_codes, enc, cb, label="", cap_fraction=True):
+    """cap_fraction=False for hand-made inputs built to sit on decision
+    boundaries, where the 1e-4 budget for random data does not apply."""
     n_mis, n_exc, n_unexc, total, _ = compare_codes(gpu_codes, enc, cb)
     assert n_unexc == 0, f"{label}: {n_unexc} unexcused index mismatches of {total}"
-    assert n_exc <= MAX_EXCUSED_FRACTION * total, f"{label}: {n_exc} excused of {total}"
+    if cap_fraction:
+        assert n_exc <= MAX_EXCUSED_FRACTION * total, f"{label}: {n_exc} excused of {total}"
     return n_mis
 
 

@@ -53,7 +53,7 @@ def f64(t):
     return t.detach().float().cpu().numpy().astype(np.float64)
 
 
-def encode_and_check(d, b, keys, cap, pos0=0, qjl=False, seed=0, label=""):
+def encode_and_check(d, b, keys, cap, pos0=0, qjl=False, seed=0, label="", cap_fraction=True):
     """Encode keys [n_seq, n, d] at pos0 and check codes and gamma."""
     octo = _octo()
     g = gcb(d, b, seed, 0, qjl)
@@ -65,7 +65,7 @@ def encode_and_check(d, b, keys, cap, pos0=0, qjl=False, seed=0, label=""):
     kk = f64(keys).reshape(-1, d)
     enc = O.encode(kk, cb)
     codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, n_seq, cap, n, start=pos0)
-    n_mis = assert_codes_match(codes, enc, cb, label)
+    n_mis = assert_codes_match(codes, enc, cb, label, cap_fraction)
     gamma = cache.gamma.cpu().numpy().reshape(n_seq, cap)[:, pos0:pos0 + n].reshape(-1)
     ref_g = np.linalg.norm(kk, axis=1)
     assert np.all(np.abs(gamma - ref_g) <= 1e-6 * np.maximum(ref_g, 1e-30)), label
@@ -131,7 +131,9 @@ def test_encode_degenerate_keys():
     k[0, 5, 0] = 1e-30                   # tiny
     k[0, 6] = torch.randn(d) * 1e4       # large
     k[0, 7:] = torch.randn(63, d)
-    encode_and_check(d, 3, k.cuda(), cap=128, label="degenerate")
+    # constant and alternating keys rotate onto exact zeros and ties, so every
+    # mismatch must be excused but their share is not capped
+    encode_and_check(d, 3, k.cuda(), cap=128, label="degenerate", cap_fraction=False)
 
 
 def test_encode_is_deterministic():
@@ -372,3 +374,61 @@ def test_full_config5_qjl_logits_sampled():
             err = logit_err(f64(lg[bb, h]), ref, np.linalg.norm(qq[bb, h]), gam, d)
             assert err <= 1e-3, (s, h, err)
     say("[config5-full] sampled sequences ok")
+
+
+# ------------------------------------------------------- multi-query (MFMA) --
+def check_mq(cfg, Hq, Hkv, n_q, n, cap, seed=0, label="", heads=None, chunk=None):
+    """Multi-query attention: n_q query tokens per head over the whole cache."""
+    octo = _octo()
+    d, b = cfg.d, cfg.b
+    G = Hq // Hkv
+    keys = WL.make_keys(cfg, "cuda", seed=seed, n_seq=Hkv, n=n)
+    g = gcb(d, b)
+    cache = octo.Cache(g, Hkv, cap)
+    if chunk:   # the cache prefix, then a freshly encoded chunk at its end
+        octo.octo_encode(g, keys[:, : n - chunk].contiguous(), cache, pos0=0)
+        octo.octo_encode(g, keys[:, n - chunk:].contiguous(), cache, pos0=n - chunk)
+    else:
+        octo.octo_encode(g, keys, cache)
+    v = WL.make_values(cfg, "cuda", seed=seed, n_seq=Hkv, cap=cap)
+    q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=n_q), "cuda", seed=seed, B=1)
+    out = f64(octo.octo_decode_attn(g, q, cache, v, n, Hkv))
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    allc = unpack_device_codes(cache.packed.cpu().numpy(), cb, Hkv, cap, n)
+    gam = cache.gamma.cpu().numpy().reshape(Hkv, cap)[:, :n]
+    qq, vv = f64(q), f64(v)
+    heads = range(Hq) if heads is None else heads
+    kvs = sorted({h // G for h in heads})
+    enc = O.encode(f64(torch.stack([keys[s] for s in kvs])).reshape(-1, d), cb)
+    assert_codes_match(np.stack([allc[s] for s in kvs]), enc, cb, label)
+    worst = 0.0
+    for h in heads:
+        s = h // G
+        uh = O.decode_rotated(allc[s], cb)
+        lg = O.logits_rotated(qq[0, h], uh, gam[s], cb)          # (n_q, n)
+        ref = O.softmax_attention(lg / math.sqrt(d), vv[s, :n])
+        err = np.linalg.norm(out[0, h] - ref, axis=1) / np.linalg.norm(ref, axis=1)
+        worst = max(worst, float(err.max()))
+    say(f"[{label}] multi-query attention worst rel err {worst:.2e}")
+    assert worst <= 2e-3
+
+
+def test_mq_video_recipe_small():
+    check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
+
+
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3)])
+def test_mq_shapes_and_gqa(d, b):
+    check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
+
+
+@pytest.mark.parametrize("n_q,n", [(2, 1), (2, 255), (129, 257)])
+def test_mq_edges(n_q, n):
+    check_mq(WL.CONFIGS[4], 1, 1, n_q, n, 320, seed=n, label=f"mq-edge{n_q}x{n}")
+
+
+def test_full_config4_video_block_sampled():
+    cfg = WL.CONFIGS[4]
+    check_mq(cfg, cfg.Hq, cfg.Hkv, cfg.n_q, cfg.N, cfg.cap, seed=0, label="config4-full",
+             heads=[0, 17], chunk=cfg.chunk)
