@@ -32,6 +32,19 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0
+
+WORKLOADS = {
+    1: "toy: 1 head, d=128, 4096 fp32 keys, b=3, 1 fp32 query (logits)",
+    2: "llm_decode: B=1, Hq=32, Hkv=8, d=128, 32768 keys/KV head, b=4, bf16 K (4 outlier "
+       "channels x10) and V, 1 query token",
+    3: "extreme: B=4, Hq=32, Hkv=8, d=128, 131072 keys/KV head, b=2, bf16 Student-t(5) K with "
+       "log-normal norms, bf16 V, 1 query token",
+    4: "video_block: d=64, 24 heads, b=3, 65536-key cache with a 16384-key chunk encoded per "
+       "step, 256 bf16 queries per head (multi-query MFMA attention)",
+    5: "qjl: B=8, Hq=32, Hkv=8, d=128, 65536 keys/KV head, b=3 + 1-bit QJL residual signs, "
+       "1 query token (logits)",
+}
 PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "k_attn_llm_decode_counters.json")
 
 
@@ -47,11 +60,18 @@ def algorithmic_bytes(cfg, lay):
     """Per decode call and per encode call (measurement)."""
     n = cfg.n_seq * cfg.N
     packed = lay.n_triplets * lay.bits_per_triplet / 8.0     # bits actually used per key
-    k_bytes = n * (packed + 4.0)                             # packed stream + fp32 gamma
-    v_bytes = n * cfg.d * 2.0                                # bf16 V
-    qo = cfg.B * cfg.Hq * cfg.d * (2 + 4)                    # query in, fp32 out
-    dec = k_bytes + v_bytes + qo
-    enc = n * (cfg.d * 2.0) + k_bytes                        # bf16 keys in, packed + gamma out
+    per_key = packed + 4.0                                   # packed stream + fp32 gamma
+    if cfg.qjl:
+        per_key += cfg.d / 8.0 + 2.0                         # sign bits + fp16 residual norm
+    k_bytes = n * per_key
+    qb = 4 if cfg.qdtype == "f32" else 2
+    if cfg.mode == "logits":
+        dec = k_bytes + cfg.B * cfg.Hq * cfg.d * qb + cfg.B * cfg.Hq * cfg.N * 4.0
+    else:
+        v_bytes = n * cfg.d * 2.0                            # bf16 V
+        dec = k_bytes + v_bytes + cfg.B * cfg.Hq * cfg.n_q * cfg.d * (qb + 4)
+    kb = 4 if cfg.kdtype == "f32" else 2
+    enc = n * (cfg.d * kb + per_key)                         # keys in, packed + gamma out
     return dec, enc, n
 
 
@@ -115,6 +135,9 @@ def main():
                     help="graph replays used to time each kernel on its own")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
+                    help="workload (2 = the LLM-decode shape the metric is quoted on; the "
+                         "others are the remaining shapes of the pages' workloads)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -129,38 +152,64 @@ def main():
     import rotation_preconditioned_quantization_amd as octo
     import workloads as WL
 
-    if not torch.cuda.is_available():
+    if not torch.cuda.is_available():  # noqa: SIM102
         print(json.dumps({"error": "no GPU"}))
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
-    cfg = WL.CONFIGS[2]
-    cb = octo.Codebook(cfg.d, cfg.b, seed=0, cb_seed=0, device=0)
+    cfg = WL.CONFIGS[args.config]
+    cb = octo.Codebook(cfg.d, cfg.b, seed=0, cb_seed=0, qjl=cfg.qjl, device=0)
     lay = cb.layout
     dec_bytes, enc_bytes, n_keys_total = algorithmic_bytes(cfg, lay)
+    mq = cfg.mode == "attn_mq"
+    logits_mode = cfg.mode == "logits"
 
-    set_bytes = (cfg.n_seq * cfg.cap * cfg.d * 2 * 2 + cb.packed_words(cfg.n_seq, cfg.cap) * 4
+    kdt_bytes = 4 if cfg.kdtype == "f32" else 2
+    set_bytes = (cfg.n_seq * cfg.cap * cfg.d * kdt_bytes + cb.packed_words(cfg.n_seq, cfg.cap) * 4
                  + cfg.n_seq * cfg.cap * 4)
+    if not logits_mode:
+        set_bytes += cfg.n_seq * cfg.cap * cfg.d * 2
     R = max(2, int(math.ceil(args.rotate_gib * (1 << 30) / set_bytes)))
-    ws_bytes = cb.workspace_bytes(1, cfg.B, cfg.Hq, cfg.Hkv, 1, cfg.N)
+    mode = 0 if logits_mode else 1
+    ws_bytes = cb.workspace_bytes(mode, cfg.B, cfg.Hq, cfg.Hkv, cfg.n_q, cfg.N)
     sets = []
     for r in range(R):
         keys = WL.make_keys(cfg, dev, seed=r)
-        v = WL.make_values(cfg, dev, seed=r)
+        v = None if logits_mode else WL.make_values(cfg, dev, seed=r)
         q = WL.make_queries(cfg, dev, seed=r).contiguous()
-        cache = octo.Cache(cb, cfg.n_seq, cfg.cap)
-        out = torch.empty((cfg.B, cfg.Hq, 1, cfg.d), dtype=torch.float32, device=dev)
+        if logits_mode:
+            q = q[:, :, 0].contiguous()
+        cache = octo.Cache(cb, cfg.n_seq, cfg.cap, qjl=cfg.qjl)
+        if logits_mode:
+            out = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
+        else:
+            out = torch.empty((cfg.B, cfg.Hq, cfg.n_q, cfg.d), dtype=torch.float32, device=dev)
         ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
         sets.append(dict(keys=keys, v=v, q=q, cache=cache, out=out, ws=ws))
 
+    # the video-block workload encodes only the newest chunk at the end of the cache
+    enc_pos0 = cfg.N - cfg.chunk if cfg.chunk else 0
+    if cfg.chunk:
+        n_keys_total = cfg.n_seq * cfg.chunk
+        enc_bytes = n_keys_total * (cfg.d * kdt_bytes + lay.n_triplets * lay.bits_per_triplet / 8 + 4)
+
     def encode(s):
-        octo.octo_encode(cb, s["keys"], s["cache"])
+        k = s["keys"][:, enc_pos0:] if enc_pos0 else s["keys"]
+        octo.octo_encode(cb, k, s["cache"], pos0=enc_pos0)
 
     def decode(s, stages=octo.STAGE_ALL):
-        octo.octo_decode_attn(cb, s["q"], s["cache"], s["v"], cfg.N, cfg.Hkv, out=s["out"],
-                              workspace=s["ws"], stages=stages)
+        if logits_mode:
+            octo.octo_decode_logits(cb, s["q"], s["cache"], cfg.N, cfg.Hkv, logits=s["out"],
+                                    workspace=s["ws"], stages=stages & 3)
+        else:
+            octo.octo_decode_attn(cb, s["q"], s["cache"], s["v"], cfg.N, cfg.Hkv, out=s["out"],
+                                  workspace=s["ws"], stages=stages)
 
-    # eager warm-up and reference outputs
+    # eager warm-up (the prefix of a chunked cache is encoded once here) and
+    # reference outputs
+    for s in sets:
+        if enc_pos0:
+            octo.octo_encode(cb, s["keys"][:, :enc_pos0], s["cache"], pos0=0)
     for i in range(max(1, args.warmup)):
         for s in sets:
             encode(s)
@@ -179,7 +228,7 @@ def main():
     step_graphs = [capture(lambda s=s: (encode(s), decode(s))) for s in sets]
     enc_graph = capture(lambda: [encode(s) for s in sets])
     dec_graph = capture(lambda: [decode(s) for s in sets])
-    attn_graph = capture(lambda: [decode(s, octo.STAGE_MAIN) for s in sets])
+    main_graph = capture(lambda: [decode(s, octo.STAGE_MAIN) for s in sets])
     torch.cuda.synchronize()
     # each replay must reproduce the eager result (checked on every set once)
     for r, g in enumerate(step_graphs):
@@ -204,7 +253,7 @@ def main():
 
     t_enc = time_graph(enc_graph, args.kernel_reps) / R
     t_dec = time_graph(dec_graph, args.kernel_reps) / R
-    t_attn = time_graph(attn_graph, args.kernel_reps) / R
+    t_main = time_graph(main_graph, args.kernel_reps) / R
 
     # timed region: exactly K steps
     for w in range(args.warmup):
@@ -218,13 +267,28 @@ def main():
     ms_per_step = wall / args.steps * 1e3
 
     dec_gbs = dec_bytes / t_dec / 1e9
-    attn_gbs = dec_bytes / t_attn / 1e9
+    main_gbs = dec_bytes / t_main / 1e9
     traffic = None
-    if os.path.exists(PROFILE_COUNTERS):
+    if os.path.exists(PROFILE_COUNTERS) and args.config == 2:
         with open(PROFILE_COUNTERS) as f:
             pc = json.load(f)
         if pc.get("kernel_source_hash") == kernel_source_hash():
             traffic = pc.get("hbm_bytes_per_launch")
+    kernel_name = {"logits": "k_logits (fused compressed-K logits)",
+                   "attn": "k_attn (fused decode attention)",
+                   "attn_mq": "k_mq_attn (multi-query MFMA attention)"}[cfg.mode]
+    roofline = {"bound": "hbm", "kernel": kernel_name, "achieved": round(main_gbs, 2),
+                "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(main_gbs / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel_us": round(t_main * 1e6, 3),
+                "algorithmic_bytes_per_launch": int(dec_bytes)}
+    if mq:
+        flops = 4.0 * cfg.B * cfg.Hq * cfg.n_q * cfg.N * cfg.d
+        tf = flops / t_main / 1e12
+        roofline = {"bound": "mfma", "kernel": kernel_name, "achieved": round(tf, 2),
+                    "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                    "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                    "kernel_us": round(t_main * 1e6, 3), "algorithmic_flops_per_launch": int(flops),
+                    "hbm_gbs": round(main_gbs, 2)}
 
     line = {
         "metric": "fused compressed-K decode GB/s (% HBM peak) + encode Mkeys/s, d=128",
@@ -237,25 +301,19 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16" if cfg.kdtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": "llm_decode: B=1, Hq=32, Hkv=8, d=128, 32768 keys/KV head, b=4, "
-                               "bf16 K (4 outlier channels x10) and V, 1 query token",
-                   "global_batch": cfg.B, "seq_len": cfg.N, "parallelism": "none (1 GPU)",
-                   "rotating_copies": R},
+        "config": {"workload": WORKLOADS[args.config], "global_batch": cfg.B, "seq_len": cfg.N,
+                   "parallelism": "none (1 GPU)", "rotating_copies": R},
         "pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(t_dec * 1e6, 3),
         "encode_mkeys_per_s": round(n_keys_total / t_enc / 1e6, 1),
         "encode_gbs": round(enc_bytes / t_enc / 1e9, 2),
         "encode_us": round(t_enc * 1e6, 3),
         "encode_pct_hbm_peak": round(100 * enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS, 2),
-        "roofline": {"bound": "hbm", "kernel": "k_attn (fused decode attention)",
-                     "achieved": round(attn_gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(attn_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
-                     "kernel_us": round(t_attn * 1e6, 3),
-                     "algorithmic_bytes_per_launch": int(dec_bytes)},
+        "roofline": roofline,
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and args.config == 2:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

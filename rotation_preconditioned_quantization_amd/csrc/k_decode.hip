@@ -6,11 +6,11 @@
 //                <q, k^> = gamma <R q, u'^> and keys are never inverse-rotated);
 //                with QJL also p = sqrt(pi/2)/d * S q' ([YL] 可选的残差修正).
 //   k_logits     one wavefront per 64-key tile, one key per lane: unpack the
-//                word-major tile (coalesced), look up unit directions and rho
-//                centroids in LDS, dot with the G query heads of the KV head.
+//                word-major tile (coalesced), rebuild rho^ n^ per triplet from
+//                LDS tables, contract with 4 query heads on fp32 MFMA.
 //   k_attn       the same per-key logits, then a wave-wide online softmax and
-//                P.V over bf16 V with 16 lanes per V row (coalesced), split-K
-//                over the sequence; k_combine merges the splits (log-sum-exp).
+//                P.V over bf16 V (one coalesced row per load, fp32 MFMA),
+//                split-K over the sequence; k_combine merges the splits.
 //   k_reconstruct  test helper writing k^ = gamma R^T u'^.
 #include "octo_device.hpp"
 
@@ -83,247 +83,257 @@ __global__ __launch_bounds__(64) void k_rotate(RotateArgs a) {
   }
 }
 
-// Shared per-block setup: direction / rho tables and the QJL byte table.
-// lut[m][byte] holds, for the HP heads, sum_k (+1 if bit k of byte else -1) * p[8m+k].
-template <int D, int B, int HP, bool QJL>
-__device__ __forceinline__ void load_decode_tables(const DecodeArgs& a, int64_t seq, int g0,
-                                                   float4* s_dir, float* s_rho, float4* s_lut) {
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+// LDS of the single-query kernels.  kCombined: for up to 10 bits per triplet
+// one float4 per triplet code holds rho^ n^ directly; otherwise unit
+// directions per (i_xi, i_eta) plus the rho centroids.  q holds the rotated
+// queries of the (up to) 4 heads of this pass, rows padded with zeros.
+template <int D, int B, bool QJL>
+struct SQShared {
   using C = Codec<D, B>;
+  static constexpr bool kCombined = C::BT <= 10;
+  static constexpr int QD = ((3 * C::T + 3) / 4) * 4;
+  float4 tab[kCombined ? (1 << C::BT) : C::NDIR];
+  float rho[C::LR];
+  float q[4][QD];
+  float4 lut[QJL ? (D / 8) * 256 : 1];
+};
+
+// Fill the per-block tables.  QJL byte table: lut[m][byte] holds, per head,
+// sum_k (+1 if bit k of byte else -1) * p[8m + k] with p = sqrt(pi/2)/d S q'.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, int64_t seq, int g0, int hcount,
+                                               SQShared<D, B, QJL>& sh) {
+  using C = Codec<D, B>;
+  using SH = SQShared<D, B, QJL>;
+  constexpr int T = C::T;
   const int tid = threadIdx.x;
-  for (int i = tid; i < C::NDIR; i += blockDim.x) s_dir[i] = a.t.dirtab[i];
-  if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
+  if constexpr (SH::kCombined) {
+    for (int i = tid; i < (1 << C::BT); i += blockDim.x) sh.tab[i] = a.t.trip_tab[i];
+  } else {
+    for (int i = tid; i < C::NDIR; i += blockDim.x) sh.tab[i] = a.t.dirtab[i];
+  }
+  if (tid < C::LR) sh.rho[tid] = a.t.rho_tab[tid];
+  for (int e = tid; e < 4 * SH::QD; e += blockDim.x) {
+    const int h = e / SH::QD, j = e % SH::QD;
+    sh.q[h][j] = (h < hcount && j < 3 * T) ? a.qrot[(seq * a.G + g0 + h) * (3 * T) + j] : 0.f;
+  }
   if constexpr (QJL) {
     const float* p = a.qp + (seq * a.G + g0) * D;
     for (int e = tid; e < (D / 8) * 256; e += blockDim.x) {
       const int m = e >> 8, byte = e & 255;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int h = 0; h < HP; ++h) {
+      for (int h = 0; h < hcount; ++h) {
 #pragma unroll
         for (int k = 0; k < 8; ++k) {
           const float pv = p[h * D + 8 * m + k];
           acc[h] += ((byte >> k) & 1) ? pv : -pv;
         }
       }
-      s_lut[e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
+      sh.lut[e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
   }
 }
 
-// Logits of the lane's key for HP query heads: acc[h] = <q'_h, u'^> (+ QJL).
-template <int D, int B, int HP, bool QJL>
-__device__ __forceinline__ void key_logits(const DecodeArgs& a, cfloat* qr,
-                                           const float4* s_dir, const float* s_rho,
-                                           const float4* s_lut, int64_t seq, int64_t t, int lane,
-                                           float (&acc)[HP]) {
+// Logits of a 64-key tile, one key per lane, for 4 query heads at once:
+// returns acc[h] = <q'_h, u'^_key> (+ the QJL term).  The contraction over
+// the rotated dims runs on v_mfma_f32_4x4x1_16b_f32: in every 4-lane block
+// the A operand is q'[head = lane % 4][dim] and the B operand is the lane's
+// own rebuilt coordinate, so block b produces the 4 x 4 outer product for
+// keys 4b..4b+3 and lane l ends up holding the 4 heads of key l.  Exact fp32.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ floatx4 tile_logits(const DecodeArgs& a, const SQShared<D, B, QJL>& sh,
+                                               int64_t seq, int64_t t, int lane) {
   using C = Codec<D, B>;
+  using SH = SQShared<D, B, QJL>;
   constexpr int T = C::T, W = C::W;
-  constexpr int kTripletGroup = HP >= 4 ? 4 : 8;
+  constexpr int kGroup = 4;
   const int64_t tiles = a.cap / kTile;
   const uint32_t* src = a.packed + ((seq * tiles + t) * W) * kTile + lane;
   uint32_t words[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) words[w] = src[w * kTile];
+  const float* qrow = sh.q[lane & 3];
+  floatx4 acc[3];
 #pragma unroll
-  for (int h = 0; h < HP; ++h) acc[h] = 0.f;
+  for (int c = 0; c < 3; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
-    const float4 n = s_dir[code & C::DIR_MASK];
-    const float rh = s_rho[code >> (C::BX + C::BE)];
-    const float tx = rh * n.x, ty = rh * n.y, tz = rh * n.z;
-#pragma unroll
-    for (int h = 0; h < HP; ++h) {
-      cfloat* qh = qr + h * (3 * T) + 3 * i;
-      acc[h] = __builtin_fmaf(tx, qh[0], __builtin_fmaf(ty, qh[1], __builtin_fmaf(tz, qh[2], acc[h])));
+    float tv[3];
+    if constexpr (SH::kCombined) {
+      const float4 e = sh.tab[code];
+      tv[0] = e.x; tv[1] = e.y; tv[2] = e.z;
+    } else {
+      const float4 n = sh.tab[code & C::DIR_MASK];
+      const float rh = sh.rho[code >> (C::BX + C::BE)];
+      tv[0] = rh * n.x; tv[1] = rh * n.y; tv[2] = rh * n.z;
     }
-    // Issue the LDS gathers and scalar q' loads a few triplets at a time: the
-    // accumulators pass through an opaque asm with a memory clobber, so the
-    // next group's loads cannot be hoisted above this group's FMAs (bounded
-    // VGPR/SGPR live ranges instead of all 3T gathers in flight).
-    if (i % kTripletGroup == kTripletGroup - 1) {
 #pragma unroll
-      for (int h = 0; h < HP; ++h) asm volatile("" : "+v"(acc[h])::"memory");
+    for (int c = 0; c < 3; ++c)
+      acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[c], 0, 0, 0);
+    // a few triplets at a time: keeps the LDS gathers from all being hoisted
+    if (i % kGroup == kGroup - 1) {
+#pragma unroll
+      for (int c = 0; c < 3; ++c) asm volatile("" : "+v"(acc[c])::"memory");
     }
   }
+  floatx4 r = acc[0] + acc[1] + acc[2];
   if constexpr (QJL) {
     const uint32_t* sb = a.qjl_bits + ((seq * tiles + t) * (D / 32)) * kTile + lane;
     uint32_t sw[D / 32];
 #pragma unroll
     for (int w = 0; w < D / 32; ++w) sw[w] = sb[w * kTile];
     const float nu = __half2float(__ushort_as_half(a.qjl_norm[seq * a.cap + t * kTile + lane]));
-    float corr[4] = {0.f, 0.f, 0.f, 0.f};
+    float4 corr = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
     for (int m = 0; m < D / 8; ++m) {
       const uint32_t byte = (sw[m >> 2] >> (8 * (m & 3))) & 255u;
-      const float4 e = s_lut[(m << 8) + byte];
-      corr[0] += e.x;
-      if (HP > 1) corr[1] += e.y;
-      if (HP > 2) { corr[2] += e.z; corr[3] += e.w; }
+      const float4 e = sh.lut[(m << 8) + byte];
+      corr.x += e.x; corr.y += e.y; corr.z += e.z; corr.w += e.w;
     }
-#pragma unroll
-    for (int h = 0; h < HP; ++h) acc[h] = __builtin_fmaf(nu, corr[h], acc[h]);
+    r[0] = __builtin_fmaf(nu, corr.x, r[0]);
+    r[1] = __builtin_fmaf(nu, corr.y, r[1]);
+    r[2] = __builtin_fmaf(nu, corr.z, r[2]);
+    r[3] = __builtin_fmaf(nu, corr.w, r[3]);
   }
+  return r;
 }
 
 // ---------------------------------------------------------------------------
-// Logits.  grid = (blocks over key tiles, n_seq, G / HP); 4 waves per block.
+// Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 waves.
 // ---------------------------------------------------------------------------
-template <int D, int B, int HP, bool QJL>
+template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
-  using C = Codec<D, B>;
-  constexpr int T = C::T;
-  __shared__ float4 s_dir[C::NDIR];
-  __shared__ float s_rho[C::LR];
-  __shared__ float4 s_lut[QJL ? (D / 8) * 256 : 1];
+  __shared__ SQShared<D, B, QJL> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
-  const int g0 = blockIdx.z * HP;
-  load_decode_tables<D, B, HP, QJL>(a, seq, g0, s_dir, s_rho, s_lut);
+  const int g0 = blockIdx.z * 4;
+  const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
+  load_sq_tables<D, B, QJL>(a, seq, g0, hcount, sh);
   __syncthreads();
-  cfloat* qr = (cfloat*)(a.qrot + (seq * a.G + g0) * (3 * T));
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < ntile; t += (int64_t)gridDim.x * 4) {
-    // q' is read through the scalar cache every tile (SGPR operands), not
-    // hoisted into 3T*HP vector registers.
-    cfloat* qt = qr + opaque_zero();
-    float acc[HP];
-    key_logits<D, B, HP, QJL>(a, qt, s_dir, s_rho, s_lut, seq, t, lane, acc);
+    const floatx4 acc = tile_logits<D, B, QJL>(a, sh, seq, t, lane);
     const int64_t key = t * kTile + lane;
     if (key < a.n_keys) {
       const float gamma = a.gamma[seq * a.cap + key];
 #pragma unroll
-      for (int h = 0; h < HP; ++h) {
-        const int64_t hq = kvh * a.G + g0 + h;
-        a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = gamma * acc[h];
+      for (int h = 0; h < 4; ++h) {
+        if (h < hcount) {
+          const int64_t hq = kvh * a.G + g0 + h;
+          a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = gamma * acc[h];
+        }
       }
     }
   }
 }
 
 // ---------------------------------------------------------------------------
-// Single-query split-K attention.  grid = (n_split, n_seq, G / HP), 4 waves.
-// Partial (m, l, o) per (query head, split); m in log2 units.
+// Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4)), 4
+// waves per block, each wave a stream of 64-key tiles.  Per tile: logits by
+// tile_logits, a wave-wide online softmax per head (DPP max), then
+// O[head][dim] += p[head][key] V[key][dim] on v_mfma_f32_4x4x1_16b_f32: the
+// A operand is p[head = lane % 4][key], the B operand is one bf16 of the V
+// row the whole wave loads with one coalesced dword load, so lane l keeps
+// O[0..3][2l] and O[0..3][2l+1] (d = 128; for d = 64 the two half-waves take
+// alternate keys).  Partial (m, l, o) per (query head, split); m in log2 units.
 // ---------------------------------------------------------------------------
-template <int D, int B, int HP, bool QJL>
+template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
-  using C = Codec<D, B>;
-  constexpr int T = C::T;
-  constexpr int DPL = D / 16;             // V dims per lane (16 lanes per V row)
-  __shared__ float4 s_dir[C::NDIR];
-  __shared__ float s_rho[C::LR];
-  __shared__ float4 s_lut[QJL ? (D / 8) * 256 : 1];
-  __shared__ float s_p[4][kTile][HP];
-  __shared__ float s_ml[4][HP][2];
-  __shared__ float s_o[4][HP][D];
+  constexpr int KPI = 128 / D;          // keys per V load / PV MFMA
+  constexpr int NV = kTile / KPI;       // V loads per tile per lane
+  __shared__ SQShared<D, B, QJL> sh;
+  __shared__ float s_p[4][4][kTile];
+  __shared__ float s_ml[4][4][2];
+  __shared__ float s_o[4][4][D];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int gq = lane >> 4, li = lane & 15;
   const int64_t seq = blockIdx.y;
-  const int g0 = blockIdx.z * HP;
-  load_decode_tables<D, B, HP, QJL>(a, seq, g0, s_dir, s_rho, s_lut);
+  const int g0 = blockIdx.z * 4;
+  const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
+  load_sq_tables<D, B, QJL>(a, seq, g0, hcount, sh);
   __syncthreads();
 
-  cfloat* qr = (cfloat*)(a.qrot + (seq * a.G + g0) * (3 * T));
+  const int kk_off = KPI == 2 ? (lane >> 5) : 0;   // key of the pair this lane serves
+  const int dl = KPI == 2 ? (lane & 31) : lane;     // dims 2 dl, 2 dl + 1
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
-  const unsigned short* vbase = (const unsigned short*)a.v + seq * a.cap * D + li * DPL;
+  const uint32_t* vbase = (const uint32_t*)a.v + (seq * a.cap * D) / 2 + dl;
 
-  float m[HP], l[HP], o[HP][DPL];
+  float m[4], l[4];
+  floatx4 olo[2], ohi[2];
 #pragma unroll
-  for (int h = 0; h < HP; ++h) {
-    m[h] = -INFINITY;
-    l[h] = 0.f;
+  for (int h = 0; h < 4; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
 #pragma unroll
-    for (int c = 0; c < DPL; ++c) o[h][c] = 0.f;
-  }
+  for (int k = 0; k < 2; ++k) { olo[k] = floatx4{0.f, 0.f, 0.f, 0.f}; ohi[k] = olo[k]; }
 
   for (int64_t t = t_begin + wave; t < t_end; t += 4) {
-    // V rows of this tile: lane group gq takes keys 4*jj + gq.
-    uint32_t vraw[16][DPL / 2];
+    uint32_t vw[NV];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      const int64_t kv = t * kTile + 4 * jj + gq;
-      if (kv < a.n_keys) {
-        const unsigned short* src = vbase + kv * D;
-        if constexpr (DPL == 8) {
-          const uint4 u = *(const uint4*)src;
-          vraw[jj][0] = u.x; vraw[jj][1] = u.y; vraw[jj][2] = u.z; vraw[jj][3] = u.w;
-        } else {
-          const uint2 u = *(const uint2*)src;
-          vraw[jj][0] = u.x; vraw[jj][1] = u.y;
-        }
-      } else {
-#pragma unroll
-        for (int c = 0; c < DPL / 2; ++c) vraw[jj][c] = 0u;
-      }
+    for (int j = 0; j < NV; ++j) {
+      const int64_t kv = t * kTile + KPI * j + kk_off;
+      vw[j] = kv < a.n_keys ? vbase[(kv * D) / 2] : 0u;
     }
-    cfloat* qt = qr + opaque_zero();
-    float acc[HP];
-    key_logits<D, B, HP, QJL>(a, qt, s_dir, s_rho, s_lut, seq, t, lane, acc);
+    const floatx4 acc = tile_logits<D, B, QJL>(a, sh, seq, t, lane);
     const int64_t key = t * kTile + lane;
     const bool valid = key < a.n_keys;
     const float gamma = valid ? a.gamma[seq * a.cap + key] : 0.f;
+    float al[4];
 #pragma unroll
-    for (int h = 0; h < HP; ++h) {
+    for (int h = 0; h < 4; ++h) {
       const float sc = valid ? gamma * acc[h] : -INFINITY;
       const float mn = fmaxf(m[h], wave_max(sc));
-      const float alpha = exp2f(m[h] - mn);
+      al[h] = exp2f(m[h] - mn);
       const float p = exp2f(sc - mn);
-      l[h] = __builtin_fmaf(l[h], alpha, p);
-#pragma unroll
-      for (int c = 0; c < DPL; ++c) o[h][c] *= alpha;
+      l[h] = __builtin_fmaf(l[h], al[h], p);
       m[h] = mn;
-      s_p[wave][lane][h] = p;
+      s_p[wave][h][lane] = p;
     }
+#pragma unroll
+    for (int k = 0; k < 2; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) { olo[k][r] *= al[r]; ohi[k][r] *= al[r]; }
     __builtin_amdgcn_wave_barrier();
+    const float* prow = s_p[wave][lane & 3];
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      float pv[HP];
-#pragma unroll
-      for (int h = 0; h < HP; ++h) pv[h] = s_p[wave][4 * jj + gq][h];
-#pragma unroll
-      for (int c = 0; c < DPL / 2; ++c) {
-        const float v0 = bf16_lo(vraw[jj][c]), v1 = bf16_hi(vraw[jj][c]);
-#pragma unroll
-        for (int h = 0; h < HP; ++h) {
-          o[h][2 * c] = __builtin_fmaf(pv[h], v0, o[h][2 * c]);
-          o[h][2 * c + 1] = __builtin_fmaf(pv[h], v1, o[h][2 * c + 1]);
-        }
-      }
+    for (int j = 0; j < NV; ++j) {
+      const float pa = prow[KPI * j + kk_off];
+      olo[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_lo(vw[j]), olo[j & 1], 0, 0, 0);
+      ohi[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_hi(vw[j]), ohi[j & 1], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
   }
 
-  // Reduce inside the wave: l over all lanes, o over the 4 lane groups.
+  floatx4 olo_s = olo[0] + olo[1], ohi_s = ohi[0] + ohi[1];
+  if constexpr (KPI == 2) {
 #pragma unroll
-  for (int h = 0; h < HP; ++h) {
-    l[h] = wave_sum(l[h]);
-#pragma unroll
-    for (int c = 0; c < DPL; ++c) {
-      float x = o[h][c];
-      x += __shfl_xor(x, 16, 64);
-      x += __shfl_xor(x, 32, 64);
-      o[h][c] = x;
+    for (int r = 0; r < 4; ++r) {
+      olo_s[r] += __shfl_xor(olo_s[r], 32, 64);
+      ohi_s[r] += __shfl_xor(ohi_s[r], 32, 64);
     }
   }
-  if (lane < 16) {
 #pragma unroll
-    for (int h = 0; h < HP; ++h)
+  for (int h = 0; h < 4; ++h) l[h] = wave_sum(l[h]);
+  if (kk_off == 0) {
 #pragma unroll
-      for (int c = 0; c < DPL; ++c) s_o[wave][h][li * DPL + c] = o[h][c];
+    for (int h = 0; h < 4; ++h) {
+      s_o[wave][h][2 * dl] = olo_s[h];
+      s_o[wave][h][2 * dl + 1] = ohi_s[h];
+    }
   }
   if (lane == 0) {
 #pragma unroll
-    for (int h = 0; h < HP; ++h) { s_ml[wave][h][0] = m[h]; s_ml[wave][h][1] = l[h]; }
+    for (int h = 0; h < 4; ++h) { s_ml[wave][h][0] = m[h]; s_ml[wave][h][1] = l[h]; }
   }
   __syncthreads();
   // Merge the 4 waves and write this block's partial.
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
-  for (int e = threadIdx.x; e < HP * (D + 2); e += blockDim.x) {
+  for (int e = threadIdx.x; e < hcount * (D + 2); e += blockDim.x) {
     const int h = e / (D + 2), c = e % (D + 2);
     float M = -INFINITY;
 #pragma unroll
@@ -455,51 +465,38 @@ hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int D, int B, int HP, bool QJL>
+template <int D, int B, bool QJL>
 static hipError_t logits_t(const DecodeArgs& a, int64_t n_seq, int nbx, hipStream_t s) {
-  hipLaunchKernelGGL((k_logits<D, B, HP, QJL>), dim3(nbx, (unsigned)n_seq, a.G / HP), dim3(256), 0,
+  hipLaunchKernelGGL((k_logits<D, B, QJL>), dim3(nbx, (unsigned)n_seq, (a.G + 3) / 4), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }
 
-template <int D, int B, int HP, bool QJL>
+template <int D, int B, bool QJL>
 static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<D, B, HP, QJL>), dim3(a.n_split, (unsigned)n_seq, a.G / HP),
+  hipLaunchKernelGGL((k_attn<D, B, QJL>), dim3(a.n_split, (unsigned)n_seq, (a.G + 3) / 4),
                      dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
-#define OCTO_DISPATCH_DBHQ(FN, ...)                                                      \
-  switch (d * 100 + b * 10 + hp) {                                                       \
-    case 6421: return qjl ? FN<64, 2, 1, true>(__VA_ARGS__) : FN<64, 2, 1, false>(__VA_ARGS__);     \
-    case 6422: return qjl ? FN<64, 2, 2, true>(__VA_ARGS__) : FN<64, 2, 2, false>(__VA_ARGS__);     \
-    case 6424: return qjl ? FN<64, 2, 4, true>(__VA_ARGS__) : FN<64, 2, 4, false>(__VA_ARGS__);     \
-    case 6431: return qjl ? FN<64, 3, 1, true>(__VA_ARGS__) : FN<64, 3, 1, false>(__VA_ARGS__);     \
-    case 6432: return qjl ? FN<64, 3, 2, true>(__VA_ARGS__) : FN<64, 3, 2, false>(__VA_ARGS__);     \
-    case 6434: return qjl ? FN<64, 3, 4, true>(__VA_ARGS__) : FN<64, 3, 4, false>(__VA_ARGS__);     \
-    case 6441: return qjl ? FN<64, 4, 1, true>(__VA_ARGS__) : FN<64, 4, 1, false>(__VA_ARGS__);     \
-    case 6442: return qjl ? FN<64, 4, 2, true>(__VA_ARGS__) : FN<64, 4, 2, false>(__VA_ARGS__);     \
-    case 6444: return qjl ? FN<64, 4, 4, true>(__VA_ARGS__) : FN<64, 4, 4, false>(__VA_ARGS__);     \
-    case 12821: return qjl ? FN<128, 2, 1, true>(__VA_ARGS__) : FN<128, 2, 1, false>(__VA_ARGS__);  \
-    case 12822: return qjl ? FN<128, 2, 2, true>(__VA_ARGS__) : FN<128, 2, 2, false>(__VA_ARGS__);  \
-    case 12824: return qjl ? FN<128, 2, 4, true>(__VA_ARGS__) : FN<128, 2, 4, false>(__VA_ARGS__);  \
-    case 12831: return qjl ? FN<128, 3, 1, true>(__VA_ARGS__) : FN<128, 3, 1, false>(__VA_ARGS__);  \
-    case 12832: return qjl ? FN<128, 3, 2, true>(__VA_ARGS__) : FN<128, 3, 2, false>(__VA_ARGS__);  \
-    case 12834: return qjl ? FN<128, 3, 4, true>(__VA_ARGS__) : FN<128, 3, 4, false>(__VA_ARGS__);  \
-    case 12841: return qjl ? FN<128, 4, 1, true>(__VA_ARGS__) : FN<128, 4, 1, false>(__VA_ARGS__);  \
-    case 12842: return qjl ? FN<128, 4, 2, true>(__VA_ARGS__) : FN<128, 4, 2, false>(__VA_ARGS__);  \
-    case 12844: return qjl ? FN<128, 4, 4, true>(__VA_ARGS__) : FN<128, 4, 4, false>(__VA_ARGS__);  \
-  }                                                                                      \
+#define OCTO_DISPATCH_DBQ(FN, ...)                                                              \
+  switch (d * 10 + b) {                                                                         \
+    case 642: return qjl ? FN<64, 2, true>(__VA_ARGS__) : FN<64, 2, false>(__VA_ARGS__);        \
+    case 643: return qjl ? FN<64, 3, true>(__VA_ARGS__) : FN<64, 3, false>(__VA_ARGS__);        \
+    case 644: return qjl ? FN<64, 4, true>(__VA_ARGS__) : FN<64, 4, false>(__VA_ARGS__);        \
+    case 1282: return qjl ? FN<128, 2, true>(__VA_ARGS__) : FN<128, 2, false>(__VA_ARGS__);     \
+    case 1283: return qjl ? FN<128, 3, true>(__VA_ARGS__) : FN<128, 3, false>(__VA_ARGS__);     \
+    case 1284: return qjl ? FN<128, 4, true>(__VA_ARGS__) : FN<128, 4, false>(__VA_ARGS__);     \
+  }                                                                                             \
   return hipErrorInvalidValue;
 
-hipError_t launch_logits(int d, int b, int hp, bool qjl, const DecodeArgs& a, int64_t n_seq,
-                         int nbx, hipStream_t s) {
-  OCTO_DISPATCH_DBHQ(logits_t, a, n_seq, nbx, s)
+hipError_t launch_logits(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq, int nbx,
+                         hipStream_t s) {
+  OCTO_DISPATCH_DBQ(logits_t, a, n_seq, nbx, s)
 }
 
-hipError_t launch_attn(int d, int b, int hp, bool qjl, const DecodeArgs& a, int64_t n_seq,
-                       hipStream_t s) {
-  OCTO_DISPATCH_DBHQ(attn_t, a, n_seq, s)
+hipError_t launch_attn(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
+  OCTO_DISPATCH_DBQ(attn_t, a, n_seq, s)
 }
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {

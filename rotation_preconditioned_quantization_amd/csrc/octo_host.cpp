@@ -223,6 +223,20 @@ octo_status build_device_tables(octo_codebook* cb) {
       dir[o + 3] = 0.f;
     }
   std::vector<float> rho(cb->c_rho.begin(), cb->c_rho.end());
+  // rho^ n^ per full triplet code, for streams of at most 10 bits per triplet
+  std::vector<float> trip;
+  if (cb->bt <= 10) {
+    trip.resize(4 * ((size_t)1 << cb->bt));
+    for (int code = 0; code < (1 << cb->bt); ++code) {
+      const int ix = code & ((1 << cb->bx) - 1);
+      const int ie = (code >> cb->bx) & ((1 << cb->be) - 1);
+      const int ir = code >> (cb->bx + cb->be);
+      double v[3];
+      octa_decode(cb->c_xi[ix], cb->c_eta[ie], v);
+      for (int c = 0; c < 3; ++c) trip[4 * (size_t)code + c] = (float)(cb->c_rho[ir] * v[c]);
+      trip[4 * (size_t)code + 3] = 0.f;
+    }
+  }
 
   // One device allocation, 256-byte aligned regions.
   struct Region { const void* src; size_t bytes; size_t off; };
@@ -231,7 +245,8 @@ octo_status build_device_tables(octo_codebook* cb) {
       {qx.mid.data(), qx.mid.size() * 4, 0},     {qe.mid.data(), qe.mid.size() * 4, 0},
       {qr2.mid.data(), qr2.mid.size() * 4, 0},   {qx.lut.data(), qx.lut.size(), 0},
       {qe.lut.data(), qe.lut.size(), 0},         {qr2.lut.data(), qr2.lut.size(), 0},
-      {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0}};
+      {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0},
+      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0}};
   size_t total = 0;
   for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
   int prev = 0;
@@ -273,6 +288,7 @@ octo_status build_device_tables(octo_codebook* cb) {
   t.qe = qt(qe, 3, 6);
   t.qr2 = qt(qr2, 4, 7);
   t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[8].off);
+  t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[9].off);
   for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
   return OCTO_OK;
 }
@@ -299,7 +315,8 @@ octo_status hip_status(hipError_t e, const char* what) {
   return fail(OCTO_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-int heads_per_pass(int G) { return G % 4 == 0 ? 4 : (G % 2 == 0 ? 2 : 1); }
+// The single-query kernels handle up to 4 query heads of a KV head per pass.
+int head_passes(int G) { return (G + 3) / 4; }
 
 struct Split { int n_split, tiles_per_split; };
 
@@ -342,8 +359,7 @@ WsLayout ws_layout(const octo_codebook* cb, int mode, int B, int Hq, int Hkv, in
     off += align256(rows * (size_t)sp.n_split * (cb->d + 2) * sizeof(float));
   } else if (mode == 1) {
     const int G = Hkv > 0 ? Hq / Hkv : 1;
-    const int hp = heads_per_pass(std::max(G, 1));
-    const Split sp = attn_split(n_keys, (int64_t)B * Hkv, std::max(G, 1) / hp);
+    const Split sp = attn_split(n_keys, (int64_t)B * Hkv, head_passes(std::max(G, 1)));
     off += align256(rows * (size_t)sp.n_split * (cb->d + 2) * sizeof(float));
   }
   w.total = off;
@@ -642,7 +658,7 @@ octo_status octo_decode_logits_stages(const octo_codebook* cb, const void* q, oc
     if (st != OCTO_OK) return st;
   }
   if (!(stages & OCTO_STAGE_MAIN)) return OCTO_OK;
-  const int G = Hq / Hkv, hp = heads_per_pass(G);
+  const int G = Hq / Hkv;
   DecodeArgs a{};
   a.t = cb->tables;
   a.qrot = r.qrot;
@@ -659,10 +675,10 @@ octo_status octo_decode_logits_stages(const octo_codebook* cb, const void* q, oc
   a.logits = logits;
   const int64_t n_seq = (int64_t)B * Hkv;
   const int64_t ntile = (n_keys + kTile - 1) / kTile;
-  const int64_t rows = n_seq * (G / hp);
+  const int64_t rows = n_seq * head_passes(G);
   int64_t nbx = (2048 + rows - 1) / rows;
   nbx = std::max<int64_t>(1, std::min<int64_t>(nbx, (ntile + 3) / 4));
-  return hip_status(launch_logits(cb->d, cb->b, hp, qjl, a, n_seq, (int)nbx, s), "logits launch");
+  return hip_status(launch_logits(cb->d, cb->b, qjl, a, n_seq, (int)nbx, s), "logits launch");
 }
 
 octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
@@ -748,9 +764,8 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
     c.d = cb->d;
     return hip_status(launch_combine(c, s), "combine launch");
   }
-  const int hp = heads_per_pass(G);
   const int64_t n_seq = (int64_t)B * Hkv;
-  const Split sp = attn_split(n_keys, n_seq, G / hp);
+  const Split sp = attn_split(n_keys, n_seq, head_passes(G));
   DecodeArgs a{};
   a.t = cb->tables;
   a.qrot = r.qrot;
@@ -769,7 +784,7 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   a.n_split = sp.n_split;
   a.part = (float*)((char*)workspace + wl.part);
   if (stages & OCTO_STAGE_MAIN) {
-    st = hip_status(launch_attn(cb->d, cb->b, hp, qjl, a, n_seq, s), "attention launch");
+    st = hip_status(launch_attn(cb->d, cb->b, qjl, a, n_seq, s), "attention launch");
     if (st != OCTO_OK) return st;
   }
   if (!(stages & OCTO_STAGE_COMBINE)) return OCTO_OK;

@@ -29,6 +29,7 @@ struct QuantTable {
 struct DevTables {
   QuantTable qx, qe, qr2;   // xi, eta, rho^2 (squared midpoints)
   const float4* dirtab;     // 2^(b_xi+b_eta) unit directions, index i_xi | i_eta << b_xi
+  const float4* trip_tab;   // 2^B_t triplets rho^ n^ by full code (only for B_t <= 10)
   const float* rho_tab;     // 2^b_rho rho centroids
   const float* S;           // QJL matrix d x d row-major (nullptr without QJL)
   uint32_t sign_bits[4];    // bit j of the 128-bit mask set <=> WHT sign s_j = -1
@@ -102,10 +103,9 @@ struct MQArgs {
 hipError_t launch_encode(int d, int b, int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq,
                          hipStream_t s);
 hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s);
-hipError_t launch_logits(int d, int b, int hp, bool qjl, const DecodeArgs& a, int64_t n_seq,
+hipError_t launch_logits(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq,
                          int n_blocks_x, hipStream_t s);
-hipError_t launch_attn(int d, int b, int hp, bool qjl, const DecodeArgs& a, int64_t n_seq,
-                       hipStream_t s);
+hipError_t launch_attn(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s);
