@@ -2,9 +2,11 @@
 // the packed indices in registers, never written out; q.k, then online
 // softmax and P.V, FlashAttention-style tiling).
 //
-//   k_rotate     q' = mult * R q once per query ([YL] 旋转魔法: R orthogonal, so
-//                <q, k^> = gamma <R q, u'^> and keys are never inverse-rotated);
-//                with QJL also p = sqrt(pi/2)/d * S q' ([YL] 可选的残差修正).
+//   k_rotate     q' = mult * R q per query row ([YL] 旋转魔法: R orthogonal, so
+//                <q, k^> = gamma <R q, u'^> and keys are never inverse-rotated),
+//                for the multi-query kernel; the single-query kernels rotate
+//                their own heads in the prologue (with QJL also p = sqrt(pi/2)/d
+//                * S q', [YL] 可选的残差修正).
 //   k_logits     one wavefront per 64-key tile, one key per lane: unpack the
 //                word-major tile (coalesced), rebuild rho^ n^ per triplet from
 //                LDS tables, contract with 4 query heads on fp32 MFMA.
@@ -88,7 +90,8 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // LDS of the single-query kernels.  kCombined: for up to 10 bits per triplet
 // one float4 per triplet code holds rho^ n^ directly; otherwise unit
 // directions per (i_xi, i_eta) plus the rho centroids.  q holds the rotated
-// queries of the (up to) 4 heads of this pass, rows padded with zeros.
+// queries of the (up to) 4 heads of this pass, rows padded with zeros; with
+// QJL, qp holds p = sqrt(pi/2)/d S q' and lut its nibble sums.
 template <int D, int B, bool QJL>
 struct SQShared {
   using C = Codec<D, B>;
@@ -97,17 +100,78 @@ struct SQShared {
   float4 tab[kCombined ? (1 << C::BT) : C::NDIR];
   float rho[C::LR];
   float q[4][QD];
-  float4 lut[QJL ? (D / 8) * 256 : 1];
+  float qp[QJL ? 4 : 1][QJL ? D : 1];
+  float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
-// Fill the per-block tables.  QJL byte table: lut[m][byte] holds, per head,
-// sum_k (+1 if bit k of byte else -1) * p[8m + k] with p = sqrt(pi/2)/d S q'.
+// Query rotation in the block prologue: wave w rotates query head g0 + w of
+// the block's KV head (q' = mult * R q, R = d^-1/2 H diag(s)), lane l holding
+// elements l + 64 k; butterflies of stride < 64 pair lanes (shuffles).  With
+// QJL the wave also forms p = sqrt(pi/2)/d * S q'.
 template <int D, int B, bool QJL>
-__device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, int64_t seq, int g0, int hcount,
-                                               SQShared<D, B, QJL>& sh) {
+__device__ __forceinline__ void rotate_head(const DecodeArgs& a, int64_t seq, int g0, int hcount,
+                                            SQShared<D, B, QJL>& sh) {
+  using SH = SQShared<D, B, QJL>;
+  constexpr int NV = D / 64;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w >= hcount) {
+    for (int j = lane; j < SH::QD; j += 64) sh.q[w][j] = 0.f;
+    return;
+  }
+  const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
+  const int64_t r = bidx * a.Hq + kvh * a.G + g0 + w;
+  float x[NV];
+#pragma unroll
+  for (int k = 0; k < NV; ++k) {
+    const int j = lane + 64 * k;
+    float v;
+    if (a.qdt == DT_F32) {
+      v = ((const float*)a.q)[r * D + j];
+    } else {
+      const unsigned short u = ((const unsigned short*)a.q)[r * D + j];
+      v = a.qdt == DT_BF16 ? __uint_as_float((uint32_t)u << 16) : __half2float(__ushort_as_half(u));
+    }
+    if ((a.t.sign_bits[j >> 5] >> (j & 31)) & 1u) v = -v;
+    x[k] = v;
+  }
+#pragma unroll
+  for (int hh = 1; hh < 64; hh <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const float o = __shfl_xor(x[k], hh, 64);
+      x[k] = (lane & hh) ? (o - x[k]) : (x[k] + o);
+    }
+  }
+  if constexpr (NV == 2) {
+    const float a0 = x[0], a1 = x[1];
+    x[0] = a0 + a1;
+    x[1] = a0 - a1;
+  }
+  const float mult = a.mult * rsqrtf((float)D);
+#pragma unroll
+  for (int k = 0; k < NV; ++k) sh.q[w][lane + 64 * k] = x[k] * mult;
+  for (int j = D + lane; j < SH::QD; j += 64) sh.q[w][j] = 0.f;
+  if constexpr (QJL) {
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int j = lane + 64 * k;
+      const float* row = a.t.S + (int64_t)j * D;
+      float acc = 0.f;
+#pragma unroll 8
+      for (int c = 0; c < D; ++c) acc = __builtin_fmaf(row[c], sh.q[w][c], acc);
+      sh.qp[w][j] = acc * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+    }
+  }
+}
+
+// Tables of the block (after the rotation; needs a block barrier before the
+// QJL nibble table reads qp of all heads).
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, SQShared<D, B, QJL>& sh) {
   using C = Codec<D, B>;
   using SH = SQShared<D, B, QJL>;
-  constexpr int T = C::T;
   const int tid = threadIdx.x;
   if constexpr (SH::kCombined) {
     for (int i = tid; i < (1 << C::BT); i += blockDim.x) sh.tab[i] = a.t.trip_tab[i];
@@ -115,24 +179,55 @@ __device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, int64_t seq,
     for (int i = tid; i < C::NDIR; i += blockDim.x) sh.tab[i] = a.t.dirtab[i];
   }
   if (tid < C::LR) sh.rho[tid] = a.t.rho_tab[tid];
-  for (int e = tid; e < 4 * SH::QD; e += blockDim.x) {
-    const int h = e / SH::QD, j = e % SH::QD;
-    sh.q[h][j] = (h < hcount && j < 3 * T) ? a.qrot[(seq * a.G + g0 + h) * (3 * T) + j] : 0.f;
-  }
+}
+
+// QJL nibble table: lut[m][nib] holds, per head, sum_k (+1 if bit k of nib
+// else -1) * p[4m + k].
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void build_qjl_lut(int hcount, SQShared<D, B, QJL>& sh) {
   if constexpr (QJL) {
-    const float* p = a.qp + (seq * a.G + g0) * D;
-    for (int e = tid; e < (D / 8) * 256; e += blockDim.x) {
-      const int m = e >> 8, byte = e & 255;
+    for (int e = threadIdx.x; e < (D / 4) * 16; e += blockDim.x) {
+      const int m = e >> 4, nib = e & 15;
       float acc[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int h = 0; h < hcount; ++h) {
 #pragma unroll
-        for (int k = 0; k < 8; ++k) {
-          const float pv = p[h * D + 8 * m + k];
-          acc[h] += ((byte >> k) & 1) ? pv : -pv;
+      for (int h = 0; h < 4; ++h) {
+        if (h < hcount) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const float pv = sh.qp[h][4 * m + k];
+            acc[h] += ((nib >> k) & 1) ? pv : -pv;
+          }
         }
       }
       sh.lut[e] = make_float4(acc[0], acc[1], acc[2], acc[3]);
     }
+  }
+}
+
+// The compressed words of one 64-key tile, as loaded by one wavefront.
+template <int D, int B, bool QJL>
+struct KTile {
+  uint32_t words[Codec<D, B>::W];
+  uint32_t sw[QJL ? D / 32 : 1];
+  float gamma;
+  float nu;
+};
+
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void load_ktile(const DecodeArgs& a, int64_t seq, int64_t t, int lane,
+                                           KTile<D, B, QJL>& k) {
+  constexpr int W = Codec<D, B>::W;
+  const int64_t tiles = a.cap / kTile;
+  const uint32_t* src = a.packed + ((seq * tiles + t) * W) * kTile + lane;
+#pragma unroll
+  for (int w = 0; w < W; ++w) k.words[w] = src[w * kTile];
+  const int64_t key = t * kTile + lane;
+  k.gamma = key < a.n_keys ? a.gamma[seq * a.cap + key] : 0.f;
+  if constexpr (QJL) {
+    const uint32_t* sb = a.qjl_bits + ((seq * tiles + t) * (D / 32)) * kTile + lane;
+#pragma unroll
+    for (int w = 0; w < D / 32; ++w) k.sw[w] = sb[w * kTile];
+    k.nu = __half2float(__ushort_as_half(a.qjl_norm[seq * a.cap + key]));
   }
 }
 
@@ -143,24 +238,19 @@ __device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, int64_t seq,
 // own rebuilt coordinate, so block b produces the 4 x 4 outer product for
 // keys 4b..4b+3 and lane l ends up holding the 4 heads of key l.  Exact fp32.
 template <int D, int B, bool QJL>
-__device__ __forceinline__ floatx4 tile_logits(const DecodeArgs& a, const SQShared<D, B, QJL>& sh,
-                                               int64_t seq, int64_t t, int lane) {
+__device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
+                                               const KTile<D, B, QJL>& k, int lane) {
   using C = Codec<D, B>;
   using SH = SQShared<D, B, QJL>;
   constexpr int T = C::T, W = C::W;
   constexpr int kGroup = 4;
-  const int64_t tiles = a.cap / kTile;
-  const uint32_t* src = a.packed + ((seq * tiles + t) * W) * kTile + lane;
-  uint32_t words[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) words[w] = src[w * kTile];
   const float* qrow = sh.q[lane & 3];
   floatx4 acc[3];
 #pragma unroll
   for (int c = 0; c < 3; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
+    const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
     float tv[3];
     if constexpr (SH::kCombined) {
       const float4 e = sh.tab[code];
@@ -174,35 +264,41 @@ __device__ __forceinline__ floatx4 tile_logits(const DecodeArgs& a, const SQShar
     for (int c = 0; c < 3; ++c)
       acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[c], 0, 0, 0);
     // a few triplets at a time: keeps the LDS gathers from all being hoisted
-    if (i % kGroup == kGroup - 1) {
-#pragma unroll
-      for (int c = 0; c < 3; ++c) asm volatile("" : "+v"(acc[c])::"memory");
-    }
+    if (i % kGroup == kGroup - 1) asm volatile("" ::: "memory");
   }
   floatx4 r = acc[0] + acc[1] + acc[2];
   if constexpr (QJL) {
-    const uint32_t* sb = a.qjl_bits + ((seq * tiles + t) * (D / 32)) * kTile + lane;
-    uint32_t sw[D / 32];
-#pragma unroll
-    for (int w = 0; w < D / 32; ++w) sw[w] = sb[w * kTile];
-    const float nu = __half2float(__ushort_as_half(a.qjl_norm[seq * a.cap + t * kTile + lane]));
     float4 corr = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
-    for (int m = 0; m < D / 8; ++m) {
-      const uint32_t byte = (sw[m >> 2] >> (8 * (m & 3))) & 255u;
-      const float4 e = sh.lut[(m << 8) + byte];
+    for (int m = 0; m < D / 4; ++m) {
+      const uint32_t nib = (k.sw[m >> 3] >> (4 * (m & 7))) & 15u;
+      const float4 e = sh.lut[(m << 4) + nib];
       corr.x += e.x; corr.y += e.y; corr.z += e.z; corr.w += e.w;
     }
-    r[0] = __builtin_fmaf(nu, corr.x, r[0]);
-    r[1] = __builtin_fmaf(nu, corr.y, r[1]);
-    r[2] = __builtin_fmaf(nu, corr.z, r[2]);
-    r[3] = __builtin_fmaf(nu, corr.w, r[3]);
+    r[0] = __builtin_fmaf(k.nu, corr.x, r[0]);
+    r[1] = __builtin_fmaf(k.nu, corr.y, r[1]);
+    r[2] = __builtin_fmaf(k.nu, corr.z, r[2]);
+    r[3] = __builtin_fmaf(k.nu, corr.w, r[3]);
   }
   return r;
 }
 
+// Prologue shared by both single-query kernels: rotation, tables, barrier.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void sq_prologue(const DecodeArgs& a, int64_t seq, int g0, int hcount,
+                                            SQShared<D, B, QJL>& sh) {
+  rotate_head<D, B, QJL>(a, seq, g0, hcount, sh);
+  load_sq_tables<D, B, QJL>(a, sh);
+  __syncthreads();
+  if constexpr (QJL) {
+    build_qjl_lut<D, B, QJL>(hcount, sh);
+    __syncthreads();
+  }
+}
+
 // ---------------------------------------------------------------------------
-// Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 waves.
+// Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 waves, each
+// a stream of 64-key tiles with the next tile's words loaded ahead.
 // ---------------------------------------------------------------------------
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
@@ -211,42 +307,69 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
   const int64_t seq = blockIdx.y;
   const int g0 = blockIdx.z * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
-  load_sq_tables<D, B, QJL>(a, seq, g0, hcount, sh);
-  __syncthreads();
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
+  const int64_t stride = (int64_t)gridDim.x * 4;
+  int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  KTile<D, B, QJL> cur;
+  if (t < ntile) load_ktile<D, B, QJL>(a, seq, t, lane, cur);
+  sq_prologue<D, B, QJL>(a, seq, g0, hcount, sh);
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
-  for (int64_t t = (int64_t)blockIdx.x * 4 + wave; t < ntile; t += (int64_t)gridDim.x * 4) {
-    const floatx4 acc = tile_logits<D, B, QJL>(a, sh, seq, t, lane);
+  for (; t < ntile; t += stride) {
+    KTile<D, B, QJL> nxt;
+    if (t + stride < ntile) load_ktile<D, B, QJL>(a, seq, t + stride, lane, nxt);
+    const floatx4 acc = tile_logits<D, B, QJL>(sh, cur, lane);
     const int64_t key = t * kTile + lane;
     if (key < a.n_keys) {
-      const float gamma = a.gamma[seq * a.cap + key];
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if (h < hcount) {
           const int64_t hq = kvh * a.G + g0 + h;
-          a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = gamma * acc[h];
+          a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = cur.gamma * acc[h];
         }
       }
     }
+    cur = nxt;
   }
 }
 
 // ---------------------------------------------------------------------------
 // Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4)), 4
-// waves per block, each wave a stream of 64-key tiles.  Per tile: logits by
-// tile_logits, a wave-wide online softmax per head (DPP max), then
-// O[head][dim] += p[head][key] V[key][dim] on v_mfma_f32_4x4x1_16b_f32: the
-// A operand is p[head = lane % 4][key], the B operand is one bf16 of the V
-// row the whole wave loads with one coalesced dword load, so lane l keeps
-// O[0..3][2l] and O[0..3][2l+1] (d = 128; for d = 64 the two half-waves take
-// alternate keys).  Partial (m, l, o) per (query head, split); m in log2 units.
+// waves per block, each wave a stream of 64-key tiles whose next tile (V rows
+// and compressed words) is loaded while the current one is computed.  Per
+// tile: logits by tile_logits, a wave-wide online softmax per head (DPP
+// max), then O[head][dim] += p[head][key] V[key][dim] on
+// v_mfma_f32_4x4x1_16b_f32: the A operand is p[head = lane % 4][key], the B
+// operand one bf16 of the V row the whole wave reads with one coalesced dword
+// load, so lane l keeps O[0..3][2l] and O[0..3][2l+1] (d = 128; for d = 64
+// the two half-waves take alternate keys).  Partial (m, l, o) per (query
+// head, split); m in log2 units.
 // ---------------------------------------------------------------------------
+// The V rows of a 64-key tile as the PV MFMA wants them: lane l takes the
+// dword (bf16 pair 2 dl, 2 dl + 1) of keys KPI * j + kk_off.  Full tiles
+// use constant offsets from one base; the last partial tile checks each key.
+template <int D, int NV, int KPI>
+__device__ __forceinline__ void load_vtile(const uint32_t* vbase, int64_t t, int64_t n_keys,
+                                           int kk_off, uint32_t (&vw)[NV]) {
+  constexpr int ROWW = D / 2;  // dwords per V row
+  const uint32_t* vt = vbase + (t * kTile + kk_off) * ROWW;
+  if ((t + 1) * kTile <= n_keys) {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) vw[j] = vt[j * KPI * ROWW];
+  } else {
+#pragma unroll
+    for (int j = 0; j < NV; ++j) {
+      const int64_t kv = t * kTile + KPI * j + kk_off;
+      vw[j] = kv < n_keys ? vt[j * KPI * ROWW] : 0u;
+    }
+  }
+}
+
 template <int D, int B, bool QJL>
-__global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(DecodeArgs a) {
   constexpr int KPI = 128 / D;          // keys per V load / PV MFMA
   constexpr int NV = kTile / KPI;       // V loads per tile per lane
   __shared__ SQShared<D, B, QJL> sh;
-  __shared__ float s_p[4][4][kTile];
+  __shared__ float s_p[4][4][kTile + 4];   // padded rows: the 4 heads hit different banks
   __shared__ float s_ml[4][4][2];
   __shared__ float s_o[4][4][D];
 
@@ -254,16 +377,23 @@ __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
   const int64_t seq = blockIdx.y;
   const int g0 = blockIdx.z * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
-  load_sq_tables<D, B, QJL>(a, seq, g0, hcount, sh);
-  __syncthreads();
-
   const int kk_off = KPI == 2 ? (lane >> 5) : 0;   // key of the pair this lane serves
   const int dl = KPI == 2 ? (lane & 31) : lane;     // dims 2 dl, 2 dl + 1
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
-  const uint32_t* vbase = (const uint32_t*)a.v + (seq * a.cap * D) / 2 + dl;
+  const uint32_t* vbase = (const uint32_t*)a.v + (seq * a.cap * D) / 2 + dl;  // lane's dword column
+
+  // first tile's loads go out before the prologue
+  int64_t t = t_begin + wave;
+  KTile<D, B, QJL> cur;
+  uint32_t vw[NV];
+  if (t < t_end) {
+    load_vtile<D, NV, KPI>(vbase, t, a.n_keys, kk_off, vw);
+    load_ktile<D, B, QJL>(a, seq, t, lane, cur);
+  }
+  sq_prologue<D, B, QJL>(a, seq, g0, hcount, sh);
 
   float m[4], l[4];
   floatx4 olo[2], ohi[2];
@@ -272,24 +402,18 @@ __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
 #pragma unroll
   for (int k = 0; k < 2; ++k) { olo[k] = floatx4{0.f, 0.f, 0.f, 0.f}; ohi[k] = olo[k]; }
 
-  for (int64_t t = t_begin + wave; t < t_end; t += 4) {
-    uint32_t vw[NV];
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t kv = t * kTile + KPI * j + kk_off;
-      vw[j] = kv < a.n_keys ? vbase[(kv * D) / 2] : 0u;
-    }
-    const floatx4 acc = tile_logits<D, B, QJL>(a, sh, seq, t, lane);
-    const int64_t key = t * kTile + lane;
+  // One tile: logits, online softmax per head, P.V.
+  auto process = [&](const KTile<D, B, QJL>& kt, const uint32_t (&vv)[NV], int64_t tt) {
+    const floatx4 acc = tile_logits<D, B, QJL>(sh, kt, lane);
+    const int64_t key = tt * kTile + lane;
     const bool valid = key < a.n_keys;
-    const float gamma = valid ? a.gamma[seq * a.cap + key] : 0.f;
     float al[4];
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float sc = valid ? gamma * acc[h] : -INFINITY;
+      const float sc = valid ? kt.gamma * acc[h] : -INFINITY;
       const float mn = fmaxf(m[h], wave_max(sc));
-      al[h] = exp2f(m[h] - mn);
-      const float p = exp2f(sc - mn);
+      al[h] = __builtin_amdgcn_exp2f(m[h] - mn);
+      const float p = __builtin_amdgcn_exp2f(sc - mn);
       l[h] = __builtin_fmaf(l[h], al[h], p);
       m[h] = mn;
       s_p[wave][h][lane] = p;
@@ -303,10 +427,27 @@ __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
 #pragma unroll
     for (int j = 0; j < NV; ++j) {
       const float pa = prow[KPI * j + kk_off];
-      olo[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_lo(vw[j]), olo[j & 1], 0, 0, 0);
-      ohi[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_hi(vw[j]), ohi[j & 1], 0, 0, 0);
+      olo[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_lo(vv[j]), olo[j & 1], 0, 0, 0);
+      ohi[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_hi(vv[j]), ohi[j & 1], 0, 0, 0);
     }
     __builtin_amdgcn_wave_barrier();
+  };
+
+  // Two register sets, used alternately: the next tile loads while one computes.
+  KTile<D, B, QJL> kb;
+  uint32_t vb[NV];
+  for (; t < t_end; t += 8) {
+    if (t + 4 < t_end) {
+      load_vtile<D, NV, KPI>(vbase, t + 4, a.n_keys, kk_off, vb);
+      load_ktile<D, B, QJL>(a, seq, t + 4, lane, kb);
+    }
+    process(cur, vw, t);
+    if (t + 4 >= t_end) break;
+    if (t + 8 < t_end) {
+      load_vtile<D, NV, KPI>(vbase, t + 8, a.n_keys, kk_off, vw);
+      load_ktile<D, B, QJL>(a, seq, t + 8, lane, cur);
+    }
+    process(kb, vb, t + 4);
   }
 
   floatx4 olo_s = olo[0] + olo[1], ohi_s = ohi[0] + ohi[1];
@@ -355,25 +496,38 @@ __global__ __launch_bounds__(256) void k_attn(DecodeArgs a) {
 }
 
 // out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s, one block per
-// row.  The split weights are formed once in LDS; every thread then sums an
-// independent strided slice of the splits for its output column, so the
-// partial loads are issued back to back instead of one latency at a time.
+// row.  The o values of the first splits are loaded before anything else so
+// they travel together with the (m, l) loads; the split weights are formed
+// once in LDS; thread (c, part) sums the splits part, part + P, ... of column
+// c and the P partial sums meet in LDS.
 constexpr int kCombineThreads = 256;
 constexpr int kMaxSplit = 1024;
+constexpr int kCombinePre = 32;
 
 __global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
   __shared__ float s_w[kMaxSplit];
+  __shared__ float s_l[kMaxSplit];
   __shared__ float s_red[kCombineThreads];
   const int64_t row = blockIdx.x;
   const int tid = threadIdx.x;
   const int ns = a.n_split, stride = a.d + 2;
+  const int P = kCombineThreads / a.d;
+  const int c = tid % a.d, part = tid / a.d;
+  const bool worker = part < P;
   const float* p = a.part + row * ns * stride;
-  float mloc = -INFINITY;
-  for (int s = tid; s < ns; s += kCombineThreads) {
-    const float m = p[s * stride];
-    s_w[s] = m;
-    mloc = fmaxf(mloc, m);
+  float pre[kCombinePre];
+#pragma unroll
+  for (int k = 0; k < kCombinePre; ++k) {
+    const int s = part + P * k;
+    pre[k] = (worker && s < ns) ? p[s * stride + 2 + c] : 0.f;
   }
+  for (int s = tid; s < ns; s += kCombineThreads) {
+    s_w[s] = p[s * stride];
+    s_l[s] = p[s * stride + 1];
+  }
+  __syncthreads();
+  float mloc = -INFINITY;
+  for (int s = tid; s < ns; s += kCombineThreads) mloc = fmaxf(mloc, s_w[s]);
   s_red[tid] = mloc;
   __syncthreads();
   for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
@@ -387,7 +541,7 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
     const float m = s_w[s];
     const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
     s_w[s] = w;
-    lden = __builtin_fmaf(w, p[s * stride + 1], lden);
+    lden = __builtin_fmaf(w, s_l[s], lden);
   }
   s_red[tid] = lden;
   __syncthreads();
@@ -397,19 +551,20 @@ __global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
   }
   const float den = s_red[0];
   __syncthreads();
-  // kCombineThreads / d threads per output column, each over a slice of splits
-  const int per_col = kCombineThreads / a.d;
-  const int c = tid % a.d, part = tid / a.d;
   float num = 0.f;
-  if (part < per_col) {
-#pragma unroll 4
-    for (int s = part; s < ns; s += per_col) num = __builtin_fmaf(s_w[s], p[s * stride + 2 + c], num);
+  if (worker) {
+#pragma unroll
+    for (int k = 0; k < kCombinePre; ++k) {
+      const int s = part + P * k;
+      if (s < ns) num = __builtin_fmaf(s_w[s], pre[k], num);
+    }
+    for (int s = part + P * kCombinePre; s < ns; s += P) num = __builtin_fmaf(s_w[s], p[s * stride + 2 + c], num);
   }
   s_red[tid] = num;
   __syncthreads();
   if (tid < a.d) {
     float tot = 0.f;
-    for (int k = 0; k < per_col; ++k) tot += s_red[k * a.d + tid];
+    for (int k = 0; k < P; ++k) tot += s_red[k * a.d + tid];
     a.out[row * a.d + tid] = den > 0.f ? tot / den : 0.f;
   }
 }

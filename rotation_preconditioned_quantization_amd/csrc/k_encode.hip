@@ -6,35 +6,157 @@
 //   ([YL] 旋转魔法 / 工程实现), triplets t_i of the zero-padded y, rho_i^2 =
 //   |t_i|^2/|y|^2, octahedral (xi, eta) of t_i ([YL] 八面体折叠), Lloyd-Max
 //   nearest-centroid indices from bucketed LDS tables, bit-pack, store.
-// The key tile is staged through LDS so that HBM reads are coalesced 16-byte
-// loads; packed words are stored word-major per tile (256 contiguous bytes per
+// The key tile is read with coalesced 16-byte loads and handed to the lanes
+// through LDS in two halves (small LDS footprint, several waves per SIMD);
+// packed words are stored word-major per tile (256 contiguous bytes per
 // store instruction).  With QJL the same lane also forms the rotated residual
 // r' = u' - u'^, its fp16 norm and the signs of S r' ([YL] 可选的残差修正).
 #include "octo_device.hpp"
 
 namespace octo {
 
-// y = H (s .* k * 2^-sexp) for the lane's staged key row, and the energies
-// of its zero-padded triplets.
+// Stage the key rows [r0, r0 + NR) of the wave's 64-key tile into LDS with
+// coalesced 16-byte loads (consecutive lanes read consecutive chunks).  The
+// WHT sign flips are applied here, on the raw chunk bits: every lane always
+// handles the same chunk column, so one 16-byte mask per lane does it.
 template <int D, int KT>
-__device__ __forceinline__ void rotate_energy(const unsigned char* row, int sexp,
-                                              const uint32_t (&sign_bits)[4], float (&v)[D],
-                                              float (&e)[(D + 2) / 3], float& tot) {
-  constexpr int T = (D + 2) / 3;
-  constexpr int VPC = 16 / DtSize<KT>::v;
+struct Stage {
+  static constexpr int ES = DtSize<KT>::v;
+  static constexpr int ROWB = D * ES;       // bytes per key row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int PITCH = ROWB + 16;   // padded pitch: conflict-free row reads
+  static constexpr int VPC = 16 / ES;       // values per chunk
+  static constexpr int NR = 32;             // rows staged per phase
+  static constexpr int PER_LANE = NR * CPR / 64;
+};
+
+// Sign mask of the chunk a lane stages: sign bit of every element whose WHT
+// sign is -1 (bit 15 of a 16-bit element, bit 31 of an fp32 one).
+template <int D, int KT>
+__device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[4], int col) {
+  using S = Stage<D, KT>;
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
-  for (int c = 0; c < D / VPC; ++c) {
-    const uint4 w = *(const uint4*)(row + c * 16);
-    cvt_chunk<KT>(w, &v[c * VPC]);
+  for (int e = 0; e < S::VPC; ++e) {
+    const int j = col * S::VPC + e;
+    const uint32_t bit = (sign_bits[j >> 5] >> (j & 31)) & 1u;
+    if constexpr (S::ES == 2) m[e >> 1] |= bit << (16 * (e & 1) + 15);
+    else m[e] |= bit << 31;
   }
-  if (sexp != 0) {
+  return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+// Bring the lane's own key row (already sign-flipped, raw bits) into
+// registers: coalesced 16-byte global loads of the whole tile, then two
+// rounds through a half-tile LDS buffer (rows 0..31, then 32..63).
+template <int D, int KT>
+__device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                           unsigned char* s_keys, const uint4& smask,
+                                           uint4 (&rowbits)[Stage<D, KT>::CPR]) {
+  using S = Stage<D, KT>;
+  const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
+  const int col = lane % S::CPR;
+  uint4 raw[2][S::PER_LANE];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int k = 0; k < S::PER_LANE; ++k) {
+      const int f = lane + 64 * k;
+      const int64_t j = j0 + h * S::NR + f / S::CPR;
+      raw[h][k] = make_uint4(0, 0, 0, 0);
+      if (j < a.n_new) raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + col * 16);
+    }
+  }
+  const int my_half = lane / S::NR;
+  const unsigned char* row = s_keys + (lane % S::NR) * S::PITCH;
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+#pragma unroll
+    for (int k = 0; k < S::PER_LANE; ++k) {
+      const int f = lane + 64 * k;
+      uint4 u = raw[h][k];
+      u.x ^= smask.x; u.y ^= smask.y; u.z ^= smask.z; u.w ^= smask.w;
+      *(uint4*)(s_keys + (f / S::CPR) * S::PITCH + col * 16) = u;
+    }
+    __syncthreads();
+    if (my_half == h) {
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) rowbits[c] = *(const uint4*)(row + c * 16);
+    }
+    __syncthreads();
+  }
+}
+
+// #{k : x > m_k} by the window rule (see WindowTable).
+__device__ __forceinline__ int quant_window(float x, const float* w, float half_levels, float lm1) {
+  const float f = __builtin_amdgcn_fmed3f((x + 1.0f) * half_levels, 0.0f, lm1);
+  const int b = (int)f;
+  return b - 1 + (x > w[b] ? 1 : 0) + (x > w[b + 1] ? 1 : 0);
+}
+
+template <int D, int B, int KT, bool QJL>
+__global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
+  using C = Codec<D, B>;
+  using S = Stage<D, KT>;
+  constexpr int T = C::T, W = C::W;
+
+  __shared__ __align__(16) unsigned char s_keys[S::NR * S::PITCH];
+  __shared__ float s_wx[C::LX + 1], s_we[C::LE + 1];
+
+  const int lane = threadIdx.x;
+  const int64_t seq = blockIdx.y;
+  const int64_t j0 = (int64_t)blockIdx.x * kTile;
+
+  if (lane < C::LX + 1) s_wx[lane] = a.t.wx.w[lane];
+  if (lane < C::LE + 1) s_we[lane] = a.t.we.w[lane];
+  const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
+  float v[D];
+  {
+    uint4 rowbits[S::CPR];
+    gather_row<D, KT>(a, seq, j0, lane, s_keys, smask, rowbits);
+    if constexpr (KT == DT_F32) {
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
+    } else {
+      // stride-1 butterflies straight from the packed 16-bit pairs
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) {
+        const uint32_t wd[4] = {rowbits[c].x, rowbits[c].y, rowbits[c].z, rowbits[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) stage1_pair<KT>(wd[k], v[8 * c + 2 * k], v[8 * c + 2 * k + 1]);
+      }
+    }
+  }
+  // Keys with entries far from 1 in magnitude are scaled by an exact power of
+  // two (changes no ratio) so that no triplet energy under- or overflows.
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < D; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+  int ex = 0;
+  __builtin_frexpf(amax, &ex);
+  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+  if (__any(sexp != 0)) {
     const float scale = __builtin_ldexpf(1.0f, -sexp);
 #pragma unroll
     for (int j = 0; j < D; ++j) v[j] *= scale;
   }
-  apply_signs<D>(v, sign_bits);
-  wht_regs<D>(v);
-  tot = 0.f;
+  if constexpr (KT == DT_F32) wht_regs<D>(v);
+  else wht_regs_from<D, 2>(v);
+
+  const float hx = 0.5f * C::LX, lx = (float)(C::LX - 1);
+  const float he = 0.5f * C::LE, le = (float)(C::LE - 1);
+  uint32_t words[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) words[w] = 0u;
+  uint32_t codes[QJL ? T : 1];
+  float e[T];
+  float tot = 0.f;
+
+  // Pass 1: triplet energies and the octahedral (xi, eta) indices by the
+  // window rule, packed into place.  p = (x, y)/l1; in the lower hemisphere
+  // (z < 0) the fold (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (and
+  // likewise for y), with sgn(0) = +1.  A zero triplet maps to (0, 0), i.e.
+  // n = (0, 0, 1).
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const float x = v[3 * i];
@@ -42,107 +164,32 @@ __device__ __forceinline__ void rotate_energy(const unsigned char* row, int sexp
     const float z = (3 * i + 2 < D) ? v[3 * i + 2] : 0.f;
     e[i] = __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x));
     tot += e[i];
-  }
-}
-
-template <int D, int B, int KT, bool QJL>
-__global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
-  using C = Codec<D, B>;
-  constexpr int T = C::T, W = C::W;
-  constexpr int ES = DtSize<KT>::v;
-  constexpr int ROWB = D * ES;            // bytes per key row
-  constexpr int CPR = ROWB / 16;          // 16-byte chunks per row
-  constexpr int PITCH = ROWB + 16;        // padded LDS row pitch: conflict-free row reads
-  constexpr int VPC = 16 / ES;            // values per chunk
-
-  __shared__ __align__(16) unsigned char s_keys[64 * PITCH];
-  __shared__ float s_midx[C::LX + 1], s_mide[C::LE + 1], s_midr[C::LR + 1];
-  __shared__ uint8_t s_lutx[kMaxLut], s_lute[kMaxLut], s_lutr[kMaxLut];
-
-  const int lane = threadIdx.x;
-  const int64_t seq = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * kTile;
-
-  for (int i = lane; i < a.t.qx.nb; i += 64) s_lutx[i] = a.t.qx.lut[i];
-  for (int i = lane; i < a.t.qe.nb; i += 64) s_lute[i] = a.t.qe.lut[i];
-  for (int i = lane; i < a.t.qr2.nb; i += 64) s_lutr[i] = a.t.qr2.lut[i];
-  if (lane < C::LX + 1) s_midx[lane] = a.t.qx.mid[lane];
-  if (lane < C::LE + 1) s_mide[lane] = a.t.qe.mid[lane];
-  if (lane < C::LR + 1) s_midr[lane] = a.t.qr2.mid[lane];
-
-  // Stage the 64 key rows: consecutive lanes read consecutive 16-byte chunks.
-  const unsigned char* kbase =
-      (const unsigned char*)a.keys + (seq * a.seq_stride) * ES;
-#pragma unroll 4
-  for (int f = lane; f < 64 * CPR; f += 64) {
-    const int r = f / CPR, c = f % CPR;
-    const int64_t j = j0 + r;
-    uint4 val = make_uint4(0, 0, 0, 0);
-    if (j < a.n_new) val = *(const uint4*)(kbase + (j * a.key_stride) * ES + c * 16);
-    *(uint4*)(s_keys + r * PITCH + c * 16) = val;
-  }
-  __syncthreads();
-
-  // Rotate and take triplet energies; |y|^2 = D |k|^2.  Keys whose energy
-  // would under- or overflow fp32 (norms far from 1, rare) are redone scaled
-  // by an exact power of two, which changes no ratio.
-  float v[D];
-  float e[T];
-  float tot = 0.f;
-  int sexp = 0;
-  const unsigned char* row = s_keys + lane * PITCH;
-  rotate_energy<D, KT>(row, 0, a.t.sign_bits, v, e, tot);
-  const bool redo = !(tot >= 0x1p-100f && tot <= 0x1p+100f);
-  if (__any(redo)) {
-    asm volatile("" ::: "memory");  // reload the row from LDS; keep no raw copy live
-    if (redo) {
-      float amax = 0.f;
-#pragma unroll
-      for (int c = 0; c < CPR; ++c) {
-        float f[VPC];
-        cvt_chunk<KT>(*(const uint4*)(row + c * 16), f);
-#pragma unroll
-        for (int k = 0; k < VPC; ++k) amax = __builtin_fmaxf(amax, __builtin_fabsf(f[k]));
-      }
-      int ex = 0;
-      __builtin_frexpf(amax, &ex);   // amax = m * 2^ex, m in [0.5, 1)
-      sexp = amax > 0.f ? ex : 0;
-      rotate_energy<D, KT>(row, sexp, a.t.sign_bits, v, e, tot);
-    }
+    const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
+    const float il = __builtin_amdgcn_rcpf(__builtin_fmaxf(l1, 1e-37f));
+    const float px = x * il, py = y * il;
+    const float tz = __builtin_fmaxf(-z, 0.0f) * il;
+    const float xi = px + (px >= 0.f ? tz : -tz);
+    const float eta = py + (py >= 0.f ? tz : -tz);
+    const int ix = quant_window(xi, s_wx, hx, lx);
+    const int ie = quant_window(eta, s_we, he, le);
+    const uint32_t code = (uint32_t)ix | ((uint32_t)ie << C::BX);
+    if constexpr (QJL) codes[i] = code;
+    const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
+    words[wi] |= code << off;
+    if (off + C::BT > 32) words[wi + 1] |= code >> (32 - off);
   }
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
   const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
 
-  const float lox = a.t.qx.lo, iwx = a.t.qx.inv_w, nbx = (float)(a.t.qx.nb - 1);
-  const float loe = a.t.qe.lo, iwe = a.t.qe.inv_w, nbe = (float)(a.t.qe.nb - 1);
-  const float lor = a.t.qr2.lo, iwr = a.t.qr2.inv_w, nbr = (float)(a.t.qr2.nb - 1);
-
-  uint32_t words[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) words[w] = 0u;
-  uint32_t codes[QJL ? T : 1];
-
-  // Pass 2: quantise and pack.
+  // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const float x = v[3 * i];
-    const float y = (3 * i + 1 < D) ? v[3 * i + 1] : 0.f;
-    const float z = (3 * i + 2 < D) ? v[3 * i + 2] : 0.f;
-    const int ir = quant_lookup(e[i] * inv_tot, s_lutr, s_midr, lor, iwr, nbr);
-    const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
-    const float il = l1 > 0.f ? __builtin_amdgcn_rcpf(l1) : 0.f;
-    const float px = x * il, py = y * il;
-    float xi = px, eta = py;
-    if (z < 0.f) {  // fold the lower hemisphere onto the square's corners; sgn(0) = +1
-      const float fx = 1.0f - __builtin_fabsf(py);
-      const float fy = 1.0f - __builtin_fabsf(px);
-      xi = px >= 0.f ? fx : -fx;
-      eta = py >= 0.f ? fy : -fy;
-    }
-    const int ix = quant_lookup(xi, s_lutx, s_midx, lox, iwx, nbx);
-    const int ie = quant_lookup(eta, s_lute, s_mide, loe, iwe, nbe);
-    const uint32_t code = (uint32_t)ix | ((uint32_t)ie << C::BX) | ((uint32_t)ir << (C::BX + C::BE));
-    if constexpr (QJL) codes[i] = code;
+    const float r2 = e[i] * inv_tot;
+    uint32_t ir = 0;
+#pragma unroll
+    for (int k = 0; k < C::LR - 1; ++k) ir += r2 > a.t.rho2_mid[k] ? 1u : 0u;
+    const uint32_t code = ir << (C::BX + C::BE);
+    if constexpr (QJL) codes[i] |= code;
     const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
     words[wi] |= code << off;
     if (off + C::BT > 32) words[wi + 1] |= code >> (32 - off);
@@ -182,16 +229,16 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
     uint32_t sbits[D / 32];
 #pragma unroll
     for (int w = 0; w < D / 32; ++w) sbits[w] = 0u;
-    const float* __restrict__ S = a.t.S;
+    const float* __restrict__ Sm = a.t.S;
 #pragma unroll 1
     for (int r = 0; r < D; r += 32) {
       uint32_t m = 0u;
 #pragma unroll 2
       for (int rr = 0; rr < 32; ++rr) {
-        const float* __restrict__ row = S + (int64_t)(r + rr) * D;
+        const float* __restrict__ srow = Sm + (int64_t)(r + rr) * D;
         float acc = 0.f;
 #pragma unroll
-        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(row[k], v[k], acc);
+        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(srow[k], v[k], acc);
         m |= (acc >= 0.f ? 1u : 0u) << rr;
       }
 #pragma unroll

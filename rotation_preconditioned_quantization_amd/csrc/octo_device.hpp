@@ -69,6 +69,42 @@ __device__ __forceinline__ void wht_regs(float (&v)[D]) {
   }
 }
 
+// Butterfly stages of stride h >= H0 only (the earlier ones already done).
+template <int D, int H0>
+__device__ __forceinline__ void wht_regs_from(float (&v)[D]) {
+#pragma unroll
+  for (int h = H0; h < D; h <<= 1) {
+#pragma unroll
+    for (int i = 0; i < D; i += 2 * h) {
+#pragma unroll
+      for (int j = i; j < i + h; ++j) {
+        const float a = v[j], b = v[j + h];
+        v[j] = a + b;
+        v[j + h] = a - b;
+      }
+    }
+  }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// First butterfly stage (stride 1) straight from a packed pair of 16-bit
+// inputs: a + b and a - b with one v_dot2 each (weights +-1, products exact,
+// fp32 sum), no separate conversion.
+template <int DT>
+__device__ __forceinline__ void stage1_pair(uint32_t w, float& s, float& d) {
+  if constexpr (DT == DT_BF16) {
+    const bf16x2_t a = __builtin_bit_cast(bf16x2_t, w);
+    s = __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), 0.0f, false);
+    d = __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, 0xbf803f80u), 0.0f, false);
+  } else {
+    const f16x2_t a = __builtin_bit_cast(f16x2_t, w);
+    s = __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, 0x3c003c00u), 0.0f, false);
+    d = __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, 0xbc003c00u), 0.0f, false);
+  }
+}
+
 // s .* v where bit j of the mask means s_j = -1 (flip the IEEE sign bit).
 template <int D>
 __device__ __forceinline__ void apply_signs(float (&v)[D], const uint32_t (&bits)[4]) {

@@ -174,6 +174,32 @@ bool build_quant(const std::vector<double>& mids, double lo, double hi, HostQuan
   return false;
 }
 
+// Window table for L uniform buckets over [-1, 1] (see WindowTable); false if
+// some bucket's true index can leave b-1 .. b+1.
+bool build_window(const std::vector<double>& mids, std::vector<float>* w) {
+  const int L = (int)mids.size() + 1;
+  std::vector<float> mf(mids.size());
+  for (size_t k = 0; k < mids.size(); ++k) mf[k] = (float)mids[k];
+  const double bw = 2.0 / L, margin = 1e-3 * bw;
+  auto m = [&](int k) -> double {
+    if (k < 0) return -INFINITY;
+    if (k >= L - 1) return INFINITY;
+    return (double)mf[k];
+  };
+  for (int b = 0; b < L; ++b) {
+    const double lo = b == 0 ? -INFINITY : -1.0 + b * bw - margin;
+    const double hi = b == L - 1 ? INFINITY : -1.0 + (b + 1) * bw + margin;
+    // every midpoint below index b-1 lies under the bucket, every one above b over it
+    if (b >= 2 && !(m(b - 2) < lo)) return false;
+    if (b + 1 <= L - 2 && !(m(b + 1) >= hi)) return false;
+  }
+  w->assign(L + 1, 0.f);
+  (*w)[0] = -INFINITY;
+  for (int k = 0; k < L - 1; ++k) (*w)[k + 1] = mf[k];
+  (*w)[L] = INFINITY;
+  return true;
+}
+
 std::vector<double> midpoints(const std::vector<double>& c) {
   std::vector<double> m(c.size() - 1);
   for (size_t k = 0; k + 1 < c.size(); ++k) m[k] = 0.5 * (c[k] + c[k + 1]);
@@ -209,6 +235,11 @@ octo_status build_device_tables(octo_codebook* cb) {
   const double hi = m2.empty() ? 1.0 : std::min(1.0, 1.25 * m2.back() + 1e-3);
   if (!build_quant(m2, 0.0, hi, &qr2))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
+
+  std::vector<float> wx, we;
+  if (!build_window(midpoints(cb->c_xi), &wx) || !build_window(midpoints(cb->c_eta), &we))
+    return fail(OCTO_ERR_UNSUPPORTED, "xi/eta codebook too far from uniform for the window rule");
+  if ((1 << cb->br) - 1 > 8) return fail(OCTO_ERR_UNSUPPORTED, "too many rho levels");
 
   const int ndir = 1 << (cb->bx + cb->be);
   std::vector<float> dir(4 * (size_t)ndir);
@@ -246,7 +277,8 @@ octo_status build_device_tables(octo_codebook* cb) {
       {qr2.mid.data(), qr2.mid.size() * 4, 0},   {qx.lut.data(), qx.lut.size(), 0},
       {qe.lut.data(), qe.lut.size(), 0},         {qr2.lut.data(), qr2.lut.size(), 0},
       {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0},
-      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0}};
+      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0},
+      {wx.data(), wx.size() * 4, 0},             {we.data(), we.size() * 4, 0}};
   size_t total = 0;
   for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
   int prev = 0;
@@ -289,6 +321,11 @@ octo_status build_device_tables(octo_codebook* cb) {
   t.qr2 = qt(qr2, 4, 7);
   t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[8].off);
   t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[9].off);
+  t.wx.w = (const float*)(base + reg[10].off);
+  t.wx.levels = (int)wx.size() - 1;
+  t.we.w = (const float*)(base + reg[11].off);
+  t.we.levels = (int)we.size() - 1;
+  for (int k = 0; k < 8; ++k) t.rho2_mid[k] = k < (int)m2.size() ? (float)m2[k] : INFINITY;
   for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
   return OCTO_OK;
 }
@@ -642,27 +679,14 @@ octo_status octo_decode_logits_stages(const octo_codebook* cb, const void* q, oc
   if (B == 0 || Hq == 0 || n_keys == 0) return OCTO_OK;
   hipStream_t s = (hipStream_t)stream;
   const bool qjl = qjl_bits != nullptr;
-  RotateArgs r{};
-  r.t = cb->tables;
-  r.q = q;
-  r.qdt = (int)qdt;
-  r.B = B;
-  r.Hq = Hq;
-  r.Hkv = Hkv;
-  r.n_q = 1;
-  r.mult = 1.0f;
-  r.qrot = (float*)((char*)workspace + wl.qrot);
-  r.qp = qjl ? (float*)((char*)workspace + wl.qp) : nullptr;
-  if (stages & OCTO_STAGE_ROTATE) {
-    st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
-    if (st != OCTO_OK) return st;
-  }
+  // the rotation runs in the fused kernel's prologue (OCTO_STAGE_ROTATE is a no-op here)
   if (!(stages & OCTO_STAGE_MAIN)) return OCTO_OK;
   const int G = Hq / Hkv;
   DecodeArgs a{};
   a.t = cb->tables;
-  a.qrot = r.qrot;
-  a.qp = r.qp;
+  a.q = q;
+  a.qdt = (int)qdt;
+  a.mult = 1.0f;
   a.packed = (const uint32_t*)packed;
   a.gamma = gamma;
   a.qjl_bits = (const uint32_t*)qjl_bits;
@@ -726,14 +750,14 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   r.n_q = n_q;
   r.mult = sc * 1.4426950408889634f;  // logits in log2 units for exp2
   r.qrot = (float*)((char*)workspace + wl.qrot);
-  r.qp = qjl ? (float*)((char*)workspace + wl.qp) : nullptr;
-  if (stages & OCTO_STAGE_ROTATE) {
-    st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
-    if (st != OCTO_OK) return st;
-  }
+  r.qp = nullptr;
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
+    if (stages & OCTO_STAGE_ROTATE) {
+      st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
+      if (st != OCTO_OK) return st;
+    }
     const Split sp = mq_split(n_keys, cb->d, mq_rows(B, Hq, n_q));
     MQArgs m{};
     m.t = cb->tables;
@@ -766,10 +790,12 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   }
   const int64_t n_seq = (int64_t)B * Hkv;
   const Split sp = attn_split(n_keys, n_seq, head_passes(G));
+  // single query: the rotation runs in the fused kernel's prologue
   DecodeArgs a{};
   a.t = cb->tables;
-  a.qrot = r.qrot;
-  a.qp = r.qp;
+  a.q = q;
+  a.qdt = (int)qdt;
+  a.mult = r.mult;
   a.packed = (const uint32_t*)packed;
   a.gamma = gamma;
   a.qjl_bits = (const uint32_t*)qjl_bits;

@@ -26,8 +26,19 @@ struct QuantTable {
   int nmid;
 };
 
+// Encoder nearest-centroid for xi / eta: L uniform buckets over [-1, 1]; for
+// x in bucket b the index #{k : x > m_k} is (b - 1) + (x > w[b]) + (x > w[b+1])
+// with w = [-inf, m_0 .. m_{L-2}, +inf] (the host checks that the true index
+// never leaves b-1 .. b+1, including a rounding margin at the bucket edges).
+struct WindowTable {
+  const float* w;  // L + 1 entries
+  int levels;      // L
+};
+
 struct DevTables {
   QuantTable qx, qe, qr2;   // xi, eta, rho^2 (squared midpoints)
+  WindowTable wx, we;       // xi, eta windows (encoder)
+  float rho2_mid[8];        // squared rho midpoints (2^b_rho - 1 <= 7 used)
   const float4* dirtab;     // 2^(b_xi+b_eta) unit directions, index i_xi | i_eta << b_xi
   const float4* trip_tab;   // 2^B_t triplets rho^ n^ by full code (only for B_t <= 10)
   const float* rho_tab;     // 2^b_rho rho centroids
@@ -59,8 +70,9 @@ struct RotateArgs {
 
 struct DecodeArgs {
   DevTables t;
-  const float* qrot;
-  const float* qp;
+  const void* q;         // queries [B][Hq][d] (one token), rotated in each block's prologue
+  int qdt;
+  float mult;            // folded into q' (attention: scale * log2(e); logits: 1)
   const uint32_t* packed;
   const float* gamma;
   const uint32_t* qjl_bits;
