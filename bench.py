@@ -135,6 +135,9 @@ def main():
                     help="graph replays used to time each kernel on its own")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--counters", action="store_true",
+                    help="counter-collection run for rocprofv3 --pmc: per step a plain copy "
+                         "kernel of 64 MiB (the counter scale), then encode and decode, eagerly")
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
                     help="workload (2 = the LLM-decode shape the metric is quoted on; the "
                          "others are the remaining shapes of the pages' workloads)")
@@ -184,7 +187,7 @@ def main():
             out = torch.empty((cfg.B, cfg.Hq, cfg.N), dtype=torch.float32, device=dev)
         else:
             out = torch.empty((cfg.B, cfg.Hq, cfg.n_q, cfg.d), dtype=torch.float32, device=dev)
-        ws = torch.empty(ws_bytes, dtype=torch.uint8, device=dev)
+        ws = torch.zeros(ws_bytes, dtype=torch.uint8, device=dev)
         sets.append(dict(keys=keys, v=v, q=q, cache=cache, out=out, ws=ws))
 
     # the video-block workload encodes only the newest chunk at the end of the cache
@@ -204,6 +207,24 @@ def main():
         else:
             octo.octo_decode_attn(cb, s["q"], s["cache"], s["v"], cfg.N, cfg.Hkv, out=s["out"],
                                   workspace=s["ws"], stages=stages)
+
+    if args.counters:
+        # torch.mul over 16 Mi fp32: one elementwise kernel reading and writing
+        # exactly 64 MiB, whose FETCH_SIZE / WRITE_SIZE give the counter scale
+        src = torch.ones(16 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for s in sets:
+            if enc_pos0:
+                octo.octo_encode(cb, s["keys"][:, :enc_pos0], s["cache"], pos0=0)
+        for k in range(args.steps):
+            torch.mul(src, 1.0, out=dst)
+            encode(sets[k % R])
+            decode(sets[k % R])
+        torch.cuda.synchronize()
+        print(json.dumps({"counters_run": True, "steps": args.steps, "config": args.config,
+                          "copy_bytes_each_way": 64 << 20,
+                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+        return
 
     # eager warm-up (the prefix of a chunked cache is encoded once here) and
     # reference outputs

@@ -22,6 +22,7 @@
  * Conventions for every call:
  *   - Device pointers are HIP device memory owned by the caller; host
  *     pointers are marked "host".  The library owns only the codebook.
+ *     packed and qjl_bits must be 16-byte aligned, gamma and q 4-byte.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Calls only enqueue work: no call below synchronises the host, and no
  *     call allocates device memory except octo_codebook_build.
@@ -85,12 +86,17 @@ typedef struct {
 
 /* Packed-cache geometry of a codebook.
  * Keys of one sequence (one batch x KV-head) live in tiles of tile_keys (64)
- * keys; word w of key j is at packed[seq][j / 64][w][j % 64] (u32).  Inside a
- * key, triplet i occupies bits [i*B_t, (i+1)*B_t) of its little-endian word
- * stream, LSB first, as code = i_xi | i_eta << b_xi | i_rho << (b_xi+b_eta);
- * unused high bits are 0.  gamma is fp32 [seq][cap].  With QJL, sign bit j of
- * key j' is bit j%32 of word j/32 at qjl_bits[seq][j'/64][j/32][j'%64]
- * (1 = positive) and the residual norm is fp16 [seq][cap]. */
+ * keys, W = words_per_key u32 words per key.  Inside a tile the words of all
+ * keys are cut into groups of 4 consecutive words (the last group holds the
+ * W % 4 left over); group g is stored key-major, [key][4] (last group
+ * [key][W % 4]), and the groups follow each other: word w of key j is the u32
+ * at packed[seq][j / 64][64 * 4 * (w / 4) + (j % 64) * width + w % 4], width =
+ * 4 for full groups and W % 4 for the last.  Inside a key, triplet i occupies
+ * bits [i*B_t, (i+1)*B_t) of its little-endian word stream, LSB first, as
+ * code = i_xi | i_eta << b_xi | i_rho << (b_xi+b_eta); unused high bits are 0.
+ * gamma is fp32 [seq][cap].  With QJL, the d/32 sign words of a key use the
+ * same tile layout in qjl_bits (bit j%32 of word j/32 = sign j, 1 = positive)
+ * and the residual norm is fp16 [seq][cap]. */
 typedef struct {
   int d, n_triplets, pad_dim;
   int b_xi, b_eta, b_rho, bits_per_triplet, bits_per_key;
@@ -133,7 +139,8 @@ octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kd
 
 /* Workspace for the decode calls.  mode 0 = octo_decode_logits, 1 =
  * octo_decode_attn.  The workspace holds the rotated queries and, for
- * attention, the split-K partial results. */
+ * attention, the split-K partial results (one call at a time per
+ * workspace). */
 size_t octo_decode_workspace_bytes(const octo_codebook* cb, int mode, int B, int Hq, int Hkv,
                                    int n_q, int64_t n_keys);
 
@@ -166,10 +173,11 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
 
 /* The launches of the two decode calls, for callers that schedule or time
  * them one by one: OCTO_STAGE_ROTATE writes the rotated queries into the
- * workspace; OCTO_STAGE_MAIN runs the fused kernel, which reads them;
- * OCTO_STAGE_COMBINE (attention only) merges the split-K partials into out.
- * Stages must run in this order on one stream with the same arguments and
- * workspace; octo_decode_logits / octo_decode_attn run all of them. */
+ * workspace (multi-query attention only; the other kernels rotate in their
+ * prologue); OCTO_STAGE_MAIN runs the fused kernel; OCTO_STAGE_COMBINE
+ * (attention only) merges the split-K partials into out.  Stages must run in
+ * this order on one stream with the same arguments and workspace;
+ * octo_decode_logits / octo_decode_attn run all of them. */
 #define OCTO_STAGE_ROTATE 1
 #define OCTO_STAGE_MAIN 2
 #define OCTO_STAGE_COMBINE 4

@@ -394,8 +394,13 @@ def joint_round(t: np.ndarray, cb: Codebook, exhaustive: bool = False) -> np.nda
 # [YL] 工程实现).  READING: per key, triplet i occupies bits
 # [i*B_t, (i+1)*B_t) of a little-endian stream of u32 words, LSB first, code
 # = i_xi | i_eta << b_xi | i_rho << (b_xi + b_eta); unused bits are 0.
-# Keys are stored in tiles of 64: word w of key j of sequence s lives at
-# packed[s][j // 64][w][j % 64].
+# Keys are stored in tiles of 64.  Inside a tile the W words of every key are
+# cut into groups of 4 consecutive words (the last group holds the W % 4 left
+# over); group g of all 64 keys is stored key-major, [key][words of group g],
+# and the groups follow each other.  Word w of key j of sequence s is thus the
+# element (j % 64) * width(g) + w % 4 of group g = w // 4 in tile j // 64, with
+# width(g) = 4 for full groups and W % 4 for the last.  The same layout holds
+# the d/32 QJL sign words of a key.
 # ----------------------------------------------------------------------------
 TILE = 64
 
@@ -437,18 +442,30 @@ def unpack_codes(words: np.ndarray, T: int, alloc) -> np.ndarray:
     return codes
 
 
+def tile_groups(W: int):
+    """[(first word, width)] of the word groups of the tile layout."""
+    return [(w0, min(4, W - w0)) for w0 in range(0, W, 4)]
+
+
 def to_tiles(words: np.ndarray, cap: int) -> np.ndarray:
-    """(n_seq, n <= cap, W) per-key words -> (n_seq, cap//64, W, 64) tiled buffer."""
+    """(n_seq, n <= cap, W) per-key words -> (n_seq, cap//64, 64*W) tiled buffer."""
     n_seq, n, W = words.shape
     full = np.zeros((n_seq, cap, W), dtype=np.uint32)
     full[:, :n] = words
-    return full.reshape(n_seq, cap // TILE, TILE, W).transpose(0, 1, 3, 2).copy()
+    t = full.reshape(n_seq, cap // TILE, TILE, W)
+    parts = [t[:, :, :, w0:w0 + wd].reshape(n_seq, cap // TILE, TILE * wd)
+             for w0, wd in tile_groups(W)]
+    return np.concatenate(parts, axis=2)
 
 
-def from_tiles(tiles: np.ndarray, n: int) -> np.ndarray:
-    """(n_seq, cap//64, W, 64) -> (n_seq, n, W) per-key words."""
-    n_seq, nt, W, _ = tiles.shape
-    return tiles.transpose(0, 1, 3, 2).reshape(n_seq, nt * TILE, W)[:, :n]
+def from_tiles(tiles: np.ndarray, W: int, n: int) -> np.ndarray:
+    """(n_seq, cap//64, 64*W) tiled buffer -> (n_seq, n, W) per-key words."""
+    n_seq, nt = tiles.shape[:2]
+    tiles = tiles.reshape(n_seq, nt, TILE * W)
+    out = np.zeros((n_seq, nt, TILE, W), dtype=tiles.dtype)
+    for w0, wd in tile_groups(W):
+        out[:, :, :, w0:w0 + wd] = tiles[:, :, TILE * w0:TILE * (w0 + wd)].reshape(n_seq, nt, TILE, wd)
+    return out.reshape(n_seq, nt * TILE, W)[:, :n]
 
 
 # ----------------------------------------------------------------------------

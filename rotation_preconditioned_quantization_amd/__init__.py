@@ -212,7 +212,7 @@ def _workspace(cb, mode, B, Hq, Hkv, n_q, n_keys, workspace, device):
     import torch
     need = cb.workspace_bytes(mode, B, Hq, Hkv, n_q, n_keys)
     if workspace is None:
-        workspace = torch.empty(max(need, 256), dtype=torch.uint8, device=device)
+        workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
     return workspace, need
 
 

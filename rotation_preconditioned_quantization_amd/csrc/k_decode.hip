@@ -104,13 +104,69 @@ struct SQShared {
   float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
-// Query rotation in the block prologue: wave w rotates query head g0 + w of
-// the block's KV head (q' = mult * R q, R = d^-1/2 H diag(s)), lane l holding
-// elements l + 64 k; butterflies of stride < 64 pair lanes (shuffles).  With
-// QJL the wave also forms p = sqrt(pi/2)/d * S q'.
+// Values the block prologue loads from global memory.  They are loaded
+// before the first key tiles are requested, so that waiting for them does not
+// wait for the tiles: wave w's query head g0 + w (lane l holds elements
+// l + 64 k) and this thread's share of the LDS tables.
 template <int D, int B, bool QJL>
-__device__ __forceinline__ void rotate_head(const DecodeArgs& a, int64_t seq, int g0, int hcount,
-                                            SQShared<D, B, QJL>& sh) {
+struct SQPre {
+  using C = Codec<D, B>;
+  static constexpr int NT = SQShared<D, B, QJL>::kCombined ? (1 << C::BT) : C::NDIR;
+  static constexpr int PER = (NT + 255) / 256;
+  float rho;
+  uint32_t qw[D / 64];
+};
+
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void sq_issue_prologue(const DecodeArgs& a, int64_t seq, int g0,
+                                                  int hcount, SQPre<D, B, QJL>& pre,
+                                                  SQShared<D, B, QJL>& sh) {
+  using C = Codec<D, B>;
+  using P = SQPre<D, B, QJL>;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const float4* src = SQShared<D, B, QJL>::kCombined ? a.t.trip_tab : a.t.dirtab;
+  // the table goes straight from global memory into LDS (no registers held)
+#pragma unroll
+  for (int k = 0; k < P::PER; ++k) {
+    const int i0 = 256 * k + 64 * w;  // this wave's 64 entries of round k
+    if (P::NT % 256 == 0 || i0 < P::NT)
+      __builtin_amdgcn_global_load_lds((const void*)(src + i0 + lane),
+                                       (__attribute__((address_space(3))) void*)(sh.tab + i0), 16,
+                                       0, 0);
+  }
+  if (tid < C::LR) pre.rho = a.t.rho_tab[tid];
+  // one 32-bit load per element whatever the dtype (the word holding a
+  // 16-bit element), decoded by selects: no branch between these loads and
+  // the tile loads that follow
+  const int wq = w < hcount ? w : 0;
+  const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
+  const int64_t r = bidx * a.Hq + kvh * a.G + g0 + wq;
+  const int esz = a.qdt == DT_F32 ? 4 : 2;
+  const unsigned char* qrow = (const unsigned char*)a.q + r * D * esz;
+#pragma unroll
+  for (int k = 0; k < D / 64; ++k) {
+    const int j = lane + 64 * k;
+    pre.qw[k] = *(const uint32_t*)(qrow + ((j * esz) & ~3));
+  }
+}
+
+// Element l + 64 k of the wave's query from the raw words of sq_issue_prologue.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ float sq_query_elem(const DecodeArgs& a, const SQPre<D, B, QJL>& pre,
+                                               int k, int lane) {
+  const uint32_t wd = pre.qw[k];
+  const uint32_t h16 = (lane & 1) ? (wd >> 16) : (wd & 0xffffu);
+  const float fb = __uint_as_float(h16 << 16);
+  const float fh = __half2float(__ushort_as_half((unsigned short)h16));
+  return a.qdt == DT_F32 ? __uint_as_float(wd) : (a.qdt == DT_BF16 ? fb : fh);
+}
+
+// Query rotation (q' = mult * R q, R = d^-1/2 H diag(s)): butterflies of
+// stride < 64 pair lanes (shuffles), stride 64 pairs a lane's two values.
+// With QJL the wave also forms p = sqrt(pi/2)/d * S q'.
+template <int D, int B, bool QJL>
+__device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
+                                            const SQPre<D, B, QJL>& pre, SQShared<D, B, QJL>& sh) {
   using SH = SQShared<D, B, QJL>;
   constexpr int NV = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
@@ -118,21 +174,13 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int64_t seq, in
     for (int j = lane; j < SH::QD; j += 64) sh.q[w][j] = 0.f;
     return;
   }
-  const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
-  const int64_t r = bidx * a.Hq + kvh * a.G + g0 + w;
   float x[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int j = lane + 64 * k;
-    float v;
-    if (a.qdt == DT_F32) {
-      v = ((const float*)a.q)[r * D + j];
-    } else {
-      const unsigned short u = ((const unsigned short*)a.q)[r * D + j];
-      v = a.qdt == DT_BF16 ? __uint_as_float((uint32_t)u << 16) : __half2float(__ushort_as_half(u));
-    }
-    if ((a.t.sign_bits[j >> 5] >> (j & 31)) & 1u) v = -v;
-    x[k] = v;
+    const float qv = sq_query_elem<D, B, QJL>(a, pre, k, lane);
+    const uint32_t sb = (lane < 32) ? a.t.sign_bits[2 * k] : a.t.sign_bits[2 * k + 1];
+    x[k] = ((sb >> (j & 31)) & 1u) ? -qv : qv;
   }
 #pragma unroll
   for (int hh = 1; hh < 64; hh <<= 1) {
@@ -166,19 +214,11 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int64_t seq, in
   }
 }
 
-// Tables of the block (after the rotation; needs a block barrier before the
-// QJL nibble table reads qp of all heads).
 template <int D, int B, bool QJL>
-__device__ __forceinline__ void load_sq_tables(const DecodeArgs& a, SQShared<D, B, QJL>& sh) {
+__device__ __forceinline__ void store_sq_tables(const SQPre<D, B, QJL>& pre,
+                                                SQShared<D, B, QJL>& sh) {
   using C = Codec<D, B>;
-  using SH = SQShared<D, B, QJL>;
-  const int tid = threadIdx.x;
-  if constexpr (SH::kCombined) {
-    for (int i = tid; i < (1 << C::BT); i += blockDim.x) sh.tab[i] = a.t.trip_tab[i];
-  } else {
-    for (int i = tid; i < C::NDIR; i += blockDim.x) sh.tab[i] = a.t.dirtab[i];
-  }
-  if (tid < C::LR) sh.rho[tid] = a.t.rho_tab[tid];
+  if (threadIdx.x < C::LR) sh.rho[threadIdx.x] = pre.rho;
 }
 
 // QJL nibble table: lut[m][nib] holds, per head, sum_k (+1 if bit k of nib
@@ -218,15 +258,11 @@ __device__ __forceinline__ void load_ktile(const DecodeArgs& a, int64_t seq, int
                                            KTile<D, B, QJL>& k) {
   constexpr int W = Codec<D, B>::W;
   const int64_t tiles = a.cap / kTile;
-  const uint32_t* src = a.packed + ((seq * tiles + t) * W) * kTile + lane;
-#pragma unroll
-  for (int w = 0; w < W; ++w) k.words[w] = src[w * kTile];
-  const int64_t key = t * kTile + lane;
-  k.gamma = key < a.n_keys ? a.gamma[seq * a.cap + key] : 0.f;
+  TileWords<W>::load(a.packed + (seq * tiles + t) * W * kTile, lane, k.words);
+  const int64_t key = t * kTile + lane;   // < cap: in bounds (masked by the caller)
+  k.gamma = a.gamma[seq * a.cap + key];
   if constexpr (QJL) {
-    const uint32_t* sb = a.qjl_bits + ((seq * tiles + t) * (D / 32)) * kTile + lane;
-#pragma unroll
-    for (int w = 0; w < D / 32; ++w) k.sw[w] = sb[w * kTile];
+    TileWords<D / 32>::load(a.qjl_bits + (seq * tiles + t) * (D / 32) * kTile, lane, k.sw);
     k.nu = __half2float(__ushort_as_half(a.qjl_norm[seq * a.cap + key]));
   }
 }
@@ -245,9 +281,11 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
   constexpr int T = C::T, W = C::W;
   constexpr int kGroup = 4;
   const float* qrow = sh.q[lane & 3];
-  floatx4 acc[3];
+  // two accumulator sets (even / odd triplets): the dependent-MFMA latency
+  // then hides behind the other set's issue
+  floatx4 acc[6];
 #pragma unroll
-  for (int c = 0; c < 3; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+  for (int c = 0; c < 6; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
@@ -262,11 +300,12 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
     }
 #pragma unroll
     for (int c = 0; c < 3; ++c)
-      acc[c] = __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[c], 0, 0, 0);
+      acc[3 * (i & 1) + c] =
+          __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[3 * (i & 1) + c], 0, 0, 0);
     // a few triplets at a time: keeps the LDS gathers from all being hoisted
     if (i % kGroup == kGroup - 1) asm volatile("" ::: "memory");
   }
-  floatx4 r = acc[0] + acc[1] + acc[2];
+  floatx4 r = (acc[0] + acc[3]) + (acc[1] + acc[4]) + (acc[2] + acc[5]);
   if constexpr (QJL) {
     float4 corr = make_float4(0.f, 0.f, 0.f, 0.f);
 #pragma unroll
@@ -283,12 +322,14 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
   return r;
 }
 
-// Prologue shared by both single-query kernels: rotation, tables, barrier.
+// Second half of the prologue shared by both single-query kernels: rotation,
+// tables, barrier (and the QJL nibble table).
 template <int D, int B, bool QJL>
-__device__ __forceinline__ void sq_prologue(const DecodeArgs& a, int64_t seq, int g0, int hcount,
-                                            SQShared<D, B, QJL>& sh) {
-  rotate_head<D, B, QJL>(a, seq, g0, hcount, sh);
-  load_sq_tables<D, B, QJL>(a, sh);
+__device__ __forceinline__ void sq_finish_prologue(const DecodeArgs& a, int hcount,
+                                                   const SQPre<D, B, QJL>& pre,
+                                                   SQShared<D, B, QJL>& sh) {
+  rotate_head<D, B, QJL>(a, hcount, pre, sh);
+  store_sq_tables<D, B, QJL>(pre, sh);
   __syncthreads();
   if constexpr (QJL) {
     build_qjl_lut<D, B, QJL>(hcount, sh);
@@ -310,9 +351,12 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
   const int64_t stride = (int64_t)gridDim.x * 4;
   int64_t t = (int64_t)blockIdx.x * 4 + wave;
+  SQPre<D, B, QJL> pre;
+  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
+  asm volatile("" ::: "memory");  // the prologue loads go out before the tile loads
   KTile<D, B, QJL> cur;
   if (t < ntile) load_ktile<D, B, QJL>(a, seq, t, lane, cur);
-  sq_prologue<D, B, QJL>(a, seq, g0, hcount, sh);
+  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (; t < ntile; t += stride) {
     KTile<D, B, QJL> nxt;
@@ -334,42 +378,47 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
 
 // ---------------------------------------------------------------------------
 // Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4)), 4
-// waves per block, each wave a stream of 64-key tiles whose next tile (V rows
-// and compressed words) is loaded while the current one is computed.  Per
-// tile: logits by tile_logits, a wave-wide online softmax per head (DPP
-// max), then O[head][dim] += p[head][key] V[key][dim] on
-// v_mfma_f32_4x4x1_16b_f32: the A operand is p[head = lane % 4][key], the B
-// operand one bf16 of the V row the whole wave reads with one coalesced dword
-// load, so lane l keeps O[0..3][2l] and O[0..3][2l+1] (d = 128; for d = 64
-// the two half-waves take alternate keys).  Partial (m, l, o) per (query
-// head, split); m in log2 units.
+// waves per block; wave w takes tiles t_begin + w, + 4, ... of the block's
+// split, with the next tile (V rows and compressed words) in flight while
+// the current one is computed.  Per tile: logits by tile_logits, a wave-wide
+// online softmax per head (DPP max), then O[head][dim] += p[head][key]
+// V[key][dim] on v_mfma_f32_4x4x4_16b_bf16.  V is read with 16-byte loads:
+// lane l takes the 8 dims 8c .. 8c+7 (c = l % (d/8)) of keys KPL j + l/(d/8)
+// (KPL = 512/d keys per wave load), so after 4 loads a lane holds 4 keys of
+// each of its 8 dims: byte permutes turn them into the B operands (4 keys x
+// 1 dim, bf16 exactly as stored).  Every 4-lane MFMA block shares its 4 keys;
+// the A operand is p[head = lane % 4][those keys], split into bf16 high and
+// low parts (p = hi + lo to 16 bits) and fed as two MFMAs.  Lanes serving
+// different keys hold partial sums of the same dims, added at the end.  The
+// block merges its 4 waves into one (m, l, o) partial per head (m in log2
+// units); k_combine merges the splits.
 // ---------------------------------------------------------------------------
-// The V rows of a 64-key tile as the PV MFMA wants them: lane l takes the
-// dword (bf16 pair 2 dl, 2 dl + 1) of keys KPI * j + kk_off.  Full tiles
-// use constant offsets from one base; the last partial tile checks each key.
-template <int D, int NV, int KPI>
-__device__ __forceinline__ void load_vtile(const uint32_t* vbase, int64_t t, int64_t n_keys,
-                                           int kk_off, uint32_t (&vw)[NV]) {
-  constexpr int ROWW = D / 2;  // dwords per V row
-  const uint32_t* vt = vbase + (t * kTile + kk_off) * ROWW;
-  if ((t + 1) * kTile <= n_keys) {
+template <int D>
+struct VGeom {
+  static constexpr int CPR = D / 8;        // 16-byte chunks per V row
+  static constexpr int KPL = 64 / CPR;     // keys per wavefront load
+  static constexpr int NVL = kTile / KPL;  // loads per 64-key tile
+};
+
+// The V rows of a 64-key tile.  V holds cap rows per sequence and cap is a
+// multiple of 64, so the whole tile is always in bounds: the loads carry no
+// conditions (rows past n_keys are zeroed where the tile is used).
+template <int D>
+__device__ __forceinline__ void load_vtile(const uint4* vlane, int64_t t, uint4 (&vv)[VGeom<D>::NVL]) {
+  using VG = VGeom<D>;
+  const uint4* vt = vlane + (t * kTile) * VG::CPR;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) vw[j] = vt[j * KPI * ROWW];
-  } else {
-#pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const int64_t kv = t * kTile + KPI * j + kk_off;
-      vw[j] = kv < n_keys ? vt[j * KPI * ROWW] : 0u;
-    }
-  }
+  for (int j = 0; j < VG::NVL; ++j) vv[j] = vt[j * VG::KPL * VG::CPR];
 }
 
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(DecodeArgs a) {
-  constexpr int KPI = 128 / D;          // keys per V load / PV MFMA
-  constexpr int NV = kTile / KPI;       // V loads per tile per lane
+  using VG = VGeom<D>;
+  constexpr int NVL = VG::NVL;
   __shared__ SQShared<D, B, QJL> sh;
-  __shared__ float s_p[4][4][kTile + 4];   // padded rows: the 4 heads hit different banks
+  // p of the tile per head, stored so that the 4 keys one MFMA block shares
+  // are 4 consecutive floats; padded rows: the 4 heads hit different banks
+  __shared__ __align__(16) float s_p[4][4][kTile + 4];
   __shared__ float s_ml[4][4][2];
   __shared__ float s_o[4][4][D];
 
@@ -377,33 +426,46 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int64_t seq = blockIdx.y;
   const int g0 = blockIdx.z * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
-  const int kk_off = KPI == 2 ? (lane >> 5) : 0;   // key of the pair this lane serves
-  const int dl = KPI == 2 ? (lane & 31) : lane;     // dims 2 dl, 2 dl + 1
+  const int kq = lane / VG::CPR;                     // key of the wave load this lane serves
+  // slot of this lane's key (= lane) in the p rows: key 4 KPL g + KPL j' + q
+  // goes to 4 KPL g + 4 q + j'
+  const int p_slot = (lane / (4 * VG::KPL)) * (4 * VG::KPL) + (lane % VG::KPL) * 4 +
+                     (lane % (4 * VG::KPL)) / VG::KPL;
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
-  const uint32_t* vbase = (const uint32_t*)a.v + (seq * a.cap * D) / 2 + dl;  // lane's dword column
+  const uint4* vlane = (const uint4*)a.v + seq * a.cap * VG::CPR + kq * VG::CPR + lane % VG::CPR;
 
-  // first tile's loads go out before the prologue
+  // prologue loads, then the first two tiles of this wave
+  SQPre<D, B, QJL> pre;
+  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
+  asm volatile("" ::: "memory");  // the prologue loads go out before the tile loads
   int64_t t = t_begin + wave;
-  KTile<D, B, QJL> cur;
-  uint32_t vw[NV];
+  KTile<D, B, QJL> cur, nxt;
+  uint4 vv[NVL];
   if (t < t_end) {
-    load_vtile<D, NV, KPI>(vbase, t, a.n_keys, kk_off, vw);
     load_ktile<D, B, QJL>(a, seq, t, lane, cur);
+    load_vtile<D>(vlane, t, vv);
   }
-  sq_prologue<D, B, QJL>(a, seq, g0, hcount, sh);
+  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
 
   float m[4], l[4];
-  floatx4 olo[2], ohi[2];
+  floatx4 o[8];
 #pragma unroll
   for (int h = 0; h < 4; ++h) { m[h] = -INFINITY; l[h] = 0.f; }
 #pragma unroll
-  for (int k = 0; k < 2; ++k) { olo[k] = floatx4{0.f, 0.f, 0.f, 0.f}; ohi[k] = olo[k]; }
+  for (int k = 0; k < 8; ++k) o[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 
   // One tile: logits, online softmax per head, P.V.
-  auto process = [&](const KTile<D, B, QJL>& kt, const uint32_t (&vv)[NV], int64_t tt) {
+  auto process = [&](const KTile<D, B, QJL>& kt, uint4 (&vv)[NVL], int64_t tt) {
+    if ((tt + 1) * kTile > a.n_keys) {
+      // last, partial tile: rows past n_keys hold arbitrary bits (p is 0 there,
+      // but 0 * NaN is not)
+#pragma unroll
+      for (int j = 0; j < NVL; ++j)
+        if (tt * kTile + VG::KPL * j + kq >= a.n_keys) vv[j] = make_uint4(0u, 0u, 0u, 0u);
+    }
     const floatx4 acc = tile_logits<D, B, QJL>(sh, kt, lane);
     const int64_t key = tt * kTile + lane;
     const bool valid = key < a.n_keys;
@@ -416,56 +478,77 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const float p = __builtin_amdgcn_exp2f(sc - mn);
       l[h] = __builtin_fmaf(l[h], al[h], p);
       m[h] = mn;
-      s_p[wave][h][lane] = p;
+      s_p[wave][h][p_slot] = p;
     }
 #pragma unroll
-    for (int k = 0; k < 2; ++k)
+    for (int k = 0; k < 8; ++k)
 #pragma unroll
-      for (int r = 0; r < 4; ++r) { olo[k][r] *= al[r]; ohi[k][r] *= al[r]; }
+      for (int r = 0; r < 4; ++r) o[k][r] *= al[r];
     __builtin_amdgcn_wave_barrier();
-    const float* prow = s_p[wave][lane & 3];
+    const float* prow = s_p[wave][lane & 3] + 4 * kq;
 #pragma unroll
-    for (int j = 0; j < NV; ++j) {
-      const float pa = prow[KPI * j + kk_off];
-      olo[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_lo(vv[j]), olo[j & 1], 0, 0, 0);
-      ohi[j & 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(pa, bf16_hi(vv[j]), ohi[j & 1], 0, 0, 0);
+    for (int g = 0; g < NVL / 4; ++g) {
+      // A: p of keys 4 KPL g + KPL j' + kq (j' = 0..3) as bf16 hi + lo parts
+      const float4 pf = *(const float4*)(prow + 4 * VG::KPL * g);
+      const uint32_t u0 = __float_as_uint(pf.x), u1 = __float_as_uint(pf.y);
+      const uint32_t u2 = __float_as_uint(pf.z), u3 = __float_as_uint(pf.w);
+      const float r0 = pf.x - __uint_as_float(u0 & 0xffff0000u);
+      const float r1 = pf.y - __uint_as_float(u1 & 0xffff0000u);
+      const float r2 = pf.z - __uint_as_float(u2 & 0xffff0000u);
+      const float r3 = pf.w - __uint_as_float(u3 & 0xffff0000u);
+      const bf16x4 phi = pack_bf16x4(__builtin_amdgcn_perm(u1, u0, 0x07060302u),
+                                     __builtin_amdgcn_perm(u3, u2, 0x07060302u));
+      const bf16x4 plo = pack_bf16x4(
+          __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u),
+          __builtin_amdgcn_perm(__float_as_uint(r3), __float_as_uint(r2), 0x07060302u));
+      const uint4& e0 = vv[4 * g];
+      const uint4& e1 = vv[4 * g + 1];
+      const uint4& e2 = vv[4 * g + 2];
+      const uint4& e3 = vv[4 * g + 3];
+      const uint32_t w0[4] = {e0.x, e0.y, e0.z, e0.w}, w1[4] = {e1.x, e1.y, e1.z, e1.w};
+      const uint32_t w2[4] = {e2.x, e2.y, e2.z, e2.w}, w3[4] = {e3.x, e3.y, e3.z, e3.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        // B: dims 8c + 2k (low halves) and 8c + 2k + 1 (high halves), 4 keys each
+        const bf16x4 blo = pack_bf16x4(__builtin_amdgcn_perm(w1[k], w0[k], 0x05040100u),
+                                       __builtin_amdgcn_perm(w3[k], w2[k], 0x05040100u));
+        const bf16x4 bhi = pack_bf16x4(__builtin_amdgcn_perm(w1[k], w0[k], 0x07060302u),
+                                       __builtin_amdgcn_perm(w3[k], w2[k], 0x07060302u));
+        o[2 * k] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(phi, blo, o[2 * k], 0, 0, 0);
+        o[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(phi, bhi, o[2 * k + 1], 0, 0, 0);
+        o[2 * k] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(plo, blo, o[2 * k], 0, 0, 0);
+        o[2 * k + 1] = __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(plo, bhi, o[2 * k + 1], 0, 0, 0);
+      }
     }
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Two register sets, used alternately: the next tile loads while one computes.
-  KTile<D, B, QJL> kb;
-  uint32_t vb[NV];
-  for (; t < t_end; t += 8) {
-    if (t + 4 < t_end) {
-      load_vtile<D, NV, KPI>(vbase, t + 4, a.n_keys, kk_off, vb);
-      load_ktile<D, B, QJL>(a, seq, t + 4, lane, kb);
-    }
-    process(cur, vw, t);
-    if (t + 4 >= t_end) break;
-    if (t + 8 < t_end) {
-      load_vtile<D, NV, KPI>(vbase, t + 8, a.n_keys, kk_off, vw);
-      load_ktile<D, B, QJL>(a, seq, t + 8, lane, cur);
-    }
-    process(kb, vb, t + 4);
+  // The next tile's code words load while this tile's logits are formed; its
+  // V rows as soon as this tile's P.V has consumed the V registers.  Other
+  // waves on the SIMD cover the remaining latency.
+  for (; t < t_end; t += 4) {
+    const bool more = t + 4 < t_end;
+    if (more) load_ktile<D, B, QJL>(a, seq, t + 4, lane, nxt);
+    process(cur, vv, t);
+    if (more) load_vtile<D>(vlane, t + 4, vv);
+    cur = nxt;
   }
 
-  floatx4 olo_s = olo[0] + olo[1], ohi_s = ohi[0] + ohi[1];
-  if constexpr (KPI == 2) {
+  // lanes serving different keys of a load hold partial sums of the same dims
 #pragma unroll
-    for (int r = 0; r < 4; ++r) {
-      olo_s[r] += __shfl_xor(olo_s[r], 32, 64);
-      ohi_s[r] += __shfl_xor(ohi_s[r], 32, 64);
-    }
-  }
+  for (int sft = VG::CPR; sft < 64; sft <<= 1)
+#pragma unroll
+    for (int k = 0; k < 8; ++k)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[k][r] += __shfl_xor(o[k][r], sft, 64);
 #pragma unroll
   for (int h = 0; h < 4; ++h) l[h] = wave_sum(l[h]);
-  if (kk_off == 0) {
+  if (kq == 0) {
+    const int c0 = 8 * (lane % VG::CPR);
 #pragma unroll
-    for (int h = 0; h < 4; ++h) {
-      s_o[wave][h][2 * dl] = olo_s[h];
-      s_o[wave][h][2 * dl + 1] = ohi_s[h];
-    }
+    for (int h = 0; h < 4; ++h)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s_o[wave][h][c0 + k] = o[k][h];
   }
   if (lane == 0) {
 #pragma unroll
@@ -486,7 +569,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       val = 0.f;
 #pragma unroll
       for (int w = 0; w < 4; ++w) {
-        const float sc = (s_ml[w][h][0] == -INFINITY) ? 0.f : exp2f(s_ml[w][h][0] - M);
+        const float sc = (s_ml[w][h][0] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s_ml[w][h][0] - M);
         val += sc * (c == 1 ? s_ml[w][h][1] : s_o[w][h][c - 2]);
       }
     }
@@ -495,77 +578,64 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   }
 }
 
-// out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s, one block per
-// row.  The o values of the first splits are loaded before anything else so
-// they travel together with the (m, l) loads; the split weights are formed
-// once in LDS; thread (c, part) sums the splits part, part + P, ... of column
-// c and the P partial sums meet in LDS.
-constexpr int kCombineThreads = 256;
-constexpr int kMaxSplit = 1024;
-constexpr int kCombinePre = 32;
+// out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s, M = max_s m_s,
+// one wavefront per row.  Lane l handles the column pair 2 (l % (d/2)) of the
+// splits s = l / (d/2) (mod 64 / (d/2)), one 8-byte load per split; the o
+// values of the first splits are requested together with the (m, l) loads,
+// so the row costs about two memory round trips.
+constexpr int kCombinePre = 16;
 
-__global__ __launch_bounds__(kCombineThreads) void k_combine(CombineArgs a) {
+template <int D>
+__global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
+  constexpr int LPS = D / 2;     // lanes per split row
+  constexpr int SPI = 64 / LPS;  // splits per step
   __shared__ float s_w[kMaxSplit];
-  __shared__ float s_l[kMaxSplit];
-  __shared__ float s_red[kCombineThreads];
   const int64_t row = blockIdx.x;
-  const int tid = threadIdx.x;
-  const int ns = a.n_split, stride = a.d + 2;
-  const int P = kCombineThreads / a.d;
-  const int c = tid % a.d, part = tid / a.d;
-  const bool worker = part < P;
-  const float* p = a.part + row * ns * stride;
-  float pre[kCombinePre];
+  const int lane = threadIdx.x;
+  const int ns = a.n_split;
+  const int cp = lane % LPS, so = lane / LPS;
+  const float* p = a.part + row * ns * (D + 2);
+  float2 pre[kCombinePre];
 #pragma unroll
   for (int k = 0; k < kCombinePre; ++k) {
-    const int s = part + P * k;
-    pre[k] = (worker && s < ns) ? p[s * stride + 2 + c] : 0.f;
+    const int sp = so + SPI * k;
+    pre[k] = sp < ns ? *(const float2*)(p + (int64_t)sp * (D + 2) + 2 + 2 * cp) : make_float2(0.f, 0.f);
   }
-  for (int s = tid; s < ns; s += kCombineThreads) {
-    s_w[s] = p[s * stride];
-    s_l[s] = p[s * stride + 1];
+  float M = -INFINITY;
+  for (int sp = lane; sp < ns; sp += 64) M = fmaxf(M, p[(int64_t)sp * (D + 2)]);
+  M = wave_max(M);
+  float den = 0.f;
+  for (int sp = lane; sp < ns; sp += 64) {
+    const float2 ml = *(const float2*)(p + (int64_t)sp * (D + 2));
+    const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
+    s_w[sp] = w;
+    den = __builtin_fmaf(w, ml.y, den);
   }
+  den = wave_sum(den);
   __syncthreads();
-  float mloc = -INFINITY;
-  for (int s = tid; s < ns; s += kCombineThreads) mloc = fmaxf(mloc, s_w[s]);
-  s_red[tid] = mloc;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) s_red[tid] = fmaxf(s_red[tid], s_red[tid + o]);
-    __syncthreads();
-  }
-  const float M = s_red[0];
-  __syncthreads();
-  float lden = 0.f;
-  for (int s = tid; s < ns; s += kCombineThreads) {
-    const float m = s_w[s];
-    const float w = (m == -INFINITY) ? 0.f : exp2f(m - M);
-    s_w[s] = w;
-    lden = __builtin_fmaf(w, s_l[s], lden);
-  }
-  s_red[tid] = lden;
-  __syncthreads();
-  for (int o = kCombineThreads / 2; o > 0; o >>= 1) {
-    if (tid < o) s_red[tid] += s_red[tid + o];
-    __syncthreads();
-  }
-  const float den = s_red[0];
-  __syncthreads();
-  float num = 0.f;
-  if (worker) {
+  float2 num = make_float2(0.f, 0.f);
 #pragma unroll
-    for (int k = 0; k < kCombinePre; ++k) {
-      const int s = part + P * k;
-      if (s < ns) num = __builtin_fmaf(s_w[s], pre[k], num);
+  for (int k = 0; k < kCombinePre; ++k) {
+    const int sp = so + SPI * k;
+    if (sp < ns) {
+      num.x = __builtin_fmaf(s_w[sp], pre[k].x, num.x);
+      num.y = __builtin_fmaf(s_w[sp], pre[k].y, num.y);
     }
-    for (int s = part + P * kCombinePre; s < ns; s += P) num = __builtin_fmaf(s_w[s], p[s * stride + 2 + c], num);
   }
-  s_red[tid] = num;
-  __syncthreads();
-  if (tid < a.d) {
-    float tot = 0.f;
-    for (int k = 0; k < P; ++k) tot += s_red[k * a.d + tid];
-    a.out[row * a.d + tid] = den > 0.f ? tot / den : 0.f;
+#pragma unroll 8
+  for (int sp = so + SPI * kCombinePre; sp < ns; sp += SPI) {
+    const float2 o = *(const float2*)(p + (int64_t)sp * (D + 2) + 2 + 2 * cp);
+    num.x = __builtin_fmaf(s_w[sp], o.x, num.x);
+    num.y = __builtin_fmaf(s_w[sp], o.y, num.y);
+  }
+#pragma unroll
+  for (int sh = LPS; sh < 64; sh <<= 1) {
+    num.x += __shfl_xor(num.x, sh, 64);
+    num.y += __shfl_xor(num.y, sh, 64);
+  }
+  if (so == 0) {
+    const float inv = den > 0.f ? 1.0f / den : 0.f;
+    *(float2*)(a.out + row * D + 2 * cp) = make_float2(num.x * inv, num.y * inv);
   }
 }
 
@@ -586,10 +656,8 @@ __global__ __launch_bounds__(64) void k_reconstruct(ReconArgs a) {
   const int64_t key = (int64_t)blockIdx.x * 64 + threadIdx.x;
   if (key >= a.n_keys) return;
   const int64_t tiles = a.cap / kTile;
-  const uint32_t* src = a.packed + ((seq * tiles + (key >> 6)) * W) * kTile + (key & 63);
   uint32_t words[W];
-#pragma unroll
-  for (int w = 0; w < W; ++w) words[w] = src[w * kTile];
+  TileWords<W>::load(a.packed + (seq * tiles + (key >> 6)) * W * kTile, (int)(key & 63), words);
   float u[D];
 #pragma unroll
   for (int i = 0; i < T; ++i) {
@@ -656,8 +724,10 @@ hipError_t launch_attn(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_se
 
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
-  if (a.n_split > kMaxSplit || a.d > kCombineThreads) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_combine, dim3(a.rows), dim3(kCombineThreads), 0, s, a);
+  if (a.n_split > kMaxSplit) return hipErrorInvalidValue;
+  if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.rows), dim3(64), 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL(k_combine<128>, dim3(a.rows), dim3(64), 0, s, a);
+  else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 

@@ -8,8 +8,8 @@
 //   nearest-centroid indices from bucketed LDS tables, bit-pack, store.
 // The key tile is read with coalesced 16-byte loads and handed to the lanes
 // through LDS in two halves (small LDS footprint, several waves per SIMD);
-// packed words are stored word-major per tile (256 contiguous bytes per
-// store instruction).  With QJL the same lane also forms the rotated residual
+// packed words are stored in the tile's word-group layout (16-byte stores,
+// 1 KiB contiguous per store instruction).  With QJL the same lane also forms the rotated residual
 // r' = u' - u'^, its fp16 norm and the signs of S r' ([YL] 可选的残差修正).
 #include "octo_device.hpp"
 
@@ -200,9 +200,7 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
   const int64_t pos = a.pos0 + j;
   const int64_t tiles = a.cap / kTile;
   if (valid) {
-    uint32_t* dst = a.packed + ((seq * tiles + (pos >> 6)) * W) * kTile + (pos & 63);
-#pragma unroll
-    for (int w = 0; w < W; ++w) dst[w * kTile] = words[w];
+    TileWords<W>::store(a.packed + (seq * tiles + (pos >> 6)) * W * kTile, (int)(pos & 63), words);
     a.gamma[seq * a.cap + pos] = gamma;
   }
 
@@ -246,9 +244,8 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
         if (w == r / 32) sbits[w] = m;
     }
     if (valid) {
-      uint32_t* dst = a.qjl_bits + ((seq * tiles + (pos >> 6)) * (D / 32)) * kTile + (pos & 63);
-#pragma unroll
-      for (int w = 0; w < D / 32; ++w) dst[w * kTile] = sbits[w];
+      TileWords<D / 32>::store(a.qjl_bits + (seq * tiles + (pos >> 6)) * (D / 32) * kTile,
+                               (int)(pos & 63), sbits);
       a.qjl_norm[seq * a.cap + pos] = __half_as_ushort(__float2half_rn(nu));
     }
   }

@@ -107,11 +107,8 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
       const int64_t key = k0 + kk;
       _Float16* row = (_Float16*)(s_k + kk * KP);
       if (key < a.n_keys) {
-        const uint32_t* src =
-            a.packed + ((seq * tiles64 + (key >> 6)) * W) * kTile + (key & 63);
         uint32_t words[W];
-#pragma unroll
-        for (int w = 0; w < W; ++w) words[w] = src[w * kTile];
+        TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), words);
 #pragma unroll
         for (int i = 0; i < T; ++i) {
           const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
@@ -170,14 +167,14 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : exp2f(m_run - m_new);
+      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
       float lsum = 0.f;
       half8 pf[2][2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = (m_new == -INFINITY) ? 0.f : exp2f(s[sb][r] - m_new);
+          const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[sb][r] - m_new);
           const _Float16 ph = (_Float16)p;
           lsum += (float)ph;
           pf[sb][r >> 3][r & 7] = ph;

@@ -87,6 +87,11 @@ __device__ __forceinline__ void wht_regs_from(float (&v)[D]) {
 }
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef short bf16x4 __attribute__((ext_vector_type(4)));  // 4 bf16 bit patterns (MFMA operand)
+
+__device__ __forceinline__ bf16x4 pack_bf16x4(uint32_t lo, uint32_t hi) {
+  return __builtin_bit_cast(bf16x4, make_uint2(lo, hi));
+}
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
 // First butterfly stage (stride 1) straight from a packed pair of 16-bit
@@ -135,6 +140,45 @@ __device__ __forceinline__ uint32_t field_at(const uint32_t (&w)[W], int pos, in
   const uint32_t v = (off + bits <= 32) ? (lo >> off) : __builtin_amdgcn_alignbit(hi, lo, off);
   return v & ((1u << bits) - 1u);
 }
+
+// Tile layout of a per-key word stream (packed codes, QJL sign words): in a
+// tile of 64 keys, words 4g .. 4g+3 of all keys form group g, stored
+// [key][4]; the last W % 4 words form the last group, stored [key][W % 4];
+// groups follow each other.  A lane moves its key's whole stream with W/4
+// 16-byte accesses (+ one narrower), each wavefront access 1 KiB contiguous.
+template <int W>
+struct TileWords {
+  static constexpr int NG = W / 4, R = W % 4;
+  __device__ static __forceinline__ void load(const uint32_t* tile, int lane, uint32_t (&w)[W]) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g) {
+      const uint4 u = *(const uint4*)(tile + 256 * g + 4 * lane);
+      w[4 * g] = u.x; w[4 * g + 1] = u.y; w[4 * g + 2] = u.z; w[4 * g + 3] = u.w;
+    }
+    const uint32_t* r = tile + 256 * NG + R * lane;
+    if constexpr (R == 1) {
+      w[4 * NG] = r[0];
+    } else if constexpr (R == 2) {
+      const uint2 u = *(const uint2*)r;
+      w[4 * NG] = u.x; w[4 * NG + 1] = u.y;
+    } else if constexpr (R == 3) {
+      w[4 * NG] = r[0]; w[4 * NG + 1] = r[1]; w[4 * NG + 2] = r[2];
+    }
+  }
+  __device__ static __forceinline__ void store(uint32_t* tile, int lane, const uint32_t (&w)[W]) {
+#pragma unroll
+    for (int g = 0; g < NG; ++g)
+      *(uint4*)(tile + 256 * g + 4 * lane) = make_uint4(w[4 * g], w[4 * g + 1], w[4 * g + 2], w[4 * g + 3]);
+    uint32_t* r = tile + 256 * NG + R * lane;
+    if constexpr (R == 1) {
+      r[0] = w[4 * NG];
+    } else if constexpr (R == 2) {
+      *(uint2*)r = make_uint2(w[4 * NG], w[4 * NG + 1]);
+    } else if constexpr (R == 3) {
+      r[0] = w[4 * NG]; r[1] = w[4 * NG + 1]; r[2] = w[4 * NG + 2];
+    }
+  }
+};
 
 // Pointer into the constant address space: uniform loads through it become
 // scalar loads (s_load) whose results feed VALU ops as SGPR operands.

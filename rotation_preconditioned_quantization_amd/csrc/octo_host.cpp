@@ -599,12 +599,12 @@ octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kd
     return fail(OCTO_ERR_INVALID_ARG, "key_stride < d or seq_stride < 0");
   if (!aligned(keys, 16) || (key_stride * es) % 16 || (seq_stride * es) % 16)
     return fail(OCTO_ERR_INVALID_ARG, "key rows must be 16-byte aligned");
-  if (!aligned(packed, 4) || !aligned(gamma, 4))
+  if (!aligned(packed, 16) || !aligned(gamma, 4))
     return fail(OCTO_ERR_INVALID_ARG, "packed/gamma must be 4-byte aligned");
   if ((qjl_bits == nullptr) != (qjl_norm == nullptr))
     return fail(OCTO_ERR_INVALID_ARG, "pass both QJL buffers or neither");
   if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
-  if (qjl_bits && (!aligned(qjl_bits, 4) || !aligned(qjl_norm, 2)))
+  if (qjl_bits && (!aligned(qjl_bits, 16) || !aligned(qjl_norm, 2)))
     return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
   EncodeArgs a{};
   a.t = cb->tables;
@@ -644,11 +644,13 @@ static octo_status check_decode_common(const octo_codebook* cb, const void* q, o
   if (n_keys < 0 || cap <= 0 || cap % kTile || n_keys > cap)
     return fail(OCTO_ERR_INVALID_ARG, "need 0 <= n_keys <= cap and cap a positive multiple of 64");
   if (!q || !packed || !gamma) return fail(OCTO_ERR_INVALID_ARG, "NULL q/packed/gamma");
-  if (!aligned(q, 4) || !aligned(packed, 4) || !aligned(gamma, 4))
+  if (!aligned(q, 4) || !aligned(packed, 16) || !aligned(gamma, 4))
     return fail(OCTO_ERR_INVALID_ARG, "q/packed/gamma misaligned");
   if ((qjl_bits == nullptr) != (qjl_norm == nullptr))
     return fail(OCTO_ERR_INVALID_ARG, "pass both QJL buffers or neither");
   if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
+  if (qjl_bits && (!aligned(qjl_bits, 16) || !aligned(qjl_norm, 2)))
+    return fail(OCTO_ERR_INVALID_ARG, "qjl_bits/qjl_norm misaligned");
   if (!workspace || !aligned(workspace, 256))
     return fail(OCTO_ERR_WORKSPACE, "workspace missing or not 256-byte aligned");
   return OCTO_OK;
@@ -790,6 +792,7 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   }
   const int64_t n_seq = (int64_t)B * Hkv;
   const Split sp = attn_split(n_keys, n_seq, head_passes(G));
+  if (sp.n_split > kMaxSplit) return fail(OCTO_ERR_INVALID_ARG, "too many splits");
   // single query: the rotation runs in the fused kernel's prologue
   DecodeArgs a{};
   a.t = cb->tables;

@@ -10,6 +10,7 @@ namespace octo {
 constexpr int kTile = 64;          // keys per packed tile (one wavefront)
 constexpr int kMaxLut = 1024;      // max buckets of an encoder lookup table
 constexpr int kMaxLevels = 32;     // max centroids of one component (5 bits)
+constexpr int kMaxSplit = 1024;    // max split-K partials per output row
 
 // Nearest-centroid lookup for one scalar component (encoder).
 // Bucket b covers [lo + b/inv_w, lo + (b+1)/inv_w); lut[b] is the number of

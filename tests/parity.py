@@ -26,14 +26,14 @@ def unpack_device_codes(packed_words: np.ndarray, cb: O.Codebook, n_seq: int, ca
                         start: int = 0) -> np.ndarray:
     """Device packed buffer (flat int32/uint32) -> codes (n_seq, n, T, 3)."""
     W = cb.words_per_key
-    tiles = packed_words.astype(np.uint32).reshape(n_seq, cap // 64, W, 64)
-    words = O.from_tiles(tiles, cap)[:, start:start + n]
+    tiles = packed_words.astype(np.uint32).reshape(n_seq, cap // 64, 64 * W)
+    words = O.from_tiles(tiles, W, cap)[:, start:start + n]
     return O.unpack_codes(words.reshape(-1, W), cb.T, cb.alloc).reshape(n_seq, n, cb.T, 3)
 
 
 def unpack_device_signs(bits: np.ndarray, d: int, n_seq: int, cap: int, n: int, start: int = 0):
-    tiles = bits.astype(np.uint32).reshape(n_seq, cap // 64, d // 32, 64)
-    words = O.from_tiles(tiles, cap)[:, start:start + n]
+    tiles = bits.astype(np.uint32).reshape(n_seq, cap // 64, 64 * (d // 32))
+    words = O.from_tiles(tiles, d // 32, cap)[:, start:start + n]
     return O.unpack_signs(words.reshape(-1, d // 32), d).reshape(n_seq, n, d)
 
 

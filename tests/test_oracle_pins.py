@@ -277,10 +277,20 @@ def test_pack_golden_and_bijection():
             used = T * sum(alloc)
             if used % 32:
                 assert np.all((w[:, -1].astype(np.uint64) >> np.uint64(used % 32)) == 0)
+    # tile layout: groups of 4 words stored [key][4], the last W % 4 words [key][W % 4]
+    W = w.shape[1]
+    assert W == 13                                # (4,3,2) x 43 triplets = 387 bits
     tiles = O.to_tiles(w.reshape(1, 100, -1), 128)
-    assert tiles.shape == (1, 2, w.shape[1], 64)
-    assert tiles[0, 1, 3, 5] == w[64 + 5, 3]
-    assert np.array_equal(O.from_tiles(tiles, 100)[0], w)
+    assert tiles.shape == (1, 2, 64 * W)
+    assert tiles[0, 1, 5 * 4 + 3] == w[64 + 5, 3]            # group 0, key 5, word 3
+    assert tiles[0, 0, 256 + 7 * 4 + 2] == w[7, 6]            # group 1, key 7, word 6
+    assert tiles[0, 1, 768 + 35] == w[64 + 35, 12]           # last group (width 1), key 35
+    assert np.all(tiles[0, 1, 36 * 4:256] == 0)             # keys 100..127 are zero
+    assert np.array_equal(O.from_tiles(tiles, W, 100)[0], w)
+    w2 = w[:, :10]                                           # W = 10: groups 4, 4, 2
+    t2 = O.to_tiles(w2.reshape(1, 100, -1), 128)
+    assert t2[0, 0, 512 + 9 * 2 + 1] == w2[9, 9]
+    assert np.array_equal(O.from_tiles(t2, 10, 100)[0], w2)
 
 
 def test_sign_packing():
