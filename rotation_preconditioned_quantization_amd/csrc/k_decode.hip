@@ -104,10 +104,9 @@ struct SQShared {
   float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
-// Values the block prologue loads from global memory.  They are loaded
-// before the first key tiles are requested, so that waiting for them does not
-// wait for the tiles: wave w's query head g0 + w (lane l holds elements
-// l + 64 k) and this thread's share of the LDS tables.
+// Values the block prologue loads from global memory besides the LDS tables
+// (which go to LDS directly): wave w's query head g0 + w (lane l holds the
+// 32-bit words of elements l + 64 k) and the rho centroids.
 template <int D, int B, bool QJL>
 struct SQPre {
   using C = Codec<D, B>;
@@ -170,10 +169,8 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
   using SH = SQShared<D, B, QJL>;
   constexpr int NV = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (w >= hcount) {
-    for (int j = lane; j < SH::QD; j += 64) sh.q[w][j] = 0.f;
-    return;
-  }
+  // branch-free: a wave past hcount rotates a valid head and stores zeros
+  const bool live = w < hcount;
   float x[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
@@ -197,8 +194,8 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
   }
   const float mult = a.mult * rsqrtf((float)D);
 #pragma unroll
-  for (int k = 0; k < NV; ++k) sh.q[w][lane + 64 * k] = x[k] * mult;
-  for (int j = D + lane; j < SH::QD; j += 64) sh.q[w][j] = 0.f;
+  for (int k = 0; k < NV; ++k) sh.q[w][lane + 64 * k] = live ? x[k] * mult : 0.f;
+  if (lane < SH::QD - D) sh.q[w][D + lane] = 0.f;
   if constexpr (QJL) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -209,7 +206,7 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
       float acc = 0.f;
 #pragma unroll 8
       for (int c = 0; c < D; ++c) acc = __builtin_fmaf(row[c], sh.q[w][c], acc);
-      sh.qp[w][j] = acc * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+      sh.qp[w][j] = live ? acc * (1.2533141373155003f / D) : 0.f;  // sqrt(pi/2)/d
     }
   }
 }
@@ -328,8 +325,8 @@ template <int D, int B, bool QJL>
 __device__ __forceinline__ void sq_finish_prologue(const DecodeArgs& a, int hcount,
                                                    const SQPre<D, B, QJL>& pre,
                                                    SQShared<D, B, QJL>& sh) {
-  rotate_head<D, B, QJL>(a, hcount, pre, sh);
   store_sq_tables<D, B, QJL>(pre, sh);
+  rotate_head<D, B, QJL>(a, hcount, pre, sh);
   __syncthreads();
   if constexpr (QJL) {
     build_qjl_lut<D, B, QJL>(hcount, sh);
@@ -353,10 +350,9 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
   int64_t t = (int64_t)blockIdx.x * 4 + wave;
   SQPre<D, B, QJL> pre;
   sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
-  asm volatile("" ::: "memory");  // the prologue loads go out before the tile loads
+  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
   KTile<D, B, QJL> cur;
   if (t < ntile) load_ktile<D, B, QJL>(a, seq, t, lane, cur);
-  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (; t < ntile; t += stride) {
     KTile<D, B, QJL> nxt;
@@ -438,17 +434,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint4* vlane = (const uint4*)a.v + seq * a.cap * VG::CPR + kq * VG::CPR + lane % VG::CPR;
 
   // prologue loads, then the first two tiles of this wave
+  // prologue (one round trip: LDS tables by DMA, the query words), then tiles
   SQPre<D, B, QJL> pre;
   sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
-  asm volatile("" ::: "memory");  // the prologue loads go out before the tile loads
+  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
   int64_t t = t_begin + wave;
   KTile<D, B, QJL> cur, nxt;
   uint4 vv[NVL];
-  if (t < t_end) {
-    load_ktile<D, B, QJL>(a, seq, t, lane, cur);
-    load_vtile<D>(vlane, t, vv);
-  }
-  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
+  // Loads are issued without conditions (a wave with no tile, or past its
+  // last one, re-reads a tile of the block that is already in flight, so
+  // nothing extra comes from HBM): no control flow between them keeps the
+  // compiler's memory-counter waits exact.
+  const int64_t t0 = t < t_end ? t : t_begin;
+  load_ktile<D, B, QJL>(a, seq, t0, lane, cur);
+  load_vtile<D>(vlane, t0, vv);
 
   float m[4], l[4];
   floatx4 o[8];
@@ -527,10 +526,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // V rows as soon as this tile's P.V has consumed the V registers.  Other
   // waves on the SIMD cover the remaining latency.
   for (; t < t_end; t += 4) {
-    const bool more = t + 4 < t_end;
-    if (more) load_ktile<D, B, QJL>(a, seq, t + 4, lane, nxt);
+    const int64_t tn = t + 4 < t_end ? t + 4 : t;
+    load_ktile<D, B, QJL>(a, seq, tn, lane, nxt);
     process(cur, vv, t);
-    if (more) load_vtile<D>(vlane, t + 4, vv);
+    load_vtile<D>(vlane, tn, vv);
     cur = nxt;
   }
 
