@@ -26,7 +26,8 @@ struct Stage {
   static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
   static constexpr int PITCH = ROWB + 16;   // padded pitch: conflict-free row reads
   static constexpr int VPC = 16 / ES;       // values per chunk
-  static constexpr int NR = 32;             // rows staged per phase
+  static constexpr int NR = 16;             // rows staged per phase
+  static constexpr int NP = kTile / NR;     // phases
   static constexpr int PER_LANE = NR * CPR / 64;
 };
 
@@ -47,8 +48,9 @@ __device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[4],
 }
 
 // Bring the lane's own key row (already sign-flipped, raw bits) into
-// registers: coalesced 16-byte global loads of the whole tile, then two
-// rounds through a half-tile LDS buffer (rows 0..31, then 32..63).
+// registers: coalesced 16-byte global loads of the whole tile (rows past
+// n_new re-read the last key, so the loads carry no conditions), then NP
+// rounds through the wave's LDS buffer of NR rows.
 template <int D, int KT>
 __device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
                                            unsigned char* s_keys, const uint4& smask,
@@ -56,21 +58,21 @@ __device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int
   using S = Stage<D, KT>;
   const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
   const int col = lane % S::CPR;
-  uint4 raw[2][S::PER_LANE];
+  uint4 raw[S::NP][S::PER_LANE];
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < S::NP; ++h) {
 #pragma unroll
     for (int k = 0; k < S::PER_LANE; ++k) {
       const int f = lane + 64 * k;
-      const int64_t j = j0 + h * S::NR + f / S::CPR;
-      raw[h][k] = make_uint4(0, 0, 0, 0);
-      if (j < a.n_new) raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + col * 16);
+      int64_t j = j0 + h * S::NR + f / S::CPR;
+      j = j < a.n_new ? j : a.n_new - 1;
+      raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + col * 16);
     }
   }
-  const int my_half = lane / S::NR;
+  const int my_phase = lane / S::NR;
   const unsigned char* row = s_keys + (lane % S::NR) * S::PITCH;
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
+  for (int h = 0; h < S::NP; ++h) {
 #pragma unroll
     for (int k = 0; k < S::PER_LANE; ++k) {
       const int f = lane + 64 * k;
@@ -78,42 +80,60 @@ __device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int
       u.x ^= smask.x; u.y ^= smask.y; u.z ^= smask.z; u.w ^= smask.w;
       *(uint4*)(s_keys + (f / S::CPR) * S::PITCH + col * 16) = u;
     }
-    __syncthreads();
-    if (my_half == h) {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (my_phase == h) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) rowbits[c] = *(const uint4*)(row + c * 16);
     }
-    __syncthreads();
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
-// #{k : x > m_k} by the window rule (see WindowTable).
-__device__ __forceinline__ int quant_window(float x, const float* w, float half_levels, float lm1) {
-  const float f = __builtin_amdgcn_fmed3f((x + 1.0f) * half_levels, 0.0f, lm1);
-  const int b = (int)f;
-  return b - 1 + (x > w[b] ? 1 : 0) + (x > w[b + 1] ? 1 : 0);
+// #{k : x > m_k} from a one-midpoint-per-bucket table in LDS (see Bucket1),
+// for x in [-1, 1] up to rounding: the bucket position is then above -1, so
+// truncation toward zero gives bucket 0 at the bottom, and the guard entries
+// cover the top.
+__device__ __forceinline__ uint32_t quant1(float x, const uint2* t, float scale, float bias) {
+  const uint2 e = t[(int)__builtin_fmaf(x, scale, bias)];
+  return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
 }
 
+// The same for x >= 0 of unbounded range (rho^2), clamped to the last bucket.
+__device__ __forceinline__ uint32_t quant1_clamp(float x, const uint2* t, float scale, float nbm1) {
+  const uint2 e = t[(uint32_t)__builtin_fminf(x * scale, nbm1)];
+  return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
+}
+
+constexpr int kEncWaves = 4;  // waves (64-key tiles) per encoder block
+
 template <int D, int B, int KT, bool QJL>
-__global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
+__global__ __launch_bounds__(64 * kEncWaves) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
   using S = Stage<D, KT>;
   constexpr int T = C::T, W = C::W;
 
-  __shared__ __align__(16) unsigned char s_keys[S::NR * S::PITCH];
-  __shared__ float s_wx[C::LX + 1], s_we[C::LE + 1];
+  __shared__ __align__(16) unsigned char s_keys[kEncWaves][S::NR * S::PITCH];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
-  const int64_t j0 = (int64_t)blockIdx.x * kTile;
+  const int64_t j0 = ((int64_t)blockIdx.x * kEncWaves + wave) * kTile;
 
-  if (lane < C::LX + 1) s_wx[lane] = a.t.wx.w[lane];
-  if (lane < C::LE + 1) s_we[lane] = a.t.we.w[lane];
+  // the block's waves share the quantiser tables
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 64 * kEncWaves) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * kEncWaves) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * kEncWaves) s_qr[i] = a.t.qr2.t[i];
+  __syncthreads();
+  if (j0 >= a.n_new) return;
   const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
   float v[D];
   {
     uint4 rowbits[S::CPR];
-    gather_row<D, KT>(a, seq, j0, lane, s_keys, smask, rowbits);
+    gather_row<D, KT>(a, seq, j0, lane, s_keys[wave], smask, rowbits);
     if constexpr (KT == DT_F32) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
@@ -143,8 +163,8 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
   if constexpr (KT == DT_F32) wht_regs<D>(v);
   else wht_regs_from<D, 2>(v);
 
-  const float hx = 0.5f * C::LX, lx = (float)(C::LX - 1);
-  const float he = 0.5f * C::LE, le = (float)(C::LE - 1);
+  const float sx = a.t.qx.scale, bx = a.t.qx.bias;
+  const float se = a.t.qe.scale, be = a.t.qe.bias;
   uint32_t words[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) words[w] = 0u;
@@ -152,11 +172,11 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
   float e[T];
   float tot = 0.f;
 
-  // Pass 1: triplet energies and the octahedral (xi, eta) indices by the
-  // window rule, packed into place.  p = (x, y)/l1; in the lower hemisphere
-  // (z < 0) the fold (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (and
-  // likewise for y), with sgn(0) = +1.  A zero triplet maps to (0, 0), i.e.
-  // n = (0, 0, 1).
+  // Pass 1: triplet energies and the octahedral (xi, eta) indices, packed
+  // into place.  p = (x, y)/l1; in the lower hemisphere (z < 0) the fold
+  // (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (likewise for y), with
+  // sgn(0) = +1 (the sign bit is copied; -0 only occurs for an all-zero
+  // triplet, where |z| = 0).  A zero triplet maps to (0, 0), i.e. n = (0,0,1).
 #pragma unroll
   for (int i = 0; i < T; ++i) {
     const float x = v[3 * i];
@@ -166,13 +186,10 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
     tot += e[i];
     const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
     const float il = __builtin_amdgcn_rcpf(__builtin_fmaxf(l1, 1e-37f));
-    const float px = x * il, py = y * il;
-    const float tz = __builtin_fmaxf(-z, 0.0f) * il;
-    const float xi = px + (px >= 0.f ? tz : -tz);
-    const float eta = py + (py >= 0.f ? tz : -tz);
-    const int ix = quant_window(xi, s_wx, hx, lx);
-    const int ie = quant_window(eta, s_we, he, le);
-    const uint32_t code = (uint32_t)ix | ((uint32_t)ie << C::BX);
+    const float tz = __builtin_fmaxf(-z, 0.0f);
+    const float xi = (x + __builtin_copysignf(tz, x)) * il;
+    const float eta = (y + __builtin_copysignf(tz, y)) * il;
+    const uint32_t code = quant1(xi, s_qx, sx, bx) | (quant1(eta, s_qe, se, be) << C::BX);
     if constexpr (QJL) codes[i] = code;
     const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
     words[wi] |= code << off;
@@ -182,13 +199,11 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
   const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
 
   // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
+  // (the rho^2 table starts at 0: bias 0)
+  const float sr = a.t.qr2.scale, mr = (float)(a.t.qr2.nb - 1);
 #pragma unroll
   for (int i = 0; i < T; ++i) {
-    const float r2 = e[i] * inv_tot;
-    uint32_t ir = 0;
-#pragma unroll
-    for (int k = 0; k < C::LR - 1; ++k) ir += r2 > a.t.rho2_mid[k] ? 1u : 0u;
-    const uint32_t code = ir << (C::BX + C::BE);
+    const uint32_t code = quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE);
     if constexpr (QJL) codes[i] |= code;
     const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
     words[wi] |= code << off;
@@ -253,8 +268,10 @@ __global__ __launch_bounds__(64) void k_encode(EncodeArgs a) {
 
 template <int D, int B, int KT, bool QJL>
 static hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
-  const dim3 grid((unsigned)((a.n_new + kTile - 1) / kTile), (unsigned)n_seq);
-  hipLaunchKernelGGL((k_encode<D, B, KT, QJL>), grid, dim3(64), 0, s, a);
+  if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  const int64_t per = (int64_t)kEncWaves * kTile;
+  const dim3 grid((unsigned)((a.n_new + per - 1) / per), (unsigned)n_seq);
+  hipLaunchKernelGGL((k_encode<D, B, KT, QJL>), grid, dim3(64 * kEncWaves), 0, s, a);
   return hipGetLastError();
 }
 

@@ -131,73 +131,52 @@ std::vector<double> antisymmetrize(const std::vector<double>& c) {
   return o;
 }
 
-// Bucketed nearest-centroid table (see QuantTable).  Returns false if no
-// bucket count up to kMaxLut keeps <= 2 midpoints per widened bucket.
-struct HostQuant {
-  std::vector<float> mid;     // nmid + 2 sentinels
-  std::vector<uint8_t> lut;
-  float lo = 0, inv_w = 0;
-  int nb = 0, nmid = 0;
+// One-midpoint-per-bucket table (see Bucket1) for the value range [lo, hi)
+// cut into nb buckets; the first bucket extends to -inf, the last to +inf.
+// Tries several bucket counts; false if none keeps <= 1 midpoint in every
+// bucket widened by the rounding margin of the device's bucket formula.
+struct HostB1 {
+  std::vector<uint32_t> t;  // 2 words per bucket: base, float bits of the midpoint
+  float scale = 0, bias = 0;
+  int nb = 0;
 };
 
-bool build_quant(const std::vector<double>& mids, double lo, double hi, HostQuant* q) {
+bool build_bucket1(const std::vector<double>& mids, double lo, double hi, HostB1* q) {
   const int nmid = (int)mids.size();
   std::vector<float> mf(nmid);
   for (int k = 0; k < nmid; ++k) mf[k] = (float)mids[k];
-  for (int nb = 256; nb <= kMaxLut; nb *= 2) {
+  const double eps = 1e-6 * (hi - lo);
+  for (int nb : {256, 128, 64}) {
+    if (nb > kMaxLut) continue;
     const double w = (hi - lo) / nb;
-    const double margin = 0.01 * w;
-    std::vector<uint8_t> lut(nb);
+    std::vector<uint32_t> t(2 * (size_t)nb);
     bool ok = true;
     for (int b = 0; b < nb && ok; ++b) {
-      const double L = b == 0 ? -INFINITY : lo + b * w - margin;
-      const double U = b == nb - 1 ? INFINITY : lo + (b + 1) * w + margin;
+      const double L = b == 0 ? -INFINITY : lo + b * w - eps;
+      const double U = b == nb - 1 ? INFINITY : lo + (b + 1) * w + eps;
       int below = 0, inside = 0;
+      float m_in = INFINITY;
       for (int k = 0; k < nmid; ++k) {
         if ((double)mf[k] < L) ++below;
-        else if ((double)mf[k] < U) ++inside;
+        else if ((double)mf[k] <= U) { ++inside; m_in = mf[k]; }
       }
-      if (inside > 2 || below > 255) ok = false;
-      lut[b] = (uint8_t)below;
+      if (inside > 1) ok = false;
+      uint32_t bits;
+      std::memcpy(&bits, &m_in, 4);
+      t[2 * b] = (uint32_t)below;
+      t[2 * b + 1] = bits;
     }
     if (!ok) continue;
-    q->mid = mf;
-    q->mid.push_back(INFINITY);
-    q->mid.push_back(INFINITY);
-    q->lut = lut;
-    q->lo = (float)lo;
-    q->inv_w = (float)(nb / (hi - lo));
+    // two guard buckets repeating the last one: a value a rounding step above
+    // hi lands in bucket nb without a clamp
+    for (int g = 0; g < 2; ++g) { t.push_back(t[2 * (nb - 1)]); t.push_back(t[2 * (nb - 1) + 1]); }
+    q->t = t;
+    q->scale = (float)(nb / (hi - lo));
+    q->bias = (float)(-lo * (nb / (hi - lo)));
     q->nb = nb;
-    q->nmid = nmid;
     return true;
   }
   return false;
-}
-
-// Window table for L uniform buckets over [-1, 1] (see WindowTable); false if
-// some bucket's true index can leave b-1 .. b+1.
-bool build_window(const std::vector<double>& mids, std::vector<float>* w) {
-  const int L = (int)mids.size() + 1;
-  std::vector<float> mf(mids.size());
-  for (size_t k = 0; k < mids.size(); ++k) mf[k] = (float)mids[k];
-  const double bw = 2.0 / L, margin = 1e-3 * bw;
-  auto m = [&](int k) -> double {
-    if (k < 0) return -INFINITY;
-    if (k >= L - 1) return INFINITY;
-    return (double)mf[k];
-  };
-  for (int b = 0; b < L; ++b) {
-    const double lo = b == 0 ? -INFINITY : -1.0 + b * bw - margin;
-    const double hi = b == L - 1 ? INFINITY : -1.0 + (b + 1) * bw + margin;
-    // every midpoint below index b-1 lies under the bucket, every one above b over it
-    if (b >= 2 && !(m(b - 2) < lo)) return false;
-    if (b + 1 <= L - 2 && !(m(b + 1) >= hi)) return false;
-  }
-  w->assign(L + 1, 0.f);
-  (*w)[0] = -INFINITY;
-  for (int k = 0; k < L - 1; ++k) (*w)[k + 1] = mf[k];
-  (*w)[L] = INFINITY;
-  return true;
 }
 
 std::vector<double> midpoints(const std::vector<double>& c) {
@@ -226,20 +205,15 @@ struct octo_codebook {
 namespace {
 
 octo_status build_device_tables(octo_codebook* cb) {
-  HostQuant qx, qe, qr2;
-  if (!build_quant(midpoints(cb->c_xi), -1.0, 1.0, &qx) ||
-      !build_quant(midpoints(cb->c_eta), -1.0, 1.0, &qe))
+  HostB1 qx, qe, qr2;
+  if (!build_bucket1(midpoints(cb->c_xi), -1.0, 1.0, &qx) ||
+      !build_bucket1(midpoints(cb->c_eta), -1.0, 1.0, &qe))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the xi/eta midpoints");
   std::vector<double> m2 = midpoints(cb->c_rho);
   for (double& m : m2) m = m * m;
   const double hi = m2.empty() ? 1.0 : std::min(1.0, 1.25 * m2.back() + 1e-3);
-  if (!build_quant(m2, 0.0, hi, &qr2))
+  if (!build_bucket1(m2, 0.0, hi, &qr2))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
-
-  std::vector<float> wx, we;
-  if (!build_window(midpoints(cb->c_xi), &wx) || !build_window(midpoints(cb->c_eta), &we))
-    return fail(OCTO_ERR_UNSUPPORTED, "xi/eta codebook too far from uniform for the window rule");
-  if ((1 << cb->br) - 1 > 8) return fail(OCTO_ERR_UNSUPPORTED, "too many rho levels");
 
   const int ndir = 1 << (cb->bx + cb->be);
   std::vector<float> dir(4 * (size_t)ndir);
@@ -273,12 +247,10 @@ octo_status build_device_tables(octo_codebook* cb) {
   struct Region { const void* src; size_t bytes; size_t off; };
   std::vector<Region> reg = {
       {dir.data(), dir.size() * 4, 0},           {rho.data(), rho.size() * 4, 0},
-      {qx.mid.data(), qx.mid.size() * 4, 0},     {qe.mid.data(), qe.mid.size() * 4, 0},
-      {qr2.mid.data(), qr2.mid.size() * 4, 0},   {qx.lut.data(), qx.lut.size(), 0},
-      {qe.lut.data(), qe.lut.size(), 0},         {qr2.lut.data(), qr2.lut.size(), 0},
+      {qx.t.data(), qx.t.size() * 4, 0},         {qe.t.data(), qe.t.size() * 4, 0},
+      {qr2.t.data(), qr2.t.size() * 4, 0},
       {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0},
-      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0},
-      {wx.data(), wx.size() * 4, 0},             {we.data(), we.size() * 4, 0}};
+      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0}};
   size_t total = 0;
   for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
   int prev = 0;
@@ -306,26 +278,19 @@ octo_status build_device_tables(octo_codebook* cb) {
   DevTables& t = cb->tables;
   t.dirtab = (const float4*)(base + reg[0].off);
   t.rho_tab = (const float*)(base + reg[1].off);
-  auto qt = [&](const HostQuant& h, int mid_r, int lut_r) {
-    QuantTable q;
-    q.mid = (const float*)(base + reg[mid_r].off);
-    q.lut = (const uint8_t*)(base + reg[lut_r].off);
-    q.lo = h.lo;
-    q.inv_w = h.inv_w;
+  auto qt = [&](const HostB1& h, int r) {
+    Bucket1 q;
+    q.t = (const uint2*)(base + reg[r].off);
+    q.scale = h.scale;
+    q.bias = h.bias;
     q.nb = h.nb;
-    q.nmid = h.nmid;
     return q;
   };
-  t.qx = qt(qx, 2, 5);
-  t.qe = qt(qe, 3, 6);
-  t.qr2 = qt(qr2, 4, 7);
-  t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[8].off);
-  t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[9].off);
-  t.wx.w = (const float*)(base + reg[10].off);
-  t.wx.levels = (int)wx.size() - 1;
-  t.we.w = (const float*)(base + reg[11].off);
-  t.we.levels = (int)we.size() - 1;
-  for (int k = 0; k < 8; ++k) t.rho2_mid[k] = k < (int)m2.size() ? (float)m2[k] : INFINITY;
+  t.qx = qt(qx, 2);
+  t.qe = qt(qe, 3);
+  t.qr2 = qt(qr2, 4);
+  t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[5].off);
+  t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[6].off);
   for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
   return OCTO_OK;
 }

@@ -8,38 +8,28 @@
 namespace octo {
 
 constexpr int kTile = 64;          // keys per packed tile (one wavefront)
-constexpr int kMaxLut = 1024;      // max buckets of an encoder lookup table
+constexpr int kMaxLut = 256;       // max buckets of an encoder lookup table
 constexpr int kMaxLevels = 32;     // max centroids of one component (5 bits)
 constexpr int kMaxSplit = 1024;    // max split-K partials per output row
 
-// Nearest-centroid lookup for one scalar component (encoder).
-// Bucket b covers [lo + b/inv_w, lo + (b+1)/inv_w); lut[b] is the number of
-// midpoints below the bucket start minus a small margin, and at most two
-// midpoints fall in the widened bucket, so the index #{k : x > m_k} is
-// lut[b] + (x > mid[lut[b]]) + (x > mid[lut[b]+1]).  mid holds the sorted
-// midpoints followed by two +inf sentinels.
-struct QuantTable {
-  const float* mid;
-  const uint8_t* lut;
-  float lo;
-  float inv_w;
+// Nearest-centroid lookup for one scalar component (encoder): the index
+// #{k : x > m_k} of the midpoint rule.  The value range is cut into nb equal
+// buckets, b = (int) clamp(fma(x, scale, bias), 0, nb - 1); every bucket,
+// widened by the rounding of that formula, holds at most one midpoint, so the
+// index is t[b].x + (x > t[b].y as float): t[b].x counts the midpoints below
+// the bucket, t[b].y is the one inside it (+inf if none).  The host checks
+// the one-midpoint property when it builds the table.  Two guard entries
+// t[nb], t[nb + 1] repeat t[nb - 1], so values that can exceed the range only
+// by rounding (xi, eta in [-1, 1]) need no upper clamp; the float-to-unsigned
+// conversion already saturates below at 0.
+struct Bucket1 {
+  const uint2* t;     // nb + 2 entries
+  float scale, bias;
   int nb;
-  int nmid;
-};
-
-// Encoder nearest-centroid for xi / eta: L uniform buckets over [-1, 1]; for
-// x in bucket b the index #{k : x > m_k} is (b - 1) + (x > w[b]) + (x > w[b+1])
-// with w = [-inf, m_0 .. m_{L-2}, +inf] (the host checks that the true index
-// never leaves b-1 .. b+1, including a rounding margin at the bucket edges).
-struct WindowTable {
-  const float* w;  // L + 1 entries
-  int levels;      // L
 };
 
 struct DevTables {
-  QuantTable qx, qe, qr2;   // xi, eta, rho^2 (squared midpoints)
-  WindowTable wx, we;       // xi, eta windows (encoder)
-  float rho2_mid[8];        // squared rho midpoints (2^b_rho - 1 <= 7 used)
+  Bucket1 qx, qe, qr2;      // xi, eta over [-1, 1]; rho^2 (squared midpoints) over [0, inf)
   const float4* dirtab;     // 2^(b_xi+b_eta) unit directions, index i_xi | i_eta << b_xi
   const float4* trip_tab;   // 2^B_t triplets rho^ n^ by full code (only for B_t <= 10)
   const float* rho_tab;     // 2^b_rho rho centroids
