@@ -124,6 +124,51 @@ def cpu_baseline(cfg, seconds: float):
     }
 
 
+def qjl_bias_study(cfg, dev, n_seeds: int = 64, n_keys: int = 4096):
+    """Seed-averaged bias of the QJL and the plain logit estimates on the GPU path.
+
+    For seeds 0..n_seeds-1 (WHT signs and QJL matrix; cb_seed fixed) the same
+    bf16 keys of one KV head are encoded and their logits against G query heads
+    computed with and without the 1-bit residual term.  bias(q, k) =
+    mean_s l^_s - <q, k>; reported as the slope beta = sum bias l / sum l^2
+    (mean and standard error over the per-seed slopes) and as the mean and RMS
+    of the bias, in units of the RMS exact logit.
+    """
+    import numpy as np
+    import torch
+
+    import rotation_preconditioned_quantization_amd as octo
+    import workloads as WL
+    kc = cfg.scaled(B=1, Hq=cfg.G, Hkv=1, N=n_keys)
+    keys = WL.make_keys(kc, dev, seed=11, n_seq=1, n=n_keys)
+    q = WL.make_queries(kc, dev, seed=11)[:, :, 0].contiguous()
+    exact = q[0].double().cpu().numpy() @ keys[0].double().cpu().numpy().T   # [G, N]
+    ee = float(np.sum(exact * exact))
+    slopes = {"qjl": [], "octopus": []}
+    acc = {"qjl": np.zeros_like(exact), "octopus": np.zeros_like(exact)}
+    t0 = time.perf_counter()
+    for s in range(n_seeds):
+        cb = octo.Codebook(cfg.d, cfg.b, seed=s, cb_seed=0, qjl=True, device=0)
+        cache = octo.Cache(cb, 1, kc.cap, qjl=True)
+        octo.octo_encode(cb, keys, cache)
+        for name, use in (("qjl", True), ("octopus", False)):
+            lg = octo.octo_decode_logits(cb, q, cache, n_keys, 1, use_qjl=use)[0].double().cpu().numpy()
+            acc[name] += lg
+            slopes[name].append(float(np.sum((lg - exact) * exact)) / ee)
+        cb.close()
+    rms_l = math.sqrt(ee / exact.size)
+    out = {"seeds": n_seeds, "keys": n_keys, "query_heads": cfg.G,
+           "seconds": round(time.perf_counter() - t0, 1)}
+    for name in ("qjl", "octopus"):
+        bias = acc[name] / n_seeds - exact
+        sl = np.array(slopes[name])
+        out[f"beta_{name}"] = float(sl.mean())
+        out[f"beta_{name}_se"] = float(sl.std(ddof=1) / math.sqrt(n_seeds))
+        out[f"mean_bias_{name}"] = float(bias.mean() / rms_l)
+        out[f"rms_bias_{name}"] = float(math.sqrt(np.mean(bias * bias)) / rms_l)
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -135,6 +180,8 @@ def main():
                     help="graph replays used to time each kernel on its own")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-qjl-bias", action="store_true",
+                    help="skip the 64-seed bias study of the QJL workload")
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection run for rocprofv3 --pmc: per step a plain copy "
                          "kernel of 64 MiB (the counter scale), then encode and decode, eagerly")
@@ -334,6 +381,8 @@ def main():
         "encode_pct_hbm_peak": round(100 * enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS, 2),
         "roofline": roofline,
     }
+    if cfg.qjl and not args.no_qjl_bias:
+        line["qjl_bias"] = qjl_bias_study(cfg, dev)
     if not args.no_cpu_baseline and args.config == 2:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)

@@ -8,6 +8,7 @@
 #include <cstdio>
 #include <cstring>
 #include <limits>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -428,9 +429,26 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
       cb->signs[j] = neg ? -1 : 1;
       if (neg && j < 128) cb->sign_bits[j >> 5] |= 1u << (j & 31);
     }
+    // The centroid tables depend only on (d, allocation, cb_seed, samples):
+    // the last fit is kept, so codebooks that differ only in `seed` (signs,
+    // QJL matrix) reuse it.
+    static std::mutex fit_mutex;
+    static std::vector<int64_t> fit_key;
+    static std::vector<double> fit_xi, fit_eta, fit_rho;
+    const std::vector<int64_t> key = {d, bx, be, br, (int64_t)p->cb_seed, cb->mc};
+    bool fitted = false;
+    {
+      std::lock_guard<std::mutex> lock(fit_mutex);
+      if (key == fit_key) {
+        cb->c_xi = fit_xi;
+        cb->c_eta = fit_eta;
+        cb->c_rho = fit_rho;
+        fitted = true;
+      }
+    }
     // Monte-Carlo samples of the rotated triplet marginals: normalised
     // Gaussian vectors are uniform on the sphere, so their rotation is too.
-    const int T = cb->T, M = cb->mc;
+    const int T = cb->T, M = fitted ? 0 : cb->mc;
     std::vector<double> g((size_t)d);
     std::vector<double> rho;
     std::vector<double> dirs;
@@ -465,11 +483,18 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     const size_t half = dirs.size();
     for (size_t i = 0; i < half; ++i) dirs.push_back(-dirs[i]);
     std::vector<double>().swap(all);
-    std::sort(rho.begin(), rho.end());
-    std::sort(dirs.begin(), dirs.end());
-    cb->c_xi = antisymmetrize(lloyd_max_sorted(dirs, 1 << bx));
-    cb->c_eta = (be == bx) ? cb->c_xi : antisymmetrize(lloyd_max_sorted(dirs, 1 << be));
-    cb->c_rho = lloyd_max_sorted(rho, 1 << br);
+    if (!fitted) {
+      std::sort(rho.begin(), rho.end());
+      std::sort(dirs.begin(), dirs.end());
+      cb->c_xi = antisymmetrize(lloyd_max_sorted(dirs, 1 << bx));
+      cb->c_eta = (be == bx) ? cb->c_xi : antisymmetrize(lloyd_max_sorted(dirs, 1 << be));
+      cb->c_rho = lloyd_max_sorted(rho, 1 << br);
+      std::lock_guard<std::mutex> lock(fit_mutex);
+      fit_key = key;
+      fit_xi = cb->c_xi;
+      fit_eta = cb->c_eta;
+      fit_rho = cb->c_rho;
+    }
     if (cb->qjl) {
       std::vector<double> s((size_t)d * d);
       gaussians(p->seed, kTagQJL, s.size(), s.data());

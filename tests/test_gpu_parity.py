@@ -432,3 +432,33 @@ def test_full_config4_video_block_sampled():
     cfg = WL.CONFIGS[4]
     check_mq(cfg, cfg.Hq, cfg.Hkv, cfg.n_q, cfg.N, cfg.cap, seed=0, label="config4-full",
              heads=[0, 17], chunk=cfg.chunk)
+
+
+# ---------------------------------------------------------- QJL seed average --
+@pytest.mark.gpu
+def test_qjl_seed_averaged_bias():
+    """Over independent seeds (signs and S) the OCTOPUS-QJL logit is unbiased
+    while the plain estimate shrinks towards zero ([YL] 可选的残差修正: the 1-bit
+    residual sketch removes the inner-product bias).  Slope of the per-seed
+    error against the exact logit: QJL within 3 standard errors of 0, plain
+    OCTOPUS clearly negative."""
+    octo = _octo()
+    cfg = WL.CONFIGS[5].scaled(B=1, Hq=4, Hkv=1, N=2048)
+    keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=1, n=cfg.N)
+    q = WL.make_queries(cfg, "cuda", seed=3)[:, :, 0].contiguous()
+    exact = f64(q[0]) @ f64(keys[0]).T
+    ee = float(np.sum(exact * exact))
+    slopes = {True: [], False: []}
+    for s in range(16):
+        g = gcb(cfg.d, cfg.b, seed=s, cb_seed=0, qjl=True)
+        cache = octo.Cache(g, 1, cfg.cap, qjl=True)
+        octo.octo_encode(g, keys, cache)
+        for use in (True, False):
+            lg = f64(octo.octo_decode_logits(g, q, cache, cfg.N, 1, use_qjl=use)[0])
+            slopes[use].append(float(np.sum((lg - exact) * exact)) / ee)
+        g.close()
+    bq, bo = np.array(slopes[True]), np.array(slopes[False])
+    se_q, se_o = bq.std(ddof=1) / 4.0, bo.std(ddof=1) / 4.0
+    say(f"[qjl-bias] beta qjl {bq.mean():.5f} +- {se_q:.5f}, octopus {bo.mean():.5f} +- {se_o:.5f}")
+    assert abs(bq.mean()) <= 3 * se_q + 1e-4
+    assert bo.mean() < -5 * se_o
