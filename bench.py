@@ -45,7 +45,7 @@ WORKLOADS = {
     5: "qjl: B=8, Hq=32, Hkv=8, d=128, 65536 keys/KV head, b=3 + 1-bit QJL residual signs, "
        "1 query token (logits)",
 }
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "k_attn_llm_decode_counters.json")
+PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "llm_decode_hbm_traffic.txt")
 
 
 def kernel_source_hash() -> str:
@@ -256,15 +256,15 @@ def main():
                                   workspace=s["ws"], stages=stages)
 
     if args.counters:
-        # torch.mul over 16 Mi fp32: one elementwise kernel reading and writing
-        # exactly 64 MiB, whose FETCH_SIZE / WRITE_SIZE give the counter scale
+        # a plain 64 MiB copy with the codec kernels' access pattern: its
+        # FETCH_SIZE / WRITE_SIZE readings for known bytes give the counter scale
         src = torch.ones(16 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
         for s in sets:
             if enc_pos0:
                 octo.octo_encode(cb, s["keys"][:, :enc_pos0], s["cache"], pos0=0)
         for k in range(args.steps):
-            torch.mul(src, 1.0, out=dst)
+            octo.octo_debug_copy(dst, src)
             encode(sets[k % R])
             decode(sets[k % R])
         torch.cuda.synchronize()
@@ -338,10 +338,14 @@ def main():
     main_gbs = dec_bytes / t_main / 1e9
     traffic = None
     if os.path.exists(PROFILE_COUNTERS) and args.config == 2:
+        pc = {}
         with open(PROFILE_COUNTERS) as f:
-            pc = json.load(f)
+            for ln in f:
+                if ":" in ln and not ln.startswith(("#", "|", "command")):
+                    k, v = ln.split(":", 1)
+                    pc[k.strip()] = v.strip()
         if pc.get("kernel_source_hash") == kernel_source_hash():
-            traffic = pc.get("hbm_bytes_per_launch")
+            traffic = int(float(pc["k_attn.hbm_bytes_per_launch"]))
     kernel_name = {"logits": "k_logits (fused compressed-K logits)",
                    "attn": "k_attn (fused decode attention)",
                    "attn_mq": "k_mq_attn (multi-query MFMA attention)"}[cfg.mode]

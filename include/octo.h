@@ -202,6 +202,14 @@ octo_status octo_debug_reconstruct(const octo_codebook* cb, const void* packed, 
                                    int64_t n_seq, int64_t n_keys, int64_t cap, float* keys_out,
                                    void* stream);
 
+/* Measurement aid: copy `bytes` (a multiple of 16, both pointers 16-byte
+ * aligned) from device src to device dst with 16-byte loads and stores, 1 KiB
+ * contiguous per wavefront access -- the access pattern of the codec kernels.
+ * Its reading of the HBM traffic counters (rocprofv3 FETCH_SIZE, WRITE_SIZE)
+ * for a known byte count is the scale that turns their readings for the codec
+ * kernels into bytes. */
+octo_status octo_debug_copy(void* dst, const void* src, size_t bytes, void* stream);
+
 const char* octo_status_str(octo_status s);
 const char* octo_last_error(void);
 

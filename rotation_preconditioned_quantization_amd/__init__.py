@@ -63,6 +63,7 @@ _SIGS = {
     "octo_decode_attn_stages": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64,
                                      _F, _P, _P, _SZ, _P, _I]),
     "octo_debug_reconstruct": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
+    "octo_debug_copy": (_I, [_P, _P, _SZ, _P]),
     "octo_status_str": (ctypes.c_char_p, [_I]),
     "octo_last_error": (ctypes.c_char_p, []),
 }
@@ -260,6 +261,14 @@ def octo_decode_attn(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, ou
                                          _ptr(workspace), workspace.numel(), _stream(stream), stages),
            "octo_decode_attn")
     return out
+
+
+def octo_debug_copy(dst, src, stream=None):
+    """Plain 16-byte-access device copy of src into dst (same byte size)."""
+    nbytes = src.numel() * src.element_size()
+    if dst.numel() * dst.element_size() != nbytes:
+        raise ValueError("dst and src differ in size")
+    _check(lib().octo_debug_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "octo_debug_copy")
 
 
 def octo_debug_reconstruct(cb: Codebook, cache: Cache, n_keys: int, out=None, stream=None):

@@ -431,7 +431,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
-  const uint4* vlane = (const uint4*)a.v + seq * a.cap * VG::CPR + kq * VG::CPR + lane % VG::CPR;
+  const uint4* vlane0 = (const uint4*)a.v + kq * VG::CPR + lane % VG::CPR;
+  const uint4* vlane = vlane0 + seq * a.cap * VG::CPR;
 
   // prologue loads, then the first two tiles of this wave
   // prologue (one round trip: LDS tables by DMA, the query words), then tiles
@@ -442,12 +443,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   KTile<D, B, QJL> cur, nxt;
   uint4 vv[NVL];
   // Loads are issued without conditions (a wave with no tile, or past its
-  // last one, re-reads a tile of the block that is already in flight, so
-  // nothing extra comes from HBM): no control flow between them keeps the
-  // compiler's memory-counter waits exact.
-  const int64_t t0 = t < t_end ? t : t_begin;
-  load_ktile<D, B, QJL>(a, seq, t0, lane, cur);
-  load_vtile<D>(vlane, t0, vv);
+  // last one, reads tile 0 of sequence 0 instead, which stays in the L2): no
+  // control flow between them keeps the compiler's memory-counter waits exact.
+  const bool any = t < t_end;
+  load_ktile<D, B, QJL>(a, any ? seq : 0, any ? t : 0, lane, cur);
+  load_vtile<D>(any ? vlane : vlane0, any ? t : 0, vv);
 
   float m[4], l[4];
   floatx4 o[8];
@@ -526,10 +526,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // V rows as soon as this tile's P.V has consumed the V registers.  Other
   // waves on the SIMD cover the remaining latency.
   for (; t < t_end; t += 4) {
-    const int64_t tn = t + 4 < t_end ? t + 4 : t;
-    load_ktile<D, B, QJL>(a, seq, tn, lane, nxt);
+    // past the wave's last tile the loads go to tile 0 of sequence 0, which
+    // every wave shares and the L2 keeps
+    const bool more = t + 4 < t_end;
+    const int64_t tn = more ? t + 4 : 0;
+    load_ktile<D, B, QJL>(a, more ? seq : 0, tn, lane, nxt);
     process(cur, vv, t);
-    load_vtile<D>(vlane, tn, vv);
+    load_vtile<D>(more ? vlane : vlane0, tn, vv);
     cur = nxt;
   }
 
@@ -636,6 +639,21 @@ __global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
     const float inv = den > 0.f ? 1.0f / den : 0.f;
     *(float2*)(a.out + row * D + 2 * cp) = make_float2(num.x * inv, num.y * inv);
   }
+}
+
+__global__ __launch_bounds__(256) void k_copy16(uint4* dst, const uint4* src, int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    dst[i] = src[i];
+}
+
+hipError_t launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s) {
+  if (n16 <= 0) return hipSuccess;
+  int64_t blocks = (n16 + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(k_copy16, dim3((unsigned)blocks), dim3(256), 0, s, (uint4*)dst,
+                     (const uint4*)src, n16);
+  return hipGetLastError();
 }
 
 __global__ void k_fill_zero(float* p, int64_t n) {

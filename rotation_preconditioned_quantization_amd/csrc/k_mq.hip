@@ -26,11 +26,49 @@ constexpr int kMQQueries = 128;  // queries per workgroup (32 per wave)
 
 template <int D>
 struct MQShape {
-  static constexpr int KT = D == 64 ? 256 : 128;  // keys per tile
-  static constexpr int KPW = KT / 4;              // keys rebuilt per wave
+  static constexpr int KT = 128;                  // keys per tile
+  static constexpr int KPW = KT / 4;              // keys rebuilt per wave (lanes 0..31)
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
   static constexpr int VP = KT * 2 + 16;          // V^T row pitch in bytes (fp16)
+  static constexpr int KPT = KT * D / (8 * 256);  // keys per thread of the V transpose
 };
+
+// Registers carrying one tile's global data from its loads (issued during
+// the previous tile's matrix work) to its LDS staging.
+template <int D, int B>
+struct MQStage {
+  uint32_t words[Codec<D, B>::W];   // the lane's key (lanes 0..31)
+  float gamma;
+  uint4 v[MQShape<D>::KPT];         // KPT V rows, 8 dims each
+};
+
+// Loads of tile t (rows past n_keys read the last key; they are masked later).
+template <int D, int B>
+__device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int tid,
+                                        MQStage<D, B>& st) {
+  using S = MQShape<D>;
+  constexpr int W = Codec<D, B>::W;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int64_t tiles64 = a.cap / kTile;
+  int64_t key = t * S::KT + wave * S::KPW + (lane & 31);
+  key = key < a.n_keys ? key : a.n_keys - 1;
+  TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), st.words);
+  st.gamma = a.gamma[seq * a.cap + key];
+  const int c = tid % (D / 8), kg = tid / (D / 8);
+  const uint4* vseq = (const uint4*)a.v + seq * a.cap * (D / 8) + c;
+#pragma unroll
+  for (int i = 0; i < S::KPT; ++i) {
+    int64_t kv = t * S::KT + kg * S::KPT + i;
+    kv = kv < a.n_keys ? kv : a.n_keys - 1;
+    st.v[i] = vseq[kv * (D / 8)];
+  }
+}
+
+// bf16 pair -> f16 pair (V of the multi-query path must lie in fp16 range).
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
+  return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
+                                                                 __uint_as_float(w & 0xffff0000u)));
+}
 
 template <int D, int B>
 __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
@@ -95,46 +133,69 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
   const int64_t ntile = (a.n_keys + KT - 1) / KT;
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   const int64_t t_end = t_begin + a.tiles_per_split < ntile ? t_begin + a.tiles_per_split : ntile;
-  const int64_t tiles64 = a.cap / kTile;
-  const unsigned short* vseq = (const unsigned short*)a.v + seq * a.cap * D;
+  constexpr int KPT = S::KPT;
+
+  MQStage<D, B> st;
+  mq_load<D, B>(a, seq, t_begin < ntile ? t_begin : 0, tid, st);
+  __syncthreads();  // s_dir / s_rho
 
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int64_t k0 = t * KT;
     __syncthreads();  // previous tile's LDS reads are done
-    // 1. rebuild keys
+    // 1. rebuild keys (lanes 0..31 of each wave, one key each) into fp16 rows
     if (lane < KPW) {
       const int kk = wave * KPW + lane;
-      const int64_t key = k0 + kk;
-      _Float16* row = (_Float16*)(s_k + kk * KP);
-      if (key < a.n_keys) {
-        uint32_t words[W];
-        TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), words);
+      const bool ok = k0 + kk < a.n_keys;
+      // triplets in order; each 8-dim group goes to LDS as soon as it is whole
+      float u[3 * T];
+      uint4* row = (uint4*)(s_k + kk * KP);
 #pragma unroll
-        for (int i = 0; i < T; ++i) {
-          const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
-          const float4 n = s_dir[code & C::DIR_MASK];
-          const float rh = s_rho[code >> (C::BX + C::BE)];
-          row[3 * i] = (_Float16)(rh * n.x);
-          if (3 * i + 1 < D) row[3 * i + 1] = (_Float16)(rh * n.y);
-          if (3 * i + 2 < D) row[3 * i + 2] = (_Float16)(rh * n.z);
+      for (int i = 0; i < T; ++i) {
+        const uint32_t code = field_at<W>(st.words, i * C::BT, C::BT);
+        const float4 n = s_dir[code & C::DIR_MASK];
+        const float rh = ok ? s_rho[code >> (C::BX + C::BE)] : 0.f;
+        u[3 * i] = rh * n.x;
+        u[3 * i + 1] = rh * n.y;
+        u[3 * i + 2] = rh * n.z;
+#pragma unroll
+        for (int j = 0; j < D / 8; ++j) {
+          if (8 * j + 7 >= 3 * i && 8 * j + 7 < 3 * i + 3) {   // group j completed by triplet i
+            uint32_t w[4];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(u[8 * j + 2 * e],
+                                                                             u[8 * j + 2 * e + 1]));
+            row[j] = make_uint4(w[0], w[1], w[2], w[3]);
+          }
         }
-        s_g[kk] = a.gamma[seq * a.cap + key];
-      } else {
+      }
+      s_g[kk] = ok ? st.gamma : 0.f;
+    }
+    // 2. V tile transposed to [dim][key] fp16: this thread's KPT keys x 8 dims
+    {
+      const int c = tid % (D / 8), kg = tid / (D / 8);
+      uint32_t h[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
 #pragma unroll
-        for (int j = 0; j < D; ++j) row[j] = (_Float16)0.f;
-        s_g[kk] = 0.f;
+      for (int i = 0; i < KPT; ++i) {
+        const bool ok = k0 + kg * KPT + i < a.n_keys;
+        const uint32_t src[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) h[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
+      }
+#pragma unroll
+      for (int dd = 0; dd < 8; ++dd) {
+        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+        uint32_t col[KPT / 2];
+#pragma unroll
+        for (int i = 0; i < KPT / 2; ++i)
+          col[i] = __builtin_amdgcn_perm(h[2 * i + 1][dd >> 1], h[2 * i][dd >> 1], sel);
+        unsigned char* dst = s_vt + (8 * c + dd) * VP + kg * KPT * 2;
+        if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
+        else *(uint4*)dst = make_uint4(col[0], col[1], col[2], col[3]);
       }
     }
-    // 2. V tile, transposed to [dim][key] fp16
-    for (int c = tid; c < KT * (D / 8); c += 256) {
-      const int kk = c / (D / 8), part = c % (D / 8);
-      uint4 u = make_uint4(0, 0, 0, 0);
-      if (k0 + kk < a.n_keys) u = *(const uint4*)(vseq + (k0 + kk) * D + part * 8);
-      float f[8];
-      cvt_chunk<DT_BF16>(u, f);
-#pragma unroll
-      for (int i = 0; i < 8; ++i) *(_Float16*)(s_vt + (part * 8 + i) * VP + kk * 2) = (_Float16)f[i];
-    }
+    // next tile's loads fly during this tile's matrix work
+    mq_load<D, B>(a, seq, t + 1 < t_end ? t + 1 : t, tid, st);
     __syncthreads();
 
     // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T

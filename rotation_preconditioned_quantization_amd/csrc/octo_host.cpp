@@ -816,6 +816,13 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   return hip_status(launch_combine(c, s), "combine launch");
 }
 
+octo_status octo_debug_copy(void* dst, const void* src, size_t bytes, void* stream) {
+  if (!dst || !src || !aligned(dst, 16) || !aligned(src, 16) || bytes % 16)
+    return fail(OCTO_ERR_INVALID_ARG, "copy needs 16-byte aligned pointers and size");
+  return hip_status(launch_copy16(dst, src, (int64_t)(bytes / 16), (hipStream_t)stream),
+                    "copy launch");
+}
+
 octo_status octo_debug_reconstruct(const octo_codebook* cb, const void* packed, const float* gamma,
                                    int64_t n_seq, int64_t n_keys, int64_t cap, float* keys_out,
                                    void* stream) {

@@ -111,6 +111,7 @@ hipError_t launch_logits(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_
 hipError_t launch_attn(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s);
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+hipError_t launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s);
 int mq_tile_keys(int d);  // keys per tile of the multi-query kernel

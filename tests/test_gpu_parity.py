@@ -462,3 +462,15 @@ def test_qjl_seed_averaged_bias():
     say(f"[qjl-bias] beta qjl {bq.mean():.5f} +- {se_q:.5f}, octopus {bo.mean():.5f} +- {se_o:.5f}")
     assert abs(bq.mean()) <= 3 * se_q + 1e-4
     assert bo.mean() < -5 * se_o
+
+
+@pytest.mark.gpu
+def test_debug_copy_is_exact():
+    """The traffic-calibration copy moves the bytes unchanged (ragged sizes)."""
+    octo = _octo()
+    for n in (4, 1 << 10, (1 << 20) + 12):
+        src = torch.randint(-2**31, 2**31 - 1, (n,), dtype=torch.int32, device="cuda")
+        dst = torch.zeros_like(src)
+        octo.octo_debug_copy(dst, src)
+        torch.cuda.synchronize()
+        assert torch.equal(dst, src)
