@@ -434,20 +434,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const uint4* vlane0 = (const uint4*)a.v + kq * VG::CPR + lane % VG::CPR;
   const uint4* vlane = vlane0 + seq * a.cap * VG::CPR;
 
-  // prologue loads, then the first two tiles of this wave
-  // prologue (one round trip: LDS tables by DMA, the query words), then tiles
-  SQPre<D, B, QJL> pre;
-  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
-  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
+  // The wave's first tile is requested before the prologue (LDS tables by
+  // DMA, the query words): the prologue's round trip then overlaps the
+  // tile's, and the first LDS access waits for both.  Loads are issued
+  // without conditions (a wave with no tile reads tile 0 of sequence 0
+  // instead): no control flow between them keeps the compiler's
+  // memory-counter waits exact.
   int64_t t = t_begin + wave;
   KTile<D, B, QJL> cur, nxt;
   uint4 vv[NVL];
-  // Loads are issued without conditions (a wave with no tile, or past its
-  // last one, reads tile 0 of sequence 0 instead, which stays in the L2): no
-  // control flow between them keeps the compiler's memory-counter waits exact.
   const bool any = t < t_end;
   load_ktile<D, B, QJL>(a, any ? seq : 0, any ? t : 0, lane, cur);
   load_vtile<D>(any ? vlane : vlane0, any ? t : 0, vv);
+  SQPre<D, B, QJL> pre;
+  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
+  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
 
   float m[4], l[4];
   floatx4 o[8];
@@ -524,17 +525,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   // The next tile's code words load while this tile's logits are formed; its
   // V rows as soon as this tile's P.V has consumed the V registers.  Other
-  // waves on the SIMD cover the remaining latency.
-  for (; t < t_end; t += 4) {
-    // past the wave's last tile the loads go to tile 0 of sequence 0, which
-    // every wave shares and the L2 keeps
-    const bool more = t + 4 < t_end;
-    const int64_t tn = more ? t + 4 : 0;
-    load_ktile<D, B, QJL>(a, more ? seq : 0, tn, lane, nxt);
+  // waves on the SIMD cover the remaining latency.  The last tile is peeled
+  // off so that no load is left in flight at the block's final barrier.
+  for (; t + 4 < t_end; t += 4) {
+    load_ktile<D, B, QJL>(a, seq, t + 4, lane, nxt);
     process(cur, vv, t);
-    load_vtile<D>(more ? vlane : vlane0, tn, vv);
+    load_vtile<D>(vlane, t + 4, vv);
     cur = nxt;
   }
+  if (t < t_end) process(cur, vv, t);
 
   // lanes serving different keys of a load hold partial sums of the same dims
 #pragma unroll
@@ -581,63 +580,79 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 // out[row][c] = sum_s 2^(m_s - M) o_s[c] / sum_s 2^(m_s - M) l_s, M = max_s m_s,
-// one wavefront per row.  Lane l handles the column pair 2 (l % (d/2)) of the
-// splits s = l / (d/2) (mod 64 / (d/2)), one 8-byte load per split; the o
-// values of the first splits are requested together with the (m, l) loads,
-// so the row costs about two memory round trips.
+// one 256-thread block per row.  Thread t handles the column pair 2 (t % (d/2))
+// of the splits s = t / (d/2) (mod 256 / (d/2)), one 8-byte load per split;
+// the (m, l) pairs are spread one per thread.  All of the row's loads are
+// issued together, so the row costs one memory round trip plus three LDS
+// reductions.
 constexpr int kCombinePre = 16;
 
 template <int D>
-__global__ __launch_bounds__(64) void k_combine(CombineArgs a) {
-  constexpr int LPS = D / 2;     // lanes per split row
-  constexpr int SPI = 64 / LPS;  // splits per step
+__global__ __launch_bounds__(256) void k_combine(CombineArgs a) {
+  constexpr int LPS = D / 2;      // threads per split row
+  constexpr int SPG = 256 / LPS;  // splits side by side
+  constexpr int MLP = kMaxSplit / 256;
   __shared__ float s_w[kMaxSplit];
+  __shared__ float s_red[2][4];
+  __shared__ float2 s_num[SPG][LPS];
   const int64_t row = blockIdx.x;
-  const int lane = threadIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int ns = a.n_split;
-  const int cp = lane % LPS, so = lane / LPS;
+  const int cp = tid % LPS, so = tid / LPS;
   const float* p = a.part + row * ns * (D + 2);
   float2 pre[kCombinePre];
 #pragma unroll
   for (int k = 0; k < kCombinePre; ++k) {
-    const int sp = so + SPI * k;
+    const int sp = so + SPG * k;
     pre[k] = sp < ns ? *(const float2*)(p + (int64_t)sp * (D + 2) + 2 + 2 * cp) : make_float2(0.f, 0.f);
   }
+  float2 ml[MLP];
   float M = -INFINITY;
-  for (int sp = lane; sp < ns; sp += 64) M = fmaxf(M, p[(int64_t)sp * (D + 2)]);
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const int sp = tid + 256 * k;
+    ml[k] = sp < ns ? *(const float2*)(p + (int64_t)sp * (D + 2)) : make_float2(-INFINITY, 0.f);
+    M = fmaxf(M, ml[k].x);
+  }
   M = wave_max(M);
+  if (lane == 0) s_red[0][wave] = M;
+  __syncthreads();
+  M = fmaxf(fmaxf(s_red[0][0], s_red[0][1]), fmaxf(s_red[0][2], s_red[0][3]));
   float den = 0.f;
-  for (int sp = lane; sp < ns; sp += 64) {
-    const float2 ml = *(const float2*)(p + (int64_t)sp * (D + 2));
-    const float w = ml.x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml.x - M);
-    s_w[sp] = w;
-    den = __builtin_fmaf(w, ml.y, den);
+#pragma unroll
+  for (int k = 0; k < MLP; ++k) {
+    const int sp = tid + 256 * k;
+    const float w = ml[k].x == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ml[k].x - M);
+    if (sp < ns) s_w[sp] = w;
+    den = __builtin_fmaf(w, ml[k].y, den);
   }
   den = wave_sum(den);
+  if (lane == 0) s_red[1][wave] = den;
   __syncthreads();
+  den = (s_red[1][0] + s_red[1][1]) + (s_red[1][2] + s_red[1][3]);
   float2 num = make_float2(0.f, 0.f);
 #pragma unroll
   for (int k = 0; k < kCombinePre; ++k) {
-    const int sp = so + SPI * k;
+    const int sp = so + SPG * k;
     if (sp < ns) {
       num.x = __builtin_fmaf(s_w[sp], pre[k].x, num.x);
       num.y = __builtin_fmaf(s_w[sp], pre[k].y, num.y);
     }
   }
 #pragma unroll 8
-  for (int sp = so + SPI * kCombinePre; sp < ns; sp += SPI) {
+  for (int sp = so + SPG * kCombinePre; sp < ns; sp += SPG) {
     const float2 o = *(const float2*)(p + (int64_t)sp * (D + 2) + 2 + 2 * cp);
     num.x = __builtin_fmaf(s_w[sp], o.x, num.x);
     num.y = __builtin_fmaf(s_w[sp], o.y, num.y);
   }
+  s_num[so][cp] = num;
+  __syncthreads();
+  if (tid < LPS) {
+    float2 tot = s_num[0][tid];
 #pragma unroll
-  for (int sh = LPS; sh < 64; sh <<= 1) {
-    num.x += __shfl_xor(num.x, sh, 64);
-    num.y += __shfl_xor(num.y, sh, 64);
-  }
-  if (so == 0) {
+    for (int g = 1; g < SPG; ++g) { tot.x += s_num[g][tid].x; tot.y += s_num[g][tid].y; }
     const float inv = den > 0.f ? 1.0f / den : 0.f;
-    *(float2*)(a.out + row * D + 2 * cp) = make_float2(num.x * inv, num.y * inv);
+    *(float2*)(a.out + row * D + 2 * tid) = make_float2(tot.x * inv, tot.y * inv);
   }
 }
 
@@ -742,8 +757,8 @@ hipError_t launch_attn(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_se
 hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.rows == 0) return hipSuccess;
   if (a.n_split > kMaxSplit) return hipErrorInvalidValue;
-  if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.rows), dim3(64), 0, s, a);
-  else if (a.d == 128) hipLaunchKernelGGL(k_combine<128>, dim3(a.rows), dim3(64), 0, s, a);
+  if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.rows), dim3(256), 0, s, a);
+  else if (a.d == 128) hipLaunchKernelGGL(k_combine<128>, dim3(a.rows), dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
