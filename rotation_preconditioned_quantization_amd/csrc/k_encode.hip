@@ -11,6 +11,8 @@
 // packed words are stored in the tile's word-group layout (16-byte stores,
 // 1 KiB contiguous per store instruction).  With QJL the same lane also forms the rotated residual
 // r' = u' - u'^, its fp16 norm and the signs of S r' ([YL] 可选的残差修正).
+#include <algorithm>
+
 #include "octo_device.hpp"
 
 namespace octo {
@@ -47,18 +49,15 @@ __device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[4],
   return make_uint4(m[0], m[1], m[2], m[3]);
 }
 
-// Bring the lane's own key row (already sign-flipped, raw bits) into
-// registers: coalesced 16-byte global loads of the whole tile (rows past
-// n_new re-read the last key, so the loads carry no conditions), then NP
-// rounds through the wave's LDS buffer of NR rows.
+// The raw 16-byte chunks of the 64-key tile at j0: coalesced loads, NP
+// phases of NR rows (rows past n_new re-read the last key, so the loads
+// carry no conditions).
 template <int D, int KT>
-__device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
-                                           unsigned char* s_keys, const uint4& smask,
-                                           uint4 (&rowbits)[Stage<D, KT>::CPR]) {
+__device__ __forceinline__ void load_rows(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                          uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE]) {
   using S = Stage<D, KT>;
   const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
   const int col = lane % S::CPR;
-  uint4 raw[S::NP][S::PER_LANE];
 #pragma unroll
   for (int h = 0; h < S::NP; ++h) {
 #pragma unroll
@@ -69,6 +68,16 @@ __device__ __forceinline__ void gather_row(const EncodeArgs& a, int64_t seq, int
       raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + col * 16);
     }
   }
+}
+
+// Hand every lane its own key row (sign-flipped, raw bits) through the
+// wave's LDS buffer of NR rows, one phase at a time.
+template <int D, int KT>
+__device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE],
+                                           int lane, unsigned char* s_keys, const uint4& smask,
+                                           uint4 (&rowbits)[Stage<D, KT>::CPR]) {
+  using S = Stage<D, KT>;
+  const int col = lane % S::CPR;
   const int my_phase = lane / S::NR;
   const unsigned char* row = s_keys + (lane % S::NR) * S::PITCH;
 #pragma unroll
@@ -108,32 +117,169 @@ __device__ __forceinline__ uint32_t quant1_clamp(float x, const uint2* t, float 
   return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
 }
 
-constexpr int kEncWaves = 4;  // waves (64-key tiles) per encoder block
+// Waves (64-key tiles in flight) per encoder block.
+template <bool QJL>
+constexpr int enc_waves() { return 4; }
 
+// Triplet i of the rotated key, zero padded past D.
+template <int D>
+__device__ __forceinline__ void triplet_of(const float (&v)[D], int i, float& x, float& y, float& z) {
+  x = v[3 * i];
+  y = (3 * i + 1 < D) ? v[3 * i + 1] : 0.f;
+  z = (3 * i + 2 < D) ? v[3 * i + 2] : 0.f;
+}
+
+__device__ __forceinline__ float triplet_energy(float x, float y, float z) {
+  return __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x));
+}
+
+// The octahedral (xi, eta) indices of a triplet, i_xi | i_eta << BX
+// ([YL] 八面体折叠).  p = (x, y)/l1; in the lower hemisphere (z < 0) the fold
+// (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (likewise for y), with
+// sgn(0) = +1 (the sign bit is copied; -0 only occurs for an all-zero
+// triplet, where |z| = 0).  A zero triplet maps to (0, 0), i.e. n = (0,0,1).
+template <int BX>
+__device__ __forceinline__ uint32_t xi_eta_code(float x, float y, float z, const uint2* tx,
+                                                float sx, float bx, const uint2* te, float se,
+                                                float be) {
+  const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
+  const float il = __builtin_amdgcn_rcpf(__builtin_fmaxf(l1, 1e-37f));
+  const float tz = __builtin_fmaxf(-z, 0.0f);
+  const float xi = (x + __builtin_copysignf(tz, x)) * il;
+  const float eta = (y + __builtin_copysignf(tz, y)) * il;
+  return quant1(xi, tx, sx, bx) | (quant1(eta, te, se, be) << BX);
+}
+
+// OR a code into bits [i BT, (i + 1) BT) of the key's LSB-first word stream.
+template <int BT, int W>
+__device__ __forceinline__ void pack_code(uint32_t (&words)[W], int i, uint32_t code) {
+  const int pos = i * BT, wi = pos >> 5, off = pos & 31;
+  words[wi] |= code << off;
+  if (off + BT > 32) words[wi + 1] |= code >> (32 - off);
+}
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// v_writelane_b32: a wave-uniform value into one lane of a VGPR.
+extern "C" __device__ int octo_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// QJL matrix in LDS: planes [S_hi | S_lo] of f16 rows, padded so that the 32
+// rows one B-operand load touches fall on distinct banks.
+template <int D>
+struct SLds {
+  static constexpr int PITCH = 2 * D + 16;      // bytes per row
+  static constexpr int BYTES = 2 * D * PITCH;   // both planes
+};
+
+// QJL signs of the wave's 64 residuals on the matrix cores: P = R' S^T for
+// the 64 keys x d projections, P[key][j] = <S_j, r'_key>, bit j of the key's
+// sign words = (P >= 0) ([YL] 可选的残差修正; sgn(0) = +1).
+//   r' (one key per lane, fp32, scaled by 2^12: signs unchanged, f16 range
+//   kept) and S are split into f16 high and low parts, x = x_hi + x_lo with
+//   both parts rounded to nearest; the product is summed from the three
+//   terms hi*hi + hi*lo + lo*hi on v_mfma_f32_32x32x16_f16 (products exact,
+//   fp32 accumulate).  The dropped lo*lo term and the rounding of the low
+//   parts leave a relative error near 2^-23 |S_jk| |r'_k| per term.
+//   A operands: rows = keys.  Lane (l % 32, g = l / 32) of the 32-key block
+//   supplies dims 16 kb + 8 g .. + 7 of its row; a lane holds its own key's
+//   dims, so v_permlane32_swap exchanges the upper half of the dims 0..7
+//   words with the lower half of the dims 8..15 words, which yields the
+//   operands of key block 0 (keys 0..31) and key block 1 (keys 32..63).
+//   B operands: S rows j = 32 nb + l % 32, dims 16 kb + 8 g .. + 7, from LDS.
+//   Output register r of lane (l % 32, g) is key 8 (r / 4) + 4 g + r % 4 of the
+//   block and projection l % 32 of the block: a ballot over the wave gives the
+//   32 sign bits of two keys at once, written into those keys' lanes.
+template <int D>
+__device__ __forceinline__ void qjl_signs(const float (&v)[D], const unsigned char* s_S, int lane,
+                                          uint32_t (&sw)[D / 32]) {
+  constexpr int NK = D / 16;  // 16-dim contraction blocks
+  constexpr int NN = D / 32;  // 32-projection output blocks
+  constexpr int PITCH = SLds<D>::PITCH;
+  half8 ah[2][NK], al[2][NK];
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) {
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float x0 = v[16 * kb + 2 * p] * 4096.f, x1 = v[16 * kb + 2 * p + 1] * 4096.f;
+      const __half2 h = __float22half2_rn(make_float2(x0, x1));
+      const float2 hf = __half22float2(h);
+      const __half2 l = __float22half2_rn(make_float2(x0 - hf.x, x1 - hf.y));
+      ph[p] = __builtin_bit_cast(uint32_t, h);
+      pl[p] = __builtin_bit_cast(uint32_t, l);
+    }
+    uint32_t h0[4], h1[4], l0[4], l1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto sh = __builtin_amdgcn_permlane32_swap(ph[i], ph[4 + i], false, false);
+      h0[i] = sh[0];
+      h1[i] = sh[1];
+      const auto sl = __builtin_amdgcn_permlane32_swap(pl[i], pl[4 + i], false, false);
+      l0[i] = sl[0];
+      l1[i] = sl[1];
+    }
+    ah[0][kb] = __builtin_bit_cast(half8, make_uint4(h0[0], h0[1], h0[2], h0[3]));
+    ah[1][kb] = __builtin_bit_cast(half8, make_uint4(h1[0], h1[1], h1[2], h1[3]));
+    al[0][kb] = __builtin_bit_cast(half8, make_uint4(l0[0], l0[1], l0[2], l0[3]));
+    al[1][kb] = __builtin_bit_cast(half8, make_uint4(l1[0], l1[1], l1[2], l1[3]));
+  }
+  // The B operands are the same for every tile: an offset the compiler
+  // cannot see through (always 0) keeps their LDS reads inside the tile loop
+  // instead of hoisting all of them into registers ahead of it.
+  int opaque0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(opaque0));
+  const int ln = lane & 31, g = lane >> 5;
+  s_S += opaque0;
+#pragma unroll
+  for (int nb = 0; nb < NN; ++nb) {
+    floatx16 c[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { c[0][r] = 0.f; c[1][r] = 0.f; }
+    const unsigned char* row = s_S + (32 * nb + ln) * PITCH + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+      const half8 bh = *(const half8*)(row + 32 * kb);
+      const half8 bl = *(const half8*)(row + D * PITCH + 32 * kb);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mb][kb], bh, c[mb], 0, 0, 0);
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mb][kb], bl, c[mb], 0, 0, 0);
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[mb][kb], bh, c[mb], 0, 0, 0);
+      }
+    }
+    int w = 0;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint64_t m = __ballot(c[mb][r] >= 0.f);
+        const int key = 32 * mb + 8 * (r >> 2) + (r & 3);
+        w = octo_writelane((int)(uint32_t)m, key, w);
+        w = octo_writelane((int)(uint32_t)(m >> 32), key + 4, w);
+      }
+    sw[nb] = (uint32_t)w;
+  }
+}
+
+// Encode the 64-key tile at j0: one key per lane, entirely in registers.
 template <int D, int B, int KT, bool QJL>
-__global__ __launch_bounds__(64 * kEncWaves) void k_encode(EncodeArgs a) {
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                            unsigned char* s_keys, const uint4& smask,
+                                            const uint2* s_qx, const uint2* s_qe, const uint2* s_qr,
+                                            const unsigned char* s_S, const float4* s_dir,
+                                            const float* s_rho) {
   using C = Codec<D, B>;
   using S = Stage<D, KT>;
   constexpr int T = C::T, W = C::W;
-
-  __shared__ __align__(16) unsigned char s_keys[kEncWaves][S::NR * S::PITCH];
-  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
-
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t seq = blockIdx.y;
-  const int64_t j0 = ((int64_t)blockIdx.x * kEncWaves + wave) * kTile;
-
-  // the block's waves share the quantiser tables
-  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 64 * kEncWaves) s_qx[i] = a.t.qx.t[i];
-  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * kEncWaves) s_qe[i] = a.t.qe.t[i];
-  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * kEncWaves) s_qr[i] = a.t.qr2.t[i];
-  __syncthreads();
-  if (j0 >= a.n_new) return;
-  const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
   float v[D];
   {
     uint4 rowbits[S::CPR];
-    gather_row<D, KT>(a, seq, j0, lane, s_keys[wave], smask, rowbits);
+    {
+      uint4 raw[S::NP][S::PER_LANE];
+      load_rows<D, KT>(a, seq, j0, lane, raw);
+      stage_rows<D, KT>(raw, lane, s_keys, smask, rowbits);
+    }
     if constexpr (KT == DT_F32) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
@@ -165,113 +311,119 @@ __global__ __launch_bounds__(64 * kEncWaves) void k_encode(EncodeArgs a) {
 
   const float sx = a.t.qx.scale, bx = a.t.qx.bias;
   const float se = a.t.qe.scale, be = a.t.qe.bias;
+  // (the rho^2 table starts at 0: bias 0)
+  const float sr = a.t.qr2.scale, mr = (float)(a.t.qr2.nb - 1);
   uint32_t words[W];
 #pragma unroll
   for (int w = 0; w < W; ++w) words[w] = 0u;
-  uint32_t codes[QJL ? T : 1];
-  float e[T];
-  float tot = 0.f;
-
-  // Pass 1: triplet energies and the octahedral (xi, eta) indices, packed
-  // into place.  p = (x, y)/l1; in the lower hemisphere (z < 0) the fold
-  // (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (likewise for y), with
-  // sgn(0) = +1 (the sign bit is copied; -0 only occurs for an all-zero
-  // triplet, where |z| = 0).  A zero triplet maps to (0, 0), i.e. n = (0,0,1).
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const float x = v[3 * i];
-    const float y = (3 * i + 1 < D) ? v[3 * i + 1] : 0.f;
-    const float z = (3 * i + 2 < D) ? v[3 * i + 2] : 0.f;
-    e[i] = __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x));
-    tot += e[i];
-    const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
-    const float il = __builtin_amdgcn_rcpf(__builtin_fmaxf(l1, 1e-37f));
-    const float tz = __builtin_fmaxf(-z, 0.0f);
-    const float xi = (x + __builtin_copysignf(tz, x)) * il;
-    const float eta = (y + __builtin_copysignf(tz, y)) * il;
-    const uint32_t code = quant1(xi, s_qx, sx, bx) | (quant1(eta, s_qe, se, be) << C::BX);
-    if constexpr (QJL) codes[i] = code;
-    const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
-    words[wi] |= code << off;
-    if (off + C::BT > 32) words[wi + 1] |= code >> (32 - off);
-  }
-  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
-  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
-
-  // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
-  // (the rho^2 table starts at 0: bias 0)
-  const float sr = a.t.qr2.scale, mr = (float)(a.t.qr2.nb - 1);
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const uint32_t code = quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE);
-    if constexpr (QJL) codes[i] |= code;
-    const int pos = i * C::BT, wi = pos >> 5, off = pos & 31;
-    words[wi] |= code << off;
-    if (off + C::BT > 32) words[wi + 1] |= code >> (32 - off);
-  }
-
   const int64_t j = j0 + lane;
   const bool valid = j < a.n_new;
   const int64_t pos = a.pos0 + j;
   const int64_t tiles = a.cap / kTile;
+  float tot = 0.f;
+
+  // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
+  float e[T];
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    float x, y, z;
+    triplet_of<D>(v, i, x, y, z);
+    e[i] = triplet_energy(x, y, z);
+    tot += e[i];
+    pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+  }
+  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
+  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+  // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
+#pragma unroll
+  for (int i = 0; i < T; ++i) {
+    pack_code<C::BT>(words, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+  }
   if (valid) {
     TileWords<W>::store(a.packed + (seq * tiles + (pos >> 6)) * W * kTile, (int)(pos & 63), words);
     a.gamma[seq * a.cap + pos] = gamma;
   }
 
   if constexpr (QJL) {
-    if (a.qjl_bits == nullptr) return;
-    // Rotated unit-direction residual r' = u' - u'^ over the D real coordinates.
-    const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
-    float nu2 = 0.f;
+    if (a.qjl_bits != nullptr) {
+      // Rotated unit-direction residual r' = u' - u'^ over the D real coordinates.
+      const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+      float nu2 = 0.f;
 #pragma unroll
-    for (int i = 0; i < T; ++i) {
-      const float4 n = a.t.dirtab[codes[i] & C::DIR_MASK];
-      const float rh = a.t.rho_tab[codes[i] >> (C::BX + C::BE)];
-      const float nc[3] = {n.x, n.y, n.z};
+      for (int i = 0; i < T; ++i) {
+        const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
+        const float4 n = s_dir[code & C::DIR_MASK];
+        const float rh = s_rho[code >> (C::BX + C::BE)];
+        const float nc[3] = {n.x, n.y, n.z};
 #pragma unroll
-      for (int c = 0; c < 3; ++c) {
-        if (3 * i + c < D) {
-          const float r = __builtin_fmaf(v[3 * i + c], inv_norm, -rh * nc[c]);
-          v[3 * i + c] = r;
-          nu2 = __builtin_fmaf(r, r, nu2);
+        for (int c = 0; c < 3; ++c) {
+          if (3 * i + c < D) {
+            const float r = __builtin_fmaf(v[3 * i + c], inv_norm, -rh * nc[c]);
+            v[3 * i + c] = r;
+            nu2 = __builtin_fmaf(r, r, nu2);
+          }
         }
       }
-    }
-    const float nu = __builtin_sqrtf(nu2);
-    uint32_t sbits[D / 32];
-#pragma unroll
-    for (int w = 0; w < D / 32; ++w) sbits[w] = 0u;
-    const float* __restrict__ Sm = a.t.S;
-#pragma unroll 1
-    for (int r = 0; r < D; r += 32) {
-      uint32_t m = 0u;
-#pragma unroll 2
-      for (int rr = 0; rr < 32; ++rr) {
-        const float* __restrict__ srow = Sm + (int64_t)(r + rr) * D;
-        float acc = 0.f;
-#pragma unroll
-        for (int k = 0; k < D; ++k) acc = __builtin_fmaf(srow[k], v[k], acc);
-        m |= (acc >= 0.f ? 1u : 0u) << rr;
+      const float nu = __builtin_sqrtf(nu2);
+      uint32_t sbits[D / 32];
+      qjl_signs<D>(v, s_S, lane, sbits);
+      if (valid) {
+        TileWords<D / 32>::store(a.qjl_bits + (seq * tiles + (pos >> 6)) * (D / 32) * kTile,
+                                 (int)(pos & 63), sbits);
+        a.qjl_norm[seq * a.cap + pos] = __half_as_ushort(__float2half_rn(nu));
       }
-#pragma unroll
-      for (int w = 0; w < D / 32; ++w)
-        if (w == r / 32) sbits[w] = m;
     }
-    if (valid) {
-      TileWords<D / 32>::store(a.qjl_bits + (seq * tiles + (pos >> 6)) * (D / 32) * kTile,
-                               (int)(pos & 63), sbits);
-      a.qjl_norm[seq * a.cap + pos] = __half_as_ushort(__float2half_rn(nu));
-    }
+  }
+}
+
+template <int D, int B, int KT, bool QJL>
+__global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) {
+  using C = Codec<D, B>;
+  using S = Stage<D, KT>;
+  constexpr int EW = enc_waves<QJL>();
+  __shared__ __align__(16) unsigned char s_keys[EW][S::NR * S::PITCH];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
+  __shared__ __align__(16) unsigned char s_S[QJL ? SLds<D>::BYTES : 16];
+  __shared__ float4 s_dir[QJL ? C::NDIR : 1];
+  __shared__ float s_rho[QJL ? C::LR : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seq = blockIdx.y;
+
+  // the block's waves share the quantiser tables (and the QJL matrix)
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 64 * EW) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * EW) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * EW) s_qr[i] = a.t.qr2.t[i];
+  if constexpr (QJL) {
+    constexpr int CPRS = 2 * D / 16;  // 16-byte chunks per S row
+    for (int c = threadIdx.x; c < 2 * D * CPRS; c += 64 * EW)
+      *(uint4*)(s_S + (c / CPRS) * SLds<D>::PITCH + (c % CPRS) * 16) = a.t.S16[c];
+    for (int i = threadIdx.x; i < C::NDIR; i += 64 * EW) s_dir[i] = a.t.dirtab[i];
+    if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
+  }
+  __syncthreads();
+  const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
+  // A wave encodes one 64-key tile; with QJL the grid is smaller than the
+  // key count and the block's waves take tiles round-robin.
+  for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
+       j0 += (int64_t)gridDim.x * EW * kTile) {
+    encode_tile<D, B, KT, QJL>(a, seq, j0, lane, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S, s_dir,
+                               s_rho);
+    if constexpr (!QJL) break;
   }
 }
 
 template <int D, int B, int KT, bool QJL>
 static hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
-  const int64_t per = (int64_t)kEncWaves * kTile;
-  const dim3 grid((unsigned)((a.n_new + per - 1) / per), (unsigned)n_seq);
-  hipLaunchKernelGGL((k_encode<D, B, KT, QJL>), grid, dim3(64 * kEncWaves), 0, s, a);
+  constexpr int EW = enc_waves<QJL>();
+  const int64_t per = (int64_t)EW * kTile;
+  int64_t gx = (a.n_new + per - 1) / per;
+  // With QJL each block first stages the matrix in LDS: a grid of about two
+  // blocks per compute unit then loops over the tiles.
+  if (QJL) gx = std::min<int64_t>(gx, std::max<int64_t>(1, (512 + n_seq - 1) / n_seq));
+  const dim3 grid((unsigned)gx, (unsigned)n_seq);
+  hipLaunchKernelGGL((k_encode<D, B, KT, QJL>), grid, dim3(64 * EW), 0, s, a);
   return hipGetLastError();
 }
 

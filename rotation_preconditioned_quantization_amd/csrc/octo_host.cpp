@@ -244,6 +244,19 @@ octo_status build_device_tables(octo_codebook* cb) {
     }
   }
 
+  // QJL matrix for the encoder's matrix-core projection: S = S_hi + S_lo with
+  // S_hi = f16(S) and S_lo = f16(S - S_hi) (round to nearest even), planes
+  // [hi | lo], each d x d row-major.  S_hi + S_lo carries 22 bits of S.
+  std::vector<_Float16> s16;
+  if (!cb->S.empty()) {
+    s16.resize(2 * cb->S.size());
+    for (size_t i = 0; i < cb->S.size(); ++i) {
+      const _Float16 h = (_Float16)cb->S[i];
+      s16[i] = h;
+      s16[cb->S.size() + i] = (_Float16)(cb->S[i] - (float)h);
+    }
+  }
+
   // One device allocation, 256-byte aligned regions.
   struct Region { const void* src; size_t bytes; size_t off; };
   std::vector<Region> reg = {
@@ -251,7 +264,8 @@ octo_status build_device_tables(octo_codebook* cb) {
       {qx.t.data(), qx.t.size() * 4, 0},         {qe.t.data(), qe.t.size() * 4, 0},
       {qr2.t.data(), qr2.t.size() * 4, 0},
       {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0},
-      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0}};
+      {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0},
+      {s16.empty() ? nullptr : s16.data(), s16.size() * 2, 0}};
   size_t total = 0;
   for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
   int prev = 0;
@@ -292,6 +306,7 @@ octo_status build_device_tables(octo_codebook* cb) {
   t.qr2 = qt(qr2, 4);
   t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[5].off);
   t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[6].off);
+  t.S16 = s16.empty() ? nullptr : (const uint4*)(base + reg[7].off);
   for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
   return OCTO_OK;
 }
