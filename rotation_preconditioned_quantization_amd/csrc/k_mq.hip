@@ -3,10 +3,12 @@
 // MFMA ([YL] 工程实现: keys rebuilt on the fly, FlashAttention tiling, online
 // softmax; the block/chunk decoding of the video workloads in 实验结果).
 //
-// Workgroup = 4 wavefronts = 128 queries of one head over one split of the
-// cache.  Per tile of KT keys:
-//   1. every wave rebuilds KT/4 keys (one per lane) from the packed stream
-//      into LDS as fp16 rotated unit directions u'^ (gamma kept in fp32);
+// Workgroup = 8 wavefronts = 256 queries of one head over one split of the
+// cache, so every rebuilt key serves 256 queries.  Per tile of 128 keys:
+//   1. the keys are rebuilt from the packed stream into LDS as fp16 rotated
+//      unit directions u'^ (gamma kept in fp32): wave w takes the 64 keys of
+//      half w / 4 (one per lane) and the dim quarter w % 4 of each, i.e. only
+//      the triplets that touch those dims;
 //   2. the bf16 V tile is stored transposed in LDS as fp16;
 //   3. each wave computes S^T = K^ Q'^T for its 32 queries with
 //      v_mfma_f32_32x32x16_f16 (fp32 accumulate), scales by gamma, runs the
@@ -20,29 +22,34 @@ namespace octo {
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half4 __attribute__((ext_vector_type(4)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMQQueries = 128;  // queries per workgroup (32 per wave)
+constexpr int kMQWaves = 8;                  // waves per workgroup
+constexpr int kMQQueries = 32 * kMQWaves;    // queries per workgroup (32 per wave)
+constexpr int kMQParts = 4;                  // waves sharing the rebuild of 64 keys (dim quarters)
 
 template <int D>
 struct MQShape {
   static constexpr int KT = 128;                  // keys per tile
-  static constexpr int KPW = KT / 4;              // keys rebuilt per wave (lanes 0..31)
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
   static constexpr int VP = KT * 2 + 16;          // V^T row pitch in bytes (fp16)
-  static constexpr int KPT = KT * D / (8 * 256);  // keys per thread of the V transpose
+  static constexpr int NTH = 64 * kMQWaves;       // threads per workgroup
+  static constexpr int KPT = KT * D / (8 * NTH);  // keys per thread of the V transpose
+  static constexpr int DQ = D / kMQParts;         // dims rebuilt per lane
 };
 
 // Registers carrying one tile's global data from its loads (issued during
 // the previous tile's matrix work) to its LDS staging.
 template <int D, int B>
 struct MQStage {
-  uint32_t words[Codec<D, B>::W];   // the lane's key (lanes 0..31)
+  uint32_t words[Codec<D, B>::W];   // the lane's key
   float gamma;
   uint4 v[MQShape<D>::KPT];         // KPT V rows, 8 dims each
 };
 
 // Loads of tile t (rows past n_keys read the last key; they are masked later).
+// The four waves of a key half all load the half's words (the same lines).
 template <int D, int B>
 __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int tid,
                                         MQStage<D, B>& st) {
@@ -50,7 +57,7 @@ __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t,
   constexpr int W = Codec<D, B>::W;
   const int lane = tid & 63, wave = tid >> 6;
   const int64_t tiles64 = a.cap / kTile;
-  int64_t key = t * S::KT + wave * S::KPW + (lane & 31);
+  int64_t key = t * S::KT + 64 * (wave / kMQParts) + lane;
   key = key < a.n_keys ? key : a.n_keys - 1;
   TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), st.words);
   st.gamma = a.gamma[seq * a.cap + key];
@@ -70,18 +77,47 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
                                                                  __uint_as_float(w & 0xffff0000u)));
 }
 
+// Dims [PART DQ, (PART + 1) DQ) of the lane's rebuilt key u'^ = rho^ n^ per
+// triplet, from the triplets that touch them, to the key's fp16 row in LDS.
+template <int D, int B, int PART>
+__device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, bool ok, const float4* s_dir,
+                                           const float* s_rho, unsigned char* krow) {
+  using C = Codec<D, B>;
+  constexpr int DQ = MQShape<D>::DQ, LO = PART * DQ, HI = LO + DQ;
+  float u[DQ];
+#pragma unroll
+  for (int i = LO / 3; i <= (HI - 1) / 3; ++i) {
+    const uint32_t code = field_at<C::W>(st.words, i * C::BT, C::BT);
+    const float4 n = s_dir[code & C::DIR_MASK];
+    const float rh = ok ? s_rho[code >> (C::BX + C::BE)] : 0.f;
+    const float t3[3] = {rh * n.x, rh * n.y, rh * n.z};
+#pragma unroll
+    for (int c = 0; c < 3; ++c)
+      if (3 * i + c >= LO && 3 * i + c < HI) u[3 * i + c - LO] = t3[c];
+  }
+  uint4* row = (uint4*)(krow + LO * 2);
+#pragma unroll
+  for (int j = 0; j < DQ / 8; ++j) {
+    uint32_t w[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(u[8 * j + 2 * e], u[8 * j + 2 * e + 1]));
+    row[j] = make_uint4(w[0], w[1], w[2], w[3]);
+  }
+}
+
 template <int D, int B>
-__global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
+__global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
   using C = Codec<D, B>;
   using S = MQShape<D>;
-  constexpr int T = C::T, W = C::W;
-  constexpr int KT = S::KT, KPW = S::KPW, KP = S::KP, VP = S::VP;
+  constexpr int T = C::T;
+  constexpr int KT = S::KT, KP = S::KP, VP = S::VP, NTH = S::NTH;
   constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
 
   __shared__ __align__(16) unsigned char s_k[KT * KP];
   __shared__ __align__(16) unsigned char s_vt[D * VP];
-  __shared__ float s_g[KT];
+  __shared__ __align__(16) float s_g[KT];
   __shared__ float4 s_dir[C::NDIR];
   __shared__ float s_rho[C::LR];
 
@@ -91,10 +127,12 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
   const int b = bh / a.H, h = bh % a.H;
   const int kvh = h / a.G;
   const int64_t seq = (int64_t)b * a.Hkv + kvh;
-  const int q = blockIdx.y * kMQQueries + wave * 32 + ln;
+  const int q0 = blockIdx.y * kMQQueries + wave * 32;
+  const int q = q0 + ln;
   const bool qvalid = q < a.n_q;
+  const bool wave_q = q0 < a.n_q;            // the wave has queries (uniform)
 
-  for (int i = tid; i < C::NDIR; i += 256) s_dir[i] = a.t.dirtab[i];
+  for (int i = tid; i < C::NDIR; i += NTH) s_dir[i] = a.t.dirtab[i];
   if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
 
   // Q' fragment: B[k = dim][n = query], lane (ln, g) holds dims 16j + 8g + 0..7.
@@ -142,45 +180,28 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int64_t k0 = t * KT;
     __syncthreads();  // previous tile's LDS reads are done
-    // 1. rebuild keys (lanes 0..31 of each wave, one key each) into fp16 rows
-    if (lane < KPW) {
-      const int kk = wave * KPW + lane;
+    // 1. rebuild keys: wave w, key half w / 4, dim quarter w % 4
+    {
+      const int kk = 64 * (wave / kMQParts) + lane;
       const bool ok = k0 + kk < a.n_keys;
-      // triplets in order; each 8-dim group goes to LDS as soon as it is whole
-      float u[3 * T];
-      uint4* row = (uint4*)(s_k + kk * KP);
-#pragma unroll
-      for (int i = 0; i < T; ++i) {
-        const uint32_t code = field_at<W>(st.words, i * C::BT, C::BT);
-        const float4 n = s_dir[code & C::DIR_MASK];
-        const float rh = ok ? s_rho[code >> (C::BX + C::BE)] : 0.f;
-        u[3 * i] = rh * n.x;
-        u[3 * i + 1] = rh * n.y;
-        u[3 * i + 2] = rh * n.z;
-#pragma unroll
-        for (int j = 0; j < D / 8; ++j) {
-          if (8 * j + 7 >= 3 * i && 8 * j + 7 < 3 * i + 3) {   // group j completed by triplet i
-            uint32_t w[4];
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-              w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(u[8 * j + 2 * e],
-                                                                             u[8 * j + 2 * e + 1]));
-            row[j] = make_uint4(w[0], w[1], w[2], w[3]);
-          }
-        }
+      unsigned char* krow = s_k + kk * KP;
+      switch (wave % kMQParts) {
+        case 0: mq_rebuild<D, B, 0>(st, ok, s_dir, s_rho, krow); s_g[kk] = ok ? st.gamma : 0.f; break;
+        case 1: mq_rebuild<D, B, 1>(st, ok, s_dir, s_rho, krow); break;
+        case 2: mq_rebuild<D, B, 2>(st, ok, s_dir, s_rho, krow); break;
+        default: mq_rebuild<D, B, 3>(st, ok, s_dir, s_rho, krow); break;
       }
-      s_g[kk] = ok ? st.gamma : 0.f;
     }
     // 2. V tile transposed to [dim][key] fp16: this thread's KPT keys x 8 dims
     {
       const int c = tid % (D / 8), kg = tid / (D / 8);
-      uint32_t h[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
+      uint32_t hv[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const bool ok = k0 + kg * KPT + i < a.n_keys;
         const uint32_t src[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
 #pragma unroll
-        for (int e = 0; e < 4; ++e) h[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
+        for (int e = 0; e < 4; ++e) hv[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
       }
 #pragma unroll
       for (int dd = 0; dd < 8; ++dd) {
@@ -188,17 +209,22 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
         uint32_t col[KPT / 2];
 #pragma unroll
         for (int i = 0; i < KPT / 2; ++i)
-          col[i] = __builtin_amdgcn_perm(h[2 * i + 1][dd >> 1], h[2 * i][dd >> 1], sel);
+          col[i] = __builtin_amdgcn_perm(hv[2 * i + 1][dd >> 1], hv[2 * i][dd >> 1], sel);
         unsigned char* dst = s_vt + (8 * c + dd) * VP + kg * KPT * 2;
-        if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
+        if constexpr (KPT == 2) *(uint32_t*)dst = col[0];
+        else if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
         else *(uint4*)dst = make_uint4(col[0], col[1], col[2], col[3]);
       }
     }
     // next tile's loads fly during this tile's matrix work
     mq_load<D, B>(a, seq, t + 1 < t_end ? t + 1 : t, tid, st);
     __syncthreads();
+    if (!wave_q) continue;
 
-    // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T
+    // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T.  Scores stay
+    // unscaled by the query's power of two (s' = q'.u'^ gamma 2^sh): the max
+    // is taken on s', and exp2(s' 2^-sh - m) is one fma and one exp.
+    const bool partial = k0 + KT > a.n_keys;
 #pragma unroll 1
     for (int ch = 0; ch < KT / 64; ++ch) {
       floatx16 s[2];
@@ -213,11 +239,19 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
           const half8 kf = *(const half8*)(s_k + (kb + ln) * KP + (16 * j + 8 * g) * 2);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], acc, 0, 0, 0);
         }
+        // register r holds key row kb + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int kr = kb + 8 * (r >> 2) + 4 * g + (r & 3);
-          const float val = acc[r] * s_g[kr] * qscale_inv;
-          acc[r] = (k0 + kr < a.n_keys) ? val : -INFINITY;
+        for (int rr = 0; rr < 4; ++rr) {
+          const float4 gv = *(const float4*)(s_g + kb + 8 * rr + 4 * g);
+          acc[4 * rr] *= gv.x;
+          acc[4 * rr + 1] *= gv.y;
+          acc[4 * rr + 2] *= gv.z;
+          acc[4 * rr + 3] *= gv.w;
+        }
+        if (partial) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            if (k0 + kb + 8 * (r >> 2) + 4 * g + (r & 3) >= a.n_keys) acc[r] = -INFINITY;
         }
         s[sb] = acc;
       }
@@ -227,19 +261,27 @@ __global__ __launch_bounds__(256) void k_mq_attn(MQArgs a) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx);
-      const float alpha = (m_new == -INFINITY) ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+      const float m_new = fmaxf(m_run, mx * qscale_inv);
+      // a row with no valid key yet keeps m = -inf; exponents use 0 then
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
       float lsum = 0.f;
       half8 pf[2][2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const float p = (m_new == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f(s[sb][r] - m_new);
-          const _Float16 ph = (_Float16)p;
-          lsum += (float)ph;
-          pf[sb][r >> 3][r & 7] = ph;
-        }
+        for (int r = 0; r < 16; ++r)
+          pf[sb][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], qscale_inv, -m_use));
+      // l sums the fp16 p that P.V uses: v_dot2 over the packed pairs
+#pragma unroll
+      for (int sb = 0; sb < 2; ++sb)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const half2v pp = {pf[sb][hh][2 * e], pf[sb][hh][2 * e + 1]};
+            lsum = __builtin_amdgcn_fdot2(pp, half2v{(_Float16)1.0f, (_Float16)1.0f}, lsum, false);
+          }
       l_run = __builtin_fmaf(l_run, alpha, lsum);
       m_run = m_new;
 #pragma unroll
@@ -282,11 +324,12 @@ template <int D, int B>
 static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_split, (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries),
                   (unsigned)(a.B * a.H));
-  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(64 * kMQWaves), 0, s, a);
   return hipGetLastError();
 }
 
 int mq_tile_keys(int d) { return d == 64 ? MQShape<64>::KT : MQShape<128>::KT; }
+int mq_block_queries() { return kMQQueries; }
 
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
   switch (d * 10 + b) {

@@ -349,17 +349,38 @@ Split attn_split(int64_t n_keys, int64_t n_seq, int passes) {
   return {(int)ns, (int)tps};
 }
 
+// Compute units of the current device (one multi-query workgroup each).
+int64_t device_cus() {
+  int dev = 0, n = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+    return 256;
+  return n;
+}
+
+// Multi-query split: the number of splits that minimises the tile steps of
+// the slowest compute unit, ceil(rows * n_split / CUs) * tiles_per_split;
+// among equal costs the fewest splits (least partial traffic).
 Split mq_split(int64_t n_keys, int d, int64_t rows) {
   const int kt = mq_tile_keys(d);
   const int64_t ntile = std::max<int64_t>(1, (n_keys + kt - 1) / kt);
-  int64_t ns = (1024 + rows - 1) / std::max<int64_t>(1, rows);
-  ns = std::max<int64_t>(1, std::min<int64_t>(ns, ntile));
-  const int64_t tps = (ntile + ns - 1) / ns;
-  ns = (ntile + tps - 1) / tps;
-  return {(int)ns, (int)tps};
+  const int64_t slots = device_cus();
+  rows = std::max<int64_t>(1, rows);
+  int64_t best_ns = 1, best_cost = INT64_MAX;
+  for (int64_t ns = 1; ns <= std::min<int64_t>(ntile, kMaxSplit); ++ns) {
+    const int64_t tps = (ntile + ns - 1) / ns;
+    if ((ntile + tps - 1) / tps != ns) continue;  // same tiles per split as a smaller count
+    const int64_t cost = ((rows * ns + slots - 1) / slots) * tps;
+    if (cost < best_cost) { best_cost = cost; best_ns = ns; }
+  }
+  const int64_t tps = (ntile + best_ns - 1) / best_ns;
+  return {(int)best_ns, (int)tps};
 }
 
-int64_t mq_rows(int B, int Hq, int n_q) { return (int64_t)B * Hq * ((n_q + 127) / 128); }
+int64_t mq_rows(int B, int Hq, int n_q) {
+  const int qb = mq_block_queries();
+  return (int64_t)B * Hq * ((n_q + qb - 1) / qb);
+}
 
 struct WsLayout { size_t qrot, qp, part, total; };
 

@@ -116,5 +116,6 @@ hipError_t launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s)
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s);
 int mq_tile_keys(int d);  // keys per tile of the multi-query kernel
+int mq_block_queries();   // queries per workgroup of the multi-query kernel
 
 }  // namespace octo
