@@ -25,18 +25,24 @@ typedef _Float16 half4 __attribute__((ext_vector_type(4)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMQWaves = 8;                  // waves per workgroup
-constexpr int kMQQueries = 32 * kMQWaves;    // queries per workgroup (32 per wave)
-constexpr int kMQParts = 4;                  // waves sharing the rebuild of 64 keys (dim quarters)
+constexpr int kMQCompute = 8;                // matrix waves per workgroup
+constexpr int kMQQueries = 32 * kMQCompute;  // queries per workgroup (32 per matrix wave)
 
+// Workgroup shape.  At d = 64 the matrix waves fit three to a SIMD, so four
+// more waves do the staging (key rebuild, V transpose, loads) next to them;
+// at d = 128 the eight matrix waves stage the tiles themselves.
 template <int D>
 struct MQShape {
   static constexpr int KT = 128;                  // keys per tile
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
   static constexpr int VP = KT * 2 + 16;          // V^T row pitch in bytes (fp16)
-  static constexpr int NTH = 64 * kMQWaves;       // threads per workgroup
-  static constexpr int KPT = KT * D / (8 * NTH);  // keys per thread of the V transpose
-  static constexpr int DQ = D / kMQParts;         // dims rebuilt per lane
+  static constexpr int SW = D == 64 ? 4 : 0;      // staging-only waves
+  static constexpr int NW = kMQCompute + SW;      // waves per workgroup
+  static constexpr int NSW = SW ? SW : kMQCompute;  // waves that stage
+  static constexpr int PARTS = NSW / 2;           // staging waves per 64-key half
+  static constexpr int DQ = D / PARTS;            // dims rebuilt per lane
+  static constexpr int NTH_S = 64 * NSW;          // staging threads
+  static constexpr int KPT = KT * D / (8 * NTH_S);  // keys per thread of the V transpose
 };
 
 // Registers carrying one tile's global data from its loads (issued during
@@ -48,20 +54,21 @@ struct MQStage {
   uint4 v[MQShape<D>::KPT];         // KPT V rows, 8 dims each
 };
 
-// Loads of tile t (rows past n_keys read the last key; they are masked later).
-// The four waves of a key half all load the half's words (the same lines).
+// Loads of tile t by staging thread stid (rows past n_keys read the last
+// key; they are masked later).  The waves of a key half all load the half's
+// words (the same lines).
 template <int D, int B>
-__device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int tid,
+__device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int stid,
                                         MQStage<D, B>& st) {
   using S = MQShape<D>;
   constexpr int W = Codec<D, B>::W;
-  const int lane = tid & 63, wave = tid >> 6;
+  const int lane = stid & 63, sw = stid >> 6;
   const int64_t tiles64 = a.cap / kTile;
-  int64_t key = t * S::KT + 64 * (wave / kMQParts) + lane;
+  int64_t key = t * S::KT + 64 * (sw / S::PARTS) + lane;
   key = key < a.n_keys ? key : a.n_keys - 1;
   TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), st.words);
   st.gamma = a.gamma[seq * a.cap + key];
-  const int c = tid % (D / 8), kg = tid / (D / 8);
+  const int c = stid % (D / 8), kg = stid / (D / 8);
   const uint4* vseq = (const uint4*)a.v + seq * a.cap * (D / 8) + c;
 #pragma unroll
   for (int i = 0; i < S::KPT; ++i) {
@@ -107,17 +114,18 @@ __device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, bool ok, con
 }
 
 template <int D, int B>
-__global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
+__global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
   using C = Codec<D, B>;
   using S = MQShape<D>;
   constexpr int T = C::T;
-  constexpr int KT = S::KT, KP = S::KP, VP = S::VP, NTH = S::NTH;
+  constexpr int KT = S::KT, KP = S::KP, VP = S::VP, NTH = 64 * S::NW;
   constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
 
-  __shared__ __align__(16) unsigned char s_k[KT * KP];
-  __shared__ __align__(16) unsigned char s_vt[D * VP];
-  __shared__ __align__(16) float s_g[KT];
+  // two sets of tile buffers: tile t + 1 is staged while tile t is computed
+  __shared__ __align__(16) unsigned char s_k[2][KT * KP];
+  __shared__ __align__(16) unsigned char s_vt[2][D * VP];
+  __shared__ __align__(16) float s_g[2][KT];
   __shared__ float4 s_dir[C::NDIR];
   __shared__ float s_rho[C::LR];
 
@@ -129,8 +137,10 @@ __global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
   const int64_t seq = (int64_t)b * a.Hkv + kvh;
   const int q0 = blockIdx.y * kMQQueries + wave * 32;
   const int q = q0 + ln;
-  const bool qvalid = q < a.n_q;
-  const bool wave_q = q0 < a.n_q;            // the wave has queries (uniform)
+  const bool qvalid = wave < kMQCompute && q < a.n_q;
+  const bool wave_q = wave < kMQCompute && q0 < a.n_q;   // a matrix wave with queries (uniform)
+  const bool stager = S::SW == 0 || wave >= kMQCompute;  // (uniform)
+  const int stid = S::SW == 0 ? tid : tid - 64 * kMQCompute;  // staging thread index
 
   for (int i = tid; i < C::NDIR; i += NTH) s_dir[i] = a.t.dirtab[i];
   if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
@@ -173,54 +183,72 @@ __global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
   const int64_t t_end = t_begin + a.tiles_per_split < ntile ? t_begin + a.tiles_per_split : ntile;
   constexpr int KPT = S::KPT;
 
+  // Stage one tile from the registers of its loads into LDS buffer set bs:
+  //   keys rebuilt by wave w for key half w / 4 and dim quarter w % 4;
+  //   V transposed to [dim][key] fp16, this thread's KPT keys x 8 dims.
   MQStage<D, B> st;
-  mq_load<D, B>(a, seq, t_begin < ntile ? t_begin : 0, tid, st);
+  auto stage = [&](int64_t k0, int bs) {
+    {
+      const int sw = stid >> 6;
+      const int kk = 64 * (sw / S::PARTS) + lane;
+      const bool ok = k0 + kk < a.n_keys;
+      unsigned char* krow = s_k[bs] + kk * KP;
+      const int part = sw % S::PARTS;
+      if (part == 0) {
+        mq_rebuild<D, B, 0>(st, ok, s_dir, s_rho, krow);
+        s_g[bs][kk] = ok ? st.gamma : 0.f;
+      } else if (part == 1) {
+        mq_rebuild<D, B, 1>(st, ok, s_dir, s_rho, krow);
+      } else if constexpr (S::PARTS > 2) {
+        if (part == 2) mq_rebuild<D, B, 2>(st, ok, s_dir, s_rho, krow);
+        else mq_rebuild<D, B, 3>(st, ok, s_dir, s_rho, krow);
+      }
+    }
+    const int c = stid % (D / 8), kg = stid / (D / 8);
+    uint32_t hv[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const bool ok = k0 + kg * KPT + i < a.n_keys;
+      const uint32_t src[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) hv[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
+    }
+#pragma unroll
+    for (int dd = 0; dd < 8; ++dd) {
+      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
+      uint32_t col[KPT / 2];
+#pragma unroll
+      for (int i = 0; i < KPT / 2; ++i)
+        col[i] = __builtin_amdgcn_perm(hv[2 * i + 1][dd >> 1], hv[2 * i][dd >> 1], sel);
+      unsigned char* dst = s_vt[bs] + (8 * c + dd) * VP + kg * KPT * 2;
+      if constexpr (KPT == 2) *(uint32_t*)dst = col[0];
+      else if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
+      else *(uint4*)dst = make_uint4(col[0], col[1], col[2], col[3]);
+    }
+  };
+
+  if (stager) mq_load<D, B>(a, seq, t_begin < ntile ? t_begin : 0, stid, st);
   __syncthreads();  // s_dir / s_rho
+  if (stager && t_begin < t_end) {
+    stage(t_begin * KT, 0);
+    mq_load<D, B>(a, seq, t_begin + 1 < t_end ? t_begin + 1 : t_begin, stid, st);
+  }
+  __syncthreads();
 
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int64_t k0 = t * KT;
-    __syncthreads();  // previous tile's LDS reads are done
-    // 1. rebuild keys: wave w, key half w / 4, dim quarter w % 4
-    {
-      const int kk = 64 * (wave / kMQParts) + lane;
-      const bool ok = k0 + kk < a.n_keys;
-      unsigned char* krow = s_k + kk * KP;
-      switch (wave % kMQParts) {
-        case 0: mq_rebuild<D, B, 0>(st, ok, s_dir, s_rho, krow); s_g[kk] = ok ? st.gamma : 0.f; break;
-        case 1: mq_rebuild<D, B, 1>(st, ok, s_dir, s_rho, krow); break;
-        case 2: mq_rebuild<D, B, 2>(st, ok, s_dir, s_rho, krow); break;
-        default: mq_rebuild<D, B, 3>(st, ok, s_dir, s_rho, krow); break;
-      }
+    const int cb = (int)((t - t_begin) & 1);
+    // stage the next tile into the other buffer set (its last reader, the
+    // previous tile's matrix work, finished before the last barrier), then
+    // request the tile after it
+    if (stager && t + 1 < t_end) {
+      stage(k0 + KT, cb ^ 1);
+      mq_load<D, B>(a, seq, t + 2 < t_end ? t + 2 : t + 1, stid, st);
     }
-    // 2. V tile transposed to [dim][key] fp16: this thread's KPT keys x 8 dims
-    {
-      const int c = tid % (D / 8), kg = tid / (D / 8);
-      uint32_t hv[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
-#pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const bool ok = k0 + kg * KPT + i < a.n_keys;
-        const uint32_t src[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) hv[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
-      }
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-        uint32_t col[KPT / 2];
-#pragma unroll
-        for (int i = 0; i < KPT / 2; ++i)
-          col[i] = __builtin_amdgcn_perm(hv[2 * i + 1][dd >> 1], hv[2 * i][dd >> 1], sel);
-        unsigned char* dst = s_vt + (8 * c + dd) * VP + kg * KPT * 2;
-        if constexpr (KPT == 2) *(uint32_t*)dst = col[0];
-        else if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
-        else *(uint4*)dst = make_uint4(col[0], col[1], col[2], col[3]);
-      }
-    }
-    // next tile's loads fly during this tile's matrix work
-    mq_load<D, B>(a, seq, t + 1 < t_end ? t + 1 : t, tid, st);
-    __syncthreads();
-    if (!wave_q) continue;
-
+    const unsigned char* sk = s_k[cb];
+    const unsigned char* svt = s_vt[cb];
+    const float* sg = s_g[cb];
+    if (wave_q) {
     // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T.  Scores stay
     // unscaled by the query's power of two (s' = q'.u'^ gamma 2^sh): the max
     // is taken on s', and exp2(s' 2^-sh - m) is one fma and one exp.
@@ -236,13 +264,13 @@ __global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
         for (int r = 0; r < 16; ++r) acc[r] = 0.f;
 #pragma unroll
         for (int j = 0; j < NKS; ++j) {
-          const half8 kf = *(const half8*)(s_k + (kb + ln) * KP + (16 * j + 8 * g) * 2);
+          const half8 kf = *(const half8*)(sk + (kb + ln) * KP + (16 * j + 8 * g) * 2);
           acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], acc, 0, 0, 0);
         }
         // register r holds key row kb + 8 (r / 4) + 4 g + r % 4
 #pragma unroll
         for (int rr = 0; rr < 4; ++rr) {
-          const float4 gv = *(const float4*)(s_g + kb + 8 * rr + 4 * g);
+          const float4 gv = *(const float4*)(sg + kb + 8 * rr + 4 * g);
           acc[4 * rr] *= gv.x;
           acc[4 * rr + 1] *= gv.y;
           acc[4 * rr + 2] *= gv.z;
@@ -295,7 +323,7 @@ __global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
           const int kbase = ch * 64 + sb * 32 + 16 * half + 4 * g;
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            const unsigned char* vrow = s_vt + (32 * mb + ln) * VP;
+            const unsigned char* vrow = svt + (32 * mb + ln) * VP;
             const half4 lo = *(const half4*)(vrow + kbase * 2);
             const half4 hi = *(const half4*)(vrow + (kbase + 8) * 2);
             const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -304,6 +332,8 @@ __global__ __launch_bounds__(64 * kMQWaves) void k_mq_attn(MQArgs a) {
         }
       }
     }
+    }  // wave_q
+    __syncthreads();  // this tile's buffers are free, the next tile's staged
   }
 
   l_run += __shfl_xor(l_run, 32, 64);
@@ -324,7 +354,7 @@ template <int D, int B>
 static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_split, (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries),
                   (unsigned)(a.B * a.H));
-  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(64 * kMQWaves), 0, s, a);
+  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(64 * MQShape<D>::NW), 0, s, a);
   return hipGetLastError();
 }
 
