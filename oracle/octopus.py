@@ -17,7 +17,8 @@ Parity status of each function (what pins it, tests/test_oracle_*.py):
                              0.0071 (b=4) and 0.0897 (b=2) on d=128 Gaussian keys
   logits / attention         torch scaled_dot_product_attention (fp64, CPU)
   qjl_encode / qjl_logits    closed-form expectation (Monte Carlo over S draws)
-  joint_round                exhaustive 2^(b_xi+b_eta) search on small inputs
+  joint_round                exhaustive 2^(b_xi+b_eta) search: identical on 10000
+                             random triplets at b = 2, 3, 4, as the pages report
 """
 from __future__ import annotations
 
@@ -302,8 +303,11 @@ class Encoded:
     rotated: np.ndarray      # (n, d) fp64 u' = R u
 
 
-def encode(keys: np.ndarray, cb: Codebook, identity: bool = False) -> Encoded:
-    """Scalar (nearest-centroid) rounding, the encoder's hot-path rule.
+def encode(keys: np.ndarray, cb: Codebook, identity: bool = False,
+           rounding: str = "scalar") -> Encoded:
+    """Scalar (nearest-centroid) rounding, the encoder's hot-path rule, or
+    with rounding="joint" the pages' joint rounding of each triplet
+    ([YL] 联合取整, ``joint_round`` below).
 
     identity=True skips quantisation (codes are left empty and ``values``
     carries the exact components) so the rest of the chain can be checked
@@ -320,6 +324,8 @@ def encode(keys: np.ndarray, cb: Codebook, identity: bool = False) -> Encoded:
     values = np.stack([xi, eta, rho], axis=-1).reshape(nk, T, 3)
     if identity:
         codes = np.zeros((nk, T, 3), dtype=np.int64)
+    elif rounding == "joint":
+        codes = joint_round(split_triplets(up), cb)
     else:
         codes = np.stack([quantize(xi, cb.c_xi), quantize(eta, cb.c_eta),
                           quantize(rho, cb.c_rho)], axis=-1).reshape(nk, T, 3)

@@ -445,6 +445,40 @@ def test_qjl_logits_unbiased_over_seeds(cb128_3):
 
 
 # ------------------------------------------------------------ joint rounding --
+@pytest.mark.parametrize("b", [2, 3, 4])
+def test_joint_rounding_3x3_equals_exhaustive_on_10000_triplets(b):
+    """[YL] 联合取整: on 10000 random triplets the 3x3 neighbourhood search
+    gives exactly the exhaustive search's codes.  Triplets: the rotated
+    triplets of random d=128 Gaussian keys."""
+    cb = O.build_codebook(128, b)
+    k = np.random.default_rng(5).standard_normal((233, 128))
+    t = O.split_triplets(O.encode(k, cb).rotated).reshape(-1, 3)[:10000]
+    j3 = O.joint_round(t, cb)
+    jx = O.joint_round(t, cb, exhaustive=True)
+    assert np.array_equal(j3, jx)
+    # and the optimum: no candidate direction with its best rho does better
+    nh = O.octa_decode(cb.c_xi[j3[:, 0]], cb.c_eta[j3[:, 1]])
+    err = np.sum((cb.c_rho[j3[:, 2]][:, None] * nh - t) ** 2, axis=1)
+    for ia in range(cb.c_xi.size):
+        for ie in range(0, cb.c_eta.size, 3):
+            n2 = O.octa_decode(np.full(len(t), cb.c_xi[ia]), np.full(len(t), cb.c_eta[ie]))
+            for ir in range(cb.c_rho.size):
+                assert np.all(np.sum((cb.c_rho[ir] * n2 - t) ** 2, axis=1) >= err - 1e-12)
+
+
+def test_encode_joint_rounding_lowers_mse_and_is_the_triplet_rule(cb128_2):
+    """The joint encoder applies joint_round to every triplet of the rotated
+    unit key, and its reconstruction error is below scalar rounding's."""
+    k = np.random.default_rng(8).standard_normal((64, 128))
+    ej = O.encode(k, cb128_2, rounding="joint")
+    es = O.encode(k, cb128_2)
+    assert np.array_equal(ej.codes, O.joint_round(O.split_triplets(es.rotated), cb128_2))
+    assert np.array_equal(ej.gamma, es.gamma)
+    mse = lambda e: np.mean(np.sum((O.decode(e.codes, e.gamma, cb128_2) - k) ** 2, axis=1)  # noqa: E731
+                            / np.sum(k * k, axis=1))
+    assert mse(ej) < mse(es)
+
+
 def test_joint_rounding_3x3_vs_exhaustive_and_better_than_scalar(cb128_2):
     """[YL] 联合取整: the 3x3 neighbourhood of the scalar indices finds the
     exhaustive optimum for (nearly) all triplets and lowers the error."""
