@@ -295,6 +295,15 @@ def main():
 
     step_graphs = [capture(lambda s=s: (encode(s), decode(s))) for s in sets]
     enc_graph = capture(lambda: [encode(s) for s in sets])
+    # the joint-rounding encoder mode (reported beside the scalar encoder, not
+    # part of the step): into a scratch cache per set
+    jcaches = [octo.Cache(cb, cfg.n_seq, cfg.cap, qjl=cfg.qjl) for _ in sets]
+
+    def encode_joint(s, jc):
+        k = s["keys"][:, enc_pos0:] if enc_pos0 else s["keys"]
+        octo.octo_encode_joint(cb, k, jc, pos0=enc_pos0)
+
+    joint_graph = capture(lambda: [encode_joint(s, jc) for s, jc in zip(sets, jcaches)])
     dec_graph = capture(lambda: [decode(s) for s in sets])
     main_graph = capture(lambda: [decode(s, octo.STAGE_MAIN) for s in sets])
     torch.cuda.synchronize()
@@ -320,6 +329,7 @@ def main():
         return e0.elapsed_time(e1) / 1e3 / reps
 
     t_enc = time_graph(enc_graph, args.kernel_reps) / R
+    t_joint = time_graph(joint_graph, max(1, args.kernel_reps // 4)) / R
     t_dec = time_graph(dec_graph, args.kernel_reps) / R
     t_main = time_graph(main_graph, args.kernel_reps) / R
 
@@ -383,6 +393,8 @@ def main():
         "encode_gbs": round(enc_bytes / t_enc / 1e9, 2),
         "encode_us": round(t_enc * 1e6, 3),
         "encode_pct_hbm_peak": round(100 * enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS, 2),
+        "encode_joint_us": round(t_joint * 1e6, 3),
+        "encode_joint_mkeys_per_s": round(n_keys_total / t_joint / 1e6, 1),
         "roofline": roofline,
     }
     if cfg.qjl and not args.no_qjl_bias:

@@ -137,6 +137,19 @@ octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kd
                         int64_t pos0, int64_t cap, void* packed, float* gamma,
                         void* qjl_bits, uint16_t* qjl_norm, void* stream);
 
+/* The same encoder with joint rounding ([YL] 联合取整): per triplet t of the
+ * rotated unit key, the direction code is chosen among the 3x3 neighbours of
+ * the scalar-rounded (i_xi, i_eta) (clamped to the index range), each with
+ * the rho centroid nearest s = <n^, t>, minimising |t - rho^ n^|^2; the first
+ * strict minimum in (xi offset, eta offset) order -1, 0, +1 wins.  Arguments,
+ * layout, ownership and errors as octo_encode; gamma and the QJL residual
+ * (computed from the chosen codes) likewise.  Costs several times the
+ * scalar encoder's arithmetic. */
+octo_status octo_encode_joint(const octo_codebook* cb, const void* keys, octo_dtype kdt,
+                              int64_t n_seq, int64_t n_new, int64_t seq_stride,
+                              int64_t key_stride, int64_t pos0, int64_t cap, void* packed,
+                              float* gamma, void* qjl_bits, uint16_t* qjl_norm, void* stream);
+
 /* Workspace for the decode calls.  mode 0 = octo_decode_logits, 1 =
  * octo_decode_attn.  The workspace holds the rotated queries and, for
  * attention, the split-K partial results (one call at a time per

@@ -54,6 +54,7 @@ _SIGS = {
     "octo_packed_bytes": (_SZ, [_P, _I64, _I64]),
     "octo_qjl_bits_bytes": (_SZ, [_P, _I64, _I64]),
     "octo_encode": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "octo_encode_joint": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "octo_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I64]),
     "octo_decode_logits": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "octo_decode_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64, _F,
@@ -198,15 +199,23 @@ class Cache:
                          if use_qjl else None)
 
 
-def octo_encode(cb: Codebook, keys, cache: Cache, pos0: int = 0, stream=None):
-    """keys: device tensor [n_seq, n_new, d] (f32/bf16/f16, last dim contiguous)."""
+def _encode(fn, name, cb: Codebook, keys, cache: Cache, pos0: int, stream):
     n_seq, n_new, d = keys.shape
     if d != cb.d or keys.stride(2) != 1:
         raise ValueError("keys must be [n_seq, n_new, d] with a contiguous last dim")
-    _check(lib().octo_encode(cb.handle, _ptr(keys), _dtype_code(keys), n_seq, n_new, keys.stride(0),
-                             keys.stride(1), pos0, cache.cap, _ptr(cache.packed), _ptr(cache.gamma),
-                             _ptr(cache.qjl_bits), _ptr(cache.qjl_norm), _stream(stream)),
-           "octo_encode")
+    _check(fn(cb.handle, _ptr(keys), _dtype_code(keys), n_seq, n_new, keys.stride(0),
+              keys.stride(1), pos0, cache.cap, _ptr(cache.packed), _ptr(cache.gamma),
+              _ptr(cache.qjl_bits), _ptr(cache.qjl_norm), _stream(stream)), name)
+
+
+def octo_encode(cb: Codebook, keys, cache: Cache, pos0: int = 0, stream=None):
+    """keys: device tensor [n_seq, n_new, d] (f32/bf16/f16, last dim contiguous)."""
+    _encode(lib().octo_encode, "octo_encode", cb, keys, cache, pos0, stream)
+
+
+def octo_encode_joint(cb: Codebook, keys, cache: Cache, pos0: int = 0, stream=None):
+    """octo_encode with joint 3x3 rounding of every triplet."""
+    _encode(lib().octo_encode_joint, "octo_encode_joint", cb, keys, cache, pos0, stream)
 
 
 def _workspace(cb, mode, B, Hq, Hkv, n_q, n_keys, workspace, device):

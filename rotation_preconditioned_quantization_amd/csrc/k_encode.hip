@@ -263,7 +263,7 @@ __device__ __forceinline__ void qjl_signs(const float (&v)[D], const unsigned ch
 }
 
 // Encode the 64-key tile at j0: one key per lane, entirely in registers.
-template <int D, int B, int KT, bool QJL>
+template <int D, int B, int KT, bool QJL, bool JR>
 __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
                                             unsigned char* s_keys, const uint4& smask,
                                             const uint2* s_qx, const uint2* s_qe, const uint2* s_qr,
@@ -321,24 +321,77 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   const int64_t pos = a.pos0 + j;
   const int64_t tiles = a.cap / kTile;
   float tot = 0.f;
-
-  // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
-  float e[T];
+  if constexpr (!JR) {
+    // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
+    float e[T];
 #pragma unroll
-  for (int i = 0; i < T; ++i) {
-    float x, y, z;
-    triplet_of<D>(v, i, x, y, z);
-    e[i] = triplet_energy(x, y, z);
-    tot += e[i];
-    pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      e[i] = triplet_energy(x, y, z);
+      tot += e[i];
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+    }
+    const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+    // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      pack_code<C::BT>(words, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+  } else {
+    // Joint rounding ([YL] 联合取整).  Pass 1: the energy and the scalar
+    // (xi, eta) indices, the centre of the search.  Pass 2, per triplet t of
+    // the unit key: for each of the 3x3 neighbouring direction codes (clamped
+    // to the index range) with unit direction n^, the best rho^ is the
+    // centroid nearest s = <n^, t> (the squared-midpoint table on max(s, 0)^2;
+    // s <= 0 takes index 0), with error |t - rho^ n^|^2 - |t|^2 = rho^ (rho^ - 2s);
+    // the first strict minimum in (xi, eta) offset order wins.
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      tot += triplet_energy(x, y, z);
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+    }
+    const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+    uint32_t wj[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) wj[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      x *= inv_norm;
+      y *= inv_norm;
+      z *= inv_norm;
+      const uint32_t c0 = field_at<W>(words, i * C::BT, C::BX + C::BE);
+      const int ix = (int)(c0 & (C::LX - 1)), ie = (int)(c0 >> C::BX);
+      float best_e = INFINITY;
+      uint32_t best = 0u;
+#pragma unroll
+      for (int da = -1; da <= 1; ++da) {
+        const int ja = min(max(ix + da, 0), C::LX - 1);
+#pragma unroll
+        for (int dc = -1; dc <= 1; ++dc) {
+          const int jc = min(max(ie + dc, 0), C::LE - 1);
+          const uint32_t xe = (uint32_t)ja | ((uint32_t)jc << C::BX);
+          const float4 n = s_dir[xe];
+          const float sdot = __builtin_fmaf(n.x, x, __builtin_fmaf(n.y, y, n.z * z));
+          const float sp = __builtin_fmaxf(sdot, 0.f);
+          const uint32_t jr = quant1_clamp(sp * sp, s_qr, sr, mr);
+          const float r = s_rho[jr];
+          const float err = r * (r - 2.f * sdot);
+          if (err < best_e) {
+            best_e = err;
+            best = xe | (jr << (C::BX + C::BE));
+          }
+        }
+      }
+      pack_code<C::BT>(wj, i, best);
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) words[w] = wj[w];
   }
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
-  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
-  // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    pack_code<C::BT>(words, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
-  }
   if (valid) {
     TileWords<W>::store(a.packed + (seq * tiles + (pos >> 6)) * W * kTile, (int)(pos & 63), words);
     a.gamma[seq * a.cap + pos] = gamma;
@@ -376,7 +429,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   }
 }
 
-template <int D, int B, int KT, bool QJL>
+template <int D, int B, int KT, bool QJL, bool JR>
 __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
   using S = Stage<D, KT>;
@@ -384,8 +437,10 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
   __shared__ __align__(16) unsigned char s_keys[EW][S::NR * S::PITCH];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
   __shared__ __align__(16) unsigned char s_S[QJL ? SLds<D>::BYTES : 16];
-  __shared__ float4 s_dir[QJL ? C::NDIR : 1];
-  __shared__ float s_rho[QJL ? C::LR : 1];
+  // unit directions and rho centroids (QJL residual, joint rounding)
+  constexpr bool TABS = QJL || JR;
+  __shared__ float4 s_dir[TABS ? C::NDIR : 1];
+  __shared__ float s_rho[TABS ? C::LR : 1];
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
@@ -398,6 +453,8 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
     constexpr int CPRS = 2 * D / 16;  // 16-byte chunks per S row
     for (int c = threadIdx.x; c < 2 * D * CPRS; c += 64 * EW)
       *(uint4*)(s_S + (c / CPRS) * SLds<D>::PITCH + (c % CPRS) * 16) = a.t.S16[c];
+  }
+  if constexpr (TABS) {
     for (int i = threadIdx.x; i < C::NDIR; i += 64 * EW) s_dir[i] = a.t.dirtab[i];
     if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
   }
@@ -407,13 +464,13 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
   // key count and the block's waves take tiles round-robin.
   for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
        j0 += (int64_t)gridDim.x * EW * kTile) {
-    encode_tile<D, B, KT, QJL>(a, seq, j0, lane, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S, s_dir,
+    encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S, s_dir,
                                s_rho);
     if constexpr (!QJL) break;
   }
 }
 
-template <int D, int B, int KT, bool QJL>
+template <int D, int B, int KT, bool QJL, bool JR>
 static hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
   constexpr int EW = enc_waves<QJL>();
@@ -423,42 +480,45 @@ static hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_
   // blocks per compute unit then loops over the tiles.
   if (QJL) gx = std::min<int64_t>(gx, std::max<int64_t>(1, (512 + n_seq - 1) / n_seq));
   const dim3 grid((unsigned)gx, (unsigned)n_seq);
-  hipLaunchKernelGGL((k_encode<D, B, KT, QJL>), grid, dim3(64 * EW), 0, s, a);
+  hipLaunchKernelGGL((k_encode<D, B, KT, QJL, JR>), grid, dim3(64 * EW), 0, s, a);
   return hipGetLastError();
 }
 
 template <int D, int B, int KT>
-static hipError_t enc_q(bool qjl, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
-  return qjl ? launch_encode_t<D, B, KT, true>(a, n_seq, s)
-             : launch_encode_t<D, B, KT, false>(a, n_seq, s);
+static hipError_t enc_q(bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  if (joint)
+    return qjl ? launch_encode_t<D, B, KT, true, true>(a, n_seq, s)
+               : launch_encode_t<D, B, KT, false, true>(a, n_seq, s);
+  return qjl ? launch_encode_t<D, B, KT, true, false>(a, n_seq, s)
+             : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
 }
 
 template <int D, int B>
-static hipError_t enc_kt(int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+static hipError_t enc_kt(int kdt, bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   switch (kdt) {
-    case DT_F32: return enc_q<D, B, DT_F32>(qjl, a, n_seq, s);
-    case DT_BF16: return enc_q<D, B, DT_BF16>(qjl, a, n_seq, s);
-    case DT_F16: return enc_q<D, B, DT_F16>(qjl, a, n_seq, s);
+    case DT_F32: return enc_q<D, B, DT_F32>(qjl, joint, a, n_seq, s);
+    case DT_BF16: return enc_q<D, B, DT_BF16>(qjl, joint, a, n_seq, s);
+    case DT_F16: return enc_q<D, B, DT_F16>(qjl, joint, a, n_seq, s);
   }
   return hipErrorInvalidValue;
 }
 
 template <int D>
-static hipError_t enc_b(int b, int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+static hipError_t enc_b(int b, int kdt, bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   switch (b) {
-    case 2: return enc_kt<D, 2>(kdt, qjl, a, n_seq, s);
-    case 3: return enc_kt<D, 3>(kdt, qjl, a, n_seq, s);
-    case 4: return enc_kt<D, 4>(kdt, qjl, a, n_seq, s);
+    case 2: return enc_kt<D, 2>(kdt, qjl, joint, a, n_seq, s);
+    case 3: return enc_kt<D, 3>(kdt, qjl, joint, a, n_seq, s);
+    case 4: return enc_kt<D, 4>(kdt, qjl, joint, a, n_seq, s);
   }
   return hipErrorInvalidValue;
 }
 
-hipError_t launch_encode(int d, int b, int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq,
-                         hipStream_t s) {
+hipError_t launch_encode(int d, int b, int kdt, bool qjl, bool joint, const EncodeArgs& a,
+                         int64_t n_seq, hipStream_t s) {
   if (a.n_new <= 0 || n_seq <= 0) return hipSuccess;
   switch (d) {
-    case 64: return enc_b<64>(b, kdt, qjl, a, n_seq, s);
-    case 128: return enc_b<128>(b, kdt, qjl, a, n_seq, s);
+    case 64: return enc_b<64>(b, kdt, qjl, joint, a, n_seq, s);
+    case 128: return enc_b<128>(b, kdt, qjl, joint, a, n_seq, s);
   }
   return hipErrorInvalidValue;
 }

@@ -606,10 +606,11 @@ size_t octo_qjl_bits_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap) 
   return (size_t)n_seq * (size_t)((cap + kTile - 1) / kTile) * kTile * (cb->d / 32) * 4;
 }
 
-octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kdt, int64_t n_seq,
-                        int64_t n_new, int64_t seq_stride, int64_t key_stride, int64_t pos0,
-                        int64_t cap, void* packed, float* gamma, void* qjl_bits,
-                        uint16_t* qjl_norm, void* stream) {
+static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_dtype kdt,
+                               int64_t n_seq, int64_t n_new, int64_t seq_stride,
+                               int64_t key_stride, int64_t pos0, int64_t cap, void* packed,
+                               float* gamma, void* qjl_bits, uint16_t* qjl_norm, void* stream,
+                               bool joint) {
   octo_status st = check_cb(cb);
   if (st != OCTO_OK) return st;
   if (kdt != OCTO_F32 && kdt != OCTO_BF16 && kdt != OCTO_F16)
@@ -626,7 +627,7 @@ octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kd
   if (!aligned(keys, 16) || (key_stride * es) % 16 || (seq_stride * es) % 16)
     return fail(OCTO_ERR_INVALID_ARG, "key rows must be 16-byte aligned");
   if (!aligned(packed, 16) || !aligned(gamma, 4))
-    return fail(OCTO_ERR_INVALID_ARG, "packed/gamma must be 4-byte aligned");
+    return fail(OCTO_ERR_INVALID_ARG, "packed must be 16-byte and gamma 4-byte aligned");
   if ((qjl_bits == nullptr) != (qjl_norm == nullptr))
     return fail(OCTO_ERR_INVALID_ARG, "pass both QJL buffers or neither");
   if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
@@ -644,9 +645,25 @@ octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kd
   a.gamma = gamma;
   a.qjl_bits = (uint32_t*)qjl_bits;
   a.qjl_norm = qjl_norm;
-  return hip_status(launch_encode(cb->d, cb->b, (int)kdt, qjl_bits != nullptr, a, n_seq,
+  return hip_status(launch_encode(cb->d, cb->b, (int)kdt, qjl_bits != nullptr, joint, a, n_seq,
                                   (hipStream_t)stream),
                     "encode launch");
+}
+
+octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kdt, int64_t n_seq,
+                        int64_t n_new, int64_t seq_stride, int64_t key_stride, int64_t pos0,
+                        int64_t cap, void* packed, float* gamma, void* qjl_bits,
+                        uint16_t* qjl_norm, void* stream) {
+  return encode_impl(cb, keys, kdt, n_seq, n_new, seq_stride, key_stride, pos0, cap, packed, gamma,
+                     qjl_bits, qjl_norm, stream, false);
+}
+
+octo_status octo_encode_joint(const octo_codebook* cb, const void* keys, octo_dtype kdt,
+                              int64_t n_seq, int64_t n_new, int64_t seq_stride,
+                              int64_t key_stride, int64_t pos0, int64_t cap, void* packed,
+                              float* gamma, void* qjl_bits, uint16_t* qjl_norm, void* stream) {
+  return encode_impl(cb, keys, kdt, n_seq, n_new, seq_stride, key_stride, pos0, cap, packed, gamma,
+                     qjl_bits, qjl_norm, stream, true);
 }
 
 size_t octo_decode_workspace_bytes(const octo_codebook* cb, int mode, int B, int Hq, int Hkv,

@@ -104,8 +104,8 @@ struct MQArgs {
   float* part;           // [B*H][n_q][n_split][d + 2]
 };
 
-hipError_t launch_encode(int d, int b, int kdt, bool qjl, const EncodeArgs& a, int64_t n_seq,
-                         hipStream_t s);
+hipError_t launch_encode(int d, int b, int kdt, bool qjl, bool joint, const EncodeArgs& a,
+                         int64_t n_seq, hipStream_t s);
 hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s);
 hipError_t launch_logits(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq,
                          int n_blocks_x, hipStream_t s);

@@ -91,3 +91,31 @@ def logit_err(gpu: np.ndarray, ref: np.ndarray, qnorm: np.ndarray, gamma: np.nda
     """max over entries of |dl| / max(|l|, |q| gamma / sqrt(d))."""
     scale = np.maximum(np.abs(ref), qnorm * gamma / np.sqrt(d))
     return float(np.max(np.abs(gpu - ref) / np.maximum(scale, 1e-30)))
+
+
+def compare_joint_codes(gpu_codes: np.ndarray, enc: O.Encoded, cb: O.Codebook):
+    """Joint rounding (the encoder's 3x3 search): a triplet whose device code
+    differs from the oracle's is excused when the oracle's error of the
+    device's choice, |t - rho^ n^|^2 in fp64, is within 1e-6 |t|^2 of the
+    oracle's minimum (the choice was a near-tie for fp32), and the device's
+    direction code lies in the 3x3 neighbourhood of the oracle's scalar
+    indices moved by at most one more step (a scalar index on a midpoint may
+    move the search's centre).  Returns (n_mismatch, n_excused, n_unexcused,
+    total triplets)."""
+    g = gpu_codes.reshape(-1, 3)
+    o = enc.codes.reshape(-1, 3)
+    t = O.split_triplets(enc.rotated).reshape(-1, 3)
+    mism = np.any(g != o, axis=1)
+    if not mism.any():
+        return 0, 0, 0, g.shape[0]
+    err = lambda c: np.sum((cb.c_rho[c[:, 2]][:, None]  # noqa: E731
+                            * O.octa_decode(cb.c_xi[c[:, 0]], cb.c_eta[c[:, 1]]) - t) ** 2, axis=1)
+    eg, eo = err(g), err(o)
+    tt = np.sum(t * t, axis=1)
+    _, n = O.triplet_polar(t)
+    xi, eta = O.octa_encode(n)
+    sx, se = O.quantize(xi, cb.c_xi), O.quantize(eta, cb.c_eta)
+    near = (np.abs(g[:, 0] - sx) <= 2) & (np.abs(g[:, 1] - se) <= 2)
+    excused = mism & (eg - eo <= BOUNDARY_TOL * np.maximum(tt, 1e-30)) & near
+    n_mis, n_exc = int(mism.sum()), int(excused.sum())
+    return n_mis, n_exc, n_mis - n_exc, g.shape[0]

@@ -16,8 +16,9 @@ torch = pytest.importorskip("torch")
 
 import oracle as O  # noqa: E402
 import workloads as WL  # noqa: E402
-from parity import (assert_codes_match, compare_codes, logit_err, rel_err_rows,  # noqa: E402
-                    unpack_device_codes, unpack_device_signs)
+from parity import (MAX_EXCUSED_FRACTION, assert_codes_match, compare_codes,  # noqa: E402
+                    compare_joint_codes, logit_err, rel_err_rows, unpack_device_codes,
+                    unpack_device_signs)
 
 pytestmark = pytest.mark.gpu
 
@@ -92,6 +93,65 @@ def test_encode_all_shapes_ragged(d, b, kdt):
     cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=d + b, n_seq=3, n=200)
     encode_and_check(d, b, keys, cap=256, label=f"d{d}b{b}{kdt}")
+
+
+@pytest.mark.parametrize("d,b,kdt", [(128, 2, "bf16"), (128, 3, "bf16"), (128, 4, "bf16"),
+                                     (64, 3, "bf16"), (128, 4, "f32")])
+def test_encode_joint_rounding(d, b, kdt):
+    """octo_encode_joint against the oracle's joint rounding ([YL] 联合取整),
+    ragged tail, with the same gamma as the scalar encoder."""
+    octo = _octo()
+    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    keys = WL.make_keys(cfg, "cuda", seed=40 + d + b, n_seq=3, n=200)
+    g = gcb(d, b)
+    cache = octo.Cache(g, 3, 256)
+    octo.octo_encode_joint(g, keys, cache)
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    kk = f64(keys).reshape(-1, d)
+    enc = O.encode(kk, cb, rounding="joint")
+    codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, 3, 256, 200)
+    n_mis, n_exc, n_unexc, total = compare_joint_codes(codes, enc, cb)
+    say(f"[joint d{d} b{b} {kdt}] {total} triplets, {n_mis} differ, {n_exc} excused near-ties")
+    assert n_unexc == 0
+    assert n_exc <= max(1, MAX_EXCUSED_FRACTION * total)
+    gamma = cache.gamma.cpu().numpy().reshape(3, 256)[:, :200].reshape(-1)
+    ref_g = np.linalg.norm(kk, axis=1)
+    assert np.all(np.abs(gamma - ref_g) <= 1e-6 * ref_g)
+    # joint rounding changes a good share of the scalar codes and lowers the error
+    scal = O.encode(kk, cb)
+    assert np.mean(np.any(enc.codes != scal.codes, axis=-1)) > 0.05
+    mse = lambda c: np.mean(np.sum((O.decode(c, enc.gamma, cb) - kk) ** 2, 1) / np.sum(kk * kk, 1))  # noqa: E731
+    assert mse(codes.reshape(-1, cb.T, 3)) < mse(scal.codes)
+
+
+def test_encode_joint_rounding_with_qjl():
+    """Joint rounding with the QJL residual: the residual follows the chosen codes."""
+    octo = _octo()
+    cfg = WL.CONFIGS[5]
+    keys = WL.make_keys(cfg, "cuda", seed=9, n_seq=2, n=130)
+    g = gcb(128, 3, 0, 0, True)
+    cache = octo.Cache(g, 2, 192, qjl=True)
+    octo.octo_encode_joint(g, keys, cache)
+    torch.cuda.synchronize()
+    cb = ocb(128, 3)
+    kk = f64(keys).reshape(-1, 128)
+    enc = O.encode(kk, cb, rounding="joint")
+    codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, 2, 192, 130)
+    n_mis, n_exc, n_unexc, total = compare_joint_codes(codes, enc, cb)
+    assert n_unexc == 0 and n_exc <= max(1, MAX_EXCUSED_FRACTION * total)
+    # signs of S r' with r' from the device's own codes
+    S = O.qjl_matrix(128, 0)
+    uh = O.decode_rotated(codes.reshape(-1, cb.T, 3), cb)
+    qe = O.qjl_encode(enc.rotated, uh, S)
+    signs = unpack_device_signs(cache.qjl_bits.cpu().numpy(), 128, 2, 192, 130).reshape(-1, 128)
+    r = enc.rotated - uh
+    proj = r @ S.T
+    bad = (signs != qe.signs) & (np.abs(proj) > 1e-6 * np.linalg.norm(S, axis=1)[None, :]
+                                 * np.linalg.norm(r, axis=1)[:, None])
+    assert not bad.any()
+    gnu = cache.qjl_norm.cpu().numpy().view(np.float16).reshape(2, 192)[:, :130].reshape(-1)
+    assert np.allclose(gnu.astype(np.float64), qe.nu.astype(np.float64), rtol=1e-3, atol=1e-6)
 
 
 def test_encode_f16_keys():
