@@ -169,6 +169,54 @@ def qjl_bias_study(cfg, dev, n_seeds: int = 64, n_keys: int = 4096):
     return out
 
 
+def quality_harness(dev, repeats: int = 64, bits=(2, 3, 4)):
+    """The pages' synthetic quality experiment on the GPU path ([YL] 实验结果:
+    d=128 isotropic Gaussian keys, 1024 random keys and 16 queries, 64 repeats;
+    the needle among 2048 random distractors; [YL] 可选的残差修正 for the QJL
+    inner products).  Keys go through octo_encode, their reconstruction through
+    octo_debug_reconstruct, the inner products through octo_decode_logits.
+    Per bit width: normalised MSE E|k - k^|^2/|k|^2, mean cosine(k, k^),
+    inner-product error RMS(<q,k^> - <q,k>)/RMS(<q,k>) without and with the
+    1-bit QJL term, and the softmax mass (scale 1/sqrt(d)) on the needle when
+    the query is the needle key (the exact keys' mass beside it).  The
+    needle's query and the softmax scale are readings: the pages do not print
+    them."""
+    import numpy as np
+    import torch
+
+    import rotation_preconditioned_quantization_amd as octo
+    import workloads as WL
+    d = 128
+    out = {"repeats": repeats, "keys": 1024, "queries": 16, "distractors": 2048, "d": d,
+           "printed": {"mse_b4": 0.0071, "mse_b2": 0.0897, "needle_mass_b2": 0.92}}
+    rms = lambda x: float(torch.sqrt(torch.mean(x.double() ** 2)))  # noqa: E731
+    for b in bits:
+        cb = octo.Codebook(d, b, qjl=True, device=0)
+        acc = {k: [] for k in ("mse", "cos", "ip", "ip_qjl", "needle", "needle_exact")}
+        for r in range(repeats):
+            keys, q, nk, nq, pos = WL.make_quality_inputs(dev, seed=r)
+            cache = octo.Cache(cb, 1, 1024, qjl=True)
+            octo.octo_encode(cb, keys, cache)
+            kh = octo.octo_debug_reconstruct(cb, cache, 1024)[0].double()
+            kk = keys[0].double()
+            acc["mse"].append(float(torch.mean(((kh - kk) ** 2).sum(1) / (kk ** 2).sum(1))))
+            acc["cos"].append(float(torch.mean((kh * kk).sum(1) / (kh.norm(dim=1) * kk.norm(dim=1)))))
+            exact = q[0].double() @ kk.T
+            lg = octo.octo_decode_logits(cb, q, cache, 1024, 1, use_qjl=False)[0].double()
+            lq = octo.octo_decode_logits(cb, q, cache, 1024, 1, use_qjl=True)[0].double()
+            acc["ip"].append(rms(lg - exact) / rms(exact))
+            acc["ip_qjl"].append(rms(lq - exact) / rms(exact))
+            ncache = octo.Cache(cb, 1, ((nk.shape[1] + 63) // 64) * 64, qjl=True)
+            octo.octo_encode(cb, nk, ncache)
+            nl = octo.octo_decode_logits(cb, nq, ncache, nk.shape[1], 1, use_qjl=False)[0, 0].double()
+            acc["needle"].append(float(torch.softmax(nl / math.sqrt(d), 0)[pos]))
+            ne = (nq[0, 0].double() @ nk[0].double().T) / math.sqrt(d)
+            acc["needle_exact"].append(float(torch.softmax(ne, 0)[pos]))
+        cb.close()
+        out[f"b{b}"] = {k: round(float(np.mean(v)), 5) for k, v in acc.items()}
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -182,6 +230,10 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl-bias", action="store_true",
                     help="skip the 64-seed bias study of the QJL workload")
+    ap.add_argument("--quality", action="store_true",
+                    help="run the pages' synthetic quality experiment on the GPU path and print "
+                         "its JSON line (no timing)")
+    ap.add_argument("--quality-repeats", type=int, default=64)
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection run for rocprofv3 --pmc: per step a plain copy "
                          "kernel of 64 MiB (the counter scale), then encode and decode, eagerly")
@@ -207,6 +259,9 @@ def main():
         sys.exit(2)
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.quality:
+        print(json.dumps({"quality": quality_harness(dev, args.quality_repeats)}), flush=True)
+        return
     cfg = WL.CONFIGS[args.config]
     cb = octo.Codebook(cfg.d, cfg.b, seed=0, cb_seed=0, qjl=cfg.qjl, device=0)
     lay = cb.layout

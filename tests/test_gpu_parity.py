@@ -534,3 +534,19 @@ def test_debug_copy_is_exact():
         octo.octo_debug_copy(dst, src)
         torch.cuda.synchronize()
         assert torch.equal(dst, src)
+
+
+# ------------------------------------------------------------------ quality --
+def test_quality_harness_reproduces_printed_mse():
+    """The pages' synthetic experiment ([YL] 实验结果: d=128 Gaussian keys,
+    1024 keys x 16 queries) run through the GPU encoder and reconstruction
+    gives the printed normalised MSEs, 0.0071 at b=4 and 0.0897 at b=2
+    (within 3 %, 8 of the 64 repeats)."""
+    import bench
+    q = bench.quality_harness(torch.device("cuda:0"), repeats=8, bits=(2, 4))
+    say(f"[quality] {q}")
+    for b, printed in ((4, 0.0071), (2, 0.0897)):
+        assert abs(q[f"b{b}"]["mse"] - printed) <= 0.03 * printed, (b, q[f"b{b}"])
+    assert q["b4"]["cos"] > 0.99
+    # at 4 bits the needle keeps nearly all of the exact keys' softmax mass
+    assert abs(q["b4"]["needle"] - q["b4"]["needle_exact"]) < 0.02

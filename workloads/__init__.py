@@ -131,3 +131,19 @@ def make_queries(cfg: Config, device="cpu", seed: int = 0, B: int | None = None)
     g = _gen(device, seed, 3)
     q = torch.randn((B, cfg.Hq, cfg.n_q, cfg.d), generator=g, device=device)
     return q.to(_DT[cfg.qdtype])
+
+
+def make_quality_inputs(device="cpu", seed: int = 0, d: int = 128, n_keys: int = 1024,
+                        n_queries: int = 16, n_distractors: int = 2048):
+    """Inputs of the pages' synthetic quality experiment: isotropic Gaussian
+    fp32 keys [1, n_keys, d] and queries [1, n_queries, d]; and a needle set,
+    n_distractors Gaussian keys with one more key (the needle) at a seeded
+    position, [1, n_distractors + 1, d], whose query is the needle itself.
+    Returns (keys, queries, needle_keys, needle_query [1, 1, d], needle_pos)."""
+    g = _gen(device, seed, 5)
+    keys = torch.randn((1, n_keys, d), generator=g, device=device)
+    queries = torch.randn((1, n_queries, d), generator=g, device=device)
+    needle_keys = torch.randn((1, n_distractors + 1, d), generator=g, device=device)
+    pos = int(torch.randint(0, n_distractors + 1, (1,), generator=g, device=device).item())
+    needle_query = needle_keys[:, pos:pos + 1].clone()
+    return keys, queries, needle_keys, needle_query, pos
