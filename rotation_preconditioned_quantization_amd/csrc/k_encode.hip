@@ -15,6 +15,11 @@
 
 #include "octo_device.hpp"
 
+// Floating-point expressions here are evaluated exactly as written (fma only
+// where a builtin says so): the bulk and the one-key encoders then round the
+// same operations the same way and write identical words and gamma.
+#pragma clang fp contract(off)
+
 namespace octo {
 
 // Stage the key rows [r0, r0 + NR) of the wave's 64-key tile into LDS with
@@ -470,6 +475,141 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
   }
 }
 
+// ---------------------------------------------------------------------------
+// Latency-optimised encoder for a few keys per sequence (the autoregressive
+// step appends one key per sequence, [YL] 工程实现 / [AB] online): one
+// wavefront per key, lane l holding elements l + 64 r, the WHT butterflies
+// across lanes by shuffles (as in the query rotation), one triplet per lane,
+// and the packed words assembled in LDS.  Every value goes through the same
+// fp32 operations in the same order as in k_encode (stage 1 by v_dot2 on the
+// sign-flipped 16-bit pair, the serial energy sum over triplets, the same
+// quantiser tables), so both kernels write identical words and gamma.
+// ---------------------------------------------------------------------------
+template <int D, int B, int KT>
+__global__ __launch_bounds__(256) void k_encode_one(EncodeArgs a) {
+  using C = Codec<D, B>;
+  constexpr int T = C::T, W = C::W, NV = D / 64;
+  __shared__ float s_v[4][3 * T];
+  __shared__ float s_e[4][T];
+  __shared__ uint32_t s_w[4][W];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  __syncthreads();
+  const int64_t k = (int64_t)blockIdx.x * 4 + wave;  // keys flattened over (seq, new key)
+  if (k >= a.n_new * a.seq_count) return;
+  const int64_t seq = k / a.n_new, j = k % a.n_new;
+  const int64_t pos = a.pos0 + j;
+
+  // element j of the sign-flipped key, stage 1 applied (Sylvester order):
+  // lane pairs (2m, 2m+1) take x_2m + x_2m+1 and x_2m - x_2m+1
+  float x[NV];
+  if constexpr (KT == DT_F32) {
+    const float* row = (const float*)a.keys + seq * a.seq_stride + j * a.key_stride;
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int e = lane + 64 * r;
+      const uint32_t sb = (a.t.sign_bits[e >> 5] >> (e & 31)) & 1u;
+      x[r] = __uint_as_float(__float_as_uint(row[e]) ^ (sb << 31));
+    }
+  } else {
+    const uint32_t* row = (const uint32_t*)((const unsigned short*)a.keys + seq * a.seq_stride +
+                                            j * a.key_stride);
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const int e = lane + 64 * r, m = e >> 1;
+      const uint32_t s0 = (a.t.sign_bits[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
+      const uint32_t s1 = (a.t.sign_bits[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
+      const uint32_t wd = row[m] ^ ((s0 << 15) | (s1 << 31));
+      float sum, dif;
+      stage1_pair<KT>(wd, sum, dif);
+      x[r] = (e & 1) ? dif : sum;
+    }
+  }
+  float amax = 0.f;
+#pragma unroll
+  for (int r = 0; r < NV; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[r]));
+  amax = wave_max(amax);
+  int ex = 0;
+  __builtin_frexpf(amax, &ex);
+  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+  if (sexp != 0) {
+    const float scale = __builtin_ldexpf(1.0f, -sexp);
+#pragma unroll
+    for (int r = 0; r < NV; ++r) x[r] *= scale;
+  }
+  // remaining butterflies: stride 1 (fp32 keys only), then 2 .. 32 across
+  // lanes, then 64 between a lane's two values
+#pragma unroll
+  for (int h = (KT == DT_F32 ? 1 : 2); h < 64 && h < D; h <<= 1) {
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      const float o = __shfl_xor(x[r], h, 64);
+      x[r] = (lane & h) ? (o - x[r]) : (x[r] + o);
+    }
+  }
+  if constexpr (NV == 2) {
+    const float a0 = x[0], a1 = x[1];
+    x[0] = a0 + a1;
+    x[1] = a0 - a1;
+  }
+  float* sv = s_v[wave];
+#pragma unroll
+  for (int r = 0; r < NV; ++r) sv[lane + 64 * r] = x[r];
+  if (lane < 3 * T - D) sv[D + lane] = 0.f;
+  if (lane < W) s_w[wave][lane] = 0u;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+
+  // one triplet per lane
+  const int i = lane < T ? lane : T - 1;
+  const float tx = sv[3 * i], ty = sv[3 * i + 1], tz = sv[3 * i + 2];
+  const float e = triplet_energy(tx, ty, tz);
+  const uint32_t xe = xi_eta_code<C::BX>(tx, ty, tz, s_qx, a.t.qx.scale, a.t.qx.bias, s_qe,
+                                         a.t.qe.scale, a.t.qe.bias);
+  if (lane < T) s_e[wave][lane] = e;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  // the energy summed serially in triplet order, as the bulk encoder does
+  float tot = 0.f;
+  for (int t = 0; t < T; ++t) tot += s_e[wave][t];
+  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
+  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+  const uint32_t rc =
+      quant1_clamp(e * inv_tot, s_qr, a.t.qr2.scale, (float)(a.t.qr2.nb - 1));
+  const uint32_t code = xe | (rc << (C::BX + C::BE));
+  if (lane < T) {
+    const int p = lane * C::BT, wi = p >> 5, off = p & 31;
+    atomicOr(&s_w[wave][wi], code << off);
+    if (off + C::BT > 32) atomicOr(&s_w[wave][wi + 1], code >> (32 - off));
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (lane < W) {
+    // word lane of the key in the tile's word-group layout
+    constexpr int NG = W / 4, R = W % 4;
+    const int g = lane / 4;
+    const int width = g < NG ? 4 : R;
+    const int64_t tiles = a.cap / kTile;
+    uint32_t* tile = a.packed + (seq * tiles + (pos >> 6)) * W * kTile;
+    tile[256 * g + (int)(pos & 63) * width + (lane & 3)] = s_w[wave][lane];
+  }
+  if (lane == 0) a.gamma[seq * a.cap + pos] = gamma;
+}
+
+template <int D, int B, int KT>
+static hipError_t launch_encode_one_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  const int64_t keys = a.n_new * n_seq;
+  hipLaunchKernelGGL((k_encode_one<D, B, KT>), dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int B, int KT, bool QJL, bool JR>
 static hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
@@ -513,9 +653,35 @@ static hipError_t enc_b(int b, int kdt, bool qjl, bool joint, const EncodeArgs& 
   return hipErrorInvalidValue;
 }
 
+// Few keys per sequence without QJL or joint rounding: the one-key kernel.
+template <int D>
+static hipError_t enc_one_b(int b, int kdt, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+#define OCTO_ENC_ONE_KT(BB)                                                          \
+  switch (kdt) {                                                                   \
+    case DT_F32: return launch_encode_one_t<D, BB, DT_F32>(a, n_seq, s);           \
+    case DT_BF16: return launch_encode_one_t<D, BB, DT_BF16>(a, n_seq, s);         \
+    case DT_F16: return launch_encode_one_t<D, BB, DT_F16>(a, n_seq, s);           \
+  }                                                                                \
+  return hipErrorInvalidValue;
+  switch (b) {
+    case 2: OCTO_ENC_ONE_KT(2)
+    case 3: OCTO_ENC_ONE_KT(3)
+    case 4: OCTO_ENC_ONE_KT(4)
+  }
+#undef OCTO_ENC_ONE_KT
+  return hipErrorInvalidValue;
+}
+
 hipError_t launch_encode(int d, int b, int kdt, bool qjl, bool joint, const EncodeArgs& a,
                          int64_t n_seq, hipStream_t s) {
   if (a.n_new <= 0 || n_seq <= 0) return hipSuccess;
+  if (!qjl && !joint && a.n_new <= kEncodeOneMax) {
+    switch (d) {
+      case 64: return enc_one_b<64>(b, kdt, a, n_seq, s);
+      case 128: return enc_one_b<128>(b, kdt, a, n_seq, s);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (d) {
     case 64: return enc_b<64>(b, kdt, qjl, joint, a, n_seq, s);
     case 128: return enc_b<128>(b, kdt, qjl, joint, a, n_seq, s);

@@ -641,6 +641,7 @@ static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_d
   a.n_new = n_new;
   a.pos0 = pos0;
   a.cap = cap;
+  a.seq_count = n_seq;
   a.packed = (uint32_t*)packed;
   a.gamma = gamma;
   a.qjl_bits = (uint32_t*)qjl_bits;

@@ -11,6 +11,7 @@ constexpr int kTile = 64;          // keys per packed tile (one wavefront)
 constexpr int kMaxLut = 256;       // max buckets of an encoder lookup table
 constexpr int kMaxLevels = 32;     // max centroids of one component (5 bits)
 constexpr int kMaxSplit = 1024;    // max split-K partials per output row
+constexpr int kEncodeOneMax = 16;  // up to this many new keys per sequence: one-key encoder
 
 // Nearest-centroid lookup for one scalar component (encoder): the index
 // #{k : x > m_k} of the midpoint rule.  The value range is cut into nb equal
@@ -43,6 +44,7 @@ struct EncodeArgs {
   const void* keys;
   int64_t seq_stride, key_stride;  // elements
   int64_t n_new, pos0, cap;
+  int64_t seq_count;               // sequences (n_seq)
   uint32_t* packed;
   float* gamma;
   uint32_t* qjl_bits;

@@ -154,6 +154,31 @@ def test_encode_joint_rounding_with_qjl():
     assert np.allclose(gnu.astype(np.float64), qe.nu.astype(np.float64), rtol=1e-3, atol=1e-6)
 
 
+@pytest.mark.parametrize("d,b,kdt", [(128, 4, "bf16"), (128, 2, "f32"), (64, 3, "f16")])
+def test_encode_few_keys_equals_bulk(d, b, kdt):
+    """Appends of up to 16 keys per sequence take the one-key-per-wavefront
+    encoder; it writes the same words and gamma as the bulk encoder, bit for
+    bit (same fp32 operations in the same order), including extreme keys."""
+    octo = _octo()
+    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    keys = WL.make_keys(cfg, "cuda", seed=77 + d, n_seq=3, n=100)
+    keys[0, 3] = 0
+    keys[1, 5] *= 1e-30 if kdt == "f32" else 1e-3
+    keys[2, 7, 1] = 1e4 if kdt != "f16" else 300.0
+    g = gcb(d, b)
+    bulk = octo.Cache(g, 3, 128)
+    octo.octo_encode(g, keys, bulk)
+    few = octo.Cache(g, 3, 128)
+    p = 0
+    for n in (1, 5, 16, 1, 77):
+        octo.octo_encode(g, keys[:, p:p + n].contiguous(), few, pos0=p)
+        p += n
+    torch.cuda.synchronize()
+    assert torch.equal(bulk.packed, few.packed)
+    assert torch.equal(bulk.gamma, few.gamma)
+    encode_and_check(d, b, keys[:, 1:6].contiguous(), cap=128, pos0=1, label=f"few d{d}b{b}{kdt}")
+
+
 def test_encode_f16_keys():
     cfg = WL.CONFIGS[2].scaled(kdtype="f16", keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=2, n=130)
