@@ -359,6 +359,22 @@ def main():
         octo.octo_encode_joint(cb, k, jc, pos0=enc_pos0)
 
     joint_graph = capture(lambda: [encode_joint(s, jc) for s, jc in zip(sets, jcaches)])
+    # the autoregressive step (single-query attention workloads): append the
+    # newest key of every sequence at position N - 1, then attend over N keys
+    step_append = cfg.mode == "attn"
+    if step_append:
+        for s in sets:
+            s["new_key"] = s["keys"][:, cfg.N - 1].contiguous()
+
+        def append_step(s):
+            octo.octo_decode_attn_append(cb, s["new_key"], s["q"], s["cache"], s["v"], cfg.N,
+                                         cfg.Hkv, out=s["out"], workspace=s["ws"])
+
+        def append_encode(s):
+            octo.octo_encode(cb, s["new_key"].view(cfg.n_seq, 1, cfg.d), s["cache"], pos0=cfg.N - 1)
+
+        app_graph = capture(lambda: [append_step(s) for s in sets])
+        app_enc_graph = capture(lambda: [append_encode(s) for s in sets])
     dec_graph = capture(lambda: [decode(s) for s in sets])
     main_graph = capture(lambda: [decode(s, octo.STAGE_MAIN) for s in sets])
     torch.cuda.synchronize()
@@ -385,6 +401,9 @@ def main():
 
     t_enc = time_graph(enc_graph, args.kernel_reps) / R
     t_joint = time_graph(joint_graph, max(1, args.kernel_reps // 4)) / R
+    if step_append:
+        t_app = time_graph(app_graph, args.kernel_reps) / R
+        t_app_enc = time_graph(app_enc_graph, args.kernel_reps) / R
     t_dec = time_graph(dec_graph, args.kernel_reps) / R
     t_main = time_graph(main_graph, args.kernel_reps) / R
 
@@ -450,6 +469,8 @@ def main():
         "encode_pct_hbm_peak": round(100 * enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS, 2),
         "encode_joint_us": round(t_joint * 1e6, 3),
         "encode_joint_mkeys_per_s": round(n_keys_total / t_joint / 1e6, 1),
+        **({"append_step_us": round(t_app * 1e6, 3), "append_encode_us": round(t_app_enc * 1e6, 3),
+            "append_keys_per_step": cfg.n_seq} if step_append else {}),
         "roofline": roofline,
     }
     if cfg.qjl and not args.no_qjl_bias:

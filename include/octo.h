@@ -184,6 +184,26 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
                              octo_dtype vdt, int64_t n_keys, int64_t cap, float scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* One autoregressive decode step ([YL] 工程实现; [AB] online): the new
+ * token's key of every sequence is encoded into the cache at position
+ * n_keys - 1, then the fused attention of one query token per head runs over
+ * the n_keys cached keys, the new one included, exactly as octo_decode_attn
+ * with n_q = 1.
+ *   new_keys: device, dtype kdt, the key of sequence s = b*Hkv + kvh at
+ *     new_keys + s * key_seq_stride (elements; 16-byte aligned rows).
+ *   v must already hold the new token's value row at position n_keys - 1.
+ *   Without QJL buffers the key goes through the one-key-per-wavefront
+ *   encoder (identical words and gamma to octo_encode); with them, through
+ *   the QJL encoder, and the QJL term is used in the attention.
+ * Requires 1 <= n_keys <= cap.  Other arguments, ownership and errors as
+ * octo_encode and octo_decode_attn. */
+octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_keys, octo_dtype kdt,
+                                    int64_t key_seq_stride, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, void* packed, float* gamma, void* qjl_bits,
+                                    uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream);
+
 /* The launches of the two decode calls, for callers that schedule or time
  * them one by one: OCTO_STAGE_ROTATE writes the rotated queries into the
  * workspace (multi-query attention only; the other kernels rotate in their

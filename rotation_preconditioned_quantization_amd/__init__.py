@@ -55,6 +55,8 @@ _SIGS = {
     "octo_qjl_bits_bytes": (_SZ, [_P, _I64, _I64]),
     "octo_encode": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
     "octo_encode_joint": (_I, [_P, _P, _I, _I64, _I64, _I64, _I64, _I64, _I64, _P, _P, _P, _P, _P]),
+    "octo_decode_attn_append": (_I, [_P, _P, _I, _I64, _P, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I,
+                                     _I64, _I64, _F, _P, _P, _SZ, _P]),
     "octo_decode_workspace_bytes": (_SZ, [_P, _I, _I, _I, _I, _I, _I64]),
     "octo_decode_logits": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "octo_decode_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64, _F,
@@ -269,6 +271,34 @@ def octo_decode_attn(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, ou
                                          _dtype_code(v), n_keys, cache.cap, scale, _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream), stages),
            "octo_decode_attn")
+    return out
+
+
+def octo_decode_attn_append(cb: Codebook, new_keys, q, cache: Cache, v, n_keys: int, Hkv: int,
+                            out=None, scale: float = 0.0, workspace=None,
+                            use_qjl: bool | None = None, stream=None):
+    """One decode step: encode new_keys [B*Hkv, d] (or [B*Hkv, 1, d]) at cache
+    position n_keys - 1, then attend q [B, Hq, 1, d] over the n_keys keys."""
+    import torch
+    B, Hq, n_q, d = q.shape
+    if n_q != 1:
+        raise ValueError("one query token per head")
+    nk = new_keys.reshape(new_keys.shape[0], d)
+    if nk.stride(1) != 1:
+        raise ValueError("new_keys must have a contiguous last dim")
+    if out is None:
+        out = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=q.device)
+    workspace, _ = _workspace(cb, 1, B, Hq, Hkv, 1, n_keys, workspace, q.device)
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    if not q.is_contiguous():
+        raise ValueError("q must be contiguous")
+    _check(lib().octo_decode_attn_append(cb.handle, _ptr(nk), _dtype_code(nk), nk.stride(0),
+                                         _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(cache.packed),
+                                         _ptr(cache.gamma), _ptr(cache.qjl_bits) if qjl else None,
+                                         _ptr(cache.qjl_norm) if qjl else None, _ptr(v),
+                                         _dtype_code(v), n_keys, cache.cap, scale, _ptr(out),
+                                         _ptr(workspace), workspace.numel(), _stream(stream)),
+           "octo_decode_attn_append")
     return out
 
 

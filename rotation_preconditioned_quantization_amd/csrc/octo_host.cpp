@@ -761,6 +761,33 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
                                  OCTO_STAGE_ALL);
 }
 
+octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_keys, octo_dtype kdt,
+                                    int64_t key_seq_stride, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, void* packed, float* gamma, void* qjl_bits,
+                                    uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream) {
+  // the decode's argument checks run before the encode writes anything
+  octo_status st = check_decode_common(cb, q, qdt, B, Hq, Hkv, packed, gamma, qjl_bits, qjl_norm,
+                                       n_keys, cap, workspace);
+  if (st != OCTO_OK) return st;
+  if (n_keys < 1) return fail(OCTO_ERR_INVALID_ARG, "need 1 <= n_keys <= cap");
+  if (vdt != OCTO_BF16) return fail(OCTO_ERR_UNSUPPORTED, "V must be bf16");
+  if (!v || !aligned(v, 16)) return fail(OCTO_ERR_INVALID_ARG, "v NULL or not 16-byte aligned");
+  if (!out || !aligned(out, 4)) return fail(OCTO_ERR_INVALID_ARG, "out NULL/misaligned");
+  if (workspace_bytes < ws_layout(cb, 1, B, Hq, Hkv, 1, n_keys).total)
+    return fail(OCTO_ERR_WORKSPACE, "workspace too small");
+  const int64_t n_seq = (int64_t)B * Hkv;
+  if (n_seq == 0 || Hq == 0) return OCTO_OK;
+  if (n_seq > 1 && key_seq_stride < cb->d) return fail(OCTO_ERR_INVALID_ARG, "key_seq_stride < d");
+  st = encode_impl(cb, new_keys, kdt, n_seq, 1, key_seq_stride, cb->d, n_keys - 1, cap, packed,
+                   gamma, qjl_bits, qjl_norm, stream, false);
+  if (st != OCTO_OK) return st;
+  return octo_decode_attn_stages(cb, q, qdt, B, Hq, Hkv, 1, packed, gamma, qjl_bits, qjl_norm, v,
+                                 vdt, n_keys, cap, scale, out, workspace, workspace_bytes, stream,
+                                 OCTO_STAGE_ALL);
+}
+
 octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
                                     int Hq, int Hkv, int n_q, const void* packed,
                                     const float* gamma, const void* qjl_bits,

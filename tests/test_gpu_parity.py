@@ -379,6 +379,46 @@ def test_attention_with_qjl():
     check_attention(WL.CONFIGS[5], 1, 2, 4, 400, 448, seed=6, qjl=True, label="attn-qjl")
 
 
+@pytest.mark.parametrize("n,qjl", [(1000, False), (65, False), (1, False), (400, True)])
+def test_decode_step_append(n, qjl):
+    """octo_decode_attn_append (encode the new token's key at n - 1, then
+    attend over n keys) equals a bulk encode of all n keys followed by
+    octo_decode_attn: the same cache bytes and the same output; the output
+    also matches the oracle."""
+    octo = _octo()
+    cfg = WL.CONFIGS[5] if qjl else WL.CONFIGS[2]
+    B, Hkv, G, cap = 1, 2, 4, ((n + 63) // 64) * 64
+    Hq, n_seq, d = Hkv * G, B * Hkv, cfg.d
+    keys = WL.make_keys(cfg, "cuda", seed=n, n_seq=n_seq, n=n)
+    v = WL.make_values(cfg, "cuda", seed=n, n_seq=n_seq, cap=cap)
+    q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=1), "cuda", seed=n, B=B)
+    g = gcb(d, cfg.b, 0, 0, qjl)
+    ref_cache = octo.Cache(g, n_seq, cap, qjl=qjl)
+    octo.octo_encode(g, keys, ref_cache)
+    ref = octo.octo_decode_attn(g, q, ref_cache, v, n, Hkv)
+    step = octo.Cache(g, n_seq, cap, qjl=qjl)
+    if n > 1:
+        octo.octo_encode(g, keys[:, : n - 1].contiguous(), step)
+    out = octo.octo_decode_attn_append(g, keys[:, n - 1].contiguous(), q, step, v, n, Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(step.packed, ref_cache.packed) and torch.equal(step.gamma, ref_cache.gamma)
+    if qjl:
+        assert torch.equal(step.qjl_norm, ref_cache.qjl_norm)
+    assert torch.equal(out, ref)
+    if not qjl:
+        cb = ocb(d, cfg.b)
+        codes = unpack_device_codes(step.packed.cpu().numpy(), cb, n_seq, cap, n)
+        gam = step.gamma.cpu().numpy().reshape(n_seq, cap)[:, :n]
+        qq, vv, oo = f64(q), f64(v), f64(out)
+        for s_ in range(n_seq):
+            uh = O.decode_rotated(codes[s_], cb)
+            for gg in range(G):
+                h = s_ * G + gg
+                lg = O.logits_rotated(qq[0, h, 0], uh, gam[s_], cb)
+                r = O.softmax_attention(lg / math.sqrt(d), vv[s_, :n])
+                assert np.linalg.norm(oo[0, h, 0] - r) <= 2e-3 * np.linalg.norm(r)
+
+
 @pytest.mark.parametrize("n", [1, 63, 64, 65])
 def test_attention_tiny_caches(n):
     check_attention(WL.CONFIGS[2], 1, 1, 4, n, 128, seed=n, label=f"attn-n{n}")
