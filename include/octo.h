@@ -192,9 +192,12 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
  *   new_keys: device, dtype kdt, the key of sequence s = b*Hkv + kvh at
  *     new_keys + s * key_seq_stride (elements; 16-byte aligned rows).
  *   v must already hold the new token's value row at position n_keys - 1.
- *   Without QJL buffers the key goes through the one-key-per-wavefront
- *   encoder (identical words and gamma to octo_encode); with them, through
- *   the QJL encoder, and the QJL term is used in the attention.
+ *   For bf16 keys without QJL buffers the step is one fused pass: the
+ *   attention block that owns position n_keys - 1 encodes the key with one
+ *   wavefront (the same operations and rounding as octo_encode, so identical
+ *   words and gamma), writes it to the cache and uses it at once.  Otherwise
+ *   the key is encoded first (with the QJL encoder when QJL buffers are
+ *   given; the QJL term is then used in the attention).
  * Requires 1 <= n_keys <= cap.  Other arguments, ownership and errors as
  * octo_encode and octo_decode_attn. */
 octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_keys, octo_dtype kdt,

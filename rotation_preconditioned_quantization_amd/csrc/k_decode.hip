@@ -15,6 +15,7 @@
 //                split-K over the sequence; k_combine merges the splits.
 //   k_reconstruct  test helper writing k^ = gamma R^T u'^.
 #include "octo_device.hpp"
+#include "octo_encode_dev.hpp"
 
 namespace octo {
 
@@ -417,6 +418,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __align__(16) float s_p[4][4][kTile + 4];
   __shared__ float s_ml[4][4][2];
   __shared__ float s_o[4][4][D];
+  // append step: scratch of the one-wavefront encode and the new key's words
+  __shared__ float s_ak[4 * Codec<D, B>::T];
+  __shared__ uint32_t s_aw[Codec<D, B>::W];
+  __shared__ float s_ag;
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
@@ -449,6 +454,38 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   SQPre<D, B, QJL> pre;
   sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
   sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
+  // Decode step with append: the block whose split holds position n_keys - 1
+  // encodes the sequence's new key with one wavefront (the same code and
+  // rounding as the append encoder), the first head pass writes it to the
+  // cache, and the wave that owns the last tile substitutes it for the stale
+  // words it loaded.
+  const int64_t t_last = (a.n_keys - 1) / kTile;
+  bool app = false;
+  if constexpr (!QJL) {
+    app = a.new_keys != nullptr && t_last >= t_begin && t_last < t_end;
+    if (app) {
+      if (wave == 0) {
+        constexpr int T = Codec<D, B>::T, W = Codec<D, B>::W;
+        const void* row = (const unsigned short*)a.new_keys + seq * a.new_key_stride;
+        const float g = encode_one_key<D, B, DT_BF16>(row, a.t, a.t.qx.t, a.t.qe.t, a.t.qr2.t, lane,
+                                                      s_ak, s_ak + 3 * T, s_aw);
+        if (lane == 0) s_ag = g;
+        if (blockIdx.z == 0) {
+          if (lane < W) store_key_word<W>(a.packed_w, a.cap, seq, a.n_keys - 1, lane, s_aw[lane]);
+          if (lane == 0) a.gamma_w[seq * a.cap + a.n_keys - 1] = g;
+        }
+      }
+      __syncthreads();
+    }
+  }
+  const int new_lane = (int)((a.n_keys - 1) & (kTile - 1));
+  auto patch = [&](KTile<D, B, QJL>& kt, int64_t tt) {
+    if (app && tt == t_last && lane == new_lane) {
+#pragma unroll
+      for (int w = 0; w < Codec<D, B>::W; ++w) kt.words[w] = s_aw[w];
+      kt.gamma = s_ag;
+    }
+  };
 
   float m[4], l[4];
   floatx4 o[8];
@@ -533,7 +570,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     load_vtile<D>(vlane, t + 4, vv);
     cur = nxt;
   }
-  if (t < t_end) process(cur, vv, t);
+  // (the last tile of the cache is always the last one of its wave)
+  if (t < t_end) {
+    patch(cur, t);
+    process(cur, vv, t);
+  }
 
   // lanes serving different keys of a load hold partial sums of the same dims
 #pragma unroll

@@ -14,6 +14,7 @@
 #include <algorithm>
 
 #include "octo_device.hpp"
+#include "octo_encode_dev.hpp"
 
 // Floating-point expressions here are evaluated exactly as written (fma only
 // where a builtin says so): the bulk and the one-key encoders then round the
@@ -107,61 +108,9 @@ __device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][
   }
 }
 
-// #{k : x > m_k} from a one-midpoint-per-bucket table in LDS (see Bucket1),
-// for x in [-1, 1] up to rounding: the bucket position is then above -1, so
-// truncation toward zero gives bucket 0 at the bottom, and the guard entries
-// cover the top.
-__device__ __forceinline__ uint32_t quant1(float x, const uint2* t, float scale, float bias) {
-  const uint2 e = t[(int)__builtin_fmaf(x, scale, bias)];
-  return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
-}
-
-// The same for x >= 0 of unbounded range (rho^2), clamped to the last bucket.
-__device__ __forceinline__ uint32_t quant1_clamp(float x, const uint2* t, float scale, float nbm1) {
-  const uint2 e = t[(uint32_t)__builtin_fminf(x * scale, nbm1)];
-  return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
-}
-
 // Waves (64-key tiles in flight) per encoder block.
 template <bool QJL>
 constexpr int enc_waves() { return 4; }
-
-// Triplet i of the rotated key, zero padded past D.
-template <int D>
-__device__ __forceinline__ void triplet_of(const float (&v)[D], int i, float& x, float& y, float& z) {
-  x = v[3 * i];
-  y = (3 * i + 1 < D) ? v[3 * i + 1] : 0.f;
-  z = (3 * i + 2 < D) ? v[3 * i + 2] : 0.f;
-}
-
-__device__ __forceinline__ float triplet_energy(float x, float y, float z) {
-  return __builtin_fmaf(z, z, __builtin_fmaf(y, y, x * x));
-}
-
-// The octahedral (xi, eta) indices of a triplet, i_xi | i_eta << BX
-// ([YL] 八面体折叠).  p = (x, y)/l1; in the lower hemisphere (z < 0) the fold
-// (1 - |p_y|) sgn p_x equals p_x + sgn(p_x) |z|/l1 (likewise for y), with
-// sgn(0) = +1 (the sign bit is copied; -0 only occurs for an all-zero
-// triplet, where |z| = 0).  A zero triplet maps to (0, 0), i.e. n = (0,0,1).
-template <int BX>
-__device__ __forceinline__ uint32_t xi_eta_code(float x, float y, float z, const uint2* tx,
-                                                float sx, float bx, const uint2* te, float se,
-                                                float be) {
-  const float l1 = __builtin_fabsf(x) + __builtin_fabsf(y) + __builtin_fabsf(z);
-  const float il = __builtin_amdgcn_rcpf(__builtin_fmaxf(l1, 1e-37f));
-  const float tz = __builtin_fmaxf(-z, 0.0f);
-  const float xi = (x + __builtin_copysignf(tz, x)) * il;
-  const float eta = (y + __builtin_copysignf(tz, y)) * il;
-  return quant1(xi, tx, sx, bx) | (quant1(eta, te, se, be) << BX);
-}
-
-// OR a code into bits [i BT, (i + 1) BT) of the key's LSB-first word stream.
-template <int BT, int W>
-__device__ __forceinline__ void pack_code(uint32_t (&words)[W], int i, uint32_t code) {
-  const int pos = i * BT, wi = pos >> 5, off = pos & 31;
-  words[wi] |= code << off;
-  if (off + BT > 32) words[wi + 1] |= code >> (32 - off);
-}
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -478,17 +427,12 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
 // ---------------------------------------------------------------------------
 // Latency-optimised encoder for a few keys per sequence (the autoregressive
 // step appends one key per sequence, [YL] 工程实现 / [AB] online): one
-// wavefront per key, lane l holding elements l + 64 r, the WHT butterflies
-// across lanes by shuffles (as in the query rotation), one triplet per lane,
-// and the packed words assembled in LDS.  Every value goes through the same
-// fp32 operations in the same order as in k_encode (stage 1 by v_dot2 on the
-// sign-flipped 16-bit pair, the serial energy sum over triplets, the same
-// quantiser tables), so both kernels write identical words and gamma.
+// wavefront per key (encode_one_key), words assembled in LDS, then stored.
 // ---------------------------------------------------------------------------
 template <int D, int B, int KT>
 __global__ __launch_bounds__(256) void k_encode_one(EncodeArgs a) {
   using C = Codec<D, B>;
-  constexpr int T = C::T, W = C::W, NV = D / 64;
+  constexpr int T = C::T, W = C::W;
   __shared__ float s_v[4][3 * T];
   __shared__ float s_e[4][T];
   __shared__ uint32_t s_w[4][W];
@@ -502,103 +446,11 @@ __global__ __launch_bounds__(256) void k_encode_one(EncodeArgs a) {
   if (k >= a.n_new * a.seq_count) return;
   const int64_t seq = k / a.n_new, j = k % a.n_new;
   const int64_t pos = a.pos0 + j;
-
-  // element j of the sign-flipped key, stage 1 applied (Sylvester order):
-  // lane pairs (2m, 2m+1) take x_2m + x_2m+1 and x_2m - x_2m+1
-  float x[NV];
-  if constexpr (KT == DT_F32) {
-    const float* row = (const float*)a.keys + seq * a.seq_stride + j * a.key_stride;
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int e = lane + 64 * r;
-      const uint32_t sb = (a.t.sign_bits[e >> 5] >> (e & 31)) & 1u;
-      x[r] = __uint_as_float(__float_as_uint(row[e]) ^ (sb << 31));
-    }
-  } else {
-    const uint32_t* row = (const uint32_t*)((const unsigned short*)a.keys + seq * a.seq_stride +
-                                            j * a.key_stride);
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int e = lane + 64 * r, m = e >> 1;
-      const uint32_t s0 = (a.t.sign_bits[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
-      const uint32_t s1 = (a.t.sign_bits[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
-      const uint32_t wd = row[m] ^ ((s0 << 15) | (s1 << 31));
-      float sum, dif;
-      stage1_pair<KT>(wd, sum, dif);
-      x[r] = (e & 1) ? dif : sum;
-    }
-  }
-  float amax = 0.f;
-#pragma unroll
-  for (int r = 0; r < NV; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[r]));
-  amax = wave_max(amax);
-  int ex = 0;
-  __builtin_frexpf(amax, &ex);
-  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
-  if (sexp != 0) {
-    const float scale = __builtin_ldexpf(1.0f, -sexp);
-#pragma unroll
-    for (int r = 0; r < NV; ++r) x[r] *= scale;
-  }
-  // remaining butterflies: stride 1 (fp32 keys only), then 2 .. 32 across
-  // lanes, then 64 between a lane's two values
-#pragma unroll
-  for (int h = (KT == DT_F32 ? 1 : 2); h < 64 && h < D; h <<= 1) {
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const float o = __shfl_xor(x[r], h, 64);
-      x[r] = (lane & h) ? (o - x[r]) : (x[r] + o);
-    }
-  }
-  if constexpr (NV == 2) {
-    const float a0 = x[0], a1 = x[1];
-    x[0] = a0 + a1;
-    x[1] = a0 - a1;
-  }
-  float* sv = s_v[wave];
-#pragma unroll
-  for (int r = 0; r < NV; ++r) sv[lane + 64 * r] = x[r];
-  if (lane < 3 * T - D) sv[D + lane] = 0.f;
-  if (lane < W) s_w[wave][lane] = 0u;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
-  // one triplet per lane
-  const int i = lane < T ? lane : T - 1;
-  const float tx = sv[3 * i], ty = sv[3 * i + 1], tz = sv[3 * i + 2];
-  const float e = triplet_energy(tx, ty, tz);
-  const uint32_t xe = xi_eta_code<C::BX>(tx, ty, tz, s_qx, a.t.qx.scale, a.t.qx.bias, s_qe,
-                                         a.t.qe.scale, a.t.qe.bias);
-  if (lane < T) s_e[wave][lane] = e;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  // the energy summed serially in triplet order, as the bulk encoder does
-  float tot = 0.f;
-  for (int t = 0; t < T; ++t) tot += s_e[wave][t];
-  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
-  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
-  const uint32_t rc =
-      quant1_clamp(e * inv_tot, s_qr, a.t.qr2.scale, (float)(a.t.qr2.nb - 1));
-  const uint32_t code = xe | (rc << (C::BX + C::BE));
-  if (lane < T) {
-    const int p = lane * C::BT, wi = p >> 5, off = p & 31;
-    atomicOr(&s_w[wave][wi], code << off);
-    if (off + C::BT > 32) atomicOr(&s_w[wave][wi + 1], code >> (32 - off));
-  }
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-  if (lane < W) {
-    // word lane of the key in the tile's word-group layout
-    constexpr int NG = W / 4, R = W % 4;
-    const int g = lane / 4;
-    const int width = g < NG ? 4 : R;
-    const int64_t tiles = a.cap / kTile;
-    uint32_t* tile = a.packed + (seq * tiles + (pos >> 6)) * W * kTile;
-    tile[256 * g + (int)(pos & 63) * width + (lane & 3)] = s_w[wave][lane];
-  }
+  const void* row = (const unsigned char*)a.keys +
+                    (seq * a.seq_stride + j * a.key_stride) * DtSize<KT>::v;
+  const float gamma = encode_one_key<D, B, KT>(row, a.t, s_qx, s_qe, s_qr, lane, s_v[wave],
+                                               s_e[wave], s_w[wave]);
+  if (lane < W) store_key_word<W>(a.packed, a.cap, seq, pos, lane, s_w[wave][lane]);
   if (lane == 0) a.gamma[seq * a.cap + pos] = gamma;
 }
 

@@ -761,6 +761,22 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
                                  OCTO_STAGE_ALL);
 }
 
+// The new-key arguments of a decode step with append (see DecodeArgs).
+struct AppendKey {
+  const void* keys;
+  int64_t stride;
+  void* packed;
+  float* gamma;
+};
+
+static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, int n_q, const void* packed,
+                                    const float* gamma, const void* qjl_bits,
+                                    const uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int stages, const AppendKey* app);
+
 octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_keys, octo_dtype kdt,
                                     int64_t key_seq_stride, const void* q, octo_dtype qdt, int B,
                                     int Hq, int Hkv, void* packed, float* gamma, void* qjl_bits,
@@ -780,6 +796,16 @@ octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_key
   const int64_t n_seq = (int64_t)B * Hkv;
   if (n_seq == 0 || Hq == 0) return OCTO_OK;
   if (n_seq > 1 && key_seq_stride < cb->d) return fail(OCTO_ERR_INVALID_ARG, "key_seq_stride < d");
+  if (!qjl_bits && kdt == OCTO_BF16) {
+    // fused: the attention kernel encodes the new key itself (same code and
+    // rounding as the append encoder)
+    if (!new_keys || !aligned(new_keys, 16) || (key_seq_stride * 2) % 16)
+      return fail(OCTO_ERR_INVALID_ARG, "new key rows must be 16-byte aligned");
+    const AppendKey app{new_keys, key_seq_stride, packed, gamma};
+    return decode_attn_impl(cb, q, qdt, B, Hq, Hkv, 1, packed, gamma, nullptr, nullptr, v, vdt,
+                            n_keys, cap, scale, out, workspace, workspace_bytes, stream,
+                            OCTO_STAGE_ALL, &app);
+  }
   st = encode_impl(cb, new_keys, kdt, n_seq, 1, key_seq_stride, cb->d, n_keys - 1, cap, packed,
                    gamma, qjl_bits, qjl_norm, stream, false);
   if (st != OCTO_OK) return st;
@@ -795,6 +821,18 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
                                     int64_t n_keys, int64_t cap, float scale, float* out,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     int stages) {
+  return decode_attn_impl(cb, q, qdt, B, Hq, Hkv, n_q, packed, gamma, qjl_bits, qjl_norm, v, vdt,
+                          n_keys, cap, scale, out, workspace, workspace_bytes, stream, stages,
+                          nullptr);
+}
+
+static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, int n_q, const void* packed,
+                                    const float* gamma, const void* qjl_bits,
+                                    const uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* workspace, size_t workspace_bytes, void* stream,
+                                    int stages, const AppendKey* app) {
   octo_status st = check_decode_common(cb, q, qdt, B, Hq, Hkv, packed, gamma, qjl_bits, qjl_norm,
                                        n_keys, cap, workspace);
   if (st != OCTO_OK) return st;
@@ -883,6 +921,12 @@ octo_status octo_decode_attn_stages(const octo_codebook* cb, const void* q, octo
   a.tiles_per_split = sp.tiles_per_split;
   a.n_split = sp.n_split;
   a.part = (float*)((char*)workspace + wl.part);
+  if (app) {
+    a.new_keys = app->keys;
+    a.new_key_stride = app->stride;
+    a.packed_w = (uint32_t*)app->packed;
+    a.gamma_w = app->gamma;
+  }
   if (stages & OCTO_STAGE_MAIN) {
     st = hip_status(launch_attn(cb->d, cb->b, qjl, a, n_seq, s), "attention launch");
     if (st != OCTO_OK) return st;

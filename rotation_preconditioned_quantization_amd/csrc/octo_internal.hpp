@@ -78,6 +78,14 @@ struct DecodeArgs {
   float* logits;         // [B][Hq][n_keys]
   float* part;           // attention partials [B*Hq][n_split][d + 2]
   int n_split;
+  // decode step with append (attention only, bf16 keys, no QJL): the new key
+  // of sequence s at new_keys + s * new_key_stride (elements) is encoded
+  // into position n_keys - 1 of packed_w / gamma_w by the block that owns
+  // that position, which also uses it at once; nullptr otherwise
+  const void* new_keys;
+  int64_t new_key_stride;
+  uint32_t* packed_w;
+  float* gamma_w;
 };
 
 struct CombineArgs {
