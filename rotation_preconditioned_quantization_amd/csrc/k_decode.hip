@@ -777,12 +777,16 @@ static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
 
 #define OCTO_DISPATCH_DBQ(FN, ...)                                                              \
   switch (d * 10 + b) {                                                                         \
+    case 641: return qjl ? FN<64, 1, true>(__VA_ARGS__) : FN<64, 1, false>(__VA_ARGS__);        \
     case 642: return qjl ? FN<64, 2, true>(__VA_ARGS__) : FN<64, 2, false>(__VA_ARGS__);        \
     case 643: return qjl ? FN<64, 3, true>(__VA_ARGS__) : FN<64, 3, false>(__VA_ARGS__);        \
     case 644: return qjl ? FN<64, 4, true>(__VA_ARGS__) : FN<64, 4, false>(__VA_ARGS__);        \
     case 1282: return qjl ? FN<128, 2, true>(__VA_ARGS__) : FN<128, 2, false>(__VA_ARGS__);     \
     case 1283: return qjl ? FN<128, 3, true>(__VA_ARGS__) : FN<128, 3, false>(__VA_ARGS__);     \
     case 1284: return qjl ? FN<128, 4, true>(__VA_ARGS__) : FN<128, 4, false>(__VA_ARGS__);     \
+    case 645: return qjl ? FN<64, 5, true>(__VA_ARGS__) : FN<64, 5, false>(__VA_ARGS__);        \
+    case 1281: return qjl ? FN<128, 1, true>(__VA_ARGS__) : FN<128, 1, false>(__VA_ARGS__);     \
+    case 1285: return qjl ? FN<128, 5, true>(__VA_ARGS__) : FN<128, 5, false>(__VA_ARGS__);     \
   }                                                                                             \
   return hipErrorInvalidValue;
 
@@ -822,12 +826,16 @@ static hipError_t recon_t(const ReconArgs& a, int64_t n_seq, hipStream_t s) {
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.n_keys <= 0 || n_seq <= 0) return hipSuccess;
   switch (d * 10 + b) {
+    case 641: return recon_t<64, 1>(a, n_seq, s);
     case 642: return recon_t<64, 2>(a, n_seq, s);
     case 643: return recon_t<64, 3>(a, n_seq, s);
     case 644: return recon_t<64, 4>(a, n_seq, s);
     case 1282: return recon_t<128, 2>(a, n_seq, s);
     case 1283: return recon_t<128, 3>(a, n_seq, s);
     case 1284: return recon_t<128, 4>(a, n_seq, s);
+    case 645: return recon_t<64, 5>(a, n_seq, s);
+    case 1281: return recon_t<128, 1>(a, n_seq, s);
+    case 1285: return recon_t<128, 5>(a, n_seq, s);
   }
   return hipErrorInvalidValue;
 }

@@ -1,0 +1,535 @@
+// OCTOPUS online key encoder for gfx950.
+//
+// One wavefront encodes a tile of 64 keys, one key per lane, entirely in
+// registers ([YL] 三元组分解, steps 1-4):
+//   gamma = |k| (fp32, stored), y = H (s .* k) by in-register butterflies
+//   ([YL] 旋转魔法 / 工程实现), triplets t_i of the zero-padded y, rho_i^2 =
+//   |t_i|^2/|y|^2, octahedral (xi, eta) of t_i ([YL] 八面体折叠), Lloyd-Max
+//   nearest-centroid indices from bucketed LDS tables, bit-pack, store.
+// The key tile is read with coalesced 16-byte loads and handed to the lanes
+// through a 16-row LDS buffer per wave in four phases (small LDS footprint,
+// several waves per SIMD); packed words are stored in the tile's word-group
+// layout (16-byte stores, 1 KiB contiguous per store instruction).  With QJL
+// the same lane also forms the rotated residual r' = u' - u'^ and its fp16
+// norm, and the wave the signs of S r' on the matrix cores
+// ([YL] 可选的残差修正).  Joint rounding ([YL] 联合取整) is a template
+// variant.  Included by k_encode_b<N>.hip, one translation unit per bit budget.
+#pragma once
+
+#include <algorithm>
+
+#include "octo_device.hpp"
+#include "octo_encode_dev.hpp"
+
+// Floating-point expressions here are evaluated exactly as written (fma only
+// where a builtin says so): the bulk and the one-key encoders then round the
+// same operations the same way and write identical words and gamma.
+#pragma clang fp contract(off)
+
+namespace octo {
+
+// Stage the key rows [r0, r0 + NR) of the wave's 64-key tile into LDS with
+// coalesced 16-byte loads (consecutive lanes read consecutive chunks).  The
+// WHT sign flips are applied here, on the raw chunk bits: every lane always
+// handles the same chunk column, so one 16-byte mask per lane does it.
+template <int D, int KT>
+struct Stage {
+  static constexpr int ES = DtSize<KT>::v;
+  static constexpr int ROWB = D * ES;       // bytes per key row
+  static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
+  static constexpr int PITCH = ROWB + 16;   // padded pitch: conflict-free row reads
+  static constexpr int VPC = 16 / ES;       // values per chunk
+  static constexpr int NR = 16;             // rows staged per phase
+  static constexpr int NP = kTile / NR;     // phases
+  static constexpr int PER_LANE = NR * CPR / 64;
+};
+
+// Sign mask of the chunk a lane stages: sign bit of every element whose WHT
+// sign is -1 (bit 15 of a 16-bit element, bit 31 of an fp32 one).
+template <int D, int KT>
+__device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[4], int col) {
+  using S = Stage<D, KT>;
+  uint32_t m[4] = {0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int e = 0; e < S::VPC; ++e) {
+    const int j = col * S::VPC + e;
+    const uint32_t bit = (sign_bits[j >> 5] >> (j & 31)) & 1u;
+    if constexpr (S::ES == 2) m[e >> 1] |= bit << (16 * (e & 1) + 15);
+    else m[e] |= bit << 31;
+  }
+  return make_uint4(m[0], m[1], m[2], m[3]);
+}
+
+// The raw 16-byte chunks of the 64-key tile at j0: coalesced loads, NP
+// phases of NR rows (rows past n_new re-read the last key, so the loads
+// carry no conditions).
+template <int D, int KT>
+__device__ __forceinline__ void load_rows(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                          uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE]) {
+  using S = Stage<D, KT>;
+  const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
+  const int col = lane % S::CPR;
+#pragma unroll
+  for (int h = 0; h < S::NP; ++h) {
+#pragma unroll
+    for (int k = 0; k < S::PER_LANE; ++k) {
+      const int f = lane + 64 * k;
+      int64_t j = j0 + h * S::NR + f / S::CPR;
+      j = j < a.n_new ? j : a.n_new - 1;
+      raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + col * 16);
+    }
+  }
+}
+
+// Hand every lane its own key row (sign-flipped, raw bits) through the
+// wave's LDS buffer of NR rows, one phase at a time.
+template <int D, int KT>
+__device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE],
+                                           int lane, unsigned char* s_keys, const uint4& smask,
+                                           uint4 (&rowbits)[Stage<D, KT>::CPR]) {
+  using S = Stage<D, KT>;
+  const int col = lane % S::CPR;
+  const int my_phase = lane / S::NR;
+  const unsigned char* row = s_keys + (lane % S::NR) * S::PITCH;
+#pragma unroll
+  for (int h = 0; h < S::NP; ++h) {
+#pragma unroll
+    for (int k = 0; k < S::PER_LANE; ++k) {
+      const int f = lane + 64 * k;
+      uint4 u = raw[h][k];
+      u.x ^= smask.x; u.y ^= smask.y; u.z ^= smask.z; u.w ^= smask.w;
+      *(uint4*)(s_keys + (f / S::CPR) * S::PITCH + col * 16) = u;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (my_phase == h) {
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) rowbits[c] = *(const uint4*)(row + c * 16);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
+// Waves (64-key tiles in flight) per encoder block.
+template <bool QJL>
+constexpr int enc_waves() { return 4; }
+
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+// v_writelane_b32: a wave-uniform value into one lane of a VGPR.
+extern "C" __device__ int octo_writelane(int val, int lane, int old) __asm("llvm.amdgcn.writelane.i32");
+
+// QJL matrix in LDS: planes [S_hi | S_lo] of f16 rows, padded so that the 32
+// rows one B-operand load touches fall on distinct banks.
+template <int D>
+struct SLds {
+  static constexpr int PITCH = 2 * D + 16;      // bytes per row
+  static constexpr int BYTES = 2 * D * PITCH;   // both planes
+};
+
+// QJL signs of the wave's 64 residuals on the matrix cores: P = R' S^T for
+// the 64 keys x d projections, P[key][j] = <S_j, r'_key>, bit j of the key's
+// sign words = (P >= 0) ([YL] 可选的残差修正; sgn(0) = +1).
+//   r' (one key per lane, fp32, scaled by 2^12: signs unchanged, f16 range
+//   kept) and S are split into f16 high and low parts, x = x_hi + x_lo with
+//   both parts rounded to nearest; the product is summed from the three
+//   terms hi*hi + hi*lo + lo*hi on v_mfma_f32_32x32x16_f16 (products exact,
+//   fp32 accumulate).  The dropped lo*lo term and the rounding of the low
+//   parts leave a relative error near 2^-23 |S_jk| |r'_k| per term.
+//   A operands: rows = keys.  Lane (l % 32, g = l / 32) of the 32-key block
+//   supplies dims 16 kb + 8 g .. + 7 of its row; a lane holds its own key's
+//   dims, so v_permlane32_swap exchanges the upper half of the dims 0..7
+//   words with the lower half of the dims 8..15 words, which yields the
+//   operands of key block 0 (keys 0..31) and key block 1 (keys 32..63).
+//   B operands: S rows j = 32 nb + l % 32, dims 16 kb + 8 g .. + 7, from LDS.
+//   Output register r of lane (l % 32, g) is key 8 (r / 4) + 4 g + r % 4 of the
+//   block and projection l % 32 of the block: a ballot over the wave gives the
+//   32 sign bits of two keys at once, written into those keys' lanes.
+template <int D>
+__device__ __forceinline__ void qjl_signs(const float (&v)[D], const unsigned char* s_S, int lane,
+                                          uint32_t (&sw)[D / 32]) {
+  constexpr int NK = D / 16;  // 16-dim contraction blocks
+  constexpr int NN = D / 32;  // 32-projection output blocks
+  constexpr int PITCH = SLds<D>::PITCH;
+  half8 ah[2][NK], al[2][NK];
+#pragma unroll
+  for (int kb = 0; kb < NK; ++kb) {
+    uint32_t ph[8], pl[8];
+#pragma unroll
+    for (int p = 0; p < 8; ++p) {
+      const float x0 = v[16 * kb + 2 * p] * 4096.f, x1 = v[16 * kb + 2 * p + 1] * 4096.f;
+      const __half2 h = __float22half2_rn(make_float2(x0, x1));
+      const float2 hf = __half22float2(h);
+      const __half2 l = __float22half2_rn(make_float2(x0 - hf.x, x1 - hf.y));
+      ph[p] = __builtin_bit_cast(uint32_t, h);
+      pl[p] = __builtin_bit_cast(uint32_t, l);
+    }
+    uint32_t h0[4], h1[4], l0[4], l1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const auto sh = __builtin_amdgcn_permlane32_swap(ph[i], ph[4 + i], false, false);
+      h0[i] = sh[0];
+      h1[i] = sh[1];
+      const auto sl = __builtin_amdgcn_permlane32_swap(pl[i], pl[4 + i], false, false);
+      l0[i] = sl[0];
+      l1[i] = sl[1];
+    }
+    ah[0][kb] = __builtin_bit_cast(half8, make_uint4(h0[0], h0[1], h0[2], h0[3]));
+    ah[1][kb] = __builtin_bit_cast(half8, make_uint4(h1[0], h1[1], h1[2], h1[3]));
+    al[0][kb] = __builtin_bit_cast(half8, make_uint4(l0[0], l0[1], l0[2], l0[3]));
+    al[1][kb] = __builtin_bit_cast(half8, make_uint4(l1[0], l1[1], l1[2], l1[3]));
+  }
+  // The B operands are the same for every tile: an offset the compiler
+  // cannot see through (always 0) keeps their LDS reads inside the tile loop
+  // instead of hoisting all of them into registers ahead of it.
+  int opaque0;
+  asm volatile("v_mov_b32 %0, 0" : "=v"(opaque0));
+  const int ln = lane & 31, g = lane >> 5;
+  s_S += opaque0;
+#pragma unroll
+  for (int nb = 0; nb < NN; ++nb) {
+    floatx16 c[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) { c[0][r] = 0.f; c[1][r] = 0.f; }
+    const unsigned char* row = s_S + (32 * nb + ln) * PITCH + 16 * g;
+#pragma unroll
+    for (int kb = 0; kb < NK; ++kb) {
+      const half8 bh = *(const half8*)(row + 32 * kb);
+      const half8 bl = *(const half8*)(row + D * PITCH + 32 * kb);
+#pragma unroll
+      for (int mb = 0; mb < 2; ++mb) {
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mb][kb], bh, c[mb], 0, 0, 0);
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[mb][kb], bl, c[mb], 0, 0, 0);
+        c[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[mb][kb], bh, c[mb], 0, 0, 0);
+      }
+    }
+    int w = 0;
+#pragma unroll
+    for (int mb = 0; mb < 2; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const uint64_t m = __ballot(c[mb][r] >= 0.f);
+        const int key = 32 * mb + 8 * (r >> 2) + (r & 3);
+        w = octo_writelane((int)(uint32_t)m, key, w);
+        w = octo_writelane((int)(uint32_t)(m >> 32), key + 4, w);
+      }
+    sw[nb] = (uint32_t)w;
+  }
+}
+
+// Encode the 64-key tile at j0: one key per lane, entirely in registers.
+template <int D, int B, int KT, bool QJL, bool JR>
+__device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                            unsigned char* s_keys, const uint4& smask,
+                                            const uint2* s_qx, const uint2* s_qe, const uint2* s_qr,
+                                            const unsigned char* s_S, const float4* s_dir,
+                                            const float* s_rho) {
+  using C = Codec<D, B>;
+  using S = Stage<D, KT>;
+  constexpr int T = C::T, W = C::W;
+  float v[D];
+  {
+    uint4 rowbits[S::CPR];
+    {
+      uint4 raw[S::NP][S::PER_LANE];
+      load_rows<D, KT>(a, seq, j0, lane, raw);
+      stage_rows<D, KT>(raw, lane, s_keys, smask, rowbits);
+    }
+    if constexpr (KT == DT_F32) {
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
+    } else {
+      // stride-1 butterflies straight from the packed 16-bit pairs
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) {
+        const uint32_t wd[4] = {rowbits[c].x, rowbits[c].y, rowbits[c].z, rowbits[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) stage1_pair<KT>(wd[k], v[8 * c + 2 * k], v[8 * c + 2 * k + 1]);
+      }
+    }
+  }
+  // Keys with entries far from 1 in magnitude are scaled by an exact power of
+  // two (changes no ratio) so that no triplet energy under- or overflows.
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < D; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+  int ex = 0;
+  __builtin_frexpf(amax, &ex);
+  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+  if (__any(sexp != 0)) {
+    const float scale = __builtin_ldexpf(1.0f, -sexp);
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] *= scale;
+  }
+  if constexpr (KT == DT_F32) wht_regs<D>(v);
+  else wht_regs_from<D, 2>(v);
+
+  const float sx = a.t.qx.scale, bx = a.t.qx.bias;
+  const float se = a.t.qe.scale, be = a.t.qe.bias;
+  // (the rho^2 table starts at 0: bias 0)
+  const float sr = a.t.qr2.scale, mr = (float)(a.t.qr2.nb - 1);
+  uint32_t words[W];
+#pragma unroll
+  for (int w = 0; w < W; ++w) words[w] = 0u;
+  const int64_t j = j0 + lane;
+  const bool valid = j < a.n_new;
+  const int64_t pos = a.pos0 + j;
+  const int64_t tiles = a.cap / kTile;
+  float tot = 0.f;
+  if constexpr (!JR) {
+    // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
+    float e[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      e[i] = triplet_energy(x, y, z);
+      tot += e[i];
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+    }
+    const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+    // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
+#pragma unroll
+    for (int i = 0; i < T; ++i)
+      pack_code<C::BT>(words, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+  } else {
+    // Joint rounding ([YL] 联合取整).  Pass 1: the energy and the scalar
+    // (xi, eta) indices, the centre of the search.  Pass 2, per triplet t of
+    // the unit key: for each of the 3x3 neighbouring direction codes (clamped
+    // to the index range) with unit direction n^, the best rho^ is the
+    // centroid nearest s = <n^, t> (the squared-midpoint table on max(s, 0)^2;
+    // s <= 0 takes index 0), with error |t - rho^ n^|^2 - |t|^2 = rho^ (rho^ - 2s);
+    // the first strict minimum in (xi, eta) offset order wins.
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      tot += triplet_energy(x, y, z);
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+    }
+    const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+    uint32_t wj[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) wj[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      x *= inv_norm;
+      y *= inv_norm;
+      z *= inv_norm;
+      const uint32_t c0 = field_at<W>(words, i * C::BT, C::BX + C::BE);
+      const int ix = (int)(c0 & (C::LX - 1)), ie = (int)(c0 >> C::BX);
+      float best_e = INFINITY;
+      uint32_t best = 0u;
+#pragma unroll
+      for (int da = -1; da <= 1; ++da) {
+        const int ja = min(max(ix + da, 0), C::LX - 1);
+#pragma unroll
+        for (int dc = -1; dc <= 1; ++dc) {
+          const int jc = min(max(ie + dc, 0), C::LE - 1);
+          const uint32_t xe = (uint32_t)ja | ((uint32_t)jc << C::BX);
+          const float4 n = s_dir[xe];
+          const float sdot = __builtin_fmaf(n.x, x, __builtin_fmaf(n.y, y, n.z * z));
+          const float sp = __builtin_fmaxf(sdot, 0.f);
+          const uint32_t jr = quant1_clamp(sp * sp, s_qr, sr, mr);
+          const float r = s_rho[jr];
+          const float err = r * (r - 2.f * sdot);
+          if (err < best_e) {
+            best_e = err;
+            best = xe | (jr << (C::BX + C::BE));
+          }
+        }
+      }
+      pack_code<C::BT>(wj, i, best);
+    }
+#pragma unroll
+    for (int w = 0; w < W; ++w) words[w] = wj[w];
+  }
+  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
+  if (valid) {
+    TileWords<W>::store(a.packed + (seq * tiles + (pos >> 6)) * W * kTile, (int)(pos & 63), words);
+    a.gamma[seq * a.cap + pos] = gamma;
+  }
+
+  if constexpr (QJL) {
+    if (a.qjl_bits != nullptr) {
+      // Rotated unit-direction residual r' = u' - u'^ over the D real coordinates.
+      const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+      float nu2 = 0.f;
+#pragma unroll
+      for (int i = 0; i < T; ++i) {
+        const uint32_t code = field_at<W>(words, i * C::BT, C::BT);
+        const float4 n = s_dir[code & C::DIR_MASK];
+        const float rh = s_rho[code >> (C::BX + C::BE)];
+        const float nc[3] = {n.x, n.y, n.z};
+#pragma unroll
+        for (int c = 0; c < 3; ++c) {
+          if (3 * i + c < D) {
+            const float r = __builtin_fmaf(v[3 * i + c], inv_norm, -rh * nc[c]);
+            v[3 * i + c] = r;
+            nu2 = __builtin_fmaf(r, r, nu2);
+          }
+        }
+      }
+      const float nu = __builtin_sqrtf(nu2);
+      uint32_t sbits[D / 32];
+      qjl_signs<D>(v, s_S, lane, sbits);
+      if (valid) {
+        TileWords<D / 32>::store(a.qjl_bits + (seq * tiles + (pos >> 6)) * (D / 32) * kTile,
+                                 (int)(pos & 63), sbits);
+        a.qjl_norm[seq * a.cap + pos] = __half_as_ushort(__float2half_rn(nu));
+      }
+    }
+  }
+}
+
+template <int D, int B, int KT, bool QJL, bool JR>
+__global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) {
+  using C = Codec<D, B>;
+  using S = Stage<D, KT>;
+  constexpr int EW = enc_waves<QJL>();
+  __shared__ __align__(16) unsigned char s_keys[EW][S::NR * S::PITCH];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
+  __shared__ __align__(16) unsigned char s_S[QJL ? SLds<D>::BYTES : 16];
+  // unit directions and rho centroids (QJL residual, joint rounding)
+  constexpr bool TABS = QJL || JR;
+  __shared__ float4 s_dir[TABS ? C::NDIR : 1];
+  __shared__ float s_rho[TABS ? C::LR : 1];
+
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seq = blockIdx.y;
+
+  // the block's waves share the quantiser tables (and the QJL matrix)
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 64 * EW) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * EW) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * EW) s_qr[i] = a.t.qr2.t[i];
+  if constexpr (QJL) {
+    constexpr int CPRS = 2 * D / 16;  // 16-byte chunks per S row
+    for (int c = threadIdx.x; c < 2 * D * CPRS; c += 64 * EW)
+      *(uint4*)(s_S + (c / CPRS) * SLds<D>::PITCH + (c % CPRS) * 16) = a.t.S16[c];
+  }
+  if constexpr (TABS) {
+    for (int i = threadIdx.x; i < C::NDIR; i += 64 * EW) s_dir[i] = a.t.dirtab[i];
+    if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
+  }
+  __syncthreads();
+  const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
+  // A wave encodes one 64-key tile; with QJL the grid is smaller than the
+  // key count and the block's waves take tiles round-robin.
+  for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
+       j0 += (int64_t)gridDim.x * EW * kTile) {
+    encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S, s_dir,
+                               s_rho);
+    if constexpr (!QJL) break;
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Latency-optimised encoder for a few keys per sequence (the autoregressive
+// step appends one key per sequence, [YL] 工程实现 / [AB] online): one
+// wavefront per key (encode_one_key), words assembled in LDS, then stored.
+// ---------------------------------------------------------------------------
+template <int D, int B, int KT>
+__global__ __launch_bounds__(256) void k_encode_one(EncodeArgs a) {
+  using C = Codec<D, B>;
+  constexpr int T = C::T, W = C::W;
+  __shared__ float s_v[4][3 * T];
+  __shared__ float s_e[4][T];
+  __shared__ uint32_t s_w[4][W];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  __syncthreads();
+  const int64_t k = (int64_t)blockIdx.x * 4 + wave;  // keys flattened over (seq, new key)
+  if (k >= a.n_new * a.seq_count) return;
+  const int64_t seq = k / a.n_new, j = k % a.n_new;
+  const int64_t pos = a.pos0 + j;
+  const void* row = (const unsigned char*)a.keys +
+                    (seq * a.seq_stride + j * a.key_stride) * DtSize<KT>::v;
+  const float gamma = encode_one_key<D, B, KT>(row, a.t, s_qx, s_qe, s_qr, lane, s_v[wave],
+                                               s_e[wave], s_w[wave]);
+  if (lane < W) store_key_word<W>(a.packed, a.cap, seq, pos, lane, s_w[wave][lane]);
+  if (lane == 0) a.gamma[seq * a.cap + pos] = gamma;
+}
+
+template <int D, int B, int KT>
+inline hipError_t launch_encode_one_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  const int64_t keys = a.n_new * n_seq;
+  hipLaunchKernelGGL((k_encode_one<D, B, KT>), dim3((unsigned)((keys + 3) / 4)), dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int B, int KT, bool QJL, bool JR>
+inline hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  constexpr int EW = enc_waves<QJL>();
+  const int64_t per = (int64_t)EW * kTile;
+  int64_t gx = (a.n_new + per - 1) / per;
+  // With QJL each block first stages the matrix in LDS: a grid of about two
+  // blocks per compute unit then loops over the tiles.
+  if (QJL) gx = std::min<int64_t>(gx, std::max<int64_t>(1, (512 + n_seq - 1) / n_seq));
+  const dim3 grid((unsigned)gx, (unsigned)n_seq);
+  hipLaunchKernelGGL((k_encode<D, B, KT, QJL, JR>), grid, dim3(64 * EW), 0, s, a);
+  return hipGetLastError();
+}
+
+template <int D, int B, int KT>
+inline hipError_t enc_q(bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  // fp32 keys with QJL at d = 128, b = 5: the staging buffer, the matrix and
+  // the 4096-entry direction table exceed the LDS (the host refuses it)
+  if constexpr (D == 128 && B == 5 && KT == DT_F32) {
+    if (qjl) return hipErrorInvalidValue;
+    return joint ? launch_encode_t<D, B, KT, false, true>(a, n_seq, s)
+                 : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
+  } else {
+    if (joint)
+      return qjl ? launch_encode_t<D, B, KT, true, true>(a, n_seq, s)
+                 : launch_encode_t<D, B, KT, false, true>(a, n_seq, s);
+    return qjl ? launch_encode_t<D, B, KT, true, false>(a, n_seq, s)
+               : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
+  }
+}
+
+template <int D, int B>
+inline hipError_t enc_kt(int kdt, bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  switch (kdt) {
+    case DT_F32: return enc_q<D, B, DT_F32>(qjl, joint, a, n_seq, s);
+    case DT_BF16: return enc_q<D, B, DT_BF16>(qjl, joint, a, n_seq, s);
+    case DT_F16: return enc_q<D, B, DT_F16>(qjl, joint, a, n_seq, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+// All encoder launches for bit budget B: d in {64, 128}, the key dtypes,
+// plain / QJL / joint rounding, and the one-key path for short appends.
+// Each bit budget is instantiated in a translation unit of its own.
+template <int B>
+hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArgs& a,
+                           int64_t n_seq, hipStream_t s) {
+  if (!qjl && !joint && a.n_new <= kEncodeOneMax) {
+#define OCTO_ENC_ONE(DD)                                                          \
+  switch (kdt) {                                                                \
+    case DT_F32: return launch_encode_one_t<DD, B, DT_F32>(a, n_seq, s);        \
+    case DT_BF16: return launch_encode_one_t<DD, B, DT_BF16>(a, n_seq, s);      \
+    case DT_F16: return launch_encode_one_t<DD, B, DT_F16>(a, n_seq, s);        \
+  }                                                                             \
+  return hipErrorInvalidValue;
+    if (d == 64) { OCTO_ENC_ONE(64) }
+    if (d == 128) { OCTO_ENC_ONE(128) }
+#undef OCTO_ENC_ONE
+    return hipErrorInvalidValue;
+  }
+  if (d == 64) return enc_kt<64, B>(kdt, qjl, joint, a, n_seq, s);
+  if (d == 128) return enc_kt<128, B>(kdt, qjl, joint, a, n_seq, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace octo

@@ -363,12 +363,17 @@ int mq_block_queries() { return kMQQueries; }
 
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
   switch (d * 10 + b) {
+    case 641: return mq_t<64, 1>(a, s);
     case 642: return mq_t<64, 2>(a, s);
     case 643: return mq_t<64, 3>(a, s);
     case 644: return mq_t<64, 4>(a, s);
     case 1282: return mq_t<128, 2>(a, s);
     case 1283: return mq_t<128, 3>(a, s);
     case 1284: return mq_t<128, 4>(a, s);
+    case 645: return mq_t<64, 5>(a, s);
+    case 1281: return mq_t<128, 1>(a, s);
+    // d = 128 at b = 5: the 4096-entry direction table and the two tile
+    // buffer sets do not fit the 160 KiB of LDS together (not supported)
   }
   return hipErrorInvalidValue;
 }

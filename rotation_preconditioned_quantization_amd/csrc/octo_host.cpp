@@ -434,11 +434,11 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
   if (b < 1 || b > 8 || bx < 1 || bx > 8 || be < 1 || be > 8 || br < 0 || br > 8)
     return fail(OCTO_ERR_INVALID_ARG, "bit allocation out of range");
   if (p->mc_vectors < 0) return fail(OCTO_ERR_INVALID_ARG, "mc_vectors < 0");
-  const bool kernels = (d == 64 || d == 128) && (b >= 2 && b <= 4) && bx == b + 1 && be == b + 1 &&
+  const bool kernels = (d == 64 || d == 128) && (b >= 1 && b <= 5) && bx == b + 1 && be == b + 1 &&
                        br == b - 1;
   if (p->device >= 0 && !kernels)
     return fail(OCTO_ERR_UNSUPPORTED,
-                "kernels exist for d in {64,128}, b in {2,3,4} and the (b+1,b+1,b-1) allocation; "
+                "kernels exist for d in {64,128}, b in 1..5 and the (b+1,b+1,b-1) allocation; "
                 "build with device = -1 for host-only tables");
   octo_codebook* cb = new (std::nothrow) octo_codebook();
   if (!cb) return fail(OCTO_ERR_NOMEM, "host allocation failed");
@@ -633,6 +633,8 @@ static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_d
   if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
   if (qjl_bits && (!aligned(qjl_bits, 16) || !aligned(qjl_norm, 2)))
     return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
+  if (qjl_bits && cb->d == 128 && cb->b == 5 && kdt == OCTO_F32)
+    return fail(OCTO_ERR_UNSUPPORTED, "QJL encoder: no kernel for fp32 keys at d = 128, b = 5");
   EncodeArgs a{};
   a.t = cb->tables;
   a.keys = keys;
@@ -865,6 +867,8 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
+    if (cb->d == 128 && cb->b == 5)
+      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 128, b = 5");
     if (stages & OCTO_STAGE_ROTATE) {
       st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
       if (st != OCTO_OK) return st;

@@ -87,7 +87,8 @@ def test_encode_toy_full_config1():
     assert np.max(rel_err_rows(rec, ref)) <= 1e-3
 
 
-@pytest.mark.parametrize("d,b", [(128, 2), (128, 3), (128, 4), (64, 2), (64, 3), (64, 4)])
+@pytest.mark.parametrize("d,b", [(128, 2), (128, 3), (128, 4), (64, 2), (64, 3), (64, 4),
+                                 (128, 1), (128, 5), (64, 1), (64, 5)])
 @pytest.mark.parametrize("kdt", ["f32", "bf16"])
 def test_encode_all_shapes_ragged(d, b, kdt):
     cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
@@ -95,7 +96,8 @@ def test_encode_all_shapes_ragged(d, b, kdt):
     encode_and_check(d, b, keys, cap=256, label=f"d{d}b{b}{kdt}")
 
 
-@pytest.mark.parametrize("d,b,kdt", [(128, 2, "bf16"), (128, 3, "bf16"), (128, 4, "bf16"),
+@pytest.mark.parametrize("d,b,kdt", [(128, 2, "bf16"), (128, 3, "bf16"), (128, 4, "bf16"), (128, 5, "bf16"),
+                                     (64, 1, "bf16"),
                                      (64, 3, "bf16"), (128, 4, "f32")])
 def test_encode_joint_rounding(d, b, kdt):
     """octo_encode_joint against the oracle's joint rounding ([YL] 联合取整),
@@ -154,7 +156,8 @@ def test_encode_joint_rounding_with_qjl():
     assert np.allclose(gnu.astype(np.float64), qe.nu.astype(np.float64), rtol=1e-3, atol=1e-6)
 
 
-@pytest.mark.parametrize("d,b,kdt", [(128, 4, "bf16"), (128, 2, "f32"), (64, 3, "f16")])
+@pytest.mark.parametrize("d,b,kdt", [(128, 4, "bf16"), (128, 2, "f32"), (64, 3, "f16"), (128, 5, "bf16"),
+                                     (64, 1, "f32")])
 def test_encode_few_keys_equals_bulk(d, b, kdt):
     """Appends of up to 16 keys per sequence take the one-key-per-wavefront
     encoder; it writes the same words and gamma as the bulk encoder, bit for
@@ -296,7 +299,7 @@ def test_logits_gqa_ragged(G):
     check_logits(cfg, 2, 2, G, 333, 384, seed=G, label=f"gqa{G}")
 
 
-@pytest.mark.parametrize("d,b", [(64, 3), (128, 2)])
+@pytest.mark.parametrize("d,b", [(64, 3), (128, 2), (128, 1), (128, 5), (64, 5)])
 def test_logits_other_shapes(d, b):
     cfg = WL.CONFIGS[3].scaled(d=d, b=b)
     check_logits(cfg, 1, 2, 4, 700, 768, seed=5, label=f"d{d}b{b}")
@@ -310,6 +313,12 @@ def test_logits_qjl_small_config5_recipe():
 def test_logits_qjl_d64():
     cfg = WL.CONFIGS[5].scaled(d=64)
     check_logits(cfg, 1, 1, 2, 200, 256, seed=2, qjl=True, label="qjl-d64")
+
+
+@pytest.mark.parametrize("d,b", [(128, 1), (128, 5), (64, 5)])
+def test_logits_qjl_wider_bit_budgets(d, b):
+    cfg = WL.CONFIGS[5].scaled(d=d, b=b)
+    check_logits(cfg, 1, 1, 2, 200, 256, seed=3 + b, qjl=True, label=f"qjl-d{d}b{b}")
 
 
 # --------------------------------------------------------------- attention --
@@ -368,6 +377,14 @@ def test_attention_extreme_recipe_small():
 @pytest.mark.parametrize("G", [1, 2, 3, 8])
 def test_attention_gqa(G):
     check_attention(WL.CONFIGS[2].scaled(b=3), 1, 2, G, 300, 320, seed=G, label=f"attn-gqa{G}")
+
+
+@pytest.mark.parametrize("d,b,qjl", [(128, 1, False), (128, 5, False), (64, 5, False), (128, 5, True)])
+def test_attention_wider_bit_budgets(d, b, qjl):
+    """b = 1 (rho takes 0 bits: one level) and b = 5 (4096 directions, not the
+    combined table) through the single-query attention, with and without QJL."""
+    cfg = (WL.CONFIGS[5] if qjl else WL.CONFIGS[2]).scaled(d=d, b=b, keys="gauss")
+    check_attention(cfg, 1, 2, 4, 300, 320, seed=b + d, qjl=qjl, label=f"attn-d{d}b{b}{'q' if qjl else ''}")
 
 
 def test_attention_d64():
@@ -543,7 +560,7 @@ def test_mq_video_recipe_small():
     check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
 
 
-@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3)])
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1)])
 def test_mq_shapes_and_gqa(d, b):
     check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
 

@@ -33,7 +33,8 @@ def test_library_exports_every_header_symbol():
     assert set(names) == set(octo.exported_symbols())
 
 
-@pytest.mark.parametrize("d,b,qjl", [(128, 4, False), (128, 3, True), (128, 2, False), (64, 3, False)])
+@pytest.mark.parametrize("d,b,qjl", [(128, 4, False), (128, 3, True), (128, 2, False), (64, 3, False),
+                                      (128, 1, False), (64, 5, True)])
 def test_host_codebook_matches_oracle(d, b, qjl):
     cb = octo.Codebook(d, b, seed=5, cb_seed=7, qjl=qjl, device=None)
     cx, ce, cr, sg, S = cb.export()
