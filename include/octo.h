@@ -59,9 +59,14 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
 /* Codebook parameters.  The codebook is a pure function of these fields
  * ([AR] 位元分配: it depends only on d and the bit budget; [AB]: deterministic
  * given a seed).
- *   d         head dim: 64 or 128 have kernels (any power of two 4..1024 for a
- *             host-only codebook).
- *   b         bit budget per coordinate; kernels exist for 2, 3, 4.
+ *   d         head dim: 64, 128 and 256 have kernels (any power of two 4..1024
+ *             for a host-only codebook).  At d = 256 there is no QJL variant
+ *             (a QJL codebook is refused with OCTO_ERR_UNSUPPORTED), no joint
+ *             rounding and no multi-query path; the encoder takes a wavefront
+ *             per key there.
+ *   b         bit budget per coordinate; kernels exist for 1 .. 5 (the
+ *             multi-query path and the fp32-key QJL encoder not at d = 128,
+ *             b = 5).
  *   seed      seeds the WHT sign vector and the QJL projection.
  *   cb_seed   seeds the Monte-Carlo samples the Lloyd-Max tables are fit to.
  *   b_xi, b_eta, b_rho  bits per component; any value < 0 selects the pages'

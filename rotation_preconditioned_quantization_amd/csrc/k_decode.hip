@@ -162,7 +162,7 @@ __device__ __forceinline__ float sq_query_elem(const DecodeArgs& a, const SQPre<
 }
 
 // Query rotation (q' = mult * R q, R = d^-1/2 H diag(s)): butterflies of
-// stride < 64 pair lanes (shuffles), stride 64 pairs a lane's two values.
+// stride < 64 pair lanes (shuffles), strides 64, 128 pair a lane's values.
 // With QJL the wave also forms p = sqrt(pi/2)/d * S q'.
 template <int D, int B, bool QJL>
 __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
@@ -188,10 +188,15 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
       x[k] = (lane & hh) ? (o - x[k]) : (x[k] + o);
     }
   }
-  if constexpr (NV == 2) {
-    const float a0 = x[0], a1 = x[1];
-    x[0] = a0 + a1;
-    x[1] = a0 - a1;
+#pragma unroll
+  for (int hr = 1; hr < NV; hr <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (k & hr) continue;
+      const float a0 = x[k], a1 = x[k + hr];
+      x[k] = a0 + a1;
+      x[k + hr] = a0 - a1;
+    }
   }
   const float mult = a.mult * rsqrtf((float)D);
 #pragma unroll
@@ -374,8 +379,8 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4)), 4
-// waves per block; wave w takes tiles t_begin + w, + 4, ... of the block's
+// Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4) x
+// value parts), 4 waves per block; wave w takes tiles t_begin + w, + 4, ... of the block's
 // split, with the next tile (V rows and compressed words) in flight while
 // the current one is computed.  Per tile: logits by tile_logits, a wave-wide
 // online softmax per head (DPP max), then O[head][dim] += p[head][key]
@@ -390,22 +395,28 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
 // block merges its 4 waves into one (m, l, o) partial per head (m in log2
 // units); k_combine merges the splits.
 // ---------------------------------------------------------------------------
+// A block handles DV of the D value dims (DV = D up to 128; at d = 256 two
+// blocks take a half each, so the V tile in flight stays at 64 registers).
 template <int D>
 struct VGeom {
-  static constexpr int CPR = D / 8;        // 16-byte chunks per V row
+  static constexpr int DV = D > 128 ? 128 : D;
+  static constexpr int NVH = D / DV;       // value parts (blocks per head group)
+  static constexpr int CPR = DV / 8;       // 16-byte chunks of a V row per block
+  static constexpr int RP = D / 8;         // V row pitch in chunks
   static constexpr int KPL = 64 / CPR;     // keys per wavefront load
   static constexpr int NVL = kTile / KPL;  // loads per 64-key tile
 };
 
-// The V rows of a 64-key tile.  V holds cap rows per sequence and cap is a
-// multiple of 64, so the whole tile is always in bounds: the loads carry no
-// conditions (rows past n_keys are zeroed where the tile is used).
+// The block's part of the V rows of a 64-key tile.  V holds cap rows per
+// sequence and cap is a multiple of 64, so the whole tile is always in
+// bounds: the loads carry no conditions (rows past n_keys are zeroed where
+// the tile is used).
 template <int D>
 __device__ __forceinline__ void load_vtile(const uint4* vlane, int64_t t, uint4 (&vv)[VGeom<D>::NVL]) {
   using VG = VGeom<D>;
-  const uint4* vt = vlane + (t * kTile) * VG::CPR;
+  const uint4* vt = vlane + (t * kTile) * VG::RP;
 #pragma unroll
-  for (int j = 0; j < VG::NVL; ++j) vv[j] = vt[j * VG::KPL * VG::CPR];
+  for (int j = 0; j < VG::NVL; ++j) vv[j] = vt[j * VG::KPL * VG::RP];
 }
 
 template <int D, int B, bool QJL>
@@ -417,7 +428,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // are 4 consecutive floats; padded rows: the 4 heads hit different banks
   __shared__ __align__(16) float s_p[4][4][kTile + 4];
   __shared__ float s_ml[4][4][2];
-  __shared__ float s_o[4][4][D];
+  __shared__ float s_o[4][4][VG::DV];
   // append step: scratch of the one-wavefront encode and the new key's words
   __shared__ float s_ak[4 * Codec<D, B>::T];
   __shared__ uint32_t s_aw[Codec<D, B>::W];
@@ -425,7 +436,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
-  const int g0 = blockIdx.z * 4;
+  const int ngr = (a.G + 3) / 4;
+  const int vh = (int)blockIdx.z / ngr;              // value part of this block
+  const int g0 = ((int)blockIdx.z % ngr) * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
   const int kq = lane / VG::CPR;                     // key of the wave load this lane serves
   // slot of this lane's key (= lane) in the p rows: key 4 KPL g + KPL j' + q
@@ -436,8 +449,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
-  const uint4* vlane0 = (const uint4*)a.v + kq * VG::CPR + lane % VG::CPR;
-  const uint4* vlane = vlane0 + seq * a.cap * VG::CPR;
+  const uint4* vlane0 = (const uint4*)a.v + kq * VG::RP + vh * VG::CPR + lane % VG::CPR;
+  const uint4* vlane = vlane0 + seq * a.cap * VG::RP;
 
   // The wave's first tile is requested before the prologue (LDS tables by
   // DMA, the query words): the prologue's round trip then overlaps the
@@ -599,8 +612,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __syncthreads();
   // Merge the 4 waves and write this block's partial.
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
-  for (int e = threadIdx.x; e < hcount * (D + 2); e += blockDim.x) {
-    const int h = e / (D + 2), c = e % (D + 2);
+  for (int e = threadIdx.x; e < hcount * (VG::DV + 2); e += blockDim.x) {
+    const int h = e / (VG::DV + 2), c = e % (VG::DV + 2);
+    if (c < 2 && vh > 0) continue;  // (m, l) come from the first value part
     float M = -INFINITY;
 #pragma unroll
     for (int w = 0; w < 4; ++w) M = fmaxf(M, s_ml[w][h][0]);
@@ -616,7 +630,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       }
     }
     const int64_t row = bidx * a.Hq + kvh * a.G + g0 + h;
-    a.part[(row * a.n_split + blockIdx.x) * (D + 2) + c] = val;
+    const int col = c < 2 ? c : c + vh * VG::DV;
+    a.part[(row * a.n_split + blockIdx.x) * (D + 2) + col] = val;
   }
 }
 
@@ -770,13 +785,21 @@ static hipError_t logits_t(const DecodeArgs& a, int64_t n_seq, int nbx, hipStrea
 
 template <int D, int B, bool QJL>
 static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
-  hipLaunchKernelGGL((k_attn<D, B, QJL>), dim3(a.n_split, (unsigned)n_seq, (a.G + 3) / 4),
-                     dim3(256), 0, s, a);
+  hipLaunchKernelGGL((k_attn<D, B, QJL>),
+                     dim3(a.n_split, (unsigned)n_seq, ((a.G + 3) / 4) * VGeom<D>::NVH), dim3(256), 0,
+                     s, a);
   return hipGetLastError();
 }
 
+// d = 256: no QJL kernels
 #define OCTO_DISPATCH_DBQ(FN, ...)                                                              \
+  if (d == 256 && qjl) return hipErrorInvalidValue;                                             \
   switch (d * 10 + b) {                                                                         \
+    case 2561: return FN<256, 1, false>(__VA_ARGS__);                                           \
+    case 2562: return FN<256, 2, false>(__VA_ARGS__);                                           \
+    case 2563: return FN<256, 3, false>(__VA_ARGS__);                                           \
+    case 2564: return FN<256, 4, false>(__VA_ARGS__);                                           \
+    case 2565: return FN<256, 5, false>(__VA_ARGS__);                                           \
     case 641: return qjl ? FN<64, 1, true>(__VA_ARGS__) : FN<64, 1, false>(__VA_ARGS__);        \
     case 642: return qjl ? FN<64, 2, true>(__VA_ARGS__) : FN<64, 2, false>(__VA_ARGS__);        \
     case 643: return qjl ? FN<64, 3, true>(__VA_ARGS__) : FN<64, 3, false>(__VA_ARGS__);        \
@@ -804,6 +827,7 @@ hipError_t launch_combine(const CombineArgs& a, hipStream_t s) {
   if (a.n_split > kMaxSplit) return hipErrorInvalidValue;
   if (a.d == 64) hipLaunchKernelGGL(k_combine<64>, dim3(a.rows), dim3(256), 0, s, a);
   else if (a.d == 128) hipLaunchKernelGGL(k_combine<128>, dim3(a.rows), dim3(256), 0, s, a);
+  else if (a.d == 256) hipLaunchKernelGGL(k_combine<256>, dim3(a.rows), dim3(256), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
@@ -836,6 +860,11 @@ hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, h
     case 645: return recon_t<64, 5>(a, n_seq, s);
     case 1281: return recon_t<128, 1>(a, n_seq, s);
     case 1285: return recon_t<128, 5>(a, n_seq, s);
+    case 2561: return recon_t<256, 1>(a, n_seq, s);
+    case 2562: return recon_t<256, 2>(a, n_seq, s);
+    case 2563: return recon_t<256, 3>(a, n_seq, s);
+    case 2564: return recon_t<256, 4>(a, n_seq, s);
+    case 2565: return recon_t<256, 5>(a, n_seq, s);
   }
   return hipErrorInvalidValue;
 }

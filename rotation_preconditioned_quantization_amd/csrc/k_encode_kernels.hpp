@@ -47,7 +47,7 @@ struct Stage {
 // Sign mask of the chunk a lane stages: sign bit of every element whose WHT
 // sign is -1 (bit 15 of a 16-bit element, bit 31 of an fp32 one).
 template <int D, int KT>
-__device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[4], int col) {
+__device__ __forceinline__ uint4 chunk_sign_mask(const uint32_t (&sign_bits)[8], int col) {
   using S = Stage<D, KT>;
   uint32_t m[4] = {0u, 0u, 0u, 0u};
 #pragma unroll
@@ -508,7 +508,7 @@ inline hipError_t enc_kt(int kdt, bool qjl, bool joint, const EncodeArgs& a, int
   return hipErrorInvalidValue;
 }
 
-// All encoder launches for bit budget B: d in {64, 128}, the key dtypes,
+// All encoder launches for bit budget B: d in {64, 128, 256}, the key dtypes,
 // plain / QJL / joint rounding, and the one-key path for short appends.
 // Each bit budget is instantiated in a translation unit of its own.
 template <int B>
@@ -524,9 +524,16 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
   return hipErrorInvalidValue;
     if (d == 64) { OCTO_ENC_ONE(64) }
     if (d == 128) { OCTO_ENC_ONE(128) }
-#undef OCTO_ENC_ONE
+    if (d == 256) { OCTO_ENC_ONE(256) }
     return hipErrorInvalidValue;
   }
+  // d = 256: a key takes a wavefront (lane l holds elements l + 64 r), at
+  // every batch size; scalar rounding without QJL only
+  if (d == 256) {
+    if (qjl || joint) return hipErrorInvalidValue;
+    OCTO_ENC_ONE(256)
+  }
+#undef OCTO_ENC_ONE
   if (d == 64) return enc_kt<64, B>(kdt, qjl, joint, a, n_seq, s);
   if (d == 128) return enc_kt<128, B>(kdt, qjl, joint, a, n_seq, s);
   return hipErrorInvalidValue;

@@ -112,7 +112,7 @@ __device__ __forceinline__ void stage1_pair(uint32_t w, float& s, float& d) {
 
 // s .* v where bit j of the mask means s_j = -1 (flip the IEEE sign bit).
 template <int D>
-__device__ __forceinline__ void apply_signs(float (&v)[D], const uint32_t (&bits)[4]) {
+__device__ __forceinline__ void apply_signs(float (&v)[D], const uint32_t (&bits)[8]) {
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const uint32_t m = ((bits[j >> 5] >> (j & 31)) & 1u) << 31;

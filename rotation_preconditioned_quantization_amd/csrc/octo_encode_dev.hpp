@@ -130,7 +130,7 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
     for (int r = 0; r < NV; ++r) x[r] *= scale;
   }
   // remaining butterflies: stride 1 (fp32 keys only), then 2 .. 32 across
-  // lanes, then 64 between a lane's two values
+  // lanes, then 64, 128, ... between a lane's values (element l + 64 r)
 #pragma unroll
   for (int h = (KT == DT_F32 ? 1 : 2); h < 64 && h < D; h <<= 1) {
 #pragma unroll
@@ -139,26 +139,37 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
       x[r] = (lane & h) ? (o - x[r]) : (x[r] + o);
     }
   }
-  if constexpr (NV == 2) {
-    const float a0 = x[0], a1 = x[1];
-    x[0] = a0 + a1;
-    x[1] = a0 - a1;
+#pragma unroll
+  for (int hr = 1; hr < NV; hr <<= 1) {
+#pragma unroll
+    for (int r = 0; r < NV; ++r) {
+      if (r & hr) continue;
+      const float a0 = x[r], a1 = x[r + hr];
+      x[r] = a0 + a1;
+      x[r + hr] = a0 - a1;
+    }
   }
 #pragma unroll
   for (int r = 0; r < NV; ++r) sv[lane + 64 * r] = x[r];
   if (lane < 3 * T - D) sv[D + lane] = 0.f;
-  if (lane < W) sw[lane] = 0u;
+  for (int w = lane; w < W; w += 64) sw[w] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 
-  // one triplet per lane
-  const int i = lane < T ? lane : T - 1;
-  const float tx = sv[3 * i], ty = sv[3 * i + 1], tz = sv[3 * i + 2];
-  const float e = triplet_energy(tx, ty, tz);
-  const uint32_t xe = xi_eta_code<C::BX>(tx, ty, tz, tqx, t.qx.scale, t.qx.bias, tqe,
-                                         t.qe.scale, t.qe.bias);
-  if (lane < T) se[lane] = e;
+  // one triplet per lane (triplets lane + 64 m: two per lane up to d = 384)
+  constexpr int NT = (T + 63) / 64;
+  float e[NT];
+  uint32_t xe[NT];
+#pragma unroll
+  for (int m = 0; m < NT; ++m) {
+    const int i0 = lane + 64 * m;
+    const int i = i0 < T ? i0 : T - 1;
+    const float tx = sv[3 * i], ty = sv[3 * i + 1], tz = sv[3 * i + 2];
+    e[m] = triplet_energy(tx, ty, tz);
+    xe[m] = xi_eta_code<C::BX>(tx, ty, tz, tqx, t.qx.scale, t.qx.bias, tqe, t.qe.scale, t.qe.bias);
+    if (i0 < T) se[i0] = e[m];
+  }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
@@ -167,12 +178,16 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
   for (int i2 = 0; i2 < T; ++i2) tot += se[i2];
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
   const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
-  const uint32_t rc = quant1_clamp(e * inv_tot, tqr, t.qr2.scale, (float)(t.qr2.nb - 1));
-  const uint32_t code = xe | (rc << (C::BX + C::BE));
-  if (lane < T) {
-    const int p = lane * C::BT, wi = p >> 5, off = p & 31;
-    atomicOr(&sw[wi], code << off);
-    if (off + C::BT > 32) atomicOr(&sw[wi + 1], code >> (32 - off));
+#pragma unroll
+  for (int m = 0; m < NT; ++m) {
+    const int i0 = lane + 64 * m;
+    const uint32_t rc = quant1_clamp(e[m] * inv_tot, tqr, t.qr2.scale, (float)(t.qr2.nb - 1));
+    const uint32_t code = xe[m] | (rc << (C::BX + C::BE));
+    if (i0 < T) {
+      const int p = i0 * C::BT, wi = p >> 5, off = p & 31;
+      atomicOr(&sw[wi], code << off);
+      if (off + C::BT > 32) atomicOr(&sw[wi + 1], code >> (32 - off));
+    }
   }
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();

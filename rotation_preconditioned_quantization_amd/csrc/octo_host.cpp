@@ -198,7 +198,7 @@ struct octo_codebook {
   std::vector<double> c_xi, c_eta, c_rho;
   std::vector<int8_t> signs;
   std::vector<float> S;
-  uint32_t sign_bits[4] = {0, 0, 0, 0};
+  uint32_t sign_bits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   void* dev = nullptr;
   DevTables tables{};
 };
@@ -307,7 +307,7 @@ octo_status build_device_tables(octo_codebook* cb) {
   t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[5].off);
   t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[6].off);
   t.S16 = s16.empty() ? nullptr : (const uint4*)(base + reg[7].off);
-  for (int k = 0; k < 4; ++k) t.sign_bits[k] = cb->sign_bits[k];
+  for (int k = 0; k < 8; ++k) t.sign_bits[k] = cb->sign_bits[k];
   return OCTO_OK;
 }
 
@@ -434,12 +434,14 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
   if (b < 1 || b > 8 || bx < 1 || bx > 8 || be < 1 || be > 8 || br < 0 || br > 8)
     return fail(OCTO_ERR_INVALID_ARG, "bit allocation out of range");
   if (p->mc_vectors < 0) return fail(OCTO_ERR_INVALID_ARG, "mc_vectors < 0");
-  const bool kernels = (d == 64 || d == 128) && (b >= 1 && b <= 5) && bx == b + 1 && be == b + 1 &&
-                       br == b - 1;
+  const bool kernels = (d == 64 || d == 128 || d == 256) && (b >= 1 && b <= 5) && bx == b + 1 &&
+                       be == b + 1 && br == b - 1;
   if (p->device >= 0 && !kernels)
     return fail(OCTO_ERR_UNSUPPORTED,
-                "kernels exist for d in {64,128}, b in 1..5 and the (b+1,b+1,b-1) allocation; "
+                "kernels exist for d in {64,128,256}, b in 1..5 and the (b+1,b+1,b-1) allocation; "
                 "build with device = -1 for host-only tables");
+  if (p->device >= 0 && p->qjl && d > 128)
+    return fail(OCTO_ERR_UNSUPPORTED, "QJL kernels exist for d in {64,128}");
   octo_codebook* cb = new (std::nothrow) octo_codebook();
   if (!cb) return fail(OCTO_ERR_NOMEM, "host allocation failed");
   cb->d = d;
@@ -463,7 +465,7 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     for (int j = 0; j < d; ++j) {
       const bool neg = splitmix_out(p->seed ^ kTagSigns, (uint64_t)j) & 1ull;
       cb->signs[j] = neg ? -1 : 1;
-      if (neg && j < 128) cb->sign_bits[j >> 5] |= 1u << (j & 31);
+      if (neg && j < 256) cb->sign_bits[j >> 5] |= 1u << (j & 31);
     }
     // The centroid tables depend only on (d, allocation, cb_seed, samples):
     // the last fit is kept, so codebooks that differ only in `seed` (signs,
@@ -635,6 +637,8 @@ static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_d
     return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
   if (qjl_bits && cb->d == 128 && cb->b == 5 && kdt == OCTO_F32)
     return fail(OCTO_ERR_UNSUPPORTED, "QJL encoder: no kernel for fp32 keys at d = 128, b = 5");
+  if (joint && cb->d == 256)
+    return fail(OCTO_ERR_UNSUPPORTED, "joint rounding: no kernel for d = 256");
   EncodeArgs a{};
   a.t = cb->tables;
   a.keys = keys;
@@ -869,6 +873,8 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
     if (cb->d == 128 && cb->b == 5)
       return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 128, b = 5");
+    if (cb->d == 256)
+      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 256 (one query at a time)");
     if (stages & OCTO_STAGE_ROTATE) {
       st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
       if (st != OCTO_OK) return st;

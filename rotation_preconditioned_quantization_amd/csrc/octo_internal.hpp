@@ -36,7 +36,7 @@ struct DevTables {
   const float* rho_tab;     // 2^b_rho rho centroids
   const float* S;           // QJL matrix d x d row-major (nullptr without QJL)
   const uint4* S16;         // the same as f16 planes [S_hi | S_lo], S_hi = f16(S), S_lo = f16(S - S_hi)
-  uint32_t sign_bits[4];    // bit j of the 128-bit mask set <=> WHT sign s_j = -1
+  uint32_t sign_bits[8];    // bit j of the 256-bit mask set <=> WHT sign s_j = -1
 };
 
 struct EncodeArgs {

@@ -469,6 +469,76 @@ def test_argument_errors_on_device():
     assert e.value.status == octo.OCTO_ERR_WORKSPACE
 
 
+# ------------------------------------------------------------------ d = 256 --
+# 86 triplets (the last zero-padded by 2); a key takes a wavefront in the
+# encoder, and the attention kernel splits the value dims over two blocks.
+@pytest.mark.parametrize("b,kdt", [(2, "bf16"), (4, "bf16"), (3, "f32"), (1, "f16"), (5, "bf16")])
+def test_encode_d256(b, kdt):
+    cfg = WL.CONFIGS[2].scaled(d=256, b=b, kdtype=kdt, keys="gauss")
+    keys = WL.make_keys(cfg, "cuda", seed=256 + b, n_seq=2, n=150)
+    encode_and_check(256, b, keys, cap=192, label=f"d256b{b}{kdt}")
+
+
+def test_encode_d256_outliers_and_zero_key():
+    cfg = WL.CONFIGS[2].scaled(d=256, b=4)
+    keys = WL.make_keys(cfg, "cuda", seed=9, n_seq=1, n=70)
+    keys[0, 5] = 0
+    keys[0, 6] *= 1e-3
+    encode_and_check(256, 4, keys, cap=128, label="d256-outliers")
+
+
+@pytest.mark.parametrize("b", [2, 4, 5])
+def test_logits_d256(b):
+    cfg = WL.CONFIGS[3].scaled(d=256, b=b)
+    check_logits(cfg, 1, 2, 4, 300, 320, seed=7, label=f"logits-d256b{b}")
+
+
+@pytest.mark.parametrize("b,G", [(4, 4), (3, 6), (5, 2), (1, 4)])
+def test_attention_d256(b, G):
+    cfg = WL.CONFIGS[2].scaled(d=256, b=b, keys="gauss")
+    check_attention(cfg, 1, 2, G, 300, 320, seed=b, label=f"attn-d256b{b}g{G}")
+
+
+def test_decode_step_append_d256():
+    """The fused append step at d = 256 equals bulk encode + attention."""
+    octo = _octo()
+    cfg = WL.CONFIGS[2].scaled(d=256, b=4)
+    n, B, Hkv, G = 200, 1, 2, 4
+    cap, Hq, n_seq = 256, Hkv * G, B * Hkv
+    keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=n_seq, n=n)
+    v = WL.make_values(cfg, "cuda", seed=3, n_seq=n_seq, cap=cap)
+    q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=1), "cuda", seed=3, B=B)
+    g = gcb(256, 4)
+    ref_cache = octo.Cache(g, n_seq, cap)
+    octo.octo_encode(g, keys, ref_cache)
+    ref = octo.octo_decode_attn(g, q, ref_cache, v, n, Hkv)
+    step = octo.Cache(g, n_seq, cap)
+    octo.octo_encode(g, keys[:, : n - 1].contiguous(), step)
+    out = octo.octo_decode_attn_append(g, keys[:, n - 1].contiguous(), q, step, v, n, Hkv)
+    torch.cuda.synchronize()
+    assert torch.equal(step.packed, ref_cache.packed) and torch.equal(step.gamma, ref_cache.gamma)
+    assert torch.equal(out, ref)
+
+
+def test_d256_unsupported_paths_are_refused():
+    octo = _octo()
+    with pytest.raises(octo.OctoError) as e:
+        octo.Codebook(256, 3, qjl=True, device=0)
+    assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
+    g = gcb(256, 3)
+    cache = octo.Cache(g, 1, 128)
+    keys = torch.randn((1, 100, 256), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(octo.OctoError) as e:
+        octo.octo_encode_joint(g, keys, cache)
+    assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
+    octo.octo_encode(g, keys, cache)
+    q = torch.randn((1, 2, 8, 256), device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros((1, 128, 256), device="cuda", dtype=torch.bfloat16)
+    with pytest.raises(octo.OctoError) as e:
+        octo.octo_decode_attn(g, q, cache, v, 100, 1)
+    assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
+
+
 # ---------------------------------------------------------- full-size runs --
 def test_full_config2_attention():
     cfg = WL.CONFIGS[2]

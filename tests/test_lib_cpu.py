@@ -34,7 +34,7 @@ def test_library_exports_every_header_symbol():
 
 
 @pytest.mark.parametrize("d,b,qjl", [(128, 4, False), (128, 3, True), (128, 2, False), (64, 3, False),
-                                      (128, 1, False), (64, 5, True)])
+                                      (128, 1, False), (64, 5, True), (256, 3, False)])
 def test_host_codebook_matches_oracle(d, b, qjl):
     cb = octo.Codebook(d, b, seed=5, cb_seed=7, qjl=qjl, device=None)
     cx, ce, cr, sg, S = cb.export()
@@ -70,7 +70,7 @@ def test_argument_errors_before_any_launch():
     assert b"power of two" in lib.octo_last_error()
     p.d, p.b, p.device = 128, 9, -1
     assert lib.octo_codebook_build(ctypes.byref(p), ctypes.byref(h)) == octo.OCTO_ERR_INVALID_ARG
-    p.d, p.b, p.device = 256, 3, 0       # no kernel for d=256: refused before any upload
+    p.d, p.b, p.device = 512, 3, 0       # no kernel for d=512: refused before any upload
     assert lib.octo_codebook_build(ctypes.byref(p), ctypes.byref(h)) == octo.OCTO_ERR_UNSUPPORTED
     assert lib.octo_codebook_build(None, ctypes.byref(h)) == octo.OCTO_ERR_INVALID_ARG
     cb = octo.Codebook(128, 3, device=None)
