@@ -240,6 +240,10 @@ def main():
     ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
                     help="workload (2 = the LLM-decode shape the metric is quoted on; the "
                          "others are the remaining shapes of the pages' workloads)")
+    ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128, 256),
+                    help="override the workload's head dim (0: keep it)")
+    ap.add_argument("--bits", type=int, default=0, choices=(0, 1, 2, 3, 4, 5),
+                    help="override the workload's bit budget b (0: keep it)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -263,6 +267,12 @@ def main():
         print(json.dumps({"quality": quality_harness(dev, args.quality_repeats)}), flush=True)
         return
     cfg = WL.CONFIGS[args.config]
+    workload = WORKLOADS[args.config]
+    if args.head_dim or args.bits:
+        cfg = cfg.scaled(d=args.head_dim or cfg.d, b=args.bits or cfg.b)
+        workload += f" [overridden: d={cfg.d}, b={cfg.b}]"
+    # the joint-rounding mode has no kernel at d = 256
+    with_joint = cfg.d != 256
     cb = octo.Codebook(cfg.d, cfg.b, seed=0, cb_seed=0, qjl=cfg.qjl, device=0)
     lay = cb.layout
     dec_bytes, enc_bytes, n_keys_total = algorithmic_bytes(cfg, lay)
@@ -358,7 +368,8 @@ def main():
         k = s["keys"][:, enc_pos0:] if enc_pos0 else s["keys"]
         octo.octo_encode_joint(cb, k, jc, pos0=enc_pos0)
 
-    joint_graph = capture(lambda: [encode_joint(s, jc) for s, jc in zip(sets, jcaches)])
+    if with_joint:
+        joint_graph = capture(lambda: [encode_joint(s, jc) for s, jc in zip(sets, jcaches)])
     # the autoregressive step (single-query attention workloads): append the
     # newest key of every sequence at position N - 1, then attend over N keys
     step_append = cfg.mode == "attn"
@@ -400,7 +411,7 @@ def main():
         return e0.elapsed_time(e1) / 1e3 / reps
 
     t_enc = time_graph(enc_graph, args.kernel_reps) / R
-    t_joint = time_graph(joint_graph, max(1, args.kernel_reps // 4)) / R
+    t_joint = time_graph(joint_graph, max(1, args.kernel_reps // 4)) / R if with_joint else None
     if step_append:
         t_app = time_graph(app_graph, args.kernel_reps) / R
         t_app_enc = time_graph(app_enc_graph, args.kernel_reps) / R
@@ -421,7 +432,7 @@ def main():
     dec_gbs = dec_bytes / t_dec / 1e9
     main_gbs = dec_bytes / t_main / 1e9
     traffic = None
-    if os.path.exists(PROFILE_COUNTERS) and args.config == 2:
+    if os.path.exists(PROFILE_COUNTERS) and args.config == 2 and not (args.head_dim or args.bits):
         pc = {}
         with open(PROFILE_COUNTERS) as f:
             for ln in f:
@@ -447,7 +458,7 @@ def main():
                     "hbm_gbs": round(main_gbs, 2)}
 
     line = {
-        "metric": "fused compressed-K decode GB/s (% HBM peak) + encode Mkeys/s, d=128",
+        "metric": f"fused compressed-K decode GB/s (% HBM peak) + encode Mkeys/s, d={cfg.d}",
         "value": round(dec_gbs, 2),
         "unit": "GB/s",
         "n_gpus": 1,
@@ -459,7 +470,7 @@ def main():
         "vs_baseline": None,
         "dtype": "bf16" if cfg.kdtype == "bf16" else "f32",
         "data": "synthetic",
-        "config": {"workload": WORKLOADS[args.config], "global_batch": cfg.B, "seq_len": cfg.N,
+        "config": {"workload": workload, "global_batch": cfg.B, "seq_len": cfg.N,
                    "parallelism": "none (1 GPU)", "rotating_copies": R},
         "pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(t_dec * 1e6, 3),
@@ -467,15 +478,15 @@ def main():
         "encode_gbs": round(enc_bytes / t_enc / 1e9, 2),
         "encode_us": round(t_enc * 1e6, 3),
         "encode_pct_hbm_peak": round(100 * enc_bytes / t_enc / 1e9 / HBM_PEAK_GBS, 2),
-        "encode_joint_us": round(t_joint * 1e6, 3),
-        "encode_joint_mkeys_per_s": round(n_keys_total / t_joint / 1e6, 1),
+        **({"encode_joint_us": round(t_joint * 1e6, 3),
+            "encode_joint_mkeys_per_s": round(n_keys_total / t_joint / 1e6, 1)} if with_joint else {}),
         **({"append_step_us": round(t_app * 1e6, 3), "append_encode_us": round(t_app_enc * 1e6, 3),
             "append_keys_per_step": cfg.n_seq} if step_append else {}),
         "roofline": roofline,
     }
     if cfg.qjl and not args.no_qjl_bias:
         line["qjl_bias"] = qjl_bias_study(cfg, dev)
-    if not args.no_cpu_baseline and args.config == 2:
+    if not args.no_cpu_baseline and args.config == 2 and not (args.head_dim or args.bits):
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 
