@@ -57,7 +57,10 @@ def kernel_source_hash() -> str:
 
 
 def algorithmic_bytes(cfg, lay):
-    """Per decode call and per encode call (measurement)."""
+    """Algorithmic bytes per decode call and per encode call: the packed codes
+    at their exact bit count, gamma, the QJL signs and norm when present, the
+    bf16 V rows (attention), the queries and outputs; the encoder reads the
+    keys and writes codes and gamma."""
     n = cfg.n_seq * cfg.N
     packed = lay.n_triplets * lay.bits_per_triplet / 8.0     # bits actually used per key
     per_key = packed + 4.0                                   # packed stream + fp32 gamma
@@ -249,7 +252,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(json.dumps({"error": "this build runs on one GPU only; the multi-GPU sharding of "
-                          "the codec is a design note (DESIGN.md), not a measured path",
+                          "the codec is a design note, not a measured path",
                           "n_gpus": args.gpus}))
         sys.exit(2)
 
