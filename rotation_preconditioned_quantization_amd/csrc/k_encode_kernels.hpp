@@ -467,6 +467,233 @@ inline hipError_t launch_encode_one_t(const EncodeArgs& a, int64_t n_seq, hipStr
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Bulk encoder at d = 256: two lanes per key.  Lane l < 32 holds elements
+// 0..127 of the wave's key l, lane l + 32 elements 128..255 of the same key;
+// a wave encodes 32 keys.  Each lane runs the d = 128 machinery on its half
+// (stride-1 butterflies from the packed pairs, strides 2..64 in registers),
+// the stride-128 butterfly pairs the two lanes (v_permlane32_swap), and each
+// lane quantises 43 triplets: triplets 0..42 (the last one takes element 128
+// from the partner) and 43..85 (elements 129..255, zero padded).  The energy
+// is summed serially in triplet order across the pair and every operation
+// matches encode_one_key's, so both write identical words and gamma.
+// ---------------------------------------------------------------------------
+// The value lane ^ 32 holds.  A cross-lane read: call it with every lane
+// active (never under a lane-dependent branch).
+__device__ __forceinline__ uint32_t pair_xchg(uint32_t x, int lane) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return lane < 32 ? r[1] : r[0];
+}
+__device__ __forceinline__ float pair_xchg(float x, int lane) {
+  return __uint_as_float(pair_xchg(__float_as_uint(x), lane));
+}
+
+template <int KT>
+struct Half256 {
+  using S = Stage<128, KT>;                 // a half row: 128 elements
+  static constexpr int KPW = 32;            // keys per wave
+};
+
+// The 64 half rows of the wave's 32 keys at j0 (row r: key j0 + r % 32, half
+// r / 32), loaded with coalesced 16-byte chunks as in load_rows; keys past
+// n_new re-read the last key.
+template <int KT>
+__device__ __forceinline__ void load_half_rows(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                               uint4 (&raw)[Stage<128, KT>::NP][Stage<128, KT>::PER_LANE]) {
+  using S = Stage<128, KT>;
+  const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
+  const int col = lane % S::CPR;
+#pragma unroll
+  for (int h = 0; h < S::NP; ++h) {
+#pragma unroll
+    for (int k = 0; k < S::PER_LANE; ++k) {
+      const int r = h * S::NR + (lane + 64 * k) / S::CPR;
+      int64_t j = j0 + (r % 32);
+      j = j < a.n_new ? j : a.n_new - 1;
+      raw[h][k] = *(const uint4*)(kbase + (j * a.key_stride) * S::ES + (r / 32) * S::ROWB + col * 16);
+    }
+  }
+}
+
+template <int B, int KT>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_encode256(EncodeArgs a) {
+  constexpr int D = 256;
+  using C = Codec<D, B>;
+  using S = Stage<128, KT>;
+  constexpr int W = C::W;
+  constexpr int TH = 43;                                   // triplets per lane
+  constexpr int OFF = TH * C::BT;                          // first bit of triplet 43
+  constexpr int WL = (OFF + 31) / 32 + 1;                  // local words per lane
+  static_assert(C::T == 2 * TH, "d = 256 has 86 triplets");
+  __shared__ __align__(16) unsigned char s_keys[4][S::NR * S::PITCH];
+  __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
+  __shared__ uint32_t s_w[4][32][W | 1];                   // odd pitch: conflict-free rows
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t seq = blockIdx.y;
+  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
+  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
+  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  __syncthreads();
+  const int64_t j0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
+  if (j0 >= a.n_new) return;  // (no block barrier past this point)
+  const bool hi = lane >= 32;
+  const int col = lane % S::CPR;
+  // the sign masks of this lane's staging column in either half
+  const uint4 m0 = chunk_sign_mask<D, KT>(a.t.sign_bits, col);
+  const uint4 m1 = chunk_sign_mask<D, KT>(a.t.sign_bits, col + S::CPR);
+
+  float v[128];
+  {
+    uint4 rowbits[S::CPR];
+    {
+      uint4 raw[S::NP][S::PER_LANE];
+      load_half_rows<KT>(a, seq, j0, lane, raw);
+      // stage the half rows (phases 0, 1: first halves; 2, 3: second halves)
+      unsigned char* s_k = s_keys[wave];
+      const int my_phase = lane / S::NR;
+      const unsigned char* row = s_k + (lane % S::NR) * S::PITCH;
+#pragma unroll
+      for (int h = 0; h < S::NP; ++h) {
+        const uint4 m = (h * S::NR) / 32 ? m1 : m0;
+#pragma unroll
+        for (int k = 0; k < S::PER_LANE; ++k) {
+          uint4 u = raw[h][k];
+          u.x ^= m.x; u.y ^= m.y; u.z ^= m.z; u.w ^= m.w;
+          *(uint4*)(s_k + ((lane + 64 * k) / S::CPR) * S::PITCH + col * 16) = u;
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+        if (my_phase == h) {
+#pragma unroll
+          for (int c = 0; c < S::CPR; ++c) rowbits[c] = *(const uint4*)(row + c * 16);
+        }
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+        __builtin_amdgcn_wave_barrier();
+        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+      }
+    }
+    if constexpr (KT == DT_F32) {
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
+    } else {
+      // stride-1 butterflies straight from the packed 16-bit pairs
+#pragma unroll
+      for (int c = 0; c < S::CPR; ++c) {
+        const uint32_t wd[4] = {rowbits[c].x, rowbits[c].y, rowbits[c].z, rowbits[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) stage1_pair<KT>(wd[k], v[8 * c + 2 * k], v[8 * c + 2 * k + 1]);
+      }
+    }
+  }
+  // the key's exponent scale (as encode_one_key: from the largest stage-1 value)
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < 128; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+  amax = __builtin_fmaxf(amax, pair_xchg(amax, lane));
+  int ex = 0;
+  __builtin_frexpf(amax, &ex);
+  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+  if (__any(sexp != 0)) {
+    const float scale = __builtin_ldexpf(1.0f, -sexp);
+#pragma unroll
+    for (int j = 0; j < 128; ++j) v[j] *= scale;
+  }
+  if constexpr (KT == DT_F32) wht_regs<128>(v);
+  else wht_regs_from<128, 2>(v);
+  // stride 128: y_j = a_j + a_{j+128} (first lane), a_j - a_{j+128} (second)
+#pragma unroll
+  for (int j = 0; j < 128; ++j) {
+    const float p = pair_xchg(v[j], lane);
+    v[j] = hi ? (p - v[j]) : (v[j] + p);
+  }
+  // element 128 for the first lane's last triplet; zero padding for the
+  // second (the exchange runs on all lanes, outside any branch)
+  const float x0 = pair_xchg(v[0], lane);
+  const float ext = hi ? 0.f : x0;
+
+  const float sx = a.t.qx.scale, bx = a.t.qx.bias;
+  const float se = a.t.qe.scale, be = a.t.qe.bias;
+  const float sr = a.t.qr2.scale, mr = (float)(a.t.qr2.nb - 1);
+  auto trip = [&](int i, float& x, float& y, float& z) {
+    // first lane: elements 3i .. 3i+2; second lane: 3i+1 .. 3i+3 (of its half)
+    const float e0 = v[3 * i];
+    const float e1 = v[3 * i + 1];
+    const float e2 = 3 * i + 2 < 128 ? v[3 * i + 2] : ext;
+    const float e3 = 3 * i + 3 < 128 ? v[3 * i + 3] : 0.f;
+    x = hi ? e1 : e0;
+    y = hi ? e2 : e1;
+    z = hi ? e3 : e2;
+  };
+  uint32_t wl[WL];
+#pragma unroll
+  for (int w = 0; w < WL; ++w) wl[w] = 0u;
+  float e[TH];
+  float s1 = 0.f;
+#pragma unroll
+  for (int i = 0; i < TH; ++i) {
+    float x, y, z;
+    trip(i, x, y, z);
+    e[i] = triplet_energy(x, y, z);
+    s1 += e[i];
+    pack_code<C::BT>(wl, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+  }
+  // serial energy over the pair: the second lane continues the first's sum
+  float s2 = pair_xchg(s1, lane);
+#pragma unroll
+  for (int i = 0; i < TH; ++i) s2 += e[i];
+  const float s2p = pair_xchg(s2, lane);
+  const float tot = hi ? s2 : s2p;
+  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+#pragma unroll
+  for (int i = 0; i < TH; ++i)
+    pack_code<C::BT>(wl, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+  const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
+
+  // Assemble the key's word stream in LDS: the first lane's words hold bits
+  // 0 .. OFF-1; the second lane's, shifted to bit OFF, are ORed in after.
+  const int key = lane % 32;
+  uint32_t* kw = s_w[wave][key];
+  if (!hi) {
+#pragma unroll
+    for (int w = 0; w < (OFF + 31) / 32; ++w) kw[w] = wl[w];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  if (hi) {
+    constexpr int W0 = OFF / 32, SH = OFF % 32;
+#pragma unroll
+    for (int k = 0; W0 + k < W; ++k) {
+      const uint32_t lo = k > 0 ? wl[k - 1] : 0u;
+      const uint32_t g = SH ? __builtin_amdgcn_alignbit(wl[k], lo, 32 - SH) : wl[k];
+      if (k == 0) kw[W0] |= g;
+      else kw[W0 + k] = g;
+    }
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const int64_t j = j0 + key;
+  if (!hi && j < a.n_new) {
+    uint32_t words[W];
+#pragma unroll
+    for (int w = 0; w < W; ++w) words[w] = kw[w];
+    const int64_t pos = a.pos0 + j;
+    TileWords<W>::store(a.packed + (seq * (a.cap / kTile) + (pos >> 6)) * W * kTile, (int)(pos & 63),
+                        words);
+    a.gamma[seq * a.cap + pos] = gamma;
+  }
+}
+
+template <int B, int KT>
+inline hipError_t launch_encode256_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+  if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  const dim3 grid((unsigned)((a.n_new + 127) / 128), (unsigned)n_seq);
+  hipLaunchKernelGGL((k_encode256<B, KT>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <int D, int B, int KT, bool QJL, bool JR>
 inline hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
@@ -527,11 +754,15 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
     if (d == 256) { OCTO_ENC_ONE(256) }
     return hipErrorInvalidValue;
   }
-  // d = 256: a key takes a wavefront (lane l holds elements l + 64 r), at
-  // every batch size; scalar rounding without QJL only
+  // d = 256: two lanes per key (scalar rounding without QJL only)
   if (d == 256) {
     if (qjl || joint) return hipErrorInvalidValue;
-    OCTO_ENC_ONE(256)
+    switch (kdt) {
+      case DT_F32: return launch_encode256_t<B, DT_F32>(a, n_seq, s);
+      case DT_BF16: return launch_encode256_t<B, DT_BF16>(a, n_seq, s);
+      case DT_F16: return launch_encode256_t<B, DT_F16>(a, n_seq, s);
+    }
+    return hipErrorInvalidValue;
   }
 #undef OCTO_ENC_ONE
   if (d == 64) return enc_kt<64, B>(kdt, qjl, joint, a, n_seq, s);

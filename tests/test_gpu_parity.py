@@ -157,7 +157,7 @@ def test_encode_joint_rounding_with_qjl():
 
 
 @pytest.mark.parametrize("d,b,kdt", [(128, 4, "bf16"), (128, 2, "f32"), (64, 3, "f16"), (128, 5, "bf16"),
-                                     (64, 1, "f32")])
+                                     (64, 1, "f32"), (256, 4, "bf16"), (256, 2, "f32"), (256, 5, "f16")])
 def test_encode_few_keys_equals_bulk(d, b, kdt):
     """Appends of up to 16 keys per sequence take the one-key-per-wavefront
     encoder; it writes the same words and gamma as the bulk encoder, bit for
