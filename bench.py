@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import statistics
 import sys
 import time
 
@@ -227,8 +228,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--rotate-gib", type=float, default=1.0,
                     help="total size of the rotating input copies")
-    ap.add_argument("--kernel-reps", type=int, default=40,
-                    help="graph replays used to time each kernel on its own")
+    ap.add_argument("--kernel-reps", type=int, default=50,
+                    help="graph replays used to time each kernel on its own (median)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-qjl-bias", action="store_true",
@@ -401,17 +402,27 @@ def main():
         if not torch.equal(sets[r]["out"], eager_out[r]):
             raise RuntimeError(f"graph replay of step {r} differs from the eager result")
 
-    def time_graph(g, reps):
+    means = []  # the mean replay time of each time_graph call, in call order
+
+    def time_graph(g, reps, warm=5, per=4):
+        """One replay's time: the median over `reps` samples (after `warm`
+        untimed replays), a sample being `per` back-to-back replays between two
+        HIP events on the graph's stream (an event between every replay would
+        add its own cost to each)."""
         torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
         with torch.cuda.stream(side):
-            g.replay()                       # warm
-            e0.record(side)
-            for _ in range(reps):
+            for _ in range(warm):
                 g.replay()
-            e1.record(side)
+            evs[0].record(side)
+            for i in range(reps):
+                for _ in range(per):
+                    g.replay()
+                evs[i + 1].record(side)
         torch.cuda.synchronize()
-        return e0.elapsed_time(e1) / 1e3 / reps
+        ts = [evs[i].elapsed_time(evs[i + 1]) / per for i in range(reps)]
+        means.append(sum(ts) / reps / 1e3)
+        return statistics.median(ts) / 1e3
 
     t_enc = time_graph(enc_graph, args.kernel_reps) / R
     t_joint = time_graph(joint_graph, max(1, args.kernel_reps // 4)) / R if with_joint else None
@@ -419,7 +430,9 @@ def main():
         t_app = time_graph(app_graph, args.kernel_reps) / R
         t_app_enc = time_graph(app_enc_graph, args.kernel_reps) / R
     t_dec = time_graph(dec_graph, args.kernel_reps) / R
+    t_dec_mean = means[-1] / R
     t_main = time_graph(main_graph, args.kernel_reps) / R
+    t_main_mean = means[-1] / R
 
     # timed region: exactly K steps
     for w in range(args.warmup):
@@ -477,6 +490,8 @@ def main():
                    "parallelism": "none (1 GPU)", "rotating_copies": R},
         "pct_hbm_peak": round(100 * dec_gbs / HBM_PEAK_GBS, 2),
         "decode_us": round(t_dec * 1e6, 3),
+        "decode_us_mean": round(t_dec_mean * 1e6, 3),
+        "kernel_us_mean": round(t_main_mean * 1e6, 3),
         "encode_mkeys_per_s": round(n_keys_total / t_enc / 1e6, 1),
         "encode_gbs": round(enc_bytes / t_enc / 1e9, 2),
         "encode_us": round(t_enc * 1e6, 3),
