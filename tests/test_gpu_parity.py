@@ -546,6 +546,15 @@ def test_full_config2_attention():
                     seqs=[0, 5])
 
 
+def test_full_config2_shape_at_d256_sampled():
+    """The LLM-decode shape (8 KV heads x 32768 keys, GQA 4) at d = 256, in
+    the launch configuration bench.py --head-dim 256 times; two sequences
+    checked against the oracle in full."""
+    cfg = WL.CONFIGS[2].scaled(d=256)
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config2-d256-full",
+                    seqs=[2, 7])
+
+
 def test_full_config3_attention_sampled():
     cfg = WL.CONFIGS[3]
     check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config3-full",
