@@ -539,6 +539,83 @@ def test_d256_unsupported_paths_are_refused():
     assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
 
 
+# ------------------------------------------------------------ maximum sizes --
+def test_max_sequences_per_launch():
+    """65535 sequences (the largest count a launch takes) of 3 keys each at
+    d = 64, b = 1: encode (the short-append path) and logits, sampled
+    sequences against the oracle."""
+    octo = _octo()
+    d, b, n_seq, n, cap = 64, 1, 65535, 3, 64
+    cfg = WL.CONFIGS[4].scaled(b=b)
+    keys = WL.make_keys(cfg, "cuda", seed=8, n_seq=n_seq, n=n)
+    g = gcb(d, b)
+    cache = octo.Cache(g, n_seq, cap)
+    octo.octo_encode(g, keys, cache)
+    q = WL.make_queries(cfg.scaled(Hq=1, n_q=1), "cuda", seed=8, B=n_seq)[:, :, 0].contiguous()
+    lg = octo.octo_decode_logits(g, q, cache, n, 1)          # [n_seq, 1, n]
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    W = cb.words_per_key
+    words = cache.packed.view(n_seq, cap * W)
+    for s in (0, 4097, 40000, n_seq - 1):
+        kk = f64(keys[s])
+        enc = O.encode(kk, cb)
+        codes = unpack_device_codes(words[s].cpu().numpy(), cb, 1, cap, n)
+        assert_codes_match(codes, enc, cb, f"maxseq s{s}")
+        uh = O.decode_rotated(codes[0], cb)
+        gam = cache.gamma.view(n_seq, cap)[s, :n].cpu().numpy()
+        qq = f64(q[s, 0])
+        ref = O.logits_rotated(qq, uh, gam, cb)
+        err = logit_err(f64(lg[s, 0]), ref, np.linalg.norm(qq), gam, d)
+        assert err <= 1e-3, (s, err)
+
+
+def test_cache_past_4_gib_of_codes():
+    """One sequence of 2^26 cached keys at d = 128, b = 4: 4.8 GB of packed
+    words, 17 GB of V, so every byte offset past 2^32 goes through the 64-bit
+    index arithmetic.  The last 200 keys are encoded at the top of the cache;
+    the others stay zero keys (gamma 0, logit 0, V 0).  Logits and attention
+    over all 2^26 keys are checked against the oracle."""
+    octo = _octo()
+    d, b, G = 128, 4, 4
+    cap, n_new = 1 << 26, 200
+    pos0 = cap - n_new
+    cfg = WL.CONFIGS[2]
+    g = gcb(d, b)
+    cache = octo.Cache(g, 1, cap)
+    keys = WL.make_keys(cfg, "cuda", seed=5, n_seq=1, n=n_new)
+    octo.octo_encode(g, keys, cache, pos0=pos0)
+    q = WL.make_queries(cfg.scaled(Hq=G, n_q=1), "cuda", seed=5, B=1)
+    lg = octo.octo_decode_logits(g, q[:, :, 0].contiguous(), cache, cap, 1)   # [1, G, cap]
+    torch.cuda.synchronize()
+    assert int(torch.count_nonzero(lg[0, :, :pos0])) == 0
+    cb = ocb(d, b)
+    W = cb.words_per_key
+    t0 = pos0 // 64
+    tail = cache.packed[t0 * 64 * W:].cpu().numpy()
+    codes = unpack_device_codes(tail, cb, 1, cap - t0 * 64, n_new, start=pos0 - t0 * 64)
+    assert_codes_match(codes, O.encode(f64(keys[0]), cb), cb, "past-4GiB")
+    uh = O.decode_rotated(codes[0], cb)
+    gam = cache.gamma[pos0:].cpu().numpy()
+    qq = f64(q[0, :, 0])
+    lgt = f64(lg[0, :, pos0:])
+    v = torch.zeros((1, cap, d), dtype=torch.bfloat16, device="cuda")
+    v[0, pos0:] = WL.make_values(cfg, "cuda", seed=5, n_seq=1, cap=n_new)[0]
+    out = f64(octo.octo_decode_attn(g, q, cache, v, cap, 1))
+    torch.cuda.synchronize()
+    vv = f64(v[0, pos0:])
+    for h in range(G):
+        ref = O.logits_rotated(qq[h], uh, gam, cb)
+        assert logit_err(lgt[h], ref, np.linalg.norm(qq[h]), gam, d) <= 1e-3
+        # softmax over all 2^26 keys: pos0 zero logits with zero values
+        a = ref / math.sqrt(d)
+        m = max(0.0, float(a.max()))
+        e = np.exp(a - m)
+        o_ref = (e @ vv) / (pos0 * math.exp(-m) + e.sum())
+        assert np.linalg.norm(out[0, h, 0] - o_ref) <= 2e-3 * np.linalg.norm(o_ref), h
+    del v, cache
+
+
 # ---------------------------------------------------------- full-size runs --
 def test_full_config2_attention():
     cfg = WL.CONFIGS[2]
