@@ -35,7 +35,10 @@ template <int D>
 struct MQShape {
   static constexpr int KT = 128;                  // keys per tile
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
-  static constexpr int VP = KT * 2 + 16;          // V^T row pitch in bytes (fp16)
+  // V^T row pitch in bytes (fp16): 66 dwords keep the 8-byte P.V operand
+  // reads of 32 consecutive rows on distinct banks and halve the bank
+  // collisions of the transposing writes against a 68-dword pitch
+  static constexpr int VP = KT * 2 + 8;
   static constexpr int SW = D == 64 ? 4 : 0;      // staging-only waves
   static constexpr int NW = kMQCompute + SW;      // waves per workgroup
   static constexpr int NSW = SW ? SW : kMQCompute;  // waves that stage
