@@ -469,6 +469,107 @@ def test_argument_errors_on_device():
     assert e.value.status == octo.OCTO_ERR_WORKSPACE
 
 
+# ------------------------------------------- stages, streams, graph capture --
+def _decode_setup(cfg, n, cap, seed, n_q=1):
+    octo = _octo()
+    Hkv, G = 2, 4
+    keys = WL.make_keys(cfg, "cuda", seed=seed, n_seq=Hkv, n=n)
+    g = gcb(cfg.d, cfg.b)
+    cache = octo.Cache(g, Hkv, cap)
+    octo.octo_encode(g, keys, cache)
+    v = WL.make_values(cfg, "cuda", seed=seed, n_seq=Hkv, cap=cap)
+    q = WL.make_queries(cfg.scaled(Hq=Hkv * G, n_q=n_q), "cuda", seed=seed, B=1).contiguous()
+    return g, keys, cache, v, q, Hkv
+
+
+@pytest.mark.parametrize("mode", ["attn", "logits", "attn_mq"])
+def test_decode_stages_equal_one_call(mode):
+    """The launches run one by one (rotate, main kernel, combine, as the
+    timing harness does) give the same bytes as one call with all stages."""
+    octo = _octo()
+    cfg = WL.CONFIGS[4 if mode == "attn_mq" else 2]
+    n_q = 40 if mode == "attn_mq" else 1
+    g, _, cache, v, q, Hkv = _decode_setup(cfg, 700, 768, seed=3, n_q=n_q)
+    if mode == "logits":
+        q = q[:, :, 0].contiguous()
+        ref = octo.octo_decode_logits(g, q, cache, 700, Hkv)
+        ws = torch.zeros(g.workspace_bytes(0, 1, q.shape[1], Hkv, 1, 700), dtype=torch.uint8, device="cuda")
+        out = torch.full_like(ref, float("nan"))
+        for st in (octo.STAGE_ROTATE, octo.STAGE_MAIN, octo.STAGE_COMBINE):
+            octo.octo_decode_logits(g, q, cache, 700, Hkv, logits=out, workspace=ws, stages=st)
+    else:
+        ref = octo.octo_decode_attn(g, q, cache, v, 700, Hkv)
+        ws = torch.zeros(g.workspace_bytes(1, 1, q.shape[1], Hkv, n_q, 700), dtype=torch.uint8, device="cuda")
+        out = torch.full_like(ref, float("nan"))
+        for st in (octo.STAGE_ROTATE, octo.STAGE_MAIN, octo.STAGE_COMBINE):
+            octo.octo_decode_attn(g, q, cache, v, 700, Hkv, out=out, workspace=ws, stages=st)
+    torch.cuda.synchronize()
+    assert torch.equal(out, ref)
+
+
+def test_side_stream_equals_default_stream():
+    """Every entry point runs on the stream it is given."""
+    octo = _octo()
+    cfg = WL.CONFIGS[2]
+    g, keys, cache, v, q, Hkv = _decode_setup(cfg, 500, 512, seed=4)
+    ref = octo.octo_decode_attn(g, q, cache, v, 500, Hkv)
+    side = torch.cuda.Stream()
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        c2 = octo.Cache(g, Hkv, 512)
+        octo.octo_encode(g, keys, c2, stream=side)
+        out = octo.octo_decode_attn(g, q, c2, v, 500, Hkv, stream=side)
+    side.synchronize()
+    assert torch.equal(c2.packed, cache.packed) and torch.equal(c2.gamma, cache.gamma)
+    assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("mode", ["attn", "append", "attn_mq"])
+def test_graph_replays_equal_eager(mode):
+    """Encode + decode captured in a HIP graph: every replay, with eager work
+    and synchronisations between the replays, reproduces the eager bytes."""
+    octo = _octo()
+    cfg = WL.CONFIGS[4 if mode == "attn_mq" else 2]
+    n_q = 48 if mode == "attn_mq" else 1
+    n, cap = 600, 640
+    g, keys, cache, v, q, Hkv = _decode_setup(cfg, n, cap, seed=6, n_q=n_q)
+    ws = torch.zeros(g.workspace_bytes(1, 1, q.shape[1], Hkv, n_q, n), dtype=torch.uint8, device="cuda")
+    out = torch.empty((1, q.shape[1], n_q, cfg.d), dtype=torch.float32, device="cuda")
+    gc = octo.Cache(g, Hkv, cap)
+    new_key = keys[:, n - 1].contiguous()
+
+    def step():
+        if mode == "append":
+            octo.octo_encode(g, keys[:, : n - 1], gc)
+            octo.octo_decode_attn_append(g, new_key, q, gc, v, n, Hkv, out=out, workspace=ws)
+        else:
+            octo.octo_encode(g, keys, gc)
+            octo.octo_decode_attn(g, q, gc, v, n, Hkv, out=out, workspace=ws)
+
+    step()
+    torch.cuda.synchronize()
+    eager_out, eager_packed = out.clone(), gc.packed.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        step()  # warm on the capture stream
+        torch.cuda.synchronize()
+        with torch.cuda.graph(graph, stream=s):
+            step()
+    for r in range(3):
+        out.fill_(float("nan"))
+        gc.packed.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, eager_out), r
+        assert torch.equal(gc.packed, eager_packed), r
+        # eager work between the replays
+        octo.octo_decode_attn(g, q, cache, v, n, Hkv)
+        torch.cuda.synchronize()
+
+
 # ------------------------------------------------------------------ d = 256 --
 # 86 triplets (the last zero-padded by 2); a key takes a wavefront in the
 # encoder, and the attention kernel splits the value dims over two blocks.
