@@ -379,8 +379,8 @@ __global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// Single-query split-K attention.  grid = (n_split, n_seq, ceil(G / 4) x
-// value parts), 4 waves per block; wave w takes tiles t_begin + w, + 4, ... of the block's
+// Single-query split-K attention.  grid = (n_split x value parts, n_seq,
+// ceil(G / 4)), 4 waves per block; wave w takes tiles t_begin + w, + 4, ... of the block's
 // split, with the next tile (V rows and compressed words) in flight while
 // the current one is computed.  Per tile: logits by tile_logits, a wave-wide
 // online softmax per head (DPP max), then O[head][dim] += p[head][key]
@@ -436,9 +436,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
-  const int ngr = (a.G + 3) / 4;
-  const int vh = (int)blockIdx.z / ngr;              // value part of this block
-  const int g0 = ((int)blockIdx.z % ngr) * 4;
+  // the value parts of one split are adjacent blocks, so the second part's
+  // reads of the split's code words hit the L2 the first part filled
+  const int vh = VG::NVH > 1 ? (int)blockIdx.x % VG::NVH : 0;   // value part of this block
+  const int split = VG::NVH > 1 ? (int)blockIdx.x / VG::NVH : (int)blockIdx.x;
+  const int g0 = (int)blockIdx.z * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
   const int kq = lane / VG::CPR;                     // key of the wave load this lane serves
   // slot of this lane's key (= lane) in the p rows: key 4 KPL g + KPL j' + q
@@ -446,7 +448,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const int p_slot = (lane / (4 * VG::KPL)) * (4 * VG::KPL) + (lane % VG::KPL) * 4 +
                      (lane % (4 * VG::KPL)) / VG::KPL;
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
-  const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
+  const int64_t t_begin = (int64_t)split * a.tiles_per_split;
   int64_t t_end = t_begin + a.tiles_per_split;
   if (t_end > ntile) t_end = ntile;
   const uint4* vlane0 = (const uint4*)a.v + kq * VG::RP + vh * VG::CPR + lane % VG::CPR;
@@ -483,7 +485,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
         const float g = encode_one_key<D, B, DT_BF16>(row, a.t, a.t.qx.t, a.t.qe.t, a.t.qr2.t, lane,
                                                       s_ak, s_ak + 3 * T, s_aw);
         if (lane == 0) s_ag = g;
-        if (blockIdx.z == 0) {
+        if (blockIdx.z == 0 && vh == 0) {
           if (lane < W) store_key_word<W>(a.packed_w, a.cap, seq, a.n_keys - 1, lane, s_aw[lane]);
           if (lane == 0) a.gamma_w[seq * a.cap + a.n_keys - 1] = g;
         }
@@ -631,7 +633,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     }
     const int64_t row = bidx * a.Hq + kvh * a.G + g0 + h;
     const int col = c < 2 ? c : c + vh * VG::DV;
-    a.part[(row * a.n_split + blockIdx.x) * (D + 2) + col] = val;
+    a.part[(row * a.n_split + split) * (D + 2) + col] = val;
   }
 }
 
@@ -786,7 +788,7 @@ static hipError_t logits_t(const DecodeArgs& a, int64_t n_seq, int nbx, hipStrea
 template <int D, int B, bool QJL>
 static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
   hipLaunchKernelGGL((k_attn<D, B, QJL>),
-                     dim3(a.n_split, (unsigned)n_seq, ((a.G + 3) / 4) * VGeom<D>::NVH), dim3(256), 0,
+                     dim3(a.n_split * VGeom<D>::NVH, (unsigned)n_seq, (a.G + 3) / 4), dim3(256), 0,
                      s, a);
   return hipGetLastError();
 }
