@@ -275,8 +275,7 @@ def main():
     if args.head_dim or args.bits:
         cfg = cfg.scaled(d=args.head_dim or cfg.d, b=args.bits or cfg.b)
         workload += f" [overridden: d={cfg.d}, b={cfg.b}]"
-    # the joint-rounding mode has no kernel at d = 256
-    with_joint = cfg.d != 256
+    with_joint = True
     cb = octo.Codebook(cfg.d, cfg.b, seed=0, cb_seed=0, qjl=cfg.qjl, device=0)
     lay = cb.layout
     dec_bytes, enc_bytes, n_keys_total = algorithmic_bytes(cfg, lay)

@@ -61,9 +61,8 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
  * given a seed).
  *   d         head dim: 64, 128 and 256 have kernels (any power of two 4..1024
  *             for a host-only codebook).  At d = 256 there is no QJL variant
- *             (a QJL codebook is refused with OCTO_ERR_UNSUPPORTED), no joint
- *             rounding and no multi-query path; the encoder takes a wavefront
- *             per key there.
+ *             (a QJL codebook is refused with OCTO_ERR_UNSUPPORTED) and no
+ *             multi-query path; the encoder gives each key two lanes there.
  *   b         bit budget per coordinate; kernels exist for 1 .. 5 (the
  *             multi-query path and the fp32-key QJL encoder not at d = 128,
  *             b = 5).

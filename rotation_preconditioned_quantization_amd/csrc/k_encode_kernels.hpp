@@ -221,6 +221,41 @@ __device__ __forceinline__ void qjl_signs(const float (&v)[D], const unsigned ch
   }
 }
 
+// Joint rounding of one unit triplet (x, y, z) ([YL] 联合取整): among the
+// 3x3 direction codes around the scalar (xi, eta) indices c0 (clamped to the
+// index range), each with its best rho^ (the centroid nearest s = <n^, t>,
+// from the squared-midpoint table on max(s, 0)^2), the code with the least
+// error |t - rho^ n^|^2 - |t|^2 = rho^ (rho^ - 2s); the first strict minimum
+// in (xi, eta) offset order wins.
+template <class C>
+__device__ __forceinline__ uint32_t joint_code(float x, float y, float z, uint32_t c0,
+                                               const float4* s_dir, const float* s_rho,
+                                               const uint2* s_qr, float sr, float mr) {
+  const int ix = (int)(c0 & (C::LX - 1)), ie = (int)(c0 >> C::BX);
+  float best_e = INFINITY;
+  uint32_t best = 0u;
+#pragma unroll
+  for (int da = -1; da <= 1; ++da) {
+    const int ja = min(max(ix + da, 0), C::LX - 1);
+#pragma unroll
+    for (int dc = -1; dc <= 1; ++dc) {
+      const int jc = min(max(ie + dc, 0), C::LE - 1);
+      const uint32_t xe = (uint32_t)ja | ((uint32_t)jc << C::BX);
+      const float4 n = s_dir[xe];
+      const float sdot = __builtin_fmaf(n.x, x, __builtin_fmaf(n.y, y, n.z * z));
+      const float sp = __builtin_fmaxf(sdot, 0.f);
+      const uint32_t jr = quant1_clamp(sp * sp, s_qr, sr, mr);
+      const float r = s_rho[jr];
+      const float err = r * (r - 2.f * sdot);
+      if (err < best_e) {
+        best_e = err;
+        best = xe | (jr << (C::BX + C::BE));
+      }
+    }
+  }
+  return best;
+}
+
 // Encode the 64-key tile at j0: one key per lane, entirely in registers.
 template <int D, int B, int KT, bool QJL, bool JR>
 __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
@@ -315,6 +350,8 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
     uint32_t wj[W];
 #pragma unroll
     for (int w = 0; w < W; ++w) wj[w] = 0u;
+    // (the search of joint_code, written out: the compiler schedules this
+    // form of the loop better in this kernel)
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       float x, y, z;
@@ -515,8 +552,9 @@ __device__ __forceinline__ void load_half_rows(const EncodeArgs& a, int64_t seq,
   }
 }
 
-template <int B, int KT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_encode256(EncodeArgs a) {
+template <int B, int KT, bool JR>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(JR || KT == DT_F32 ? 2 : 3)))
+void k_encode256(EncodeArgs a) {
   constexpr int D = 256;
   using C = Codec<D, B>;
   using S = Stage<128, KT>;
@@ -528,11 +566,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   __shared__ __align__(16) unsigned char s_keys[4][S::NR * S::PITCH];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
   __shared__ uint32_t s_w[4][32][W | 1];                   // odd pitch: conflict-free rows
+  // unit directions and rho centroids (joint rounding)
+  __shared__ float4 s_dir[JR ? C::NDIR : 1];
+  __shared__ float s_rho[JR ? C::LR : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
   for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
   for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
   for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  if constexpr (JR) {
+    for (int i = threadIdx.x; i < C::NDIR; i += 256) s_dir[i] = a.t.dirtab[i];
+    if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
+  }
   __syncthreads();
   const int64_t j0 = ((int64_t)blockIdx.x * 4 + wave) * 32;
   if (j0 >= a.n_new) return;  // (no block barrier past this point)
@@ -644,10 +689,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   for (int i = 0; i < TH; ++i) s2 += e[i];
   const float s2p = pair_xchg(s2, lane);
   const float tot = hi ? s2 : s2p;
-  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+  if constexpr (!JR) {
+    const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
 #pragma unroll
-  for (int i = 0; i < TH; ++i)
-    pack_code<C::BT>(wl, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+    for (int i = 0; i < TH; ++i)
+      pack_code<C::BT>(wl, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+  } else {
+    // joint rounding of every triplet of the unit key around its scalar
+    // (xi, eta) indices
+    const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+    uint32_t wj[WL];
+#pragma unroll
+    for (int w = 0; w < WL; ++w) wj[w] = 0u;
+#pragma unroll
+    for (int i = 0; i < TH; ++i) {
+      float x, y, z;
+      trip(i, x, y, z);
+      x *= inv_norm;
+      y *= inv_norm;
+      z *= inv_norm;
+      const uint32_t c0 = field_at<WL>(wl, i * C::BT, C::BX + C::BE);
+      pack_code<C::BT>(wj, i, joint_code<C>(x, y, z, c0, s_dir, s_rho, s_qr, sr, mr));
+    }
+#pragma unroll
+    for (int w = 0; w < WL; ++w) wl[w] = wj[w];
+  }
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
 
   // Assemble the key's word stream in LDS: the first lane's words hold bits
@@ -687,10 +753,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 }
 
 template <int B, int KT>
-inline hipError_t launch_encode256_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
+inline hipError_t launch_encode256_t(const EncodeArgs& a, bool joint, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.n_new + 127) / 128), (unsigned)n_seq);
-  hipLaunchKernelGGL((k_encode256<B, KT>), grid, dim3(256), 0, s, a);
+  if (joint) hipLaunchKernelGGL((k_encode256<B, KT, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_encode256<B, KT, false>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -754,13 +821,13 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
     if (d == 256) { OCTO_ENC_ONE(256) }
     return hipErrorInvalidValue;
   }
-  // d = 256: two lanes per key (scalar rounding without QJL only)
+  // d = 256: two lanes per key (scalar or joint rounding, no QJL)
   if (d == 256) {
-    if (qjl || joint) return hipErrorInvalidValue;
+    if (qjl) return hipErrorInvalidValue;
     switch (kdt) {
-      case DT_F32: return launch_encode256_t<B, DT_F32>(a, n_seq, s);
-      case DT_BF16: return launch_encode256_t<B, DT_BF16>(a, n_seq, s);
-      case DT_F16: return launch_encode256_t<B, DT_F16>(a, n_seq, s);
+      case DT_F32: return launch_encode256_t<B, DT_F32>(a, joint, n_seq, s);
+      case DT_BF16: return launch_encode256_t<B, DT_BF16>(a, joint, n_seq, s);
+      case DT_F16: return launch_encode256_t<B, DT_F16>(a, joint, n_seq, s);
     }
     return hipErrorInvalidValue;
   }

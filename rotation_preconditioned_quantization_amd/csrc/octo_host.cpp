@@ -637,8 +637,6 @@ static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_d
     return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
   if (qjl_bits && cb->d == 128 && cb->b == 5 && kdt == OCTO_F32)
     return fail(OCTO_ERR_UNSUPPORTED, "QJL encoder: no kernel for fp32 keys at d = 128, b = 5");
-  if (joint && cb->d == 256)
-    return fail(OCTO_ERR_UNSUPPORTED, "joint rounding: no kernel for d = 256");
   EncodeArgs a{};
   a.t = cb->tables;
   a.keys = keys;
