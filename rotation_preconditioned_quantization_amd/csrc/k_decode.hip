@@ -74,15 +74,19 @@ __global__ __launch_bounds__(64) void k_rotate(RotateArgs a) {
   if (l < 3 * T - D) out[D + l] = 0.f;
   if (a.qp != nullptr) {
     __syncthreads();
+    float acc[NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int j = l + 64 * k;
-      const float* row = a.t.S + (int64_t)j * D;
-      float acc = 0.f;
+    for (int k = 0; k < NV; ++k) acc[k] = 0.f;
 #pragma unroll 8
-      for (int c = 0; c < D; ++c) acc = __builtin_fmaf(row[c], s_q[c], acc);
-      a.qp[(int64_t)orow * D + j] = acc * (1.2533141373155003f / D);  // sqrt(pi/2)/d
+    for (int c = 0; c < D; ++c) {
+      const float qc = s_q[c];
+      const float* col = a.t.St + (int64_t)c * D + l;   // coalesced column of S
+#pragma unroll
+      for (int k = 0; k < NV; ++k) acc[k] = __builtin_fmaf(col[64 * k], qc, acc[k]);
     }
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      a.qp[(int64_t)orow * D + l + 64 * k] = acc[k] * (1.2533141373155003f / D);  // sqrt(pi/2)/d
   }
 }
 
@@ -90,15 +94,26 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // LDS of the single-query kernels.  kCombined: for up to 10 bits per triplet
 // one float4 per triplet code holds rho^ n^ directly; otherwise unit
-// directions per (i_xi, i_eta) plus the rho centroids.  q holds the rotated
-// queries of the (up to) 4 heads of this pass, rows padded with zeros; with
-// QJL, qp holds p = sqrt(pi/2)/d S q' and lut its nibble sums.
-template <int D, int B, bool QJL>
+// directions per (i_xi, i_eta) plus the rho centroids.  REP (up to 8 bits of
+// direction): the table is held in 16 copies, entry e of copy c at float4
+// slot 16 e + c, and lane l reads copy l % 16, so the 16 lanes the LDS serves
+// in one pass hit 16 different 4-bank groups whatever codes they look up:
+// random gathers then run conflict-free (4 LDS cycles per wavefront read
+// instead of about 11).  With REP at 3 bits the 1024-entry combined table
+// would not fit 16 times, so the directions are replicated and rho^ is a
+// separate 4-entry (conflict-free) read.  q holds the rotated queries of the
+// (up to) 4 heads of this pass, rows padded with zeros; with QJL, qp holds
+// p = sqrt(pi/2)/d S q' and lut its nibble sums.
+template <int D, int B, bool QJL, bool REP>
 struct SQShared {
   using C = Codec<D, B>;
-  static constexpr bool kCombined = C::BT <= 10;
+  static constexpr bool kRepComb = REP && (1 << C::BT) <= 128;
+  static constexpr bool kCombined = REP ? kRepComb : C::BT <= 10;
+  static constexpr int NENT = kCombined ? (1 << C::BT) : C::NDIR;
+  static constexpr int NCOPY = REP ? 16 : 1;
+  static_assert(!REP || NENT <= 256, "replicated code table larger than 64 KiB");
   static constexpr int QD = ((3 * C::T + 3) / 4) * 4;
-  float4 tab[kCombined ? (1 << C::BT) : C::NDIR];
+  float4 tab[NENT * NCOPY];
   float rho[C::LR];
   float q[4][QD];
   float qp[QJL ? 4 : 1][QJL ? D : 1];
@@ -108,29 +123,35 @@ struct SQShared {
 // Values the block prologue loads from global memory besides the LDS tables
 // (which go to LDS directly): wave w's query head g0 + w (lane l holds the
 // 32-bit words of elements l + 64 k) and the rho centroids.
-template <int D, int B, bool QJL>
+// Waves per k_logits block: 8 with the replicated table (B <= 3), else 4.
+template <int B>
+constexpr int logits_waves() { return B <= 3 ? 8 : 4; }
+
+template <int D, int B, bool QJL, bool REP>
 struct SQPre {
-  using C = Codec<D, B>;
-  static constexpr int NT = SQShared<D, B, QJL>::kCombined ? (1 << C::BT) : C::NDIR;
-  static constexpr int PER = (NT + 255) / 256;
   float rho;
   uint32_t qw[D / 64];
 };
 
-template <int D, int B, bool QJL>
+template <int D, int B, bool QJL, bool REP, int NTH = 256>
 __device__ __forceinline__ void sq_issue_prologue(const DecodeArgs& a, int64_t seq, int g0,
-                                                  int hcount, SQPre<D, B, QJL>& pre,
-                                                  SQShared<D, B, QJL>& sh) {
+                                                  int hcount, SQPre<D, B, QJL, REP>& pre,
+                                                  SQShared<D, B, QJL, REP>& sh) {
   using C = Codec<D, B>;
-  using P = SQPre<D, B, QJL>;
+  using SH = SQShared<D, B, QJL, REP>;
+  constexpr int NS = SH::NENT * SH::NCOPY;   // float4 slots
+  constexpr int PER = (NS + NTH - 1) / NTH;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const float4* src = SQShared<D, B, QJL>::kCombined ? a.t.trip_tab : a.t.dirtab;
-  // the table goes straight from global memory into LDS (no registers held)
+  const float4* src = SH::kCombined ? a.t.trip_tab : a.t.dirtab;
+  // the table goes straight from global memory into LDS (no registers held);
+  // slot i holds entry i / NCOPY.  The condition is per lane: a table of
+  // fewer than 64 slots (16 at one bit) is copied by the first lanes only,
+  // and the others neither read past its end nor write past it in LDS.
 #pragma unroll
-  for (int k = 0; k < P::PER; ++k) {
-    const int i0 = 256 * k + 64 * w;  // this wave's 64 entries of round k
-    if (P::NT % 256 == 0 || i0 < P::NT)
-      __builtin_amdgcn_global_load_lds((const void*)(src + i0 + lane),
+  for (int k = 0; k < PER; ++k) {
+    const int i0 = NTH * k + 64 * w;  // this wave's 64 slots of round k
+    if (NS % NTH == 0 || i0 + lane < NS)
+      __builtin_amdgcn_global_load_lds((const void*)(src + (i0 + lane) / SH::NCOPY),
                                        (__attribute__((address_space(3))) void*)(sh.tab + i0), 16,
                                        0, 0);
   }
@@ -151,8 +172,8 @@ __device__ __forceinline__ void sq_issue_prologue(const DecodeArgs& a, int64_t s
 }
 
 // Element l + 64 k of the wave's query from the raw words of sq_issue_prologue.
-template <int D, int B, bool QJL>
-__device__ __forceinline__ float sq_query_elem(const DecodeArgs& a, const SQPre<D, B, QJL>& pre,
+template <int D, int B, bool QJL, bool REP>
+__device__ __forceinline__ float sq_query_elem(const DecodeArgs& a, const SQPre<D, B, QJL, REP>& pre,
                                                int k, int lane) {
   const uint32_t wd = pre.qw[k];
   const uint32_t h16 = (lane & 1) ? (wd >> 16) : (wd & 0xffffu);
@@ -164,19 +185,20 @@ __device__ __forceinline__ float sq_query_elem(const DecodeArgs& a, const SQPre<
 // Query rotation (q' = mult * R q, R = d^-1/2 H diag(s)): butterflies of
 // stride < 64 pair lanes (shuffles), strides 64, 128 pair a lane's values.
 // With QJL the wave also forms p = sqrt(pi/2)/d * S q'.
-template <int D, int B, bool QJL>
+template <int D, int B, bool QJL, bool REP>
 __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
-                                            const SQPre<D, B, QJL>& pre, SQShared<D, B, QJL>& sh) {
-  using SH = SQShared<D, B, QJL>;
+                                            const SQPre<D, B, QJL, REP>& pre, SQShared<D, B, QJL, REP>& sh) {
+  using SH = SQShared<D, B, QJL, REP>;
   constexpr int NV = D / 64;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (w >= 4) return;   // blocks of more than 4 waves: the others only stream tiles
   // branch-free: a wave past hcount rotates a valid head and stores zeros
   const bool live = w < hcount;
   float x[NV];
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int j = lane + 64 * k;
-    const float qv = sq_query_elem<D, B, QJL>(a, pre, k, lane);
+    const float qv = sq_query_elem<D, B, QJL, REP>(a, pre, k, lane);
     const uint32_t sb = (lane < 32) ? a.t.sign_bits[2 * k] : a.t.sign_bits[2 * k + 1];
     x[k] = ((sb >> (j & 31)) & 1u) ? -qv : qv;
   }
@@ -205,29 +227,35 @@ __device__ __forceinline__ void rotate_head(const DecodeArgs& a, int hcount,
   if constexpr (QJL) {
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    // p_j = sum_c S[j][c] q'_c: lane j reads element j of column c, so every
+    // load is one contiguous row of St
+    float acc[NV];
 #pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int j = lane + 64 * k;
-      const float* row = a.t.S + (int64_t)j * D;
-      float acc = 0.f;
+    for (int k = 0; k < NV; ++k) acc[k] = 0.f;
 #pragma unroll 8
-      for (int c = 0; c < D; ++c) acc = __builtin_fmaf(row[c], sh.q[w][c], acc);
-      sh.qp[w][j] = live ? acc * (1.2533141373155003f / D) : 0.f;  // sqrt(pi/2)/d
+    for (int c = 0; c < D; ++c) {
+      const float qc = sh.q[w][c];
+      const float* col = a.t.St + (int64_t)c * D + lane;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) acc[k] = __builtin_fmaf(col[64 * k], qc, acc[k]);
     }
+#pragma unroll
+    for (int k = 0; k < NV; ++k)
+      sh.qp[w][lane + 64 * k] = live ? acc[k] * (1.2533141373155003f / D) : 0.f;  // sqrt(pi/2)/d
   }
 }
 
-template <int D, int B, bool QJL>
-__device__ __forceinline__ void store_sq_tables(const SQPre<D, B, QJL>& pre,
-                                                SQShared<D, B, QJL>& sh) {
+template <int D, int B, bool QJL, bool REP>
+__device__ __forceinline__ void store_sq_tables(const SQPre<D, B, QJL, REP>& pre,
+                                                SQShared<D, B, QJL, REP>& sh) {
   using C = Codec<D, B>;
   if (threadIdx.x < C::LR) sh.rho[threadIdx.x] = pre.rho;
 }
 
 // QJL nibble table: lut[m][nib] holds, per head, sum_k (+1 if bit k of nib
 // else -1) * p[4m + k].
-template <int D, int B, bool QJL>
-__device__ __forceinline__ void build_qjl_lut(int hcount, SQShared<D, B, QJL>& sh) {
+template <int D, int B, bool QJL, bool REP>
+__device__ __forceinline__ void build_qjl_lut(int hcount, SQShared<D, B, QJL, REP>& sh) {
   if constexpr (QJL) {
     for (int e = threadIdx.x; e < (D / 4) * 16; e += blockDim.x) {
       const int m = e >> 4, nib = e & 15;
@@ -276,14 +304,15 @@ __device__ __forceinline__ void load_ktile(const DecodeArgs& a, int64_t seq, int
 // the A operand is q'[head = lane % 4][dim] and the B operand is the lane's
 // own rebuilt coordinate, so block b produces the 4 x 4 outer product for
 // keys 4b..4b+3 and lane l ends up holding the 4 heads of key l.  Exact fp32.
-template <int D, int B, bool QJL>
-__device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
+template <int D, int B, bool QJL, bool REP>
+__device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL, REP>& sh,
                                                const KTile<D, B, QJL>& k, int lane) {
   using C = Codec<D, B>;
-  using SH = SQShared<D, B, QJL>;
+  using SH = SQShared<D, B, QJL, REP>;
   constexpr int T = C::T, W = C::W;
   constexpr int kGroup = 4;
   const float* qrow = sh.q[lane & 3];
+  const float4* tab = sh.tab + (SH::NCOPY > 1 ? (lane & (SH::NCOPY - 1)) : 0);  // this lane's copy
   // two accumulator sets (even / odd triplets): the dependent-MFMA latency
   // then hides behind the other set's issue
   floatx4 acc[6];
@@ -294,10 +323,10 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
     const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
     float tv[3];
     if constexpr (SH::kCombined) {
-      const float4 e = sh.tab[code];
+      const float4 e = tab[code * SH::NCOPY];
       tv[0] = e.x; tv[1] = e.y; tv[2] = e.z;
     } else {
-      const float4 n = sh.tab[code & C::DIR_MASK];
+      const float4 n = tab[(code & C::DIR_MASK) * SH::NCOPY];
       const float rh = sh.rho[code >> (C::BX + C::BE)];
       tv[0] = rh * n.x; tv[1] = rh * n.y; tv[2] = rh * n.z;
     }
@@ -316,6 +345,10 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
       const uint32_t nib = (k.sw[m >> 3] >> (4 * (m & 7))) & 15u;
       const float4 e = sh.lut[(m << 4) + nib];
       corr.x += e.x; corr.y += e.y; corr.z += e.z; corr.w += e.w;
+      // 8 reads in flight, each group summed before the next is read (the
+      // sums are pinned as live values here)
+      if (m % 8 == 7)
+        asm volatile("" : "+v"(corr.x), "+v"(corr.y), "+v"(corr.z), "+v"(corr.w) : : "memory");
     }
     r[0] = __builtin_fmaf(k.nu, corr.x, r[0]);
     r[1] = __builtin_fmaf(k.nu, corr.y, r[1]);
@@ -327,54 +360,73 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL>& sh,
 
 // Second half of the prologue shared by both single-query kernels: rotation,
 // tables, barrier (and the QJL nibble table).
-template <int D, int B, bool QJL>
+template <int D, int B, bool QJL, bool REP>
 __device__ __forceinline__ void sq_finish_prologue(const DecodeArgs& a, int hcount,
-                                                   const SQPre<D, B, QJL>& pre,
-                                                   SQShared<D, B, QJL>& sh) {
-  store_sq_tables<D, B, QJL>(pre, sh);
-  rotate_head<D, B, QJL>(a, hcount, pre, sh);
+                                                   const SQPre<D, B, QJL, REP>& pre,
+                                                   SQShared<D, B, QJL, REP>& sh) {
+  store_sq_tables<D, B, QJL, REP>(pre, sh);
+  rotate_head<D, B, QJL, REP>(a, hcount, pre, sh);
   __syncthreads();
   if constexpr (QJL) {
-    build_qjl_lut<D, B, QJL>(hcount, sh);
+    build_qjl_lut<D, B, QJL, REP>(hcount, sh);
     __syncthreads();
   }
 }
 
 // ---------------------------------------------------------------------------
-// Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 waves, each
-// a stream of 64-key tiles with the next tile's words loaded ahead.
+// Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 or 8 waves
+// (logits_waves), each a stream of 64-key tiles with the next tile's words
+// loaded ahead.
 // ---------------------------------------------------------------------------
 template <int D, int B, bool QJL>
-__global__ __launch_bounds__(256) void k_logits(DecodeArgs a) {
-  __shared__ SQShared<D, B, QJL> sh;
+__global__ __launch_bounds__(64 * logits_waves<B>())
+__attribute__((amdgpu_waves_per_eu(logits_waves<B>() / 2))) void k_logits(DecodeArgs a) {
+  // replicated table where it fits (conflict-free gathers); the 64 KiB it can
+  // take leaves room for two blocks per CU, so such blocks have 8 waves
+  constexpr bool REP = B <= 3;
+  constexpr int NW = logits_waves<B>();
+  __shared__ SQShared<D, B, QJL, REP> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
   const int g0 = blockIdx.z * 4;
   const int hcount = a.G - g0 < 4 ? a.G - g0 : 4;
   const int64_t ntile = (a.n_keys + kTile - 1) / kTile;
-  const int64_t stride = (int64_t)gridDim.x * 4;
-  int64_t t = (int64_t)blockIdx.x * 4 + wave;
-  SQPre<D, B, QJL> pre;
-  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
-  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
-  KTile<D, B, QJL> cur;
-  if (t < ntile) load_ktile<D, B, QJL>(a, seq, t, lane, cur);
+  if (ntile == 0) return;
+  const int64_t stride = (int64_t)gridDim.x * NW;
+  int64_t t = (int64_t)blockIdx.x * NW + wave;
+  SQPre<D, B, QJL, REP> pre;
+  sq_issue_prologue<D, B, QJL, REP, 64 * NW>(a, seq, g0, hcount, pre, sh);
+  sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
+  // PF tiles in flight per wave: with the replicated table a CU holds two
+  // blocks, so the bytes in flight come from depth, not from more waves.
+  // Loads are unconditional (a tile index past the end reads the last tile
+  // again), which keeps the compiler's memory-counter waits exact.
+  constexpr int PF = 1;
+  KTile<D, B, QJL> buf[PF];
+  const int64_t last = ntile - 1;
+#pragma unroll
+  for (int p = 0; p < PF; ++p) {
+    const int64_t tp = t + p * stride;
+    load_ktile<D, B, QJL>(a, seq, tp < last ? tp : last, lane, buf[p]);
+  }
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (; t < ntile; t += stride) {
-    KTile<D, B, QJL> nxt;
-    if (t + stride < ntile) load_ktile<D, B, QJL>(a, seq, t + stride, lane, nxt);
-    const floatx4 acc = tile_logits<D, B, QJL>(sh, cur, lane);
+    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, buf[0], lane);
+    const float gamma = buf[0].gamma;
+#pragma unroll
+    for (int p = 0; p + 1 < PF; ++p) buf[p] = buf[p + 1];
+    const int64_t tn = t + PF * stride;
+    load_ktile<D, B, QJL>(a, seq, tn < last ? tn : last, lane, buf[PF - 1]);
     const int64_t key = t * kTile + lane;
     if (key < a.n_keys) {
 #pragma unroll
       for (int h = 0; h < 4; ++h) {
         if (h < hcount) {
           const int64_t hq = kvh * a.G + g0 + h;
-          a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = cur.gamma * acc[h];
+          a.logits[(bidx * a.Hq + hq) * a.n_keys + key] = gamma * acc[h];
         }
       }
     }
-    cur = nxt;
   }
 }
 
@@ -423,7 +475,8 @@ template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(DecodeArgs a) {
   using VG = VGeom<D>;
   constexpr int NVL = VG::NVL;
-  __shared__ SQShared<D, B, QJL> sh;
+  constexpr bool REP = false;
+  __shared__ SQShared<D, B, QJL, REP> sh;
   // p of the tile per head, stored so that the 4 keys one MFMA block shares
   // are 4 consecutive floats; padded rows: the 4 heads hit different banks
   __shared__ __align__(16) float s_p[4][4][kTile + 4];
@@ -466,9 +519,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   const bool any = t < t_end;
   load_ktile<D, B, QJL>(a, any ? seq : 0, any ? t : 0, lane, cur);
   load_vtile<D>(any ? vlane : vlane0, any ? t : 0, vv);
-  SQPre<D, B, QJL> pre;
-  sq_issue_prologue<D, B, QJL>(a, seq, g0, hcount, pre, sh);
-  sq_finish_prologue<D, B, QJL>(a, hcount, pre, sh);
+  SQPre<D, B, QJL, REP> pre;
+  sq_issue_prologue<D, B, QJL, REP>(a, seq, g0, hcount, pre, sh);
+  sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
   // Decode step with append: the block whose split holds position n_keys - 1
   // encodes the sequence's new key with one wavefront (the same code and
   // rounding as the append encoder), the first head pass writes it to the
@@ -518,7 +571,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int j = 0; j < NVL; ++j)
         if (tt * kTile + VG::KPL * j + kq >= a.n_keys) vv[j] = make_uint4(0u, 0u, 0u, 0u);
     }
-    const floatx4 acc = tile_logits<D, B, QJL>(sh, kt, lane);
+    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, kt, lane);
     const int64_t key = tt * kTile + lane;
     const bool valid = key < a.n_keys;
     float al[4];
@@ -780,8 +833,11 @@ hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s) {
 
 template <int D, int B, bool QJL>
 static hipError_t logits_t(const DecodeArgs& a, int64_t n_seq, int nbx, hipStream_t s) {
-  hipLaunchKernelGGL((k_logits<D, B, QJL>), dim3(nbx, (unsigned)n_seq, (a.G + 3) / 4), dim3(256), 0,
-                     s, a);
+  // nbx counts 4-wave blocks; blocks of NW waves cover NW / 4 of them
+  constexpr int NW = logits_waves<B>();
+  const int nb = (nbx * 4 + NW - 1) / NW;
+  hipLaunchKernelGGL((k_logits<D, B, QJL>), dim3(nb, (unsigned)n_seq, (a.G + 3) / 4), dim3(64 * NW),
+                     0, s, a);
   return hipGetLastError();
 }
 

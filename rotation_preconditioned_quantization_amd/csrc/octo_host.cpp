@@ -257,13 +257,23 @@ octo_status build_device_tables(octo_codebook* cb) {
     }
   }
 
+  // S transposed (column-major S): the decode kernels form p = S q' with lane
+  // j reading element j of column c, one contiguous row of St per load.
+  std::vector<float> st;
+  if (!cb->S.empty()) {
+    const int d = cb->d;
+    st.resize(cb->S.size());
+    for (int j = 0; j < d; ++j)
+      for (int c = 0; c < d; ++c) st[(size_t)c * d + j] = cb->S[(size_t)j * d + c];
+  }
+
   // One device allocation, 256-byte aligned regions.
   struct Region { const void* src; size_t bytes; size_t off; };
   std::vector<Region> reg = {
       {dir.data(), dir.size() * 4, 0},           {rho.data(), rho.size() * 4, 0},
       {qx.t.data(), qx.t.size() * 4, 0},         {qe.t.data(), qe.t.size() * 4, 0},
       {qr2.t.data(), qr2.t.size() * 4, 0},
-      {cb->S.empty() ? nullptr : cb->S.data(), cb->S.size() * 4, 0},
+      {st.empty() ? nullptr : st.data(), st.size() * 4, 0},
       {trip.empty() ? nullptr : trip.data(), trip.size() * 4, 0},
       {s16.empty() ? nullptr : s16.data(), s16.size() * 2, 0}};
   size_t total = 0;
@@ -304,7 +314,7 @@ octo_status build_device_tables(octo_codebook* cb) {
   t.qx = qt(qx, 2);
   t.qe = qt(qe, 3);
   t.qr2 = qt(qr2, 4);
-  t.S = cb->S.empty() ? nullptr : (const float*)(base + reg[5].off);
+  t.St = st.empty() ? nullptr : (const float*)(base + reg[5].off);
   t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[6].off);
   t.S16 = s16.empty() ? nullptr : (const uint4*)(base + reg[7].off);
   for (int k = 0; k < 8; ++k) t.sign_bits[k] = cb->sign_bits[k];

@@ -34,8 +34,8 @@ struct DevTables {
   const float4* dirtab;     // 2^(b_xi+b_eta) unit directions, index i_xi | i_eta << b_xi
   const float4* trip_tab;   // 2^B_t triplets rho^ n^ by full code (only for B_t <= 10)
   const float* rho_tab;     // 2^b_rho rho centroids
-  const float* S;           // QJL matrix d x d row-major (nullptr without QJL)
-  const uint4* S16;         // the same as f16 planes [S_hi | S_lo], S_hi = f16(S), S_lo = f16(S - S_hi)
+  const float* St;          // QJL matrix S transposed, St[c * d + j] = S[j][c] (nullptr without QJL)
+  const uint4* S16;         // S (row-major) as f16 planes [S_hi | S_lo], S_hi = f16(S), S_lo = f16(S - S_hi)
   uint32_t sign_bits[8];    // bit j of the 256-bit mask set <=> WHT sign s_j = -1
 };
 
