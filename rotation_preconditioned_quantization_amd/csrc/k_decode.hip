@@ -94,24 +94,23 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 
 // LDS of the single-query kernels.  kCombined: for up to 10 bits per triplet
 // one float4 per triplet code holds rho^ n^ directly; otherwise unit
-// directions per (i_xi, i_eta) plus the rho centroids.  REP (up to 8 bits of
-// direction): the table is held in 16 copies, entry e of copy c at float4
-// slot 16 e + c, and lane l reads copy l % 16, so the 16 lanes the LDS serves
-// in one pass hit 16 different 4-bank groups whatever codes they look up:
-// random gathers then run conflict-free (4 LDS cycles per wavefront read
-// instead of about 11).  With REP at 3 bits the 1024-entry combined table
-// would not fit 16 times, so the directions are replicated and rho^ is a
-// separate 4-entry (conflict-free) read.  q holds the rotated queries of the
-// (up to) 4 heads of this pass, rows padded with zeros; with QJL, qp holds
-// p = sqrt(pi/2)/d S q' and lut its nibble sums.
+// directions per (i_xi, i_eta) plus the rho centroids.  REP (up to 10 bits per
+// triplet): the combined table is held in NCOPY copies (as many as fit
+// 64 KiB, at most 16), entry e of copy c at float4 slot NCOPY e + c, and lane
+// l reads copy l % NCOPY.  The LDS serves 16 lanes per pass; with 16 copies
+// they hit 16 different 4-bank groups whatever codes they look up, so random
+// gathers are conflict-free (4 LDS cycles per wavefront read instead of about
+// 11); with 4 copies (the 1024-entry table at 3 bits) only the 4 lanes of a
+// copy can collide.  q holds the rotated queries of the (up to) 4 heads of
+// this pass, rows padded with zeros; with QJL, qp holds p = sqrt(pi/2)/d S q'
+// and lut its nibble sums.
 template <int D, int B, bool QJL, bool REP>
 struct SQShared {
   using C = Codec<D, B>;
-  static constexpr bool kRepComb = REP && (1 << C::BT) <= 128;
-  static constexpr bool kCombined = REP ? kRepComb : C::BT <= 10;
+  static_assert(!REP || C::BT <= 10, "replicated table needs the combined table");
+  static constexpr bool kCombined = C::BT <= 10;
   static constexpr int NENT = kCombined ? (1 << C::BT) : C::NDIR;
-  static constexpr int NCOPY = REP ? 16 : 1;
-  static_assert(!REP || NENT <= 256, "replicated code table larger than 64 KiB");
+  static constexpr int NCOPY = !REP ? 1 : (4096 / NENT < 16 ? 4096 / NENT : 16);
   static constexpr int QD = ((3 * C::T + 3) / 4) * 4;
   float4 tab[NENT * NCOPY];
   float rho[C::LR];
@@ -120,9 +119,6 @@ struct SQShared {
   float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
-// Values the block prologue loads from global memory besides the LDS tables
-// (which go to LDS directly): wave w's query head g0 + w (lane l holds the
-// 32-bit words of elements l + 64 k) and the rho centroids.
 // Waves per k_logits block: 8 with the replicated table (B <= 3), else 4.
 template <int B>
 constexpr int logits_waves() { return B <= 3 ? 8 : 4; }
@@ -375,8 +371,7 @@ __device__ __forceinline__ void sq_finish_prologue(const DecodeArgs& a, int hcou
 
 // ---------------------------------------------------------------------------
 // Logits.  grid = (blocks over key tiles, n_seq, ceil(G / 4)); 4 or 8 waves
-// (logits_waves), each a stream of 64-key tiles with the next tile's words
-// loaded ahead.
+// (logits_waves), each a stream of 64-key tiles.
 // ---------------------------------------------------------------------------
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(64 * logits_waves<B>())
@@ -397,26 +392,16 @@ __attribute__((amdgpu_waves_per_eu(logits_waves<B>() / 2))) void k_logits(Decode
   SQPre<D, B, QJL, REP> pre;
   sq_issue_prologue<D, B, QJL, REP, 64 * NW>(a, seq, g0, hcount, pre, sh);
   sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
-  // PF tiles in flight per wave: with the replicated table a CU holds two
-  // blocks, so the bytes in flight come from depth, not from more waves.
-  // Loads are unconditional (a tile index past the end reads the last tile
-  // again), which keeps the compiler's memory-counter waits exact.
-  constexpr int PF = 1;
-  KTile<D, B, QJL> buf[PF];
-  const int64_t last = ntile - 1;
-#pragma unroll
-  for (int p = 0; p < PF; ++p) {
-    const int64_t tp = t + p * stride;
-    load_ktile<D, B, QJL>(a, seq, tp < last ? tp : last, lane, buf[p]);
-  }
+  // One tile at a time.  The kernel is bound by instruction issue (the 4x4x1
+  // MFMAs and the code extraction), and 16 waves per CU hide the load
+  // latency: loading one or two tiles ahead measured slower (more
+  // registers, fewer waves).
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (; t < ntile; t += stride) {
-    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, buf[0], lane);
-    const float gamma = buf[0].gamma;
-#pragma unroll
-    for (int p = 0; p + 1 < PF; ++p) buf[p] = buf[p + 1];
-    const int64_t tn = t + PF * stride;
-    load_ktile<D, B, QJL>(a, seq, tn < last ? tn : last, lane, buf[PF - 1]);
+    KTile<D, B, QJL> kt;
+    load_ktile<D, B, QJL>(a, seq, t, lane, kt);
+    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, kt, lane);
+    const float gamma = kt.gamma;
     const int64_t key = t * kTile + lane;
     if (key < a.n_keys) {
 #pragma unroll
