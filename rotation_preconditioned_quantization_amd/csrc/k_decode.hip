@@ -123,6 +123,9 @@ struct SQShared {
 template <int B>
 constexpr int logits_waves() { return B <= 3 ? 8 : 4; }
 
+// Values the block prologue loads from global memory besides the LDS tables
+// (which go to LDS directly): wave w's query head g0 + w (lane l holds the
+// 32-bit words of elements l + 64 k) and the rho centroids.
 template <int D, int B, bool QJL, bool REP>
 struct SQPre {
   float rho;
