@@ -299,7 +299,7 @@ def test_logits_gqa_ragged(G):
     check_logits(cfg, 2, 2, G, 333, 384, seed=G, label=f"gqa{G}")
 
 
-@pytest.mark.parametrize("d,b", [(64, 3), (128, 2), (128, 1), (128, 5), (64, 5), (64, 1), (64, 2)])
+@pytest.mark.parametrize("d,b", [(64, 3), (128, 2), (128, 1), (128, 5), (64, 5), (64, 1), (64, 2), (64, 4)])
 def test_logits_other_shapes(d, b):
     cfg = WL.CONFIGS[3].scaled(d=d, b=b)
     check_logits(cfg, 1, 2, 4, 700, 768, seed=5, label=f"d{d}b{b}")
@@ -315,7 +315,7 @@ def test_logits_qjl_d64():
     check_logits(cfg, 1, 1, 2, 200, 256, seed=2, qjl=True, label="qjl-d64")
 
 
-@pytest.mark.parametrize("d,b", [(128, 1), (128, 5), (64, 5), (128, 2), (64, 2), (64, 1)])
+@pytest.mark.parametrize("d,b", [(128, 1), (128, 5), (64, 5), (128, 2), (64, 2), (64, 1), (128, 4), (64, 4)])
 def test_logits_qjl_wider_bit_budgets(d, b):
     cfg = WL.CONFIGS[5].scaled(d=d, b=b)
     check_logits(cfg, 1, 1, 2, 200, 256, seed=3 + b, qjl=True, label=f"qjl-d{d}b{b}")
