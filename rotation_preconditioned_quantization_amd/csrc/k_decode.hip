@@ -463,7 +463,9 @@ template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(DecodeArgs a) {
   using VG = VGeom<D>;
   constexpr int NVL = VG::NVL;
-  constexpr bool REP = false;
+  // replicated code table where it costs at most 32 KiB (b <= 2): about 1 %
+  // at the extreme workload's shape; at b = 3 and 4 it measured no faster
+  constexpr bool REP = B <= 2;
   __shared__ SQShared<D, B, QJL, REP> sh;
   // p of the tile per head, stored so that the 4 keys one MFMA block shares
   // are 4 consecutive floats; padded rows: the 4 heads hit different banks
