@@ -1,22 +1,27 @@
 #!/usr/bin/env python3
 """Benchmark: fused compressed-K decode GB/s (% of HBM peak) + encode Mkeys/s, d=128.
 
-Workload (one GPU): the LLM-decode shape -- batch 1, 32 query heads over 8 KV
-heads, head dim 128, 32768 cached keys per KV head, b = 4 (13 bits per
-triplet), bf16 keys with 4 outlier channels x10, bf16 values, one bf16 query
-token.  Synthetic seeded inputs stand in for the pages' model KV caches.
+Default workload (one GPU): the extreme-compression shape -- batch 4, 32
+query heads over 8 KV heads, head dim 128, 131072 cached keys per KV head,
+b = 2 (7 bits per triplet), bf16 Student-t(5) keys with log-normal per-token
+norms, bf16 values, one bf16 query token: 1248 MB of compressed K and V per
+decode, the largest d = 128 decode that fits one GPU.  Synthetic seeded
+inputs stand in for the pages' model KV caches.  --config selects the other
+workloads (2: the LLM-decode shape, 32768 keys per KV head at b = 4).
 
-One step = the whole hot path over one batch: encode the 262144 keys of the
-cache (octo_encode) and run the fused decode attention over it
-(octo_decode_attn: query rotation, split-K fused kernel, combine).  Inputs
-sit in HBM before the timed region; R rotating copies of every buffer
-(> 1 GiB in total) keep each step's reads out of the 256 MB Infinity Cache.
-Each step is captured once into a HIP graph and replayed.
+One step = the whole hot path over one batch: encode every key of the cache
+(octo_encode) and run the fused decode attention over it (octo_decode_attn:
+split-K fused kernel, combine).  Inputs sit in HBM before the timed region;
+R rotating copies of every buffer (>= 1 GiB in total) keep each step's reads
+out of the 256 MB Infinity Cache.  Each step is captured once into a HIP
+graph and replayed.
 
 Prints one JSON line.  `value` is the decode throughput (algorithmic bytes of
 packed K + gamma + V per decode call / its time); `roofline` prices the
-dominant kernel (the fused attention kernel) against 8 TB/s; `cpu_baseline`
-times the fp64 oracle on a bounded sample on the host cores.
+dominant kernel (the fused attention kernel) against 8 TB/s, with `traffic`
+from the committed rocprofv3 counter summary of that workload; `cpu_baseline`
+times the fp64 oracle on a bounded sample of the same workload on the host
+cores.
 """
 from __future__ import annotations
 
@@ -46,15 +51,42 @@ WORKLOADS = {
     5: "qjl: B=8, Hq=32, Hkv=8, d=128, 65536 keys/KV head, b=3 + 1-bit QJL residual signs, "
        "1 query token (logits)",
 }
-PROFILE_COUNTERS = os.path.join(ROOT, "profiles", "llm_decode_hbm_traffic.txt")
+# committed HBM-traffic summaries (rocprofv3 FETCH_SIZE / WRITE_SIZE passes of
+# `bench.py --counters --config N`), one per workload
+TRAFFIC_PROFILE = {c: os.path.join(ROOT, "profiles", f"{n}_hbm_traffic.txt") for c, n in
+                   {1: "toy", 2: "llm_decode", 3: "extreme", 4: "video_block", 5: "qjl"}.items()}
+# sources of the decode kernels whose counters a summary holds
+KERNEL_SOURCES = {"attn": ("k_decode.hip", "octo_device.hpp", "octo_internal.hpp", "octo_encode_dev.hpp"),
+                  "logits": ("k_decode.hip", "octo_device.hpp", "octo_internal.hpp", "octo_encode_dev.hpp"),
+                  "attn_mq": ("k_mq.hip", "octo_device.hpp", "octo_internal.hpp")}
+MAIN_KERNEL = {"logits": "k_logits", "attn": "k_attn", "attn_mq": "k_mq_attn"}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(mode: str) -> str:
     h = hashlib.sha256()
-    for f in ("k_decode.hip", "octo_device.hpp", "octo_internal.hpp"):
+    for f in KERNEL_SOURCES[mode]:
         with open(os.path.join(ROOT, "rotation_preconditioned_quantization_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
+
+
+def profiled_traffic(cfg):
+    """HBM bytes per launch of the workload's dominant decode kernel from its
+    committed counter summary, or None when there is none or the kernel's
+    sources changed since the counters were taken."""
+    path = TRAFFIC_PROFILE.get(cfg.cid)
+    if not path or not os.path.exists(path):
+        return None
+    pc = {}
+    with open(path) as f:
+        for ln in f:
+            if ":" in ln and not ln.startswith(("#", "|", "command")):
+                k, v = ln.split(":", 1)
+                pc[k.strip()] = v.strip()
+    if pc.get("kernel_source_hash") != kernel_source_hash(cfg.mode):
+        return None
+    v = pc.get(f"{MAIN_KERNEL[cfg.mode]}.hbm_bytes_per_launch")
+    return int(float(v)) if v else None
 
 
 def algorithmic_bytes(cfg, lay):
@@ -80,50 +112,75 @@ def algorithmic_bytes(cfg, lay):
 
 
 def cpu_baseline(cfg, seconds: float):
-    """The oracle as it stands, on a bounded sample of the same workload."""
+    """The oracle as it stands, on a bounded sample of the same workload: one
+    KV head (one head for the multi-query shape) of the workload's keys,
+    values and queries, encoded and decoded in fp64 NumPy on the host cores
+    (BLAS threads = the cores this process may run on) until `seconds` have
+    passed.  The value is the decode's algorithmic bytes per second, the same
+    per-key bytes as the GPU row."""
     import numpy as np
-    import torch
 
     import oracle as O
     import workloads as WL
+    cores = len(os.sched_getaffinity(0))
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:
-        threads = 1
+        from threadpoolctl import threadpool_limits
+        limiter = threadpool_limits(limits=cores)
+    except Exception:  # threadpoolctl absent: BLAS keeps its own default
+        limiter = None
     cb = O.build_codebook(cfg.d, cfg.b)            # setup, not timed
-    n_keys = 8192
-    keys = WL.make_keys(cfg, "cpu", seed=7, n_seq=1, n=n_keys)[0].float().numpy().astype(np.float64)
-    v = WL.make_values(cfg, "cpu", seed=7, n_seq=1, cap=n_keys)[0].float().numpy().astype(np.float64)
-    q = WL.make_queries(cfg, "cpu", seed=7)[0, : cfg.G, 0].float().numpy().astype(np.float64)
+    S = O.qjl_matrix(cfg.d, 0) if cfg.qjl else None
+    n_keys = min(8192, cfg.N)
+    f64 = lambda t: t.float().numpy().astype(np.float64)  # noqa: E731
+    keys = f64(WL.make_keys(cfg, "cpu", seed=7, n_seq=1, n=n_keys)[0])
+    qs = f64(WL.make_queries(cfg, "cpu", seed=7)[0])          # [Hq, n_q, d]
+    if cfg.mode == "attn_mq":
+        q, heads = qs[0], 1                                    # 256 queries of one head
+    else:
+        q, heads = qs[: cfg.G, 0], cfg.G                       # the G heads of one KV head
+    v = None if cfg.mode == "logits" else f64(WL.make_values(cfg, "cpu", seed=7, n_seq=1, cap=n_keys)[0])
     t_enc = t_dec = 0.0
     reps = 0
     t_start = time.perf_counter()
     while True:
         t0 = time.perf_counter()
         enc = O.encode(keys, cb)
+        qe = O.qjl_encode(enc.rotated, O.decode_rotated(enc.codes, cb), S) if cfg.qjl else None
         t1 = time.perf_counter()
-        uh = O.decode_rotated(enc.codes, cb)
-        for h in range(cfg.G):
-            lg = O.logits_rotated(q[h], uh, enc.gamma, cb)
-            O.softmax_attention(lg / math.sqrt(cfg.d), v)
+        uh = O.decode_rotated(enc.codes, cb)                   # the decode starts from the codes
+        if cfg.mode == "logits":
+            for h in range(heads):
+                (O.qjl_logits(q[h], uh, enc.gamma, qe, S, cb) if cfg.qjl
+                 else O.logits_rotated(q[h], uh, enc.gamma, cb))
+        elif cfg.mode == "attn_mq":
+            O.softmax_attention(O.logits_rotated(q, uh, enc.gamma, cb) / math.sqrt(cfg.d), v)
+        else:
+            for h in range(heads):
+                O.softmax_attention(O.logits_rotated(q[h], uh, enc.gamma, cb) / math.sqrt(cfg.d), v)
         t2 = time.perf_counter()
         t_enc += t1 - t0
         t_dec += t2 - t1
         reps += 1
         if time.perf_counter() - t_start > seconds:
             break
-    lay_bits = O.n_triplets(cfg.d) * sum(O.default_alloc(cfg.b)) / 8.0
-    dec_bytes = reps * n_keys * (lay_bits + 4.0 + 2.0 * cfg.d)
+    if limiter is not None:
+        limiter.unregister()
+    per_key = O.n_triplets(cfg.d) * sum(O.default_alloc(cfg.b)) / 8.0 + 4.0
+    if cfg.qjl:
+        per_key += cfg.d / 8.0 + 2.0
+    per_key += 4.0 * heads if cfg.mode == "logits" else 2.0 * cfg.d
+    dec_bytes = reps * n_keys * per_key
+    what = {"logits": f"{heads} query heads' logits" + (" with the QJL term" if cfg.qjl else ""),
+            "attn": f"{heads} query heads' softmax.V",
+            "attn_mq": f"{q.shape[0]} queries' softmax.V"}[cfg.mode]
     return {
         "value": dec_bytes / t_dec / 1e9,
         "unit": "GB/s",
-        "cores": int(threads),
+        "cores": cores,
         "kind": "oracle",
-        "sample": (f"1 KV head x {n_keys} keys x {cfg.G} query heads of the LLM-decode workload, "
-                   f"{reps} repetitions ({t_enc + t_dec:.1f} s): fp64 decode attention "
-                   f"{dec_bytes / t_dec / 1e9:.4f} GB/s; fp64 encode "
-                   f"{reps * n_keys / t_enc / 1e6:.4f} Mkeys/s"),
+        "sample": (f"1 {'head' if cfg.mode == 'attn_mq' else 'KV head'} x {n_keys} keys of the "
+                   f"{cfg.name} workload, {what}, {reps} repetitions ({t_enc + t_dec:.1f} s): fp64 decode "
+                   f"{dec_bytes / t_dec / 1e9:.4f} GB/s; fp64 encode {reps * n_keys / t_enc / 1e6:.4f} Mkeys/s"),
         "encode_mkeys_per_s": reps * n_keys / t_enc / 1e6,
     }
 
@@ -241,9 +298,10 @@ def main():
     ap.add_argument("--counters", action="store_true",
                     help="counter-collection run for rocprofv3 --pmc: per step a plain copy "
                          "kernel of 64 MiB (the counter scale), then encode and decode, eagerly")
-    ap.add_argument("--config", type=int, default=2, choices=sorted(WORKLOADS),
-                    help="workload (2 = the LLM-decode shape the metric is quoted on; the "
-                         "others are the remaining shapes of the pages' workloads)")
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS),
+                    help="workload (3 = the extreme-compression shape, the largest d = 128 decode "
+                         "on one GPU, which the headline is quoted on; the others are the "
+                         "remaining shapes of the pages' workloads)")
     ap.add_argument("--head-dim", type=int, default=0, choices=(0, 64, 128, 256),
                     help="override the workload's head dim (0: keep it)")
     ap.add_argument("--bits", type=int, default=0, choices=(0, 1, 2, 3, 4, 5),
@@ -338,7 +396,7 @@ def main():
         torch.cuda.synchronize()
         print(json.dumps({"counters_run": True, "steps": args.steps, "config": args.config,
                           "copy_bytes_each_way": 64 << 20,
-                          "kernel_source_hash": kernel_source_hash()}), flush=True)
+                          "kernel_source_hash": kernel_source_hash(cfg.mode)}), flush=True)
         return
 
     # eager warm-up (the prefix of a chunked cache is encoded once here) and
@@ -446,16 +504,7 @@ def main():
 
     dec_gbs = dec_bytes / t_dec / 1e9
     main_gbs = dec_bytes / t_main / 1e9
-    traffic = None
-    if os.path.exists(PROFILE_COUNTERS) and args.config == 2 and not (args.head_dim or args.bits):
-        pc = {}
-        with open(PROFILE_COUNTERS) as f:
-            for ln in f:
-                if ":" in ln and not ln.startswith(("#", "|", "command")):
-                    k, v = ln.split(":", 1)
-                    pc[k.strip()] = v.strip()
-        if pc.get("kernel_source_hash") == kernel_source_hash():
-            traffic = int(float(pc["k_attn.hbm_bytes_per_launch"]))
+    traffic = None if (args.head_dim or args.bits) else profiled_traffic(cfg)
     kernel_name = {"logits": "k_logits (fused compressed-K logits)",
                    "attn": "k_attn (fused decode attention)",
                    "attn_mq": "k_mq_attn (multi-query MFMA attention)"}[cfg.mode]
@@ -468,7 +517,7 @@ def main():
         tf = flops / t_main / 1e12
         roofline = {"bound": "mfma", "kernel": kernel_name, "achieved": round(tf, 2),
                     "peak": MFMA_F16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                    "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac": round(tf / MFMA_F16_PEAK_TFLOPS, 4), "traffic": traffic,
                     "kernel_us": round(t_main * 1e6, 3), "algorithmic_flops_per_launch": int(flops),
                     "hbm_gbs": round(main_gbs, 2)}
 
@@ -503,7 +552,7 @@ def main():
     }
     if cfg.qjl and not args.no_qjl_bias:
         line["qjl_bias"] = qjl_bias_study(cfg, dev)
-    if not args.no_cpu_baseline and args.config == 2 and not (args.head_dim or args.bits):
+    if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(cfg, args.cpu_seconds)
     print(json.dumps(line), flush=True)
 

@@ -123,6 +123,51 @@ octo_status octo_codebook_layout(const octo_codebook* cb, octo_layout* out);
 octo_status octo_codebook_export(const octo_codebook* cb, double* c_xi, double* c_eta,
                                  double* c_rho, int8_t* signs, float* qjl_S);
 
+/* The codebook tables that kernels copy from global memory into LDS. */
+typedef enum {
+  OCTO_TABLE_DIR = 0,  /* unit directions by (i_xi, i_eta): 16-byte entries    */
+  OCTO_TABLE_TRIP = 1, /* rho^ n^ by triplet code (B_t <= 10 only): 16 bytes  */
+  OCTO_TABLE_RHO = 2,  /* rho centroids: 4-byte entries                        */
+  OCTO_TABLE_QX = 3,   /* encoder bucket table of xi: 8-byte entries          */
+  OCTO_TABLE_QE = 4,   /* encoder bucket table of eta                          */
+  OCTO_TABLE_QR2 = 5,  /* encoder bucket table of rho^2                        */
+  OCTO_TABLE_S16 = 6,  /* QJL matrix as f16 high/low planes: 16-byte entries  */
+  OCTO_TABLE_COUNT = 7
+} octo_table;
+
+/* Entries of table `table` (octo_table) in the codebook's tables, device or
+ * host-only (a host-only codebook computes the same tables without uploading
+ * them); 0 for a table the codebook has no use for, -1 for a bad argument.
+ * The device allocation ends with 1 KiB of zeros past the last table. */
+int64_t octo_codebook_table_entries(const octo_codebook* cb, int table);
+
+/* Bounds-check aid: one copy of a codebook table into LDS as a kernel
+ * instantiation performs it, enumerated by index 0, 1, ... (returns
+ * OCTO_ERR_INVALID_ARG past the last).  The figures come from the same
+ * compile-time constants as the copy loops (which static_assert them):
+ *   kernel, d, b, qjl   the kernel template and instantiation (string owned
+ *                       by the library);
+ *   table               the octo_table read;
+ *   lds_slots           entries the LDS destination holds;
+ *   slots_written       1 + the highest LDS entry the copy can write;
+ *   entries_read        1 + the highest table entry it can read, or -1 for
+ *                       a loop bounded by the table's own entry count at
+ *                       run time (then that count must fit lds_slots);
+ *   copied              entries moved, one per thread per round (-1 with
+ *                       a run-time bound);
+ *   threads, masked     threads sharing the copy; 1 when the copy bounds
+ *                       each lane (needed when threads does not divide
+ *                       copied).
+ * A copy is in bounds when slots_written <= lds_slots and entries_read <=
+ * octo_codebook_table_entries of the codebook it runs with. */
+typedef struct {
+  const char* kernel;
+  int d, b, qjl, table;
+  int64_t lds_slots, slots_written, entries_read, copied;
+  int threads, masked;
+} octo_lds_copy;
+octo_status octo_debug_lds_copy(int index, octo_lds_copy* out);
+
 /* Bytes of the packed stream for n_seq sequences of capacity cap (cap % 64 == 0). */
 size_t octo_packed_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap);
 size_t octo_qjl_bits_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap);

@@ -10,7 +10,6 @@ importing works without it, but every call then raises.
 from __future__ import annotations
 
 import ctypes
-import math
 import os
 from dataclasses import dataclass
 
@@ -43,6 +42,15 @@ class octo_layout(ctypes.Structure):
         [("packed_bytes_per_key_alloc", ctypes.c_size_t)]
 
 
+class octo_lds_copy(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_char_p), ("d", ctypes.c_int), ("b", ctypes.c_int),
+                ("qjl", ctypes.c_int), ("table", ctypes.c_int), ("lds_slots", ctypes.c_int64),
+                ("slots_written", ctypes.c_int64), ("entries_read", ctypes.c_int64),
+                ("copied", ctypes.c_int64), ("threads", ctypes.c_int), ("masked", ctypes.c_int)]
+
+
+TABLES = ("dir", "trip", "rho", "qx", "qe", "qr2", "s16")   # octo_table order
+
 _lib = None
 
 _P, _I, _I64, _SZ, _F = ctypes.c_void_p, ctypes.c_int, ctypes.c_int64, ctypes.c_size_t, ctypes.c_float
@@ -67,6 +75,8 @@ _SIGS = {
                                      _F, _P, _P, _SZ, _P, _I]),
     "octo_debug_reconstruct": (_I, [_P, _P, _P, _I64, _I64, _I64, _P, _P]),
     "octo_debug_copy": (_I, [_P, _P, _SZ, _P]),
+    "octo_codebook_table_entries": (_I64, [_P, _I]),
+    "octo_debug_lds_copy": (_I, [_I, _P]),
     "octo_status_str": (ctypes.c_char_p, [_I]),
     "octo_last_error": (ctypes.c_char_p, []),
 }
@@ -112,6 +122,37 @@ def _stream(stream=None):
     import torch
     s = stream if stream is not None else torch.cuda.current_stream()
     return ctypes.c_void_p(s.cuda_stream)
+
+
+def _need(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _need_cuda(**tensors):
+    """Checked last, after the shapes: every tensor a kernel reads or writes
+    must be device memory (the C ABI receives bare pointers)."""
+    for name, t in tensors.items():
+        if t is not None and not t.is_cuda:
+            raise ValueError(f"{name} must be a CUDA tensor")
+
+
+def _need_dtype(t, name: str):
+    import torch
+    _need(t.dtype in (torch.float32, torch.bfloat16, torch.float16),
+          f"{name} must be float32, bfloat16 or float16, not {t.dtype}")
+
+
+def _need_out(t, shape, name: str):
+    import torch
+    _need(tuple(t.shape) == tuple(shape), f"{name} must have shape {tuple(shape)}, not {tuple(t.shape)}")
+    _need(t.dtype == torch.float32 and t.is_contiguous(), f"{name} must be contiguous float32")
+
+
+def _need_cache(cb, cache, n_seq: int, what: str):
+    _need(cache.cb is cb or cache.packed.numel() == cb.packed_words(cache.n_seq, cache.cap),
+          "the cache was laid out for another codebook")
+    _need(n_seq == cache.n_seq, f"{what} ({n_seq}) must equal cache.n_seq ({cache.n_seq})")
 
 
 @dataclass
@@ -173,6 +214,10 @@ class Codebook:
                "octo_codebook_export")
         return cx, ce, cr, sg, S
 
+    def table_entries(self, table: int) -> int:
+        """Entries of codebook table `table` (index into TABLES)."""
+        return lib().octo_codebook_table_entries(self.handle, table)
+
     # sizes ---------------------------------------------------------------
     def packed_words(self, n_seq: int, cap: int) -> int:
         return lib().octo_packed_bytes(self.handle, n_seq, cap) // 4
@@ -202,9 +247,15 @@ class Cache:
 
 
 def _encode(fn, name, cb: Codebook, keys, cache: Cache, pos0: int, stream):
+    _need(keys.dim() == 3, "keys must be [n_seq, n_new, d]")
     n_seq, n_new, d = keys.shape
-    if d != cb.d or keys.stride(2) != 1:
-        raise ValueError("keys must be [n_seq, n_new, d] with a contiguous last dim")
+    _need(d == cb.d and keys.stride(2) == 1, "keys must be [n_seq, n_new, d] with a contiguous last dim")
+    _need_dtype(keys, "keys")
+    _need_cache(cb, cache, n_seq, "keys.shape[0]")
+    _need(0 <= pos0 and pos0 + n_new <= cache.cap,
+          f"positions {pos0}..{pos0 + n_new - 1} exceed the cache capacity {cache.cap}")
+    _need_cuda(keys=keys, packed=cache.packed, gamma=cache.gamma, qjl_bits=cache.qjl_bits,
+               qjl_norm=cache.qjl_norm)
     _check(fn(cb.handle, _ptr(keys), _dtype_code(keys), n_seq, n_new, keys.stride(0),
               keys.stride(1), pos0, cache.cap, _ptr(cache.packed), _ptr(cache.gamma),
               _ptr(cache.qjl_bits), _ptr(cache.qjl_norm), _stream(stream)), name)
@@ -225,7 +276,29 @@ def _workspace(cb, mode, B, Hq, Hkv, n_q, n_keys, workspace, device):
     need = cb.workspace_bytes(mode, B, Hq, Hkv, n_q, n_keys)
     if workspace is None:
         workspace = torch.zeros(max(need, 256), dtype=torch.uint8, device=device)
+    _need(workspace.dtype == torch.uint8 and workspace.is_contiguous(),
+          "workspace must be a contiguous uint8 tensor")
+    _need(workspace.numel() >= need, f"workspace holds {workspace.numel()} bytes, {need} needed")
     return workspace, need
+
+
+def _need_decode(cb, q, cache, B, Hq, Hkv, n_keys, qjl):
+    _need(q.shape[-1] == cb.d, f"q's last dim ({q.shape[-1]}) must be the head dim {cb.d}")
+    _need_dtype(q, "q")
+    _need(q.is_contiguous(), "q must be contiguous")
+    _need(Hkv > 0 and Hq % Hkv == 0, f"Hq ({Hq}) must be a multiple of Hkv ({Hkv})")
+    _need_cache(cb, cache, B * Hkv, "B * Hkv")
+    _need(0 <= n_keys <= cache.cap, f"n_keys ({n_keys}) must lie in [0, cache.cap = {cache.cap}]")
+    if qjl:
+        _need(cb.qjl and cache.qjl_bits is not None and cache.qjl_norm is not None,
+              "the QJL term needs a QJL codebook and a cache with QJL buffers")
+
+
+def _need_values(v, cache, d):
+    import torch
+    _need(v is not None and tuple(v.shape) == (cache.n_seq, cache.cap, d),
+          f"v must have shape (n_seq, cap, d) = {(cache.n_seq, cache.cap, d)}")
+    _need(v.dtype == torch.bfloat16 and v.is_contiguous(), "v must be contiguous bfloat16")
 
 
 def octo_decode_logits(cb: Codebook, q, cache: Cache, n_keys: int, Hkv: int, logits=None,
@@ -233,13 +306,15 @@ def octo_decode_logits(cb: Codebook, q, cache: Cache, n_keys: int, Hkv: int, log
                        stages: int = STAGE_ALL):
     """q: [B, Hq, d]; returns fp32 logits [B, Hq, n_keys] (raw <q, k^>)."""
     import torch
+    _need(q.dim() == 3, "q must be [B, Hq, d]")
     B, Hq, d = q.shape
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    _need_decode(cb, q, cache, B, Hq, Hkv, n_keys, qjl)
     if logits is None:
         logits = torch.empty((B, Hq, n_keys), dtype=torch.float32, device=q.device)
+    _need_out(logits, (B, Hq, n_keys), "logits")
     workspace, _ = _workspace(cb, 0, B, Hq, Hkv, 1, n_keys, workspace, q.device)
-    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
+    _need_cuda(q=q, logits=logits, packed=cache.packed, workspace=workspace)
     _check(lib().octo_decode_logits_stages(cb.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv,
                                            _ptr(cache.packed), _ptr(cache.gamma),
                                            _ptr(cache.qjl_bits) if qjl else None,
@@ -257,13 +332,16 @@ def octo_decode_attn(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, ou
 
     ``stages`` selects a subset of the launches (octo_decode_attn_stages)."""
     import torch
+    _need(q.dim() == 4, "q must be [B, Hq, n_q, d]")
     B, Hq, n_q, d = q.shape
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    _need_decode(cb, q, cache, B, Hq, Hkv, n_keys, qjl)
+    _need_values(v, cache, d)
     if out is None:
         out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q.device)
+    _need_out(out, (B, Hq, n_q, d), "out")
     workspace, _ = _workspace(cb, 1, B, Hq, Hkv, n_q, n_keys, workspace, q.device)
-    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
+    _need_cuda(q=q, v=v, out=out, packed=cache.packed, workspace=workspace)
     _check(lib().octo_decode_attn_stages(cb.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, n_q,
                                          _ptr(cache.packed), _ptr(cache.gamma),
                                          _ptr(cache.qjl_bits) if qjl else None,
@@ -280,18 +358,23 @@ def octo_decode_attn_append(cb: Codebook, new_keys, q, cache: Cache, v, n_keys: 
     """One decode step: encode new_keys [B*Hkv, d] (or [B*Hkv, 1, d]) at cache
     position n_keys - 1, then attend q [B, Hq, 1, d] over the n_keys keys."""
     import torch
+    _need(q.dim() == 4, "q must be [B, Hq, 1, d]")
     B, Hq, n_q, d = q.shape
-    if n_q != 1:
-        raise ValueError("one query token per head")
+    _need(n_q == 1, "one query token per head")
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    _need_decode(cb, q, cache, B, Hq, Hkv, n_keys, qjl)
+    _need(n_keys >= 1, "the step appends at position n_keys - 1: n_keys >= 1")
+    _need(new_keys.numel() == B * Hkv * d and new_keys.shape[0] == B * Hkv and new_keys.shape[-1] == d,
+          f"new_keys must be [B * Hkv, d] = [{B * Hkv}, {d}] (or [B * Hkv, 1, d])")
+    _need_dtype(new_keys, "new_keys")
     nk = new_keys.reshape(new_keys.shape[0], d)
-    if nk.stride(1) != 1:
-        raise ValueError("new_keys must have a contiguous last dim")
+    _need(nk.stride(1) == 1, "new_keys must have a contiguous last dim")
+    _need_values(v, cache, d)
     if out is None:
         out = torch.empty((B, Hq, 1, d), dtype=torch.float32, device=q.device)
+    _need_out(out, (B, Hq, 1, d), "out")
     workspace, _ = _workspace(cb, 1, B, Hq, Hkv, 1, n_keys, workspace, q.device)
-    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
-    if not q.is_contiguous():
-        raise ValueError("q must be contiguous")
+    _need_cuda(new_keys=nk, q=q, v=v, out=out, packed=cache.packed, workspace=workspace)
     _check(lib().octo_decode_attn_append(cb.handle, _ptr(nk), _dtype_code(nk), nk.stride(0),
                                          _ptr(q), _dtype_code(q), B, Hq, Hkv, _ptr(cache.packed),
                                          _ptr(cache.gamma), _ptr(cache.qjl_bits) if qjl else None,
@@ -302,23 +385,37 @@ def octo_decode_attn_append(cb: Codebook, new_keys, q, cache: Cache, v, n_keys: 
     return out
 
 
+def octo_debug_lds_copies():
+    """Every copy of a codebook table into LDS by a kernel instantiation
+    (octo_debug_lds_copy), as a list of dicts."""
+    out, i = [], 0
+    rec = octo_lds_copy()
+    while lib().octo_debug_lds_copy(i, ctypes.byref(rec)) == OCTO_OK:
+        out.append({f: getattr(rec, f) for f, _ in octo_lds_copy._fields_})
+        out[-1]["kernel"] = rec.kernel.decode()
+        i += 1
+    return out
+
+
 def octo_debug_copy(dst, src, stream=None):
     """Plain 16-byte-access device copy of src into dst (same byte size)."""
     nbytes = src.numel() * src.element_size()
-    if dst.numel() * dst.element_size() != nbytes:
-        raise ValueError("dst and src differ in size")
+    _need(dst.numel() * dst.element_size() == nbytes, "dst and src differ in size")
+    _need(src.is_contiguous() and dst.is_contiguous(), "dst and src must be contiguous")
+    _need_cuda(dst=dst, src=src)
     _check(lib().octo_debug_copy(_ptr(dst), _ptr(src), nbytes, _stream(stream)), "octo_debug_copy")
 
 
 def octo_debug_reconstruct(cb: Codebook, cache: Cache, n_keys: int, out=None, stream=None):
     import torch
+    _need_cache(cb, cache, cache.n_seq, "cache.n_seq")
+    _need(0 <= n_keys <= cache.cap, f"n_keys ({n_keys}) must lie in [0, cache.cap = {cache.cap}]")
     if out is None:
         out = torch.empty((cache.n_seq, n_keys, cb.d), dtype=torch.float32, device=cache.packed.device)
+    _need_out(out, (cache.n_seq, n_keys, cb.d), "out")
+    _need_cuda(out=out, packed=cache.packed)
     _check(lib().octo_debug_reconstruct(cb.handle, _ptr(cache.packed), _ptr(cache.gamma), cache.n_seq,
                                         n_keys, cache.cap, _ptr(out), _stream(stream)),
            "octo_debug_reconstruct")
     return out
 
-
-def default_scale(d: int) -> float:
-    return 1.0 / math.sqrt(d)

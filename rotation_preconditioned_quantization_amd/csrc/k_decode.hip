@@ -119,9 +119,21 @@ struct SQShared {
   float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
+// The copy of a single-query kernel's code table into LDS by NTH threads.
+template <int D, int B, bool QJL, bool REP, int NTH>
+using SQTableCopy = TableCopy<SQShared<D, B, QJL, REP>::NENT * SQShared<D, B, QJL, REP>::NCOPY, NTH,
+                              SQShared<D, B, QJL, REP>::NCOPY>;
+
+// Replicated code table in k_logits (B <= 3) and in k_attn (B <= 2: at b = 3
+// and 4 it measured no faster there).
+template <int B>
+constexpr bool logits_rep() { return B <= 3; }
+template <int B>
+constexpr bool attn_rep() { return B <= 2; }
+
 // Waves per k_logits block: 8 with the replicated table (B <= 3), else 4.
 template <int B>
-constexpr int logits_waves() { return B <= 3 ? 8 : 4; }
+constexpr int logits_waves() { return logits_rep<B>() ? 8 : 4; }
 
 // Values the block prologue loads from global memory besides the LDS tables
 // (which go to LDS directly): wave w's query head g0 + w (lane l holds the
@@ -138,18 +150,20 @@ __device__ __forceinline__ void sq_issue_prologue(const DecodeArgs& a, int64_t s
                                                   SQShared<D, B, QJL, REP>& sh) {
   using C = Codec<D, B>;
   using SH = SQShared<D, B, QJL, REP>;
-  constexpr int NS = SH::NENT * SH::NCOPY;   // float4 slots
-  constexpr int PER = (NS + NTH - 1) / NTH;
+  using TC = SQTableCopy<D, B, QJL, REP, NTH>;
+  static_assert(TC::SLOTS <= SH::NENT * SH::NCOPY && TC::ENTRIES <= SH::NENT,
+                "the table copy stays inside the LDS table and the source table");
+  static_assert(C::LR <= NTH, "one rho centroid per thread");
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const float4* src = SH::kCombined ? a.t.trip_tab : a.t.dirtab;
   // the table goes straight from global memory into LDS (no registers held);
   // slot i holds entry i / NCOPY.  The condition is per lane: a table of
-  // fewer than 64 slots (16 at one bit) is copied by the first lanes only,
-  // and the others neither read past its end nor write past it in LDS.
+  // fewer slots than threads (16 at one bit) is copied by the first lanes
+  // only, and the others neither read past its end nor write past it in LDS.
 #pragma unroll
-  for (int k = 0; k < PER; ++k) {
+  for (int k = 0; k < TC::ROUNDS; ++k) {
     const int i0 = NTH * k + 64 * w;  // this wave's 64 slots of round k
-    if (NS % NTH == 0 || i0 + lane < NS)
+    if (!TC::MASKED || i0 + lane < SH::NENT * SH::NCOPY)
       __builtin_amdgcn_global_load_lds((const void*)(src + (i0 + lane) / SH::NCOPY),
                                        (__attribute__((address_space(3))) void*)(sh.tab + i0), 16,
                                        0, 0);
@@ -381,7 +395,7 @@ __global__ __launch_bounds__(64 * logits_waves<B>())
 __attribute__((amdgpu_waves_per_eu(logits_waves<B>() / 2))) void k_logits(DecodeArgs a) {
   // replicated table where it fits (conflict-free gathers); the 64 KiB it can
   // take leaves room for two blocks per CU, so such blocks have 8 waves
-  constexpr bool REP = B <= 3;
+  constexpr bool REP = logits_rep<B>();
   constexpr int NW = logits_waves<B>();
   __shared__ SQShared<D, B, QJL, REP> sh;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -464,8 +478,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   using VG = VGeom<D>;
   constexpr int NVL = VG::NVL;
   // replicated code table where it costs at most 32 KiB (b <= 2): about 1 %
-  // at the extreme workload's shape; at b = 3 and 4 it measured no faster
-  constexpr bool REP = B <= 2;
+  // at the extreme workload's shape
+  constexpr bool REP = attn_rep<B>();
   __shared__ SQShared<D, B, QJL, REP> sh;
   // p of the tile per head, stored so that the 4 keys one MFMA block shares
   // are 4 consecutive floats; padded rows: the 4 heads hit different banks
@@ -860,6 +874,43 @@ static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
     case 1285: return qjl ? FN<128, 5, true>(__VA_ARGS__) : FN<128, 5, false>(__VA_ARGS__);     \
   }                                                                                             \
   return hipErrorInvalidValue;
+
+// LDS table copies of the single-query kernels: the code table (combined
+// rho^ n^ per code, or unit directions) and the rho centroids, per
+// instantiation, from the same constants as the copy loops.
+template <int D, int B, bool QJL, bool REP, int NTH>
+static int sq_copy_recs(const char* kernel, LdsCopyRec* out, int n, int max) {
+  using SH = SQShared<D, B, QJL, REP>;
+  using TC = SQTableCopy<D, B, QJL, REP, NTH>;
+  using C = Codec<D, B>;
+  if (n < max)
+    out[n++] = {kernel, D, B, QJL, SH::kCombined ? TAB_TRIP : TAB_DIR, (int64_t)SH::NENT * SH::NCOPY,
+                TC::SLOTS, TC::ENTRIES, (int64_t)SH::NENT * SH::NCOPY, NTH, TC::MASKED};
+  if (n < max) out[n++] = {kernel, D, B, QJL, TAB_RHO, C::LR, C::LR, C::LR, C::LR, NTH, C::LR % NTH != 0};
+  return n;
+}
+
+template <int D, int B, bool QJL>
+static int decode_copy_recs(LdsCopyRec* out, int n, int max) {
+  n = sq_copy_recs<D, B, QJL, logits_rep<B>(), 64 * logits_waves<B>()>("k_logits", out, n, max);
+  n = sq_copy_recs<D, B, QJL, attn_rep<B>(), 256>("k_attn", out, n, max);
+  return n;
+}
+
+int lds_copies_decode(LdsCopyRec* out, int max) {
+  int n = 0;
+#define OCTO_REC_B(D, QJL)                                                                     \
+  n = decode_copy_recs<D, 1, QJL>(out, n, max); n = decode_copy_recs<D, 2, QJL>(out, n, max); \
+  n = decode_copy_recs<D, 3, QJL>(out, n, max); n = decode_copy_recs<D, 4, QJL>(out, n, max); \
+  n = decode_copy_recs<D, 5, QJL>(out, n, max);
+  OCTO_REC_B(64, false)
+  OCTO_REC_B(64, true)
+  OCTO_REC_B(128, false)
+  OCTO_REC_B(128, true)
+  OCTO_REC_B(256, false)
+#undef OCTO_REC_B
+  return n;
+}
 
 hipError_t launch_logits(int d, int b, bool qjl, const DecodeArgs& a, int64_t n_seq, int nbx,
                          hipStream_t s) {

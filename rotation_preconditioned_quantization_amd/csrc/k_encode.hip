@@ -1,7 +1,7 @@
 // OCTOPUS online key encoder for gfx950: launch routing by bit budget.  The
 // kernels are in k_encode_kernels.hpp; each bit budget's instantiations are
 // compiled in k_encode_b<N>.hip.
-#include "octo_internal.hpp"
+#include "k_encode_kernels.hpp"
 
 namespace octo {
 
@@ -27,6 +27,16 @@ hipError_t launch_encode(int d, int b, int kdt, bool qjl, bool joint, const Enco
     case 5: return launch_encode_b5(d, kdt, qjl, joint, a, n_seq, s);
   }
   return hipErrorInvalidValue;
+}
+
+int lds_copies_encode(LdsCopyRec* out, int max) {
+  int n = 0;
+  n = enc_copy_recs_b<1>(out, n, max);
+  n = enc_copy_recs_b<2>(out, n, max);
+  n = enc_copy_recs_b<3>(out, n, max);
+  n = enc_copy_recs_b<4>(out, n, max);
+  n = enc_copy_recs_b<5>(out, n, max);
+  return n;
 }
 
 }  // namespace octo

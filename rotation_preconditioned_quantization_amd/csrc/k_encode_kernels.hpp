@@ -129,6 +129,11 @@ template <int D>
 struct SLds {
   static constexpr int PITCH = 2 * D + 16;      // bytes per row
   static constexpr int BYTES = 2 * D * PITCH;   // both planes
+  static constexpr int CPRS = 2 * D / 16;       // 16-byte chunks per row
+  static constexpr int CHUNKS = 2 * D * CPRS;   // chunks copied (the whole f16 table)
+  // 16-byte LDS slot past the last one the copy writes
+  static constexpr int SLOT_END = ((CHUNKS - 1) / CPRS) * (PITCH / 16) + (CHUNKS - 1) % CPRS + 1;
+  static_assert(PITCH % 16 == 0 && SLOT_END * 16 <= BYTES, "the S copy stays inside its LDS rows");
 };
 
 // QJL signs of the wave's 64 residuals on the matrix cores: P = R' S^T for
@@ -446,11 +451,12 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
   for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * EW) s_qe[i] = a.t.qe.t[i];
   for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * EW) s_qr[i] = a.t.qr2.t[i];
   if constexpr (QJL) {
-    constexpr int CPRS = 2 * D / 16;  // 16-byte chunks per S row
-    for (int c = threadIdx.x; c < 2 * D * CPRS; c += 64 * EW)
+    constexpr int CPRS = SLds<D>::CPRS;
+    for (int c = threadIdx.x; c < SLds<D>::CHUNKS; c += 64 * EW)
       *(uint4*)(s_S + (c / CPRS) * SLds<D>::PITCH + (c % CPRS) * 16) = a.t.S16[c];
   }
   if constexpr (TABS) {
+    static_assert(C::LR <= 64 * EW, "one rho centroid per thread");
     for (int i = threadIdx.x; i < C::NDIR; i += 64 * EW) s_dir[i] = a.t.dirtab[i];
     if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
   }
@@ -835,6 +841,48 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
   if (d == 64) return enc_kt<64, B>(kdt, qjl, joint, a, n_seq, s);
   if (d == 128) return enc_kt<128, B>(kdt, qjl, joint, a, n_seq, s);
   return hipErrorInvalidValue;
+}
+
+// LDS table copies of the encoder kernels (the octo_lds_copy records):
+// the quantiser tables (loops bounded at run time by the table's nb + 2
+// entries, which the launchers check against the kMaxLut + 2 LDS entries),
+// and, where the variant holds them, the unit directions and rho centroids
+// (QJL residual, joint rounding) and the f16 QJL matrix.
+template <int D, int B, bool QJL, bool JR, int NTH>
+inline int enc_copy_recs(const char* kernel, LdsCopyRec* out, int n, int max) {
+  using C = Codec<D, B>;
+  for (int tab : {TAB_QX, TAB_QE, TAB_QR2})
+    if (n < max) out[n++] = {kernel, D, B, QJL, tab, kMaxLut + 2, kMaxLut + 2, -1, -1, NTH, 1};
+  if (QJL || JR) {
+    using TC = TableCopy<C::NDIR, NTH>;
+    if (n < max)
+      out[n++] = {kernel, D, B, QJL, TAB_DIR, C::NDIR, TC::SLOTS, TC::ENTRIES, C::NDIR, NTH, TC::MASKED};
+    if (n < max) out[n++] = {kernel, D, B, QJL, TAB_RHO, C::LR, C::LR, C::LR, C::LR, NTH, C::LR % NTH != 0};
+  }
+  if (QJL) {
+    using SL = SLds<D>;
+    if (n < max)
+      out[n++] = {kernel, D, B, QJL, TAB_S16, SL::BYTES / 16, SL::SLOT_END, SL::CHUNKS, SL::CHUNKS, NTH,
+                  SL::CHUNKS % NTH != 0};
+  }
+  return n;
+}
+
+template <int B>
+inline int enc_copy_recs_b(LdsCopyRec* out, int n, int max) {
+#define OCTO_REC_D(D)                                                                            \
+  n = enc_copy_recs<D, B, false, false, 64 * enc_waves<false>()>("k_encode", out, n, max);       \
+  n = enc_copy_recs<D, B, false, true, 64 * enc_waves<false>()>("k_encode (joint)", out, n, max); \
+  n = enc_copy_recs<D, B, true, false, 64 * enc_waves<true>()>("k_encode (qjl)", out, n, max);    \
+  n = enc_copy_recs<D, B, true, true, 64 * enc_waves<true>()>("k_encode (qjl, joint)", out, n, max); \
+  n = enc_copy_recs<D, B, false, false, 256>("k_encode_one", out, n, max);
+  OCTO_REC_D(64)
+  OCTO_REC_D(128)
+#undef OCTO_REC_D
+  n = enc_copy_recs<256, B, false, false, 256>("k_encode256", out, n, max);
+  n = enc_copy_recs<256, B, false, true, 256>("k_encode256 (joint)", out, n, max);
+  n = enc_copy_recs<256, B, false, false, 256>("k_encode_one", out, n, max);
+  return n;
 }
 
 }  // namespace octo

@@ -145,6 +145,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
   const bool stager = S::SW == 0 || wave >= kMQCompute;  // (uniform)
   const int stid = S::SW == 0 ? tid : tid - 64 * kMQCompute;  // staging thread index
 
+  static_assert(TableCopy<C::NDIR, NTH>::SLOTS <= C::NDIR && C::LR <= NTH, "table copies in bounds");
   for (int i = tid; i < C::NDIR; i += NTH) s_dir[i] = a.t.dirtab[i];
   if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
 
@@ -359,6 +360,32 @@ static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
                   (unsigned)(a.B * a.H));
   hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(64 * MQShape<D>::NW), 0, s, a);
   return hipGetLastError();
+}
+
+// LDS table copies of k_mq_attn<D, B>: unit directions and rho centroids.
+template <int D, int B>
+static int mq_copy_recs(LdsCopyRec* out, int n, int max) {
+  using C = Codec<D, B>;
+  constexpr int NTH = 64 * MQShape<D>::NW;
+  using TC = TableCopy<C::NDIR, NTH>;
+  if (n < max)
+    out[n++] = {"k_mq_attn", D, B, 0, TAB_DIR, C::NDIR, TC::SLOTS, TC::ENTRIES, C::NDIR, NTH, TC::MASKED};
+  if (n < max) out[n++] = {"k_mq_attn", D, B, 0, TAB_RHO, C::LR, C::LR, C::LR, C::LR, NTH, C::LR % NTH != 0};
+  return n;
+}
+
+int lds_copies_mq(LdsCopyRec* out, int max) {
+  int n = 0;
+  n = mq_copy_recs<64, 1>(out, n, max);
+  n = mq_copy_recs<64, 2>(out, n, max);
+  n = mq_copy_recs<64, 3>(out, n, max);
+  n = mq_copy_recs<64, 4>(out, n, max);
+  n = mq_copy_recs<64, 5>(out, n, max);
+  n = mq_copy_recs<128, 1>(out, n, max);
+  n = mq_copy_recs<128, 2>(out, n, max);
+  n = mq_copy_recs<128, 3>(out, n, max);
+  n = mq_copy_recs<128, 4>(out, n, max);
+  return n;
 }
 
 int mq_tile_keys(int d) { return d == 64 ? MQShape<64>::KT : MQShape<128>::KT; }

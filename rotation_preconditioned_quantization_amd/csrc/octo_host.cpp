@@ -201,12 +201,26 @@ struct octo_codebook {
   uint32_t sign_bits[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   void* dev = nullptr;
   DevTables tables{};
+  int64_t table_entries[TAB_COUNT] = {0, 0, 0, 0, 0, 0, 0};  // entries per table (octo_table)
 };
 
 namespace {
 
-octo_status build_device_tables(octo_codebook* cb) {
+// Bytes of zeros past the last table of the device allocation: a read a
+// little past a table's end stays inside the allocation.
+constexpr size_t kTableGuardBytes = 1024;
+
+// The kernels' tables, built on the host.
+struct HostTables {
   HostB1 qx, qe, qr2;
+  std::vector<float> dir, rho, trip, st;
+  std::vector<_Float16> s16;
+};
+
+octo_status make_host_tables(octo_codebook* cb, HostTables& h) {
+  HostB1& qx = h.qx;
+  HostB1& qe = h.qe;
+  HostB1& qr2 = h.qr2;
   if (!build_bucket1(midpoints(cb->c_xi), -1.0, 1.0, &qx) ||
       !build_bucket1(midpoints(cb->c_eta), -1.0, 1.0, &qe))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the xi/eta midpoints");
@@ -217,7 +231,8 @@ octo_status build_device_tables(octo_codebook* cb) {
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
 
   const int ndir = 1 << (cb->bx + cb->be);
-  std::vector<float> dir(4 * (size_t)ndir);
+  std::vector<float>& dir = h.dir;
+  dir.resize(4 * (size_t)ndir);
   for (int ie = 0; ie < (1 << cb->be); ++ie)
     for (int ix = 0; ix < (1 << cb->bx); ++ix) {
       double v[3];
@@ -228,9 +243,9 @@ octo_status build_device_tables(octo_codebook* cb) {
       dir[o + 2] = (float)v[2];
       dir[o + 3] = 0.f;
     }
-  std::vector<float> rho(cb->c_rho.begin(), cb->c_rho.end());
+  h.rho.assign(cb->c_rho.begin(), cb->c_rho.end());
   // rho^ n^ per full triplet code, for streams of at most 10 bits per triplet
-  std::vector<float> trip;
+  std::vector<float>& trip = h.trip;
   if (cb->bt <= 10) {
     trip.resize(4 * ((size_t)1 << cb->bt));
     for (int code = 0; code < (1 << cb->bt); ++code) {
@@ -247,7 +262,7 @@ octo_status build_device_tables(octo_codebook* cb) {
   // QJL matrix for the encoder's matrix-core projection: S = S_hi + S_lo with
   // S_hi = f16(S) and S_lo = f16(S - S_hi) (round to nearest even), planes
   // [hi | lo], each d x d row-major.  S_hi + S_lo carries 22 bits of S.
-  std::vector<_Float16> s16;
+  std::vector<_Float16>& s16 = h.s16;
   if (!cb->S.empty()) {
     s16.resize(2 * cb->S.size());
     for (size_t i = 0; i < cb->S.size(); ++i) {
@@ -259,15 +274,34 @@ octo_status build_device_tables(octo_codebook* cb) {
 
   // S transposed (column-major S): the decode kernels form p = S q' with lane
   // j reading element j of column c, one contiguous row of St per load.
-  std::vector<float> st;
+  std::vector<float>& st = h.st;
   if (!cb->S.empty()) {
     const int d = cb->d;
     st.resize(cb->S.size());
     for (int j = 0; j < d; ++j)
       for (int c = 0; c < d; ++c) st[(size_t)c * d + j] = cb->S[(size_t)j * d + c];
   }
+  int64_t* n = cb->table_entries;
+  n[TAB_DIR] = ndir;
+  n[TAB_TRIP] = (int64_t)trip.size() / 4;
+  n[TAB_RHO] = (int64_t)h.rho.size();
+  n[TAB_QX] = (int64_t)qx.t.size() / 2;
+  n[TAB_QE] = (int64_t)qe.t.size() / 2;
+  n[TAB_QR2] = (int64_t)qr2.t.size() / 2;
+  n[TAB_S16] = (int64_t)s16.size() / 8;
+  return OCTO_OK;
+}
 
-  // One device allocation, 256-byte aligned regions.
+octo_status upload_tables(octo_codebook* cb, const HostTables& h) {
+  const HostB1& qx = h.qx;
+  const HostB1& qe = h.qe;
+  const HostB1& qr2 = h.qr2;
+  const std::vector<float>& dir = h.dir;
+  const std::vector<float>& rho = h.rho;
+  const std::vector<float>& trip = h.trip;
+  const std::vector<float>& st = h.st;
+  const std::vector<_Float16>& s16 = h.s16;
+  // One device allocation, 256-byte aligned regions, then a zeroed guard.
   struct Region { const void* src; size_t bytes; size_t off; };
   std::vector<Region> reg = {
       {dir.data(), dir.size() * 4, 0},           {rho.data(), rho.size() * 4, 0},
@@ -278,6 +312,8 @@ octo_status build_device_tables(octo_codebook* cb) {
       {s16.empty() ? nullptr : s16.data(), s16.size() * 2, 0}};
   size_t total = 0;
   for (auto& r : reg) { r.off = total; total += align256(r.bytes); }
+  const size_t guard_off = total;
+  total += kTableGuardBytes;
   int prev = 0;
   if (hipGetDevice(&prev) != hipSuccess) return fail(OCTO_ERR_HIP, "hipGetDevice failed");
   if (hipSetDevice(cb->device) != hipSuccess)
@@ -288,10 +324,10 @@ octo_status build_device_tables(octo_codebook* cb) {
     hipSetDevice(prev);
     return fail(OCTO_ERR_NOMEM, std::string("hipMalloc of codebook tables: ") + hipGetErrorString(e));
   }
+  e = hipMemset((char*)dev + guard_off, 0, kTableGuardBytes);
   for (auto& r : reg) {
-    if (r.bytes == 0) continue;
+    if (r.bytes == 0 || e != hipSuccess) continue;
     e = hipMemcpy((char*)dev + r.off, r.src, r.bytes, hipMemcpyHostToDevice);
-    if (e != hipSuccess) break;
   }
   hipSetDevice(prev);
   if (e != hipSuccess) {
@@ -552,9 +588,13 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     delete cb;
     return fail(OCTO_ERR_NOMEM, "host allocation failed during codebook build");
   }
-  if (cb->device >= 0) {
-    const octo_status st = build_device_tables(cb);
-    if (st != OCTO_OK) {
+  if (cb->kernels) {
+    // the kernels' tables: uploaded for a device codebook; for a host-only
+    // one only their sizes are kept (octo_codebook_table_entries)
+    HostTables h;
+    octo_status st = make_host_tables(cb, h);
+    if (st == OCTO_OK && cb->device >= 0) st = upload_tables(cb, h);
+    if (st != OCTO_OK && cb->device >= 0) {
       delete cb;
       return st;
     }
@@ -605,6 +645,38 @@ octo_status octo_codebook_export(const octo_codebook* cb, double* c_xi, double* 
     if (cb->S.empty()) return fail(OCTO_ERR_INVALID_ARG, "codebook has no QJL matrix");
     std::memcpy(qjl_S, cb->S.data(), cb->S.size() * sizeof(float));
   }
+  return OCTO_OK;
+}
+
+int64_t octo_codebook_table_entries(const octo_codebook* cb, int table) {
+  if (!cb || table < 0 || table >= TAB_COUNT) return -1;
+  return cb->table_entries[table];
+}
+
+octo_status octo_debug_lds_copy(int index, octo_lds_copy* out) {
+  static const std::vector<LdsCopyRec> recs = [] {
+    std::vector<LdsCopyRec> v(1024);
+    int n = lds_copies_decode(v.data(), (int)v.size());
+    n += lds_copies_mq(v.data() + n, (int)v.size() - n);
+    n += lds_copies_encode(v.data() + n, (int)v.size() - n);
+    v.resize(n);
+    return v;
+  }();
+  if (!out) return fail(OCTO_ERR_INVALID_ARG, "out is NULL");
+  if (index < 0 || index >= (int)recs.size())
+    return fail(OCTO_ERR_INVALID_ARG, "index past the last table copy (" + std::to_string(recs.size()) + ")");
+  const LdsCopyRec& r = recs[index];
+  out->kernel = r.kernel;
+  out->d = r.d;
+  out->b = r.b;
+  out->qjl = r.qjl;
+  out->table = r.table;
+  out->lds_slots = r.lds_slots;
+  out->slots_written = r.slots_written;
+  out->entries_read = r.entries_read;
+  out->copied = r.copied;
+  out->threads = r.threads;
+  out->masked = r.masked;
   return OCTO_OK;
 }
 

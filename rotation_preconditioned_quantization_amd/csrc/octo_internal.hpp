@@ -88,6 +88,36 @@ struct DecodeArgs {
   float* gamma_w;
 };
 
+// Geometry of a copy of NS table entries into LDS by NTH threads, one entry
+// per thread per round (global_load_lds or a strided loop).  When NTH does
+// not divide NS the copy is masked per lane at NS; either way it writes LDS
+// entries [0, SLOTS) only.  NCOPY > 1: LDS entry i holds table entry
+// i / NCOPY (replicated tables), so the copy reads table entries
+// [0, ENTRIES) only.  Kernels static_assert SLOTS and ENTRIES against their
+// LDS array and table sizes; LdsCopyRec reports the same figures.
+template <int NS, int NTH, int NCOPY = 1>
+struct TableCopy {
+  static constexpr int ROUNDS = (NS + NTH - 1) / NTH;
+  static constexpr bool MASKED = NS % NTH != 0;
+  static constexpr int SLOTS = MASKED ? NS : ROUNDS * NTH;
+  static constexpr int ENTRIES = (SLOTS - 1) / NCOPY + 1;
+};
+
+// One table copy into LDS, as a kernel instantiation performs it (the
+// octo_lds_copy record of the C ABI).  copied: entries moved, one per thread
+// per round; entries_read = copied = -1: a loop bounded at run time by the
+// table's own entry count (the launcher checks that count against
+// lds_slots).
+struct LdsCopyRec {
+  const char* kernel;
+  int d, b, qjl, table;
+  int64_t lds_slots, slots_written, entries_read, copied;
+  int threads, masked;
+};
+
+enum { TAB_DIR = 0, TAB_TRIP = 1, TAB_RHO = 2, TAB_QX = 3, TAB_QE = 4, TAB_QR2 = 5, TAB_S16 = 6,
+       TAB_COUNT = 7 };
+
 struct CombineArgs {
   const float* part;
   float* out;
@@ -125,6 +155,11 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 hipError_t launch_copy16(void* dst, const void* src, int64_t n16, hipStream_t s);
 hipError_t launch_reconstruct(int d, int b, const ReconArgs& a, int64_t n_seq, hipStream_t s);
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s);
+// The LDS table copies of the kernels in each translation unit (records
+// appended to out[0 .. max), count returned).
+int lds_copies_decode(LdsCopyRec* out, int max);
+int lds_copies_mq(LdsCopyRec* out, int max);
+int lds_copies_encode(LdsCopyRec* out, int max);
 int mq_tile_keys(int d);  // keys per tile of the multi-query kernel
 int mq_block_queries();   // queries per workgroup of the multi-query kernel
 

@@ -460,7 +460,7 @@ def test_joint_rounding_3x3_equals_exhaustive_on_10000_triplets(b):
     nh = O.octa_decode(cb.c_xi[j3[:, 0]], cb.c_eta[j3[:, 1]])
     err = np.sum((cb.c_rho[j3[:, 2]][:, None] * nh - t) ** 2, axis=1)
     for ia in range(cb.c_xi.size):
-        for ie in range(0, cb.c_eta.size, 3):
+        for ie in range(cb.c_eta.size):
             n2 = O.octa_decode(np.full(len(t), cb.c_xi[ia]), np.full(len(t), cb.c_eta[ie]))
             for ir in range(cb.c_rho.size):
                 assert np.all(np.sum((cb.c_rho[ir] * n2 - t) ** 2, axis=1) >= err - 1e-12)
