@@ -72,7 +72,10 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
  *             allocation (b+1, b+1, b-1) ([YL] 非均匀比特分配, direction one bit
  *             more, length one bit less), i.e. 3b+1 bits per triplet.  Kernels
  *             exist for that allocation only; others build host-only tables.
- *   qjl       1: also draw the d x d Gaussian QJL projection ([YL] 可选的残差修正).
+ *   qjl       1: also draw the residual's random rotation for OCTOPUS-QJL
+ *             ([YL] 可选的残差修正: the residual is rotated independently and
+ *             only the signs are kept): S = sqrt(d) P, P the Haar-random
+ *             orthogonal Q factor of a seeded d x d Gaussian matrix.
  *   mc_vectors  Monte-Carlo vectors for the tables (0 = 65536).
  *   device    HIP device to upload the tables to, or -1 for a host-only
  *             codebook (octo_codebook_export / layout work; kernels refuse it).
@@ -119,7 +122,7 @@ octo_status octo_codebook_layout(const octo_codebook* cb, octo_layout* out);
 
 /* Host copies of the tables (tests).  Any pointer may be NULL to skip it.
  * c_xi: 2^b_xi, c_eta: 2^b_eta, c_rho: 2^b_rho doubles; signs: d int8 (+-1);
- * qjl_S: d*d floats row-major (only if built with qjl). */
+ * qjl_S: d*d floats row-major, S = sqrt(d) P (only if built with qjl). */
 octo_status octo_codebook_export(const octo_codebook* cb, double* c_xi, double* c_eta,
                                  double* c_rho, int8_t* signs, float* qjl_S);
 
@@ -212,7 +215,9 @@ size_t octo_decode_workspace_bytes(const octo_codebook* cb, int mode, int B, int
  * n_seq = B*Hkv sequences of capacity cap; the first n_keys positions are read.
  * logits: device fp32 [B][Hq][n_keys], the raw (unscaled) <q, k^>.  With
  * qjl_bits/qjl_norm non-NULL (QJL codebook) the OCTOPUS-QJL estimate
- *   gamma * (<q', u'^> + sqrt(pi/2)/d * nu * <S q', sigma>)  is returned. */
+ *   gamma * (<q', u'^> + kappa_d * nu * <S q', sigma>)  is returned,
+ * kappa_d = 1 / (d sqrt(d) E|u_1|) with E|u_1| = Gamma(d/2) / (sqrt(pi)
+ * Gamma((d+1)/2)) (exactly unbiased for the rotation S). */
 octo_status octo_decode_logits(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
                                int Hq, int Hkv, const void* packed, const float* gamma,
                                const void* qjl_bits, const uint16_t* qjl_norm, int64_t n_keys,
@@ -226,7 +231,12 @@ octo_status octo_decode_logits(const octo_codebook* cb, const void* q, octo_dtyp
  * n_keys keys, l the logits above (QJL-corrected when the QJL buffers are
  * given), no mask.  scale <= 0 selects 1/sqrt(d).  n_q == 1 runs the split-K
  * single-query kernels; n_q > 1 runs the multi-query MFMA kernel.  n_keys == 0
- * writes zeros. */
+ * writes zeros.
+ * Value range: the single-query kernels use V as stored (any bf16).  The
+ * multi-query kernel multiplies in fp16: bf16 values with |v| in fp16's
+ * normal range [2^-14, 65504] (and 0) are exact there, larger ones saturate
+ * at +-65504 (round toward zero), smaller ones keep fp16's subnormal
+ * precision (2^-24). */
 octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
                              int Hq, int Hkv, int n_q, const void* packed, const float* gamma,
                              const void* qjl_bits, const uint16_t* qjl_norm, const void* v,

@@ -16,7 +16,10 @@ Parity status of each function (what pins it, tests/test_oracle_*.py):
   encode / decode            identity-quantizer round trip 1e-12; printed MSEs
                              0.0071 (b=4) and 0.0897 (b=2) on d=128 Gaussian keys
   logits / attention         torch scaled_dot_product_attention (fp64, CPU)
-  qjl_encode / qjl_logits    closed-form expectation (Monte Carlo over S draws)
+  haar_rotation / qjl_scale  orthogonality; E|u_1| against the Beta(1/2, (d-1)/2)
+                             moment (scipy); closed-form sign expectation over seeds
+  qjl_encode / qjl_logits    unbiased over seeds; error ratio to the plain estimate
+                             sqrt(pi/2 - 1) as the sign-estimator variance predicts
   joint_round                exhaustive 2^(b_xi+b_eta) search: identical on 10000
                              random triplets at b = 2, 3, 4, as the pages report
 """
@@ -315,9 +318,14 @@ def encode(keys: np.ndarray, cb: Codebook, identity: bool = False,
     """
     k = np.asarray(keys, dtype=np.float64)
     gamma = np.sqrt(np.sum(k * k, axis=1))
-    safe = np.where(gamma > 0, gamma, 1.0)
-    u = np.where(gamma[:, None] > 0, k / safe[:, None], 0.0)
-    up = u @ cb.R.T
+    # u' = R (k / gamma) = H (s .* k) / (sqrt(d) gamma): R is linear, and the
+    # integer Hadamard sums of fp32 / bf16 keys are exact in fp64, so a
+    # coordinate that is exactly 0 (the signed entries cancel) stays exactly 0
+    # (a rounded 1/gamma or 1/sqrt(d) before the sums would leave +-1e-17 of
+    # either sign, turning zero triplets and sgn(0) into rounding noise)
+    y = (k * cb.signs[None, :]) @ sylvester(cb.d).T.astype(np.float64)
+    scale = np.where(gamma > 0, math.sqrt(cb.d) * gamma, 1.0)
+    up = np.where(gamma[:, None] > 0, y / scale[:, None], 0.0)
     rho, n = triplet_polar(split_triplets(up).reshape(-1, 3))
     xi, eta = octa_encode(n)
     nk, T = k.shape[0], cb.T
@@ -519,16 +527,49 @@ def gqa_attention(q: np.ndarray, khat: np.ndarray, v: np.ndarray, scale: float |
 
 
 # ----------------------------------------------------------------------------
-# OCTOPUS-QJL ([YL] 可选的残差修正; [AR] OCTOPUS-QJL; QJL estimator [TQ] 四/五).
+# OCTOPUS-QJL ([YL] 可选的残差修正; [AR] OCTOPUS-QJL; the 1-bit sign estimator
+# of QJL, [TQ] 四/五).
 # READING: the residual is taken in the rotated unit domain over the d real
-# coordinates, r' = u'[:d] - u'^[:d]; its length is stored as fp16; the
-# "independent random rotation" is a seeded Gaussian S in R^{d x d} (iid
-# N(0,1)), which keeps the estimator exactly unbiased; one sign per rotated
-# dimension, sgn(0) = +1, bit j = 1 when sign j is +1.
-#   l = gamma * ( <q', u'^> + sqrt(pi/2)/d * nu * <S q', sigma> )
+# coordinates, r' = u'[:d] - u'^[:d]; its length is stored as fp16; the page's
+# "independent random rotation" is a Haar-random orthogonal d x d matrix P
+# drawn from the seed; one sign per rotated coordinate, sgn(0) = +1, bit j = 1
+# when sign j is +1.  The matrix is kept as S = sqrt(d) P (rows of norm
+# sqrt(d), like Gaussian rows; the signs of S r' are those of P r'), and
+#   l = gamma * ( <q', u'^> + kappa_d * nu * <S q', sigma> ),
+#   kappa_d = 1 / (d sqrt(d) E|u_1|),  E|u_1| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+# the mean |coordinate| of a uniform unit vector in R^d.  For a Haar P the
+# rotated residual direction is uniform on the sphere, so
+# E[<P q', sgn(P r')>] = d E|u_1| <q', r'> / |r'| and the estimate is exactly
+# unbiased.  (A Gaussian S, the other reading, is unbiased too with
+# kappa = sqrt(pi/2)/d, but its sign estimate has about pi/2 times the
+# variance; gaussian_projection keeps it for that comparison.)
 # ----------------------------------------------------------------------------
-def qjl_matrix(d: int, seed: int) -> np.ndarray:
+def gaussian_projection(d: int, seed: int) -> np.ndarray:
+    """The seeded iid N(0,1) d x d matrix (row-major draws)."""
     return gaussians(seed, TAG_QJL, d * d).reshape(d, d)
+
+
+def haar_rotation(d: int, seed: int) -> np.ndarray:
+    """Haar-random orthogonal P: the Q factor of the seeded Gaussian matrix
+    with the signs fixed so that R has a positive diagonal (Mezzadri 2007),
+    i.e. the Gram-Schmidt orthonormalisation of its columns."""
+    Q, R = np.linalg.qr(gaussian_projection(d, seed))
+    return Q * np.where(np.diag(R) < 0, -1.0, 1.0)[None, :]
+
+
+def qjl_matrix(d: int, seed: int) -> np.ndarray:
+    """S = sqrt(d) P: the rotation the residual signs are taken in."""
+    return math.sqrt(d) * haar_rotation(d, seed)
+
+
+def mean_abs_coordinate(d: int) -> float:
+    """E|u_1| for u uniform on the unit sphere of R^d."""
+    return math.exp(math.lgamma(d / 2.0) - math.lgamma((d + 1) / 2.0)) / math.sqrt(math.pi)
+
+
+def qjl_scale(d: int) -> float:
+    """kappa_d with <q', r'> = kappa_d |r'| E<S q', sgn(S r')> for S = sqrt(d) P."""
+    return 1.0 / (d * math.sqrt(d) * mean_abs_coordinate(d))
 
 
 @dataclass
@@ -549,13 +590,15 @@ def qjl_encode(rotated: np.ndarray, uh: np.ndarray, S: np.ndarray) -> QJLEncoded
 
 
 def qjl_logits(q: np.ndarray, uh: np.ndarray, gamma: np.ndarray, enc: QJLEncoded,
-               S: np.ndarray, cb: Codebook) -> np.ndarray:
-    """q (..., d) -> (..., n) QJL-corrected raw logits."""
+               S: np.ndarray, cb: Codebook, kappa: float | None = None) -> np.ndarray:
+    """q (..., d) -> (..., n) QJL-corrected raw logits (kappa: the estimator
+    constant of S; qjl_scale(d) for the rotation reading)."""
     d = cb.d
+    kappa = qjl_scale(d) if kappa is None else kappa
     qr = np.asarray(q, dtype=np.float64) @ cb.R.T
     base = qr @ uh.T
     sq = qr @ S.T
-    corr = (sq @ enc.signs.T) * enc.nu.astype(np.float64) * (math.sqrt(math.pi / 2.0) / d)
+    corr = (sq @ enc.signs.T) * enc.nu.astype(np.float64) * kappa
     return np.asarray(gamma, dtype=np.float64) * (base + corr)
 
 

@@ -202,6 +202,7 @@ struct octo_codebook {
   void* dev = nullptr;
   DevTables tables{};
   int64_t table_entries[TAB_COUNT] = {0, 0, 0, 0, 0, 0, 0};  // entries per table (octo_table)
+  float qjl_kappa = 0.f;   // QJL estimator constant of S
 };
 
 namespace {
@@ -354,6 +355,7 @@ octo_status upload_tables(octo_codebook* cb, const HostTables& h) {
   t.trip_tab = trip.empty() ? nullptr : (const float4*)(base + reg[6].off);
   t.S16 = s16.empty() ? nullptr : (const uint4*)(base + reg[7].off);
   for (int k = 0; k < 8; ++k) t.sign_bits[k] = cb->sign_bits[k];
+  t.qjl_kappa = cb->qjl_kappa;
   return OCTO_OK;
 }
 
@@ -384,10 +386,16 @@ int head_passes(int G) { return (G + 3) / 4; }
 
 struct Split { int n_split, tiles_per_split; };
 
+// Blocks the single-query attention aims at (4-wave blocks, two resident per
+// compute unit).
+#ifndef OCTO_ATTN_TARGET_BLOCKS
+#define OCTO_ATTN_TARGET_BLOCKS 1024
+#endif
+
 Split attn_split(int64_t n_keys, int64_t n_seq, int passes) {
   const int64_t ntile = std::max<int64_t>(1, (n_keys + kTile - 1) / kTile);
   const int64_t rows = std::max<int64_t>(1, n_seq * passes);
-  int64_t ns = (1024 + rows - 1) / rows;
+  int64_t ns = (OCTO_ATTN_TARGET_BLOCKS + rows - 1) / rows;
   ns = std::min<int64_t>(ns, (ntile + 7) / 8);
   ns = std::max<int64_t>(ns, 1);
   const int64_t tps = (ntile + ns - 1) / ns;
@@ -582,7 +590,34 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     if (cb->qjl) {
       std::vector<double> s((size_t)d * d);
       gaussians(p->seed, kTagQJL, s.size(), s.data());
-      cb->S.assign(s.begin(), s.end());
+      // The residual's random rotation ([YL] 可选的残差修正): the Haar-random
+      // orthogonal P = Q of the seeded Gaussian matrix G = Q R with R's
+      // diagonal positive (Mezzadri 2007), i.e. Gram-Schmidt of G's columns
+      // (each projected out twice), kept as S = sqrt(d) P.
+      std::vector<double> col((size_t)d * d);  // col[j * d + i] = G[i][j]
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) col[(size_t)j * d + i] = s[(size_t)i * d + j];
+      for (int j = 0; j < d; ++j) {
+        double* v = &col[(size_t)j * d];
+        for (int pass = 0; pass < 2; ++pass)
+          for (int k = 0; k < j; ++k) {
+            const double* qk = &col[(size_t)k * d];
+            double dot = 0.0;
+            for (int i = 0; i < d; ++i) dot += qk[i] * v[i];
+            for (int i = 0; i < d; ++i) v[i] -= dot * qk[i];
+          }
+        double nn = 0.0;
+        for (int i = 0; i < d; ++i) nn += v[i] * v[i];
+        const double inv = 1.0 / std::sqrt(nn);
+        for (int i = 0; i < d; ++i) v[i] *= inv;
+      }
+      const double sd = std::sqrt((double)d);
+      cb->S.resize((size_t)d * d);
+      for (int i = 0; i < d; ++i)
+        for (int j = 0; j < d; ++j) cb->S[(size_t)i * d + j] = (float)(sd * col[(size_t)j * d + i]);
+      // kappa_d = 1 / (d sqrt(d) E|u_1|), E|u_1| = Gamma(d/2) / (sqrt(pi) Gamma((d+1)/2))
+      const double mean_abs = std::exp(std::lgamma(0.5 * d) - std::lgamma(0.5 * (d + 1))) / std::sqrt(M_PI);
+      cb->qjl_kappa = (float)(1.0 / ((double)d * sd * mean_abs));
     }
   } catch (const std::bad_alloc&) {
     delete cb;

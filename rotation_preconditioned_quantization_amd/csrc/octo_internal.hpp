@@ -37,6 +37,7 @@ struct DevTables {
   const float* St;          // QJL matrix S transposed, St[c * d + j] = S[j][c] (nullptr without QJL)
   const uint4* S16;         // S (row-major) as f16 planes [S_hi | S_lo], S_hi = f16(S), S_lo = f16(S - S_hi)
   uint32_t sign_bits[8];    // bit j of the 256-bit mask set <=> WHT sign s_j = -1
+  float qjl_kappa;          // QJL estimator constant: <q', r'> ~ kappa |r'| <S q', sgn(S r')>
 };
 
 struct EncodeArgs {
@@ -59,7 +60,7 @@ struct RotateArgs {
   int B, Hq, Hkv, n_q;
   float mult;          // folded into q' (attention: scale * log2(e))
   float* qrot;         // [rows][3T]
-  float* qp;           // [rows][d] = (sqrt(pi/2)/d) * S q'[:d], QJL only (else nullptr)
+  float* qp;           // [rows][d] = kappa * S q'[:d], QJL only (else nullptr)
 };
 
 struct DecodeArgs {

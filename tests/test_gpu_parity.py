@@ -481,19 +481,34 @@ def test_attention_empty_cache_writes_zeros():
 
 
 def test_argument_errors_on_device():
+    """The C library's own argument checks (called directly, past the
+    binding's shape checks): a failed check returns its status and enqueues
+    nothing."""
+    import ctypes
     octo = _octo()
+    L = octo.lib()
     g = gcb(128, 4)
     cache = octo.Cache(g, 1, 128)
     keys = torch.randn((1, 10, 128), device="cuda")
-    with pytest.raises(octo.OctoError):
-        octo.octo_encode(g, keys, cache, pos0=120)  # pos0 + n > cap
+    P = lambda t: ctypes.c_void_p(t.data_ptr())  # noqa: E731
+    st = L.octo_encode(g.handle, P(keys), octo.OCTO_F32, 1, 10, 1280, 128, 120, 128, P(cache.packed),
+                       P(cache.gamma), None, None, None)               # pos0 + n > cap
+    assert st == octo.OCTO_ERR_INVALID_ARG
     q = torch.randn((1, 3, 128), device="cuda")
-    with pytest.raises(octo.OctoError):
-        octo.octo_decode_logits(g, q, cache, 10, 2)  # Hq % Hkv != 0
-    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
-    with pytest.raises(octo.OctoError) as e:
-        octo.octo_decode_logits(g, torch.randn((1, 2, 128), device="cuda"), cache, 10, 1, workspace=ws)
-    assert e.value.status == octo.OCTO_ERR_WORKSPACE
+    lg = torch.empty((1, 3, 10), device="cuda")
+    ws = torch.empty(1 << 16, dtype=torch.uint8, device="cuda")
+    st = L.octo_decode_logits(g.handle, P(q), octo.OCTO_F32, 1, 3, 2, P(cache.packed), P(cache.gamma),
+                              None, None, 10, 128, P(lg), P(ws), ws.numel(), None)   # Hq % Hkv != 0
+    assert st == octo.OCTO_ERR_INVALID_ARG
+    q2 = torch.randn((1, 2, 128), device="cuda")
+    st = L.octo_decode_logits(g.handle, P(q2), octo.OCTO_F32, 1, 2, 1, P(cache.packed), P(cache.gamma),
+                              None, None, 10, 128, P(lg), P(ws), 16, None)           # small workspace
+    assert st == octo.OCTO_ERR_WORKSPACE
+    # and the binding refuses the same calls before reaching the library
+    with pytest.raises(ValueError):
+        octo.octo_encode(g, keys, cache, pos0=120)
+    with pytest.raises(ValueError):
+        octo.octo_decode_logits(g, q, cache, 10, 2)
 
 
 # ------------------------------------------- stages, streams, graph capture --
@@ -850,6 +865,59 @@ def test_mq_shapes_and_gqa(d, b):
 @pytest.mark.parametrize("n_q,n", [(2, 1), (2, 255), (129, 257)])
 def test_mq_edges(n_q, n):
     check_mq(WL.CONFIGS[4], 1, 1, n_q, n, 320, seed=n, label=f"mq-edge{n_q}x{n}")
+
+
+def _mq_with_values(vfix, vref):
+    """Multi-query attention over a small cache whose bf16 V is rewritten by
+    vfix(v); the oracle attends over vref(v) (float64 of the bf16 values)."""
+    octo = _octo()
+    cfg = WL.CONFIGS[4]
+    d, b, n, cap, n_q = cfg.d, cfg.b, 500, 512, 40
+    keys = WL.make_keys(cfg, "cuda", seed=21, n_seq=1, n=n)
+    g = gcb(d, b)
+    cache = octo.Cache(g, 1, cap)
+    octo.octo_encode(g, keys, cache)
+    v = vfix(WL.make_values(cfg, "cuda", seed=21, n_seq=1, cap=cap))
+    q = WL.make_queries(cfg.scaled(Hq=1, Hkv=1, n_q=n_q), "cuda", seed=21, B=1)
+    out = f64(octo.octo_decode_attn(g, q, cache, v, n, 1))
+    torch.cuda.synchronize()
+    cb = ocb(d, b)
+    codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, 1, cap, n)
+    gam = cache.gamma.cpu().numpy()[:n]
+    lg = O.logits_rotated(f64(q)[0, 0], O.decode_rotated(codes[0], cb), gam, cb)
+    ref = O.softmax_attention(lg / math.sqrt(d), vref(f64(v)[0, :n]))
+    return float(np.max(np.linalg.norm(out[0, 0] - ref, axis=1) / np.linalg.norm(ref, axis=1)))
+
+
+def test_mq_values_at_the_fp16_limits():
+    """The multi-query path holds V in fp16 (in LDS, for the f16 matrix
+    cores): bf16 values whose magnitude lies in fp16's normal range
+    [2^-14, 65504] (and 0) convert exactly, so values at both ends of that
+    range give the oracle's result."""
+    def fix(v):
+        g = torch.Generator(device="cuda").manual_seed(5)
+        m = torch.rand(v.shape, generator=g, device="cuda")
+        sgn = torch.where(torch.rand(v.shape, generator=g, device="cuda") < 0.5, -1.0, 1.0)
+        big = (sgn * 65280.0).to(torch.bfloat16)            # the largest bf16 below 65504
+        tiny = (sgn * 2.0 ** -14).to(torch.bfloat16)
+        return torch.where(m < 0.02, big, torch.where(m > 0.98, tiny, v)).contiguous()
+    err = _mq_with_values(fix, lambda x: x)
+    say(f"[mq fp16 limits] worst rel err {err:.2e}")
+    assert err <= 2e-3
+
+
+def test_mq_values_beyond_fp16_saturate():
+    """bf16 values beyond fp16's largest finite value are converted with
+    round-toward-zero, i.e. saturate at +-65504 (the documented limit of the
+    multi-query path): the result equals the oracle's over V clamped there."""
+    def fix(v):
+        w = v.clone()
+        w[0, ::7, ::5] = 1.0e5
+        w[0, 3::11, 1::9] = -3.0e6
+        return w.contiguous()
+    err = _mq_with_values(fix, lambda x: np.clip(x, -65504.0, 65504.0))
+    say(f"[mq fp16 saturation] worst rel err {err:.2e}")
+    assert err <= 2e-3
 
 
 def test_full_config4_video_block_sampled():

@@ -44,7 +44,13 @@ def test_host_codebook_matches_oracle(d, b, qjl):
     assert np.max(np.abs(cr / ref.c_rho - 1)) <= 1e-9
     assert np.array_equal(sg.astype(np.float64), ref.signs)
     if qjl:
-        assert np.array_equal(S, O.qjl_matrix(d, 5).astype(np.float32))
+        # the host orthonormalises in its own order (Gram-Schmidt) and the
+        # oracle through LAPACK's QR: the same Q up to fp64 rounding, so the
+        # fp32 S agree to within one fp32 rounding
+        Sref = O.qjl_matrix(d, 5)
+        assert np.max(np.abs(S - Sref) / np.maximum(np.abs(Sref), 1.0)) <= 2.0 ** -23
+        S64 = S.astype(np.float64)
+        assert np.max(np.abs(S64 @ S64.T - d * np.eye(d))) <= 1e-4 * d
     lay = cb.layout
     assert (lay.b_xi, lay.b_eta, lay.b_rho) == (b + 1, b + 1, b - 1)
     assert lay.bits_per_triplet == 3 * b + 1 and lay.n_triplets == O.n_triplets(d)
