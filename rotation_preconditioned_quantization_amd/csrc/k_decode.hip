@@ -462,30 +462,22 @@ struct VGeom {
   static constexpr int NVL = kTile / KPL;  // loads per 64-key tile
 };
 
-// Half H (0: the first NVL/2 loads, keys 0..31; 1: keys 32..63) of the
-// block's part of the V rows of a 64-key tile.  V holds cap rows per
+// The block's part of the V rows of a 64-key tile.  V holds cap rows per
 // sequence and cap is a multiple of 64, so the whole tile is always in
 // bounds: the loads carry no conditions (rows past n_keys are zeroed where
 // the tile is used).
-template <int D, int H>
-__device__ __forceinline__ void load_vhalf(const uint4* vlane, int64_t t, uint4 (&vv)[VGeom<D>::NVL / 2]) {
+template <int D>
+__device__ __forceinline__ void load_vtile(const uint4* vlane, int64_t t, uint4 (&vv)[VGeom<D>::NVL]) {
   using VG = VGeom<D>;
-  constexpr int NH = VG::NVL / 2;
   const uint4* vt = vlane + (t * kTile) * VG::RP;
 #pragma unroll
-  for (int j = 0; j < NH; ++j) vv[j] = vt[(H * NH + j) * VG::KPL * VG::RP];
+  for (int j = 0; j < VG::NVL; ++j) vv[j] = vt[j * VG::KPL * VG::RP];
 }
 
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k_attn(DecodeArgs a) {
   using VG = VGeom<D>;
   constexpr int NVL = VG::NVL;
-  constexpr int NH = NVL / 2;   // V loads per half tile
-  static_assert(NVL % 8 == 0, "a half tile holds whole groups of 4 loads");
-  // The first half of the next tile's V one tile ahead (32 more registers):
-  // at d = 128 without QJL it still fits two waves per SIMD unspilled; at
-  // d = 64 it would cost the third wave, at d = 256 it spills.
-  constexpr bool VPF = D == 128 && !QJL;
   // replicated code table where it costs at most 32 KiB (b <= 2): about 1 %
   // at the extreme workload's shape
   constexpr bool REP = attn_rep<B>();
@@ -528,13 +520,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   // memory-counter waits exact.
   int64_t t = t_begin + wave;
   KTile<D, B, QJL> cur, nxt;
-  // V of a tile in two halves (va, vb); with VPF the first half of the next
-  // tile is loaded a whole tile ahead into vc
-  uint4 va[NH], vb[NH], vc[VPF ? NH : 1];
+  uint4 vv[NVL];
   const bool any = t < t_end;
   load_ktile<D, B, QJL>(a, any ? seq : 0, any ? t : 0, lane, cur);
-  load_vhalf<D, 0>(any ? vlane : vlane0, any ? t : 0, va);
-  load_vhalf<D, 1>(any ? vlane : vlane0, any ? t : 0, vb);
+  load_vtile<D>(any ? vlane : vlane0, any ? t : 0, vv);
   SQPre<D, B, QJL, REP> pre;
   sq_issue_prologue<D, B, QJL, REP>(a, seq, g0, hcount, pre, sh);
   sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
@@ -578,35 +567,53 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
 #pragma unroll
   for (int k = 0; k < 8; ++k) o[k] = floatx4{0.f, 0.f, 0.f, 0.f};
 
-  // One tile: logits, online softmax per head, P.V (V in halves v0, v1).
-  auto process = [&](const KTile<D, B, QJL>& kt, uint4 (&v0)[NH], uint4 (&v1)[NH], int64_t tt) {
+  // One tile: logits, online softmax per head, P.V.
+  auto process = [&](const KTile<D, B, QJL>& kt, uint4 (&vv)[NVL], int64_t tt) {
     if ((tt + 1) * kTile > a.n_keys) {
       // last, partial tile: rows past n_keys hold arbitrary bits (p is 0 there,
       // but 0 * NaN is not)
 #pragma unroll
-      for (int j = 0; j < NH; ++j) {
-        if (tt * kTile + VG::KPL * j + kq >= a.n_keys) v0[j] = make_uint4(0u, 0u, 0u, 0u);
-        if (tt * kTile + VG::KPL * (NH + j) + kq >= a.n_keys) v1[j] = make_uint4(0u, 0u, 0u, 0u);
-      }
+      for (int j = 0; j < NVL; ++j)
+        if (tt * kTile + VG::KPL * j + kq >= a.n_keys) vv[j] = make_uint4(0u, 0u, 0u, 0u);
     }
     const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, kt, lane);
     const int64_t key = tt * kTile + lane;
     const bool valid = key < a.n_keys;
-    float al[4];
+    // Online softmax against a lazily raised reference m (log2 units, one
+    // per head and wave): p = 2^(s - m).  m is raised to the wave's maximum,
+    // and l and o rescaled, only when a score exceeds it by more than
+    // kLazyLog2; p <= 2^kLazyLog2 stays far inside fp32 and its bf16 split.
+    // After the first tile a raise is rare, so most tiles skip the max
+    // reduction and the rescale.  (m, l, o) stay consistent, which is all
+    // the merges of waves and splits need.
+    constexpr float kLazyLog2 = 8.f;
+    float sc[4];
+    bool raise = false;
 #pragma unroll
     for (int h = 0; h < 4; ++h) {
-      const float sc = valid ? kt.gamma * acc[h] : -INFINITY;
-      const float mn = fmaxf(m[h], wave_max(sc));
-      al[h] = __builtin_amdgcn_exp2f(m[h] - mn);
-      const float p = __builtin_amdgcn_exp2f(sc - mn);
-      l[h] = __builtin_fmaf(l[h], al[h], p);
-      m[h] = mn;
-      s_p[wave][h][p_slot] = p;
+      sc[h] = valid ? kt.gamma * acc[h] : -INFINITY;
+      raise |= sc[h] > m[h] + kLazyLog2;
+    }
+    if (__any(raise)) {
+      float al[4];
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+        const float mn = fmaxf(m[h], wave_max(sc[h]));
+        al[h] = mn == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m[h] - mn);
+        l[h] *= al[h];
+        m[h] = mn;
+      }
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[k][r] *= al[r];
     }
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) o[k][r] *= al[r];
+    for (int h = 0; h < 4; ++h) {
+      const float p = __builtin_amdgcn_exp2f(sc[h] - m[h]);
+      l[h] += p;
+      s_p[wave][h][p_slot] = p;
+    }
     __builtin_amdgcn_wave_barrier();
     const float* prow = s_p[wave][lane & 3] + 4 * kq;
 #pragma unroll
@@ -624,11 +631,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       const bf16x4 plo = pack_bf16x4(
           __builtin_amdgcn_perm(__float_as_uint(r1), __float_as_uint(r0), 0x07060302u),
           __builtin_amdgcn_perm(__float_as_uint(r3), __float_as_uint(r2), 0x07060302u));
-      const uint4* vh = 4 * g < NH ? &v0[4 * g] : &v1[4 * g - NH];   // (g is a constant)
-      const uint4& e0 = vh[0];
-      const uint4& e1 = vh[1];
-      const uint4& e2 = vh[2];
-      const uint4& e3 = vh[3];
+      const uint4& e0 = vv[4 * g];
+      const uint4& e1 = vv[4 * g + 1];
+      const uint4& e2 = vv[4 * g + 2];
+      const uint4& e3 = vv[4 * g + 3];
       const uint32_t w0[4] = {e0.x, e0.y, e0.z, e0.w}, w1[4] = {e1.x, e1.y, e1.z, e1.w};
       const uint32_t w2[4] = {e2.x, e2.y, e2.z, e2.w}, w3[4] = {e3.x, e3.y, e3.z, e3.w};
 #pragma unroll
@@ -647,29 +653,22 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
     __builtin_amdgcn_wave_barrier();
   };
 
-  // The next tile's code words (and with VPF the first half of its V rows)
-  // load while this tile is computed; its (other) V rows as soon as this
-  // tile's P.V has consumed theirs.  Other waves on the SIMD cover the
-  // remaining latency.  The last tile is peeled off so that no load is left
-  // in flight at the block's final barrier.
+  // The next tile's code words load while this tile's logits are formed; its
+  // V rows as soon as this tile's P.V has consumed the V registers.  Other
+  // waves on the SIMD cover the remaining latency.  (Loading the next tile's
+  // V a tile ahead, half or whole, measured slower: the registers it takes
+  // cost spills or the compiler's schedule.)  The last tile is peeled off so
+  // that no load is left in flight at the block's final barrier.
   for (; t + 4 < t_end; t += 4) {
     load_ktile<D, B, QJL>(a, seq, t + 4, lane, nxt);
-    if constexpr (VPF) load_vhalf<D, 0>(vlane, t + 4, vc);
-    process(cur, va, vb, t);
-    if constexpr (VPF) {
-      load_vhalf<D, 1>(vlane, t + 4, vb);
-#pragma unroll
-      for (int j = 0; j < NH; ++j) va[j] = vc[j];
-    } else {
-      load_vhalf<D, 0>(vlane, t + 4, va);
-      load_vhalf<D, 1>(vlane, t + 4, vb);
-    }
+    process(cur, vv, t);
+    load_vtile<D>(vlane, t + 4, vv);
     cur = nxt;
   }
   // (the last tile of the cache is always the last one of its wave)
   if (t < t_end) {
     patch(cur, t);
-    process(cur, va, vb, t);
+    process(cur, vv, t);
   }
 
   // lanes serving different keys of a load hold partial sums of the same dims
