@@ -243,6 +243,25 @@ octo_status octo_decode_attn(const octo_codebook* cb, const void* q, octo_dtype 
                              octo_dtype vdt, int64_t n_keys, int64_t cap, float scale, float* out,
                              void* workspace, size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory or hand in a workspace
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): octo_decode_attn with its scratch (the split-K partials and
+ * rotated queries) in a static device array of OCTO_STATIC_SCRATCH_BYTES
+ * that the library holds on every GPU it runs on until the process ends.
+ * The call allocates nothing.  Arguments, layout, results and errors as
+ * octo_decode_attn; a call whose scratch (octo_decode_workspace_bytes, mode
+ * 1) exceeds the array returns OCTO_ERR_WORKSPACE and enqueues nothing.
+ * All calls on one GPU share that GPU's array: calls that overlap in time on
+ * one GPU (other streams, other host threads) race and give wrong results;
+ * order them on one stream. */
+#define OCTO_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+octo_status octo_decode_attn_static(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, int n_q, const void* packed,
+                                    const float* gamma, const void* qjl_bits,
+                                    const uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* stream);
+
 /* One autoregressive decode step ([YL] 工程实现; [AB] online): the new
  * token's key of every sequence is encoded into the cache at position
  * n_keys - 1, then the fused attention of one query token per head runs over

@@ -69,6 +69,8 @@ _SIGS = {
     "octo_decode_logits": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ, _P]),
     "octo_decode_attn": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64, _F,
                               _P, _P, _SZ, _P]),
+    "octo_decode_attn_static": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64, _F,
+                                     _P, _P]),
     "octo_decode_logits_stages": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _P, _P, _I64, _I64, _P, _P, _SZ,
                                        _P, _I]),
     "octo_decode_attn_stages": (_I, [_P, _P, _I, _I, _I, _I, _I, _P, _P, _P, _P, _P, _I, _I64, _I64,
@@ -349,6 +351,31 @@ def octo_decode_attn(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, ou
                                          _dtype_code(v), n_keys, cache.cap, scale, _ptr(out),
                                          _ptr(workspace), workspace.numel(), _stream(stream), stages),
            "octo_decode_attn")
+    return out
+
+
+def octo_decode_attn_static(cb: Codebook, q, cache: Cache, v, n_keys: int, Hkv: int, out=None,
+                            scale: float = 0.0, use_qjl: bool | None = None, stream=None):
+    """octo_decode_attn with the library's static device scratch instead of
+    a workspace: allocates nothing on the device when `out` is given (calls
+    on one GPU must not overlap in time)."""
+    import torch
+    _need(q.dim() == 4, "q must be [B, Hq, n_q, d]")
+    B, Hq, n_q, d = q.shape
+    qjl = cache.qjl_bits is not None if use_qjl is None else use_qjl
+    _need_decode(cb, q, cache, B, Hq, Hkv, n_keys, qjl)
+    _need_values(v, cache, d)
+    if out is None:
+        out = torch.empty((B, Hq, n_q, d), dtype=torch.float32, device=q.device)
+    _need_out(out, (B, Hq, n_q, d), "out")
+    _need_cuda(q=q, v=v, out=out, packed=cache.packed)
+    _check(lib().octo_decode_attn_static(cb.handle, _ptr(q), _dtype_code(q), B, Hq, Hkv, n_q,
+                                         _ptr(cache.packed), _ptr(cache.gamma),
+                                         _ptr(cache.qjl_bits) if qjl else None,
+                                         _ptr(cache.qjl_norm) if qjl else None, _ptr(v),
+                                         _dtype_code(v), n_keys, cache.cap, scale, _ptr(out),
+                                         _stream(stream)),
+           "octo_decode_attn_static")
     return out
 
 

@@ -319,8 +319,16 @@ octo_status upload_tables(octo_codebook* cb, const HostTables& h) {
   if (hipGetDevice(&prev) != hipSuccess) return fail(OCTO_ERR_HIP, "hipGetDevice failed");
   if (hipSetDevice(cb->device) != hipSuccess)
     return fail(OCTO_ERR_HIP, "hipSetDevice(" + std::to_string(cb->device) + ") failed");
+  // the static decode scratch of this device is resolved at set-up, with the
+  // device current (octo_decode_attn_static)
+  void* scr = nullptr;
+  hipError_t e = static_scratch(cb->device, &scr);
+  if (e != hipSuccess) {
+    hipSetDevice(prev);
+    return fail(OCTO_ERR_HIP, std::string("static scratch address: ") + hipGetErrorString(e));
+  }
   void* dev = nullptr;
-  hipError_t e = hipMalloc(&dev, total);
+  e = hipMalloc(&dev, total);
   if (e != hipSuccess) {
     hipSetDevice(prev);
     return fail(OCTO_ERR_NOMEM, std::string("hipMalloc of codebook tables: ") + hipGetErrorString(e));
@@ -897,6 +905,32 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
                                     int64_t n_keys, int64_t cap, float scale, float* out,
                                     void* workspace, size_t workspace_bytes, void* stream,
                                     int stages, const AppendKey* app);
+
+static_assert(OCTO_STATIC_SCRATCH_BYTES == kStaticScratchBytes, "one size of the static scratch");
+
+octo_status octo_decode_attn_static(const octo_codebook* cb, const void* q, octo_dtype qdt, int B,
+                                    int Hq, int Hkv, int n_q, const void* packed,
+                                    const float* gamma, const void* qjl_bits,
+                                    const uint16_t* qjl_norm, const void* v, octo_dtype vdt,
+                                    int64_t n_keys, int64_t cap, float scale, float* out,
+                                    void* stream) {
+  octo_status st = check_cb(cb);
+  if (st != OCTO_OK) return st;
+  if (B < 0 || Hq < 0 || Hkv <= 0 || n_q < 1 || n_keys < 0)
+    return fail(OCTO_ERR_INVALID_ARG, "bad B, Hq, Hkv, n_q or n_keys");
+  const size_t need = ws_layout(cb, 1, B, Hq, Hkv, n_q, n_keys).total;
+  if (need > kStaticScratchBytes)
+    return fail(OCTO_ERR_WORKSPACE, "this call needs " + std::to_string(need) +
+                                        " bytes of decode scratch; the static scratch holds " +
+                                        std::to_string(kStaticScratchBytes));
+  void* scr = nullptr;
+  // (resolved when the codebook was built; check_cb made its device current)
+  const hipError_t e = static_scratch(cb->device, &scr);
+  if (e != hipSuccess) return hip_status(e, "static scratch address");
+  return decode_attn_impl(cb, q, qdt, B, Hq, Hkv, n_q, packed, gamma, qjl_bits, qjl_norm, v, vdt,
+                          n_keys, cap, scale, out, scr, kStaticScratchBytes, stream, OCTO_STAGE_ALL,
+                          nullptr);
+}
 
 octo_status octo_decode_attn_append(const octo_codebook* cb, const void* new_keys, octo_dtype kdt,
                                     int64_t key_seq_stride, const void* q, octo_dtype qdt, int B,

@@ -12,6 +12,8 @@ constexpr int kMaxLut = 256;       // max buckets of an encoder lookup table
 constexpr int kMaxLevels = 32;     // max centroids of one component (5 bits)
 constexpr int kMaxSplit = 1024;    // max split-K partials per output row
 constexpr int kEncodeOneMax = 16;  // up to this many new keys per sequence: one-key encoder
+constexpr size_t kStaticScratchBytes = (size_t)64 << 20;  // octo_decode_attn_static's device array
+constexpr int kMaxDevices = 64;
 
 // Nearest-centroid lookup for one scalar component (encoder): the index
 // #{k : x > m_k} of the midpoint rule.  The value range is cut into nb equal
@@ -161,6 +163,9 @@ hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s);
 int lds_copies_decode(LdsCopyRec* out, int max);
 int lds_copies_mq(LdsCopyRec* out, int max);
 int lds_copies_encode(LdsCopyRec* out, int max);
+// Device address of the static decode scratch on `device` (the current
+// device), resolved once per device.
+hipError_t static_scratch(int device, void** out);
 int mq_tile_keys(int d);  // keys per tile of the multi-query kernel
 int mq_block_queries();   // queries per workgroup of the multi-query kernel
 
