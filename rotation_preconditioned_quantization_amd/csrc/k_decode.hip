@@ -14,6 +14,8 @@
 //                P.V over bf16 V (one coalesced row per load, fp32 MFMA),
 //                split-K over the sequence; k_combine merges the splits.
 //   k_reconstruct  test helper writing k^ = gamma R^T u'^.
+#include <type_traits>
+
 #include "octo_device.hpp"
 #include "octo_encode_dev.hpp"
 
@@ -111,7 +113,7 @@ struct SQShared {
   static constexpr bool kCombined = C::BT <= 10;
   static constexpr int NENT = kCombined ? (1 << C::BT) : C::NDIR;
   static constexpr int NCOPY = !REP ? 1 : (4096 / NENT < 16 ? 4096 / NENT : 16);
-  static constexpr int QD = ((3 * C::T + 3) / 4) * 4;
+  static constexpr int QD = ((3 * C::T + 15) / 16) * 16;   // whole 16-dim groups (QRegs)
   float4 tab[NENT * NCOPY];
   float rho[C::LR];
   float q[4][QD];
@@ -289,6 +291,34 @@ __device__ __forceinline__ void build_qjl_lut(int hcount, SQShared<D, B, QJL, RE
   }
 }
 
+// The rotated queries of the (up to) 4 heads in registers, in the layout the
+// broadcast form of v_mfma_f32_4x4x1_16b_f32 reads: register r of lane
+// 4 b + h holds q'[h][16 r + b], so one register carries 16 dims of all 4
+// heads, and the MFMA with CBSZ = 4 (groups of 16 blocks) and ABID = j feeds
+// block j's 4 values (dim 16 r + j) to all 16 blocks as the A operand.
+template <int D, int B, bool QJL, bool REP>
+struct QRegs {
+  static constexpr int N = SQShared<D, B, QJL, REP>::QD / 16;
+  float v[N];
+};
+
+template <int D, int B, bool QJL, bool REP>
+__device__ __forceinline__ void load_qregs(const SQShared<D, B, QJL, REP>& sh, int lane,
+                                           QRegs<D, B, QJL, REP>& qr) {
+#pragma unroll
+  for (int r = 0; r < QRegs<D, B, QJL, REP>::N; ++r) qr.v[r] = sh.q[lane & 3][16 * r + (lane >> 2)];
+}
+
+// f(std::integral_constant<int, I>) for I = I0 .. N-1, as straight-line code:
+// the index is a constant expression in f (the MFMA broadcast controls must be).
+template <int I0, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I0 < N) {
+    f(std::integral_constant<int, I0>{});
+    static_for<I0 + 1, N>(f);
+  }
+}
+
 // The compressed words of one 64-key tile, as loaded by one wavefront.
 template <int D, int B, bool QJL>
 struct KTile {
@@ -315,41 +345,58 @@ __device__ __forceinline__ void load_ktile(const DecodeArgs& a, int64_t seq, int
 // Logits of a 64-key tile, one key per lane, for 4 query heads at once:
 // returns acc[h] = <q'_h, u'^_key> (+ the QJL term).  The contraction over
 // the rotated dims runs on v_mfma_f32_4x4x1_16b_f32: in every 4-lane block
-// the A operand is q'[head = lane % 4][dim] and the B operand is the lane's
-// own rebuilt coordinate, so block b produces the 4 x 4 outer product for
-// keys 4b..4b+3 and lane l ends up holding the 4 heads of key l.  Exact fp32.
+// the A operand is q'[head][dim] for the 4 heads (broadcast from the query
+// registers, QRegs, or read from LDS beside the direction table) and the B
+// operand is the lane's own rebuilt coordinate, so block b produces the 4 x 4
+// outer product for keys 4b..4b+3 and lane l ends up holding the 4 heads of
+// key l.  Exact fp32.
 template <int D, int B, bool QJL, bool REP>
 __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL, REP>& sh,
+                                               const QRegs<D, B, QJL, REP>& qr,
                                                const KTile<D, B, QJL>& k, int lane) {
   using C = Codec<D, B>;
   using SH = SQShared<D, B, QJL, REP>;
   constexpr int T = C::T, W = C::W;
   constexpr int kGroup = 4;
-  const float* qrow = sh.q[lane & 3];
   const float4* tab = sh.tab + (SH::NCOPY > 1 ? (lane & (SH::NCOPY - 1)) : 0);  // this lane's copy
   // two accumulator sets (even / odd triplets): the dependent-MFMA latency
   // then hides behind the other set's issue
   floatx4 acc[6];
 #pragma unroll
   for (int c = 0; c < 6; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int i = 0; i < T; ++i) {
-    const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
-    float tv[3];
-    if constexpr (SH::kCombined) {
+  if constexpr (SH::kCombined) {
+    // up to 10 bits per triplet: one table read per triplet, the queries from
+    // registers (straight-line code: the broadcast controls are constants)
+    static_for<0, T>([&](auto ic) {
+      constexpr int i = decltype(ic)::value;
+      const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
       const float4 e = tab[code * SH::NCOPY];
-      tv[0] = e.x; tv[1] = e.y; tv[2] = e.z;
-    } else {
+      // A: block (3i + c) % 16 of query register (3i + c) / 16, broadcast
+      acc[3 * (i & 1)] = __builtin_amdgcn_mfma_f32_4x4x1f32(qr.v[(3 * i) >> 4], e.x, acc[3 * (i & 1)], 4,
+                                                            (3 * i) & 15, 0);
+      acc[3 * (i & 1) + 1] = __builtin_amdgcn_mfma_f32_4x4x1f32(qr.v[(3 * i + 1) >> 4], e.y,
+                                                                acc[3 * (i & 1) + 1], 4, (3 * i + 1) & 15, 0);
+      acc[3 * (i & 1) + 2] = __builtin_amdgcn_mfma_f32_4x4x1f32(qr.v[(3 * i + 2) >> 4], e.z,
+                                                                acc[3 * (i & 1) + 2], 4, (3 * i + 2) & 15, 0);
+      // a few triplets at a time: keeps the LDS gathers from all being hoisted
+      if constexpr (i % kGroup == kGroup - 1) asm volatile("" ::: "memory");
+    });
+  } else {
+    // direction table and rho centroids: the queries from LDS (measured
+    // faster than the registers at 13 bits per triplet)
+    const float* qrow = sh.q[lane & 3];
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      const uint32_t code = field_at<W>(k.words, i * C::BT, C::BT);
       const float4 n = tab[(code & C::DIR_MASK) * SH::NCOPY];
       const float rh = sh.rho[code >> (C::BX + C::BE)];
-      tv[0] = rh * n.x; tv[1] = rh * n.y; tv[2] = rh * n.z;
-    }
+      const float tv[3] = {rh * n.x, rh * n.y, rh * n.z};
 #pragma unroll
-    for (int c = 0; c < 3; ++c)
-      acc[3 * (i & 1) + c] =
-          __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[3 * (i & 1) + c], 0, 0, 0);
-    // a few triplets at a time: keeps the LDS gathers from all being hoisted
-    if (i % kGroup == kGroup - 1) asm volatile("" ::: "memory");
+      for (int c = 0; c < 3; ++c)
+        acc[3 * (i & 1) + c] =
+            __builtin_amdgcn_mfma_f32_4x4x1f32(qrow[3 * i + c], tv[c], acc[3 * (i & 1) + c], 0, 0, 0);
+      if (i % kGroup == kGroup - 1) asm volatile("" ::: "memory");
+    }
   }
   floatx4 r = (acc[0] + acc[3]) + (acc[1] + acc[4]) + (acc[2] + acc[5]);
   if constexpr (QJL) {
@@ -410,15 +457,17 @@ __attribute__((amdgpu_waves_per_eu(logits_waves<B>() / 2))) void k_logits(Decode
   SQPre<D, B, QJL, REP> pre;
   sq_issue_prologue<D, B, QJL, REP, 64 * NW>(a, seq, g0, hcount, pre, sh);
   sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
-  // One tile at a time.  The kernel is bound by instruction issue (the 4x4x1
-  // MFMAs and the code extraction), and 16 waves per CU hide the load
-  // latency: loading one or two tiles ahead measured slower (more
-  // registers, fewer waves).
+  QRegs<D, B, QJL, REP> qr;
+  load_qregs<D, B, QJL, REP>(sh, lane, qr);
+  // One tile at a time.  The kernel is bound by instruction issue and
+  // latency (the 4x4x1 MFMAs, the code extraction, the table gathers), and
+  // 16 waves per CU hide the load latency: loading a tile ahead measured no
+  // faster (with the queries in registers) or slower (without).
   const int64_t bidx = seq / a.Hkv, kvh = seq % a.Hkv;
   for (; t < ntile; t += stride) {
     KTile<D, B, QJL> kt;
     load_ktile<D, B, QJL>(a, seq, t, lane, kt);
-    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, kt, lane);
+    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, qr, kt, lane);
     const float gamma = kt.gamma;
     const int64_t key = t * kTile + lane;
     if (key < a.n_keys) {
@@ -527,6 +576,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
   SQPre<D, B, QJL, REP> pre;
   sq_issue_prologue<D, B, QJL, REP>(a, seq, g0, hcount, pre, sh);
   sq_finish_prologue<D, B, QJL, REP>(a, hcount, pre, sh);
+  QRegs<D, B, QJL, REP> qr;
+  load_qregs<D, B, QJL, REP>(sh, lane, qr);
   // Decode step with append: the block whose split holds position n_keys - 1
   // encodes the sequence's new key with one wavefront (the same code and
   // rounding as the append encoder), the first head pass writes it to the
@@ -576,7 +627,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void k
       for (int j = 0; j < NVL; ++j)
         if (tt * kTile + VG::KPL * j + kq >= a.n_keys) vv[j] = make_uint4(0u, 0u, 0u, 0u);
     }
-    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, kt, lane);
+    const floatx4 acc = tile_logits<D, B, QJL, REP>(sh, qr, kt, lane);
     const int64_t key = tt * kTile + lane;
     const bool valid = key < a.n_keys;
     // Online softmax against a lazily raised reference m (log2 units, one
