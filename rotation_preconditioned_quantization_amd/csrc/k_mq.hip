@@ -5,15 +5,22 @@
 //
 // Workgroup = 8 wavefronts = 256 queries of one head over one split of the
 // cache, so every rebuilt key serves 256 queries.  Per tile of 128 keys:
-//   1. the keys are rebuilt from the packed stream into LDS as fp16 rotated
-//      unit directions u'^ (gamma kept in fp32): wave w takes the 64 keys of
-//      half w / 4 (one per lane) and the dim quarter w % 4 of each, i.e. only
+//   1. the keys are rebuilt from the packed stream into LDS as fp16 rows
+//      gamma 2^-e u'^, with one power of two 2^e per 64-key half (the half's
+//      largest gamma scaled into [1/2, 1)): wave w takes the 64 keys of half
+//      w / PARTS (one per lane) and the dim range w % PARTS of each, i.e. only
 //      the triplets that touch those dims;
 //   2. the bf16 V tile is stored transposed in LDS as fp16;
 //   3. each wave computes S^T = K^ Q'^T for its 32 queries with
-//      v_mfma_f32_32x32x16_f16 (fp32 accumulate), scales by gamma, runs the
-//      online softmax in the accumulator registers, and feeds P^T straight
-//      from those registers into O^T += V^T P^T (same MFMA shape).
+//      v_mfma_f32_32x32x16_f16 (fp32 accumulate), runs the online softmax in
+//      the accumulator registers (the half's 2^e folded into the one scale
+//      factor of the exponent), and feeds P^T straight from those registers
+//      into O^T += V^T P^T (same MFMA shape).
+// Folding gamma into the rows needs no per-score multiply, cannot overflow
+// fp16 (every row element is at most 1), and leaves the absolute error of a
+// score at most that of the half's largest-norm key, which fp16 rounding sets
+// anyway: a key far smaller than its neighbours loses relative precision only
+// below 2^-24 of the half's largest gamma.
 // Queries are the rotated q' = R q (keys are never inverse-rotated), scaled
 // per row by a power of two so fp16 holds them without overflow.
 #include "octo_device.hpp"
@@ -53,7 +60,7 @@ struct MQShape {
 template <int D, int B>
 struct MQStage {
   uint32_t words[Codec<D, B>::W];   // the lane's key
-  float gamma;
+  float gamma;                      // its norm
   uint4 v[MQShape<D>::KPT];         // KPT V rows, 8 dims each
 };
 
@@ -87,10 +94,11 @@ __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
                                                                  __uint_as_float(w & 0xffff0000u)));
 }
 
-// Dims [PART DQ, (PART + 1) DQ) of the lane's rebuilt key u'^ = rho^ n^ per
-// triplet, from the triplets that touch them, to the key's fp16 row in LDS.
+// Dims [PART DQ, (PART + 1) DQ) of the lane's rebuilt key gs u'^ (u'^ = rho^ n^
+// per triplet, gs = gamma 2^-e, 0 for a row past the cache), from the
+// triplets that touch them, to the key's fp16 row in LDS.
 template <int D, int B, int PART>
-__device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, bool ok, const float4* s_dir,
+__device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, float gs, const float4* s_dir,
                                            const float* s_rho, unsigned char* krow) {
   using C = Codec<D, B>;
   constexpr int DQ = MQShape<D>::DQ, LO = PART * DQ, HI = LO + DQ;
@@ -99,19 +107,21 @@ __device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, bool ok, con
   for (int i = LO / 3; i <= (HI - 1) / 3; ++i) {
     const uint32_t code = field_at<C::W>(st.words, i * C::BT, C::BT);
     const float4 n = s_dir[code & C::DIR_MASK];
-    const float rh = ok ? s_rho[code >> (C::BX + C::BE)] : 0.f;
+    const float rh = gs * s_rho[code >> (C::BX + C::BE)];
     const float t3[3] = {rh * n.x, rh * n.y, rh * n.z};
 #pragma unroll
     for (int c = 0; c < 3; ++c)
       if (3 * i + c >= LO && 3 * i + c < HI) u[3 * i + c - LO] = t3[c];
   }
+  // round to nearest: truncation would shrink every score by about 2^-12 on
+  // average, an error that grows with the score's magnitude
   uint4* row = (uint4*)(krow + LO * 2);
 #pragma unroll
   for (int j = 0; j < DQ / 8; ++j) {
     uint32_t w[4];
 #pragma unroll
     for (int e = 0; e < 4; ++e)
-      w[e] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(u[8 * j + 2 * e], u[8 * j + 2 * e + 1]));
+      w[e] = __builtin_bit_cast(uint32_t, half2v{(_Float16)u[8 * j + 2 * e], (_Float16)u[8 * j + 2 * e + 1]});
     row[j] = make_uint4(w[0], w[1], w[2], w[3]);
   }
 }
@@ -128,7 +138,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
   // two sets of tile buffers: tile t + 1 is staged while tile t is computed
   __shared__ __align__(16) unsigned char s_k[2][KT * KP];
   __shared__ __align__(16) unsigned char s_vt[2][D * VP];
-  __shared__ __align__(16) float s_g[2][KT];
+  __shared__ int s_e[2][KT / 64];   // the exponent e of each 64-key half
   __shared__ float4 s_dir[C::NDIR];
   __shared__ float s_rho[C::LR];
 
@@ -151,7 +161,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
 
   // Q' fragment: B[k = dim][n = query], lane (ln, g) holds dims 16j + 8g + 0..7.
   half8 qf[NKS];
-  float qscale_inv;
+  int qsh;   // queries held as q' 2^qsh
   {
     const float* qrow = a.qrot + (((seq * a.G + h % a.G) * a.n_q) + (qvalid ? q : 0)) * (3 * T);
     float v[NKS][8];
@@ -168,7 +178,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
     __builtin_frexpf(amax, &ex);
     const int sh = amax > 0.f ? 7 - ex : 0;   // row max into [64, 128)
     const float sc = __builtin_ldexpf(1.0f, sh);
-    qscale_inv = __builtin_ldexpf(1.0f, -sh);
+    qsh = sh;
 #pragma unroll
     for (int j = 0; j < NKS; ++j)
 #pragma unroll
@@ -198,14 +208,22 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
       const bool ok = k0 + kk < a.n_keys;
       unsigned char* krow = s_k[bs] + kk * KP;
       const int part = sw % S::PARTS;
+      // the half's exponent e: its largest gamma times 2^-e lies in [1/2, 1)
+      // (every wave of the half computes the same value; clamped so that
+      // 2^-e and 2^e are normal floats)
+      const float gk = ok ? st.gamma : 0.f;
+      int e = 0;
+      __builtin_frexpf(wave_max(gk), &e);
+      e = e < -126 ? -126 : (e > 126 ? 126 : e);
+      const float gs = gk * __builtin_ldexpf(1.0f, -e);
       if (part == 0) {
-        mq_rebuild<D, B, 0>(st, ok, s_dir, s_rho, krow);
-        s_g[bs][kk] = ok ? st.gamma : 0.f;
+        mq_rebuild<D, B, 0>(st, gs, s_dir, s_rho, krow);
+        if (lane == 0) s_e[bs][sw / S::PARTS] = e;
       } else if (part == 1) {
-        mq_rebuild<D, B, 1>(st, ok, s_dir, s_rho, krow);
+        mq_rebuild<D, B, 1>(st, gs, s_dir, s_rho, krow);
       } else if constexpr (S::PARTS > 2) {
-        if (part == 2) mq_rebuild<D, B, 2>(st, ok, s_dir, s_rho, krow);
-        else mq_rebuild<D, B, 3>(st, ok, s_dir, s_rho, krow);
+        if (part == 2) mq_rebuild<D, B, 2>(st, gs, s_dir, s_rho, krow);
+        else mq_rebuild<D, B, 3>(st, gs, s_dir, s_rho, krow);
       }
     }
     const int c = stid % (D / 8), kg = stid / (D / 8);
@@ -251,59 +269,69 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
     }
     const unsigned char* sk = s_k[cb];
     const unsigned char* svt = s_vt[cb];
-    const float* sg = s_g[cb];
     if (wave_q) {
-    // 3. 64 keys at a time: S^T, online softmax, O^T += V^T P^T.  Scores stay
-    // unscaled by the query's power of two (s' = q'.u'^ gamma 2^sh): the max
-    // is taken on s', and exp2(s' 2^-sh - m) is one fma and one exp.
+    // 3. 64 keys (one half) at a time: S^T, online softmax, O^T += V^T P^T.
+    // The accumulators hold s' = q'.(gamma 2^-e u'^) 2^qsh, so the score in
+    // log2 units is s' 2^(e - qsh): one factor per half, folded into the
+    // fma of the exponent.
     const bool partial = k0 + KT > a.n_keys;
 #pragma unroll 1
     for (int ch = 0; ch < KT / 64; ++ch) {
+      int ce = s_e[cb][ch] - qsh;
+      ce = ce < -126 ? -126 : (ce > 127 ? 127 : ce);   // a normal, nonzero factor
+      const float cs = __builtin_ldexpf(1.0f, ce);
       floatx16 s[2];
 #pragma unroll
-      for (int sb = 0; sb < 2; ++sb) {
-        const int kb = ch * 64 + sb * 32;
-        floatx16 acc;
+      for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[r] = 0.f;
+        for (int r = 0; r < 16; ++r) s[sb][r] = 0.f;
+      // the two 32-key blocks' chains interleaved: each MFMA's result is not
+      // needed by the next one issued
 #pragma unroll
-        for (int j = 0; j < NKS; ++j) {
-          const half8 kf = *(const half8*)(sk + (kb + ln) * KP + (16 * j + 8 * g) * 2);
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], acc, 0, 0, 0);
+      for (int j = 0; j < NKS; ++j)
+#pragma unroll
+        for (int sb = 0; sb < 2; ++sb) {
+          const half8 kf = *(const half8*)(sk + (ch * 64 + sb * 32 + ln) * KP + (16 * j + 8 * g) * 2);
+          s[sb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(kf, qf[j], s[sb], 0, 0, 0);
         }
-        // register r holds key row kb + 8 (r / 4) + 4 g + r % 4
+      // register r holds key row ch 64 + sb 32 + 8 (r / 4) + 4 g + r % 4
+      if (partial) {
 #pragma unroll
-        for (int rr = 0; rr < 4; ++rr) {
-          const float4 gv = *(const float4*)(sg + kb + 8 * rr + 4 * g);
-          acc[4 * rr] *= gv.x;
-          acc[4 * rr + 1] *= gv.y;
-          acc[4 * rr + 2] *= gv.z;
-          acc[4 * rr + 3] *= gv.w;
-        }
-        if (partial) {
+        for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
           for (int r = 0; r < 16; ++r)
-            if (k0 + kb + 8 * (r >> 2) + 4 * g + (r & 3) >= a.n_keys) acc[r] = -INFINITY;
-        }
-        s[sb] = acc;
+            if (k0 + ch * 64 + sb * 32 + 8 * (r >> 2) + 4 * g + (r & 3) >= a.n_keys) s[sb][r] = -INFINITY;
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
-      const float m_new = fmaxf(m_run, mx * qscale_inv);
-      // a row with no valid key yet keeps m = -inf; exponents use 0 then
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
+      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cs;
+      // Lazily raised reference m (log2 units, one per query): raised to the
+      // chunk's maximum, with l and o rescaled, only when a score exceeds it
+      // by more than kLazyLog2 (any lane of the wave), so p = 2^(s - m) <=
+      // 2^kLazyLog2, far inside fp16.  After the first chunk a raise is rare.
+      constexpr float kLazyLog2 = 8.f;
+      if (__any(mx > m_run + kLazyLog2)) {
+        const float m_new = fmaxf(m_run, mx);
+        // a row with no valid key yet keeps m = -inf (alpha is then moot)
+        const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f(m_run - m_new);
+        l_run *= alpha;
+#pragma unroll
+        for (int mb = 0; mb < NMB; ++mb)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+        m_run = m_new;
+      }
+      const float m_use = m_run == -INFINITY ? 0.f : m_run;
       float lsum = 0.f;
       half8 pf[2][2];
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r)
-          pf[sb][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], qscale_inv, -m_use));
+          pf[sb][r >> 3][r & 7] = (_Float16)__builtin_amdgcn_exp2f(__builtin_fmaf(s[sb][r], cs, -m_use));
       // l sums the fp16 p that P.V uses: v_dot2 over the packed pairs
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb)
@@ -314,12 +342,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
             const half2v pp = {pf[sb][hh][2 * e], pf[sb][hh][2 * e + 1]};
             lsum = __builtin_amdgcn_fdot2(pp, half2v{(_Float16)1.0f, (_Float16)1.0f}, lsum, false);
           }
-      l_run = __builtin_fmaf(l_run, alpha, lsum);
-      m_run = m_new;
-#pragma unroll
-      for (int mb = 0; mb < NMB; ++mb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) o[mb][r] *= alpha;
+      l_run += lsum;
 #pragma unroll
       for (int sb = 0; sb < 2; ++sb) {
 #pragma unroll

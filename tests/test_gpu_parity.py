@@ -867,13 +867,16 @@ def test_mq_edges(n_q, n):
     check_mq(WL.CONFIGS[4], 1, 1, n_q, n, 320, seed=n, label=f"mq-edge{n_q}x{n}")
 
 
-def _mq_with_values(vfix, vref):
+def _mq_with_values(vfix, vref, kfix=None):
     """Multi-query attention over a small cache whose bf16 V is rewritten by
-    vfix(v); the oracle attends over vref(v) (float64 of the bf16 values)."""
+    vfix(v) (and the keys by kfix(keys)); the oracle attends over vref(v)
+    (float64 of the bf16 values)."""
     octo = _octo()
     cfg = WL.CONFIGS[4]
     d, b, n, cap, n_q = cfg.d, cfg.b, 500, 512, 40
     keys = WL.make_keys(cfg, "cuda", seed=21, n_seq=1, n=n)
+    if kfix is not None:
+        keys = kfix(keys).contiguous()
     g = gcb(d, b)
     cache = octo.Cache(g, 1, cap)
     octo.octo_encode(g, keys, cache)
@@ -917,6 +920,20 @@ def test_mq_values_beyond_fp16_saturate():
         return w.contiguous()
     err = _mq_with_values(fix, lambda x: np.clip(x, -65504.0, 65504.0))
     say(f"[mq fp16 saturation] worst rel err {err:.2e}")
+    assert err <= 2e-3
+
+
+def test_mq_key_norms_spread_within_a_tile():
+    """The multi-query path stages each 64-key half as fp16 rows gamma 2^-e u'^
+    with one power of two per half: key norms spread over 2^-12 .. 2^2 inside
+    every half, with zero keys among them, still give the oracle's result."""
+    def kfix(k):
+        g = torch.Generator(device="cuda").manual_seed(9)
+        f = torch.exp2(torch.rand(k.shape[:-1], generator=g, device="cuda") * 14.0 - 12.0)
+        f[0, ::37] = 0.0
+        return (k.float() * f[..., None]).to(k.dtype)
+    err = _mq_with_values(lambda v: v, lambda x: x, kfix=kfix)
+    say(f"[mq key-norm spread] worst rel err {err:.2e}")
     assert err <= 2e-3
 
 
