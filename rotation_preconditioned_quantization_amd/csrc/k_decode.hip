@@ -98,12 +98,13 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 // one float4 per triplet code holds rho^ n^ directly; otherwise unit
 // directions per (i_xi, i_eta) plus the rho centroids.  REP (up to 10 bits per
 // triplet): the combined table is held in NCOPY copies (as many as fit
-// 64 KiB, at most 16), entry e of copy c at float4 slot NCOPY e + c, and lane
+// 128 KiB, at most 16), entry e of copy c at float4 slot NCOPY e + c, and lane
 // l reads copy l % NCOPY.  The LDS serves 16 lanes per pass; with 16 copies
 // they hit 16 different 4-bank groups whatever codes they look up, so random
 // gathers are conflict-free (4 LDS cycles per wavefront read instead of about
-// 11); with 4 copies (the 1024-entry table at 3 bits) only the 4 lanes of a
-// copy can collide.  q holds the rotated queries of the (up to) 4 heads of
+// 11); with 8 copies (the 1024-entry table at 3 bits) only the 2 lanes of a
+// copy can collide (8 copies measured 3.5 % faster than 4 in the logits
+// kernel at 3 bits + QJL, whose LDS is busy most of the time).  q holds the rotated queries of the (up to) 4 heads of
 // this pass, rows padded with zeros; with QJL, qp holds p = kappa S q'
 // and lut its nibble sums.
 template <int D, int B, bool QJL, bool REP>
@@ -112,7 +113,7 @@ struct SQShared {
   static_assert(!REP || C::BT <= 10, "replicated table needs the combined table");
   static constexpr bool kCombined = C::BT <= 10;
   static constexpr int NENT = kCombined ? (1 << C::BT) : C::NDIR;
-  static constexpr int NCOPY = !REP ? 1 : (4096 / NENT < 16 ? 4096 / NENT : 16);
+  static constexpr int NCOPY = !REP ? 1 : (8192 / NENT < 16 ? 8192 / NENT : 16);
   static constexpr int QD = ((3 * C::T + 15) / 16) * 16;   // whole 16-dim groups (QRegs)
   float4 tab[NENT * NCOPY];
   float rho[C::LR];
@@ -133,9 +134,11 @@ constexpr bool logits_rep() { return B <= 3; }
 template <int B>
 constexpr bool attn_rep() { return B <= 2; }
 
-// Waves per k_logits block: 8 with the replicated table (B <= 3), else 4.
+// Waves per k_logits block: with the replicated table (B <= 3) 16 at 3 bits
+// (its 128 KiB of copies allow one block per CU) and 8 below (two blocks per
+// CU), else 4; always 4 waves per SIMD.
 template <int B>
-constexpr int logits_waves() { return logits_rep<B>() ? 8 : 4; }
+constexpr int logits_waves() { return !logits_rep<B>() ? 4 : (B == 3 ? 16 : 8); }
 
 // Values the block prologue loads from global memory besides the LDS tables
 // (which go to LDS directly): wave w's query head g0 + w (lane l holds the
@@ -440,9 +443,9 @@ __device__ __forceinline__ void sq_finish_prologue(const DecodeArgs& a, int hcou
 // ---------------------------------------------------------------------------
 template <int D, int B, bool QJL>
 __global__ __launch_bounds__(64 * logits_waves<B>())
-__attribute__((amdgpu_waves_per_eu(logits_waves<B>() / 2))) void k_logits(DecodeArgs a) {
-  // replicated table where it fits (conflict-free gathers); the 64 KiB it can
-  // take leaves room for two blocks per CU, so such blocks have 8 waves
+__attribute__((amdgpu_waves_per_eu(logits_rep<B>() ? 4 : 2))) void k_logits(DecodeArgs a) {
+  // replicated table where it fits (few or no gather conflicts), blocks of
+  // logits_waves<B>() waves
   constexpr bool REP = logits_rep<B>();
   constexpr int NW = logits_waves<B>();
   __shared__ SQShared<D, B, QJL, REP> sh;

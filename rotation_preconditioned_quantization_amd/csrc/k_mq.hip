@@ -88,6 +88,19 @@ __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t,
   }
 }
 
+// max / sum of x over the lane pair (l, l ^ 32): v_permlane32_swap exchanges
+// the two halves of the wavefront without a trip through the LDS
+// (lane l < 32 finds its partner's value in the second result, lane l >= 32
+// in the first; the other result is its own)
+__device__ __forceinline__ float pair32_max(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_sum(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
 // bf16 pair -> f16 pair (V of the multi-query path must lie in fp16 range).
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t w) {
   return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(__uint_as_float(w << 16),
@@ -173,7 +186,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
         v[j][i] = qvalid ? qrow[16 * j + 8 * g + i] : 0.f;
         amax = fmaxf(amax, fabsf(v[j][i]));
       }
-    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+    amax = pair32_max(amax);
     int ex = 0;
     __builtin_frexpf(amax, &ex);
     const int sh = amax > 0.f ? 7 - ex : 0;   // row max into [64, 128)
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
       for (int sb = 0; sb < 2; ++sb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s[sb][r]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32, 64)) * cs;
+      mx = pair32_max(mx) * cs;
       // Lazily raised reference m (log2 units, one per query): raised to the
       // chunk's maximum, with l and o rescaled, only when a score exceeds it
       // by more than kLazyLog2 (any lane of the wave), so p = 2^(s - m) <=
@@ -363,7 +376,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
     __syncthreads();  // this tile's buffers are free, the next tile's staged
   }
 
-  l_run += __shfl_xor(l_run, 32, 64);
+  l_run = pair32_sum(l_run);
   if (qvalid) {
     float* dst = a.part + (((int64_t)bh * a.n_q + q) * a.n_split + blockIdx.x) * (D + 2);
     if (g == 0) {
