@@ -283,12 +283,18 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
     } else {
-      // stride-1 butterflies straight from the packed 16-bit pairs
+      // strides 1 and 2 on the matrix cores, straight from the packed 16-bit
+      // elements (h4_apply)
+      const uint2 h4 = h4_row<KT>(lane);
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) {
-        const uint32_t wd[4] = {rowbits[c].x, rowbits[c].y, rowbits[c].z, rowbits[c].w};
+        const wht4_t y0 = h4_apply<KT>(h4, rowbits[c].x, rowbits[c].y);
+        const wht4_t y1 = h4_apply<KT>(h4, rowbits[c].z, rowbits[c].w);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) stage1_pair<KT>(wd[k], v[8 * c + 2 * k], v[8 * c + 2 * k + 1]);
+        for (int k = 0; k < 4; ++k) {
+          v[8 * c + k] = y0[k];
+          v[8 * c + 4 + k] = y1[k];
+        }
       }
     }
   }
@@ -306,7 +312,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
     for (int j = 0; j < D; ++j) v[j] *= scale;
   }
   if constexpr (KT == DT_F32) wht_regs<D>(v);
-  else wht_regs_from<D, 2>(v);
+  else wht_regs_from<D, 4>(v);
 
   const float sx = a.t.qx.scale, bx = a.t.qx.bias;
   const float se = a.t.qe.scale, be = a.t.qe.bias;
@@ -331,11 +337,11 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
       tot += e[i];
       pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
     }
-    const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
     // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
+    const RhoQuant<C::LR> rq(a.t, tot);
 #pragma unroll
     for (int i = 0; i < T; ++i)
-      pack_code<C::BT>(words, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+      pack_code<C::BT>(words, i, rq.index(e[i], s_qr, sr, mr) << (C::BX + C::BE));
   } else {
     // Joint rounding ([YL] 联合取整).  Pass 1: the energy and the scalar
     // (xi, eta) indices, the centre of the search.  Pass 2, per triplet t of
@@ -628,16 +634,23 @@ void k_encode256(EncodeArgs a) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
     } else {
-      // stride-1 butterflies straight from the packed 16-bit pairs
+      // strides 1 and 2 on the matrix cores, straight from the packed 16-bit
+      // elements (h4_apply)
+      const uint2 h4 = h4_row<KT>(lane);
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) {
-        const uint32_t wd[4] = {rowbits[c].x, rowbits[c].y, rowbits[c].z, rowbits[c].w};
+        const wht4_t y0 = h4_apply<KT>(h4, rowbits[c].x, rowbits[c].y);
+        const wht4_t y1 = h4_apply<KT>(h4, rowbits[c].z, rowbits[c].w);
 #pragma unroll
-        for (int k = 0; k < 4; ++k) stage1_pair<KT>(wd[k], v[8 * c + 2 * k], v[8 * c + 2 * k + 1]);
+        for (int k = 0; k < 4; ++k) {
+          v[8 * c + k] = y0[k];
+          v[8 * c + 4 + k] = y1[k];
+        }
       }
     }
   }
-  // the key's exponent scale (as encode_one_key: from the largest stage-1 value)
+  // the key's exponent scale (as encode_one_key: from the largest value after
+  // the first two stages; fp32 keys: the raw values)
   float amax = 0.f;
 #pragma unroll
   for (int j = 0; j < 128; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
@@ -651,7 +664,7 @@ void k_encode256(EncodeArgs a) {
     for (int j = 0; j < 128; ++j) v[j] *= scale;
   }
   if constexpr (KT == DT_F32) wht_regs<128>(v);
-  else wht_regs_from<128, 2>(v);
+  else wht_regs_from<128, 4>(v);
   // stride 128: y_j = a_j + a_{j+128} (first lane), a_j - a_{j+128} (second)
 #pragma unroll
   for (int j = 0; j < 128; ++j) {
@@ -696,10 +709,10 @@ void k_encode256(EncodeArgs a) {
   const float s2p = pair_xchg(s2, lane);
   const float tot = hi ? s2 : s2p;
   if constexpr (!JR) {
-    const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+    const RhoQuant<C::LR> rq(a.t, tot);
 #pragma unroll
     for (int i = 0; i < TH; ++i)
-      pack_code<C::BT>(wl, i, quant1_clamp(e[i] * inv_tot, s_qr, sr, mr) << (C::BX + C::BE));
+      pack_code<C::BT>(wl, i, rq.index(e[i], s_qr, sr, mr) << (C::BX + C::BE));
   } else {
     // joint rounding of every triplet of the unit key around its scalar
     // (xi, eta) indices

@@ -94,19 +94,33 @@ __device__ __forceinline__ bf16x4 pack_bf16x4(uint32_t lo, uint32_t hi) {
 }
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// First butterfly stage (stride 1) straight from a packed pair of 16-bit
-// inputs: a + b and a - b with one v_dot2 each (weights +-1, products exact,
-// fp32 sum), no separate conversion.
+// The first two butterfly stages (strides 1 and 2), i.e. H_4 applied to 4
+// consecutive 16-bit elements, on the matrix cores: v_mfma_f32_4x4x4_16b_bf16
+// (or _f16) with B = a lane's own 4 elements (the two packed words as they
+// are stored, K = element order) and A = the 4 x 4 Sylvester H_4, row
+// lane % 4 supplied by each lane of a 4-lane block, so lane l receives
+// H_4 x of its own elements.  The products are exact (+-1 times a 16-bit
+// value) and the sums fp32.  Every encoder forms these two stages this way,
+// so all of them produce the same values.
+typedef float wht4_t __attribute__((ext_vector_type(4)));
 template <int DT>
-__device__ __forceinline__ void stage1_pair(uint32_t w, float& s, float& d) {
+__device__ __forceinline__ uint2 h4_row(int lane) {
+  constexpr uint32_t one = DT == DT_BF16 ? 0x3f80u : 0x3c00u;
+  const int m = lane & 3;
+  uint32_t e[4];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) e[k] = one | ((uint32_t)(__builtin_popcount(m & k) & 1) << 15);
+  return make_uint2(e[0] | (e[1] << 16), e[2] | (e[3] << 16));
+}
+template <int DT>
+__device__ __forceinline__ wht4_t h4_apply(uint2 row, uint32_t w0, uint32_t w1) {
+  const wht4_t z = {0.f, 0.f, 0.f, 0.f};
   if constexpr (DT == DT_BF16) {
-    const bf16x2_t a = __builtin_bit_cast(bf16x2_t, w);
-    s = __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, 0x3f803f80u), 0.0f, false);
-    d = __builtin_amdgcn_fdot2_f32_bf16(a, __builtin_bit_cast(bf16x2_t, 0xbf803f80u), 0.0f, false);
+    return __builtin_amdgcn_mfma_f32_4x4x4bf16_1k(pack_bf16x4(row.x, row.y), pack_bf16x4(w0, w1), z, 0, 0, 0);
   } else {
-    const f16x2_t a = __builtin_bit_cast(f16x2_t, w);
-    s = __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, 0x3c003c00u), 0.0f, false);
-    d = __builtin_amdgcn_fdot2(a, __builtin_bit_cast(f16x2_t, 0xbc003c00u), 0.0f, false);
+    typedef _Float16 f16x4_t __attribute__((ext_vector_type(4)));
+    return __builtin_amdgcn_mfma_f32_4x4x4f16(__builtin_bit_cast(f16x4_t, make_uint2(row.x, row.y)),
+                                              __builtin_bit_cast(f16x4_t, make_uint2(w0, w1)), z, 0, 0, 0);
   }
 }
 

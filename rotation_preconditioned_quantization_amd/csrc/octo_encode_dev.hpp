@@ -25,6 +25,39 @@ __device__ __forceinline__ uint32_t quant1_clamp(float x, const uint2* t, float 
   return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
 }
 
+// rho index of a triplet from its energy e = |t_i|^2 and the key's total
+// energy tot = |y|^2: rho_i^2 = e / tot against the squared midpoints, i.e.
+// #{k : e > m_k^2 tot}.  With at most 4 rho levels (b <= 3) the thresholds
+// m_k^2 tot are formed once per key and each triplet takes one compare per
+// midpoint; with more levels the index comes from the squared-midpoint
+// bucket table on e / tot.  Every encoder takes its rho index through
+// RhoQuant, so all of them round the same way.
+template <int LR>
+struct RhoQuant {
+  static constexpr bool kDirect = LR <= 4;
+  float thr[kDirect && LR > 1 ? LR - 1 : 1];
+  float inv_tot;
+  __device__ __forceinline__ RhoQuant(const DevTables& t, float tot) {
+    if constexpr (kDirect) {
+#pragma unroll
+      for (int k = 0; k < LR - 1; ++k) thr[k] = t.rho_mid2[k] * tot;
+      inv_tot = 0.f;
+    } else {
+      inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+    }
+  }
+  __device__ __forceinline__ uint32_t index(float e, const uint2* tqr, float scale, float nbm1) const {
+    if constexpr (kDirect) {
+      uint32_t i = 0u;
+#pragma unroll
+      for (int k = 0; k < LR - 1; ++k) i += e > thr[k] ? 1u : 0u;
+      return i;
+    } else {
+      return quant1_clamp(e * inv_tot, tqr, scale, nbm1);
+    }
+  }
+};
+
 // Triplet i of the rotated key, zero padded past D.
 template <int D>
 __device__ __forceinline__ void triplet_of(const float (&v)[D], int i, float& x, float& y, float& z) {
@@ -75,12 +108,12 @@ __device__ __forceinline__ void store_key_word(uint32_t* packed, int64_t cap, in
   tile[256 * g + (int)(pos & 63) * width + (w & 3)] = val;
 }
 
-// Encode one key with one wavefront: lane l holds elements l + 64 r, the WHT
-// butterflies run across lanes by shuffles (as in the query rotation), one
-// triplet per lane.  Every value goes through the same fp32 operations in
-// the same order as in the bulk encoder (stage 1 by v_dot2 on the
-// sign-flipped 16-bit pair, the serial energy sum over triplets, the same
-// quantiser tables), so both write identical words and gamma.
+// Encode one key with one wavefront: the WHT butterflies run across lanes by
+// shuffles (as in the query rotation), one triplet per lane.  Every value
+// goes through the same fp32 operations in the same order as in the bulk
+// encoders (for 16-bit keys the first two stages by the same H_4 MFMA on the
+// sign-flipped words, the serial energy sum over triplets, the same
+// quantisers), so all of them write identical words and gamma.
 //   keyrow: the key's d elements (dtype KT); tqx/tqe/tqr: the quantiser
 //   tables (LDS or global); sv (3T floats), se (T floats), sw (W words):
 //   wave-private LDS scratch.  On return sw holds the packed words (visible
@@ -93,10 +126,10 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
 #pragma clang fp contract(off)
   using C = Codec<D, B>;
   constexpr int T = C::T, W = C::W, NV = D / 64;
-  // element j of the sign-flipped key, stage 1 applied (Sylvester order):
-  // lane pairs (2m, 2m+1) take x_2m + x_2m+1 and x_2m - x_2m+1
-  float x[NV];
+  int sexp = 0;
   if constexpr (KT == DT_F32) {
+    // lane l holds elements l + 64 r of the sign-flipped key
+    float x[NV];
     const float* row = (const float*)keyrow;
 #pragma unroll
     for (int r = 0; r < NV; ++r) {
@@ -104,53 +137,86 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
       const uint32_t sb = (t.sign_bits[e >> 5] >> (e & 31)) & 1u;
       x[r] = __uint_as_float(__float_as_uint(row[e]) ^ (sb << 31));
     }
-  } else {
-    const uint32_t* row = (const uint32_t*)keyrow;
+    float amax = 0.f;
 #pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const int e = lane + 64 * r, m = e >> 1;
+    for (int r = 0; r < NV; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[r]));
+    amax = wave_max(amax);
+    int ex = 0;
+    __builtin_frexpf(amax, &ex);
+    const int sexp0 = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+    if (sexp0 != 0) {
+      const float scale = __builtin_ldexpf(1.0f, -sexp0);
+#pragma unroll
+      for (int r = 0; r < NV; ++r) x[r] *= scale;
+    }
+    sexp = sexp0;
+    // butterflies of stride 1 .. 32 across lanes, then 64, 128, ... between a
+    // lane's values
+#pragma unroll
+    for (int h = 1; h < 64 && h < D; h <<= 1) {
+#pragma unroll
+      for (int r = 0; r < NV; ++r) {
+        const float o = __shfl_xor(x[r], h, 64);
+        x[r] = (lane & h) ? (o - x[r]) : (x[r] + o);
+      }
+    }
+#pragma unroll
+    for (int hr = 1; hr < NV; hr <<= 1) {
+#pragma unroll
+      for (int r = 0; r < NV; ++r) {
+        if (r & hr) continue;
+        const float a0 = x[r], a1 = x[r + hr];
+        x[r] = a0 + a1;
+        x[r + hr] = a0 - a1;
+      }
+    }
+#pragma unroll
+    for (int r = 0; r < NV; ++r) sv[lane + 64 * r] = x[r];
+  } else {
+    // lane l takes the 4-element group g = l mod (D / 4) (lanes past D / 4
+    // repeat the first ones): strides 1 and 2 on the matrix cores from the
+    // two sign-flipped words (h4_apply, as the bulk encoders), then strides
+    // 4, 8, ... as lane pairs g, g ^ (stride / 4)
+    constexpr int NG = D / 4;
+    static_assert(NG <= 64 && (NG & (NG - 1)) == 0, "one 4-element group per lane");
+    const int g = lane & (NG - 1);
+    const uint32_t* row = (const uint32_t*)keyrow;
+    uint32_t w[2];
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int m = 2 * g + k;   // elements 2m, 2m + 1
       const uint32_t s0 = (t.sign_bits[(2 * m) >> 5] >> ((2 * m) & 31)) & 1u;
       const uint32_t s1 = (t.sign_bits[(2 * m + 1) >> 5] >> ((2 * m + 1) & 31)) & 1u;
-      const uint32_t wd = row[m] ^ ((s0 << 15) | (s1 << 31));
-      float sum, dif;
-      stage1_pair<KT>(wd, sum, dif);
-      x[r] = (e & 1) ? dif : sum;
+      w[k] = row[m] ^ ((s0 << 15) | (s1 << 31));
+    }
+    const wht4_t y = h4_apply<KT>(h4_row<KT>(lane), w[0], w[1]);
+    float x[4] = {y[0], y[1], y[2], y[3]};
+    float amax = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[i]));
+    amax = wave_max(amax);
+    int ex = 0;
+    __builtin_frexpf(amax, &ex);
+    const int sexp0 = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+    if (sexp0 != 0) {
+      const float scale = __builtin_ldexpf(1.0f, -sexp0);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) x[i] *= scale;
+    }
+    sexp = sexp0;
+#pragma unroll
+    for (int h = 1; h < NG; h <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float o = __shfl_xor(x[i], h, 64);
+        x[i] = (g & h) ? (o - x[i]) : (x[i] + o);
+      }
+    }
+    if (lane < NG) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sv[4 * g + i] = x[i];
     }
   }
-  float amax = 0.f;
-#pragma unroll
-  for (int r = 0; r < NV; ++r) amax = __builtin_fmaxf(amax, __builtin_fabsf(x[r]));
-  amax = wave_max(amax);
-  int ex = 0;
-  __builtin_frexpf(amax, &ex);
-  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
-  if (sexp != 0) {
-    const float scale = __builtin_ldexpf(1.0f, -sexp);
-#pragma unroll
-    for (int r = 0; r < NV; ++r) x[r] *= scale;
-  }
-  // remaining butterflies: stride 1 (fp32 keys only), then 2 .. 32 across
-  // lanes, then 64, 128, ... between a lane's values (element l + 64 r)
-#pragma unroll
-  for (int h = (KT == DT_F32 ? 1 : 2); h < 64 && h < D; h <<= 1) {
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      const float o = __shfl_xor(x[r], h, 64);
-      x[r] = (lane & h) ? (o - x[r]) : (x[r] + o);
-    }
-  }
-#pragma unroll
-  for (int hr = 1; hr < NV; hr <<= 1) {
-#pragma unroll
-    for (int r = 0; r < NV; ++r) {
-      if (r & hr) continue;
-      const float a0 = x[r], a1 = x[r + hr];
-      x[r] = a0 + a1;
-      x[r + hr] = a0 - a1;
-    }
-  }
-#pragma unroll
-  for (int r = 0; r < NV; ++r) sv[lane + 64 * r] = x[r];
   if (lane < 3 * T - D) sv[D + lane] = 0.f;
   for (int w = lane; w < W; w += 64) sw[w] = 0u;
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -177,11 +243,11 @@ __device__ __forceinline__ float encode_one_key(const void* keyrow, const DevTab
   float tot = 0.f;
   for (int i2 = 0; i2 < T; ++i2) tot += se[i2];
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
-  const float inv_tot = tot > 0.f ? __builtin_amdgcn_rcpf(tot) : 0.f;
+  const RhoQuant<C::LR> rq(t, tot);
 #pragma unroll
   for (int m = 0; m < NT; ++m) {
     const int i0 = lane + 64 * m;
-    const uint32_t rc = quant1_clamp(e[m] * inv_tot, tqr, t.qr2.scale, (float)(t.qr2.nb - 1));
+    const uint32_t rc = rq.index(e[m], tqr, t.qr2.scale, (float)(t.qr2.nb - 1));
     const uint32_t code = xe[m] | (rc << (C::BX + C::BE));
     if (i0 < T) {
       const int p = i0 * C::BT, wi = p >> 5, off = p & 31;

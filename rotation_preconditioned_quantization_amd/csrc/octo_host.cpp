@@ -214,6 +214,7 @@ constexpr size_t kTableGuardBytes = 1024;
 // The kernels' tables, built on the host.
 struct HostTables {
   HostB1 qx, qe, qr2;
+  std::vector<double> rho_mid2;   // squared rho midpoints
   std::vector<float> dir, rho, trip, st;
   std::vector<_Float16> s16;
 };
@@ -230,6 +231,7 @@ octo_status make_host_tables(octo_codebook* cb, HostTables& h) {
   const double hi = m2.empty() ? 1.0 : std::min(1.0, 1.25 * m2.back() + 1e-3);
   if (!build_bucket1(m2, 0.0, hi, &qr2))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
+  h.rho_mid2 = m2;
 
   const int ndir = 1 << (cb->bx + cb->be);
   std::vector<float>& dir = h.dir;
@@ -364,6 +366,8 @@ octo_status upload_tables(octo_codebook* cb, const HostTables& h) {
   t.S16 = s16.empty() ? nullptr : (const uint4*)(base + reg[7].off);
   for (int k = 0; k < 8; ++k) t.sign_bits[k] = cb->sign_bits[k];
   t.qjl_kappa = cb->qjl_kappa;
+  for (int k = 0; k < 3; ++k)
+    t.rho_mid2[k] = k < (int)h.rho_mid2.size() ? (float)h.rho_mid2[k] : INFINITY;
   return OCTO_OK;
 }
 

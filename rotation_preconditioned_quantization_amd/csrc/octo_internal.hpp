@@ -40,6 +40,7 @@ struct DevTables {
   const uint4* S16;         // S (row-major) as f16 planes [S_hi | S_lo], S_hi = f16(S), S_lo = f16(S - S_hi)
   uint32_t sign_bits[8];    // bit j of the 256-bit mask set <=> WHT sign s_j = -1
   float qjl_kappa;          // QJL estimator constant: <q', r'> ~ kappa |r'| <S q', sgn(S r')>
+  float rho_mid2[3];        // the first 3 squared rho midpoints (fp32; +inf past the last)
 };
 
 struct EncodeArgs {
