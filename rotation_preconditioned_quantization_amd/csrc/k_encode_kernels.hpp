@@ -261,9 +261,11 @@ __device__ __forceinline__ uint32_t joint_code(float x, float y, float z, uint32
   return best;
 }
 
-// Encode the 64-key tile at j0: one key per lane, entirely in registers.
+// Encode the 64-key tile at j0 from its raw rows (load_rows): one key per
+// lane, entirely in registers.
 template <int D, int B, int KT, bool QJL, bool JR>
 __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
+                                            const uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE],
                                             unsigned char* s_keys, const uint4& smask,
                                             const uint2* s_qx, const uint2* s_qe, const uint2* s_qr,
                                             const unsigned char* s_S, const float4* s_dir,
@@ -274,11 +276,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   float v[D];
   {
     uint4 rowbits[S::CPR];
-    {
-      uint4 raw[S::NP][S::PER_LANE];
-      load_rows<D, KT>(a, seq, j0, lane, raw);
-      stage_rows<D, KT>(raw, lane, s_keys, smask, rowbits);
-    }
+    stage_rows<D, KT>(raw, lane, s_keys, smask, rowbits);
     if constexpr (KT == DT_F32) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
@@ -436,8 +434,19 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   }
 }
 
+// QJL at d = 128 runs one wave per SIMD (the projection's operands, and the
+// LDS copy of S allows one block per CU); with scalar rounding the next
+// tile's rows are loaded there while the current one is encoded (2 % faster
+// on 4 M keys; with joint rounding 30 % slower: not there).
+template <int D, bool QJL, bool JR>
+constexpr bool enc_prefetch() { return QJL && !JR && D == 128; }
+
+// Two waves per SIMD except for QJL at d = 128 (the one-key-per-lane state
+// fits 256 registers; left alone the allocator took 257 at b = 1 and halved
+// the occupancy).
 template <int D, int B, int KT, bool QJL, bool JR>
-__global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) {
+__global__ __launch_bounds__(64 * enc_waves<QJL>())
+__attribute__((amdgpu_waves_per_eu(QJL && D == 128 ? 1 : 2))) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
   using S = Stage<D, KT>;
   constexpr int EW = enc_waves<QJL>();
@@ -469,12 +478,35 @@ __global__ __launch_bounds__(64 * enc_waves<QJL>()) void k_encode(EncodeArgs a) 
   __syncthreads();
   const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
   // A wave encodes one 64-key tile; with QJL the grid is smaller than the
-  // key count and the block's waves take tiles round-robin.
-  for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
-       j0 += (int64_t)gridDim.x * EW * kTile) {
-    encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S, s_dir,
-                               s_rho);
-    if constexpr (!QJL) break;
+  // key count and the block's waves take tiles round-robin (enc_prefetch:
+  // the next tile's rows loading while the current one is encoded, since no
+  // other wave on the SIMD would hide the loads; with no tile left the
+  // prefetch re-reads the current one, so every load is in bounds).
+  int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile;
+  if (j0 >= a.n_new) return;
+  const int64_t step = (int64_t)gridDim.x * EW * kTile;
+  if constexpr (!enc_prefetch<D, QJL, JR>()) {
+    for (; j0 < a.n_new; j0 += step) {
+      uint4 raw[S::NP][S::PER_LANE];
+      load_rows<D, KT>(a, seq, j0, lane, raw);
+      encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
+                                     s_dir, s_rho);
+      if constexpr (!QJL) break;
+    }
+  } else {
+    uint4 raw[S::NP][S::PER_LANE];
+    load_rows<D, KT>(a, seq, j0, lane, raw);
+    for (; j0 < a.n_new; j0 += step) {
+      const int64_t jn = j0 + step < a.n_new ? j0 + step : j0;
+      uint4 nxt[S::NP][S::PER_LANE];
+      load_rows<D, KT>(a, seq, jn, lane, nxt);
+      encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
+                                     s_dir, s_rho);
+#pragma unroll
+      for (int h = 0; h < S::NP; ++h)
+#pragma unroll
+        for (int k = 0; k < S::PER_LANE; ++k) raw[h][k] = nxt[h][k];
+    }
   }
 }
 
