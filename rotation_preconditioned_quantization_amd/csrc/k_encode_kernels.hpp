@@ -113,9 +113,13 @@ __device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][
   }
 }
 
-// Waves (64-key tiles in flight) per encoder block.
-template <bool QJL>
-constexpr int enc_waves() { return 4; }
+// Waves (64-key tiles in flight) per encoder block: 4, or 8 with QJL below
+// 5 bits, where one block per CU holds the LDS copy of S and two waves per
+// SIMD then overlap one wave's projection on the matrix cores with the
+// other's VALU work (at b = 5 the 4096-entry direction table leaves no room
+// for 8 waves' staging buffers).
+template <bool QJL, int B>
+constexpr int enc_waves() { return QJL && B < 5 ? 8 : 4; }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -422,6 +426,9 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
           }
         }
       }
+      // the norm is formed here: left to itself the compiler sinks this sum
+      // past the projection, keeping all D residuals live through it
+      asm volatile("" : "+v"(nu2));
       const float nu = __builtin_sqrtf(nu2);
       uint32_t sbits[D / 32];
       qjl_signs<D>(v, s_S, lane, sbits);
@@ -434,22 +441,15 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   }
 }
 
-// QJL at d = 128 runs one wave per SIMD (the projection's operands, and the
-// LDS copy of S allows one block per CU); with scalar rounding the next
-// tile's rows are loaded there while the current one is encoded (2 % faster
-// on 4 M keys; with joint rounding 30 % slower: not there).
-template <int D, bool QJL, bool JR>
-constexpr bool enc_prefetch() { return QJL && !JR && D == 128; }
-
-// Two waves per SIMD except for QJL at d = 128 (the one-key-per-lane state
-// fits 256 registers; left alone the allocator took 257 at b = 1 and halved
-// the occupancy).
+// Two waves per SIMD (the one-key-per-lane state fits 256 registers; left
+// alone the allocator took 257 at b = 1 and halved the occupancy), except
+// with QJL at 5 bits, where the LDS allows one wave per SIMD anyway.
 template <int D, int B, int KT, bool QJL, bool JR>
-__global__ __launch_bounds__(64 * enc_waves<QJL>())
-__attribute__((amdgpu_waves_per_eu(QJL && D == 128 ? 1 : 2))) void k_encode(EncodeArgs a) {
+__global__ __launch_bounds__((64 * enc_waves<QJL, B>()))
+__attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : 2))) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
   using S = Stage<D, KT>;
-  constexpr int EW = enc_waves<QJL>();
+  constexpr int EW = enc_waves<QJL, B>();
   __shared__ __align__(16) unsigned char s_keys[EW][S::NR * S::PITCH];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
   __shared__ __align__(16) unsigned char s_S[QJL ? SLds<D>::BYTES : 16];
@@ -478,35 +478,14 @@ __attribute__((amdgpu_waves_per_eu(QJL && D == 128 ? 1 : 2))) void k_encode(Enco
   __syncthreads();
   const uint4 smask = chunk_sign_mask<D, KT>(a.t.sign_bits, lane % S::CPR);
   // A wave encodes one 64-key tile; with QJL the grid is smaller than the
-  // key count and the block's waves take tiles round-robin (enc_prefetch:
-  // the next tile's rows loading while the current one is encoded, since no
-  // other wave on the SIMD would hide the loads; with no tile left the
-  // prefetch re-reads the current one, so every load is in bounds).
-  int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile;
-  if (j0 >= a.n_new) return;
-  const int64_t step = (int64_t)gridDim.x * EW * kTile;
-  if constexpr (!enc_prefetch<D, QJL, JR>()) {
-    for (; j0 < a.n_new; j0 += step) {
-      uint4 raw[S::NP][S::PER_LANE];
-      load_rows<D, KT>(a, seq, j0, lane, raw);
-      encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
-                                     s_dir, s_rho);
-      if constexpr (!QJL) break;
-    }
-  } else {
+  // key count and the block's waves take tiles round-robin.
+  for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
+       j0 += (int64_t)gridDim.x * EW * kTile) {
     uint4 raw[S::NP][S::PER_LANE];
     load_rows<D, KT>(a, seq, j0, lane, raw);
-    for (; j0 < a.n_new; j0 += step) {
-      const int64_t jn = j0 + step < a.n_new ? j0 + step : j0;
-      uint4 nxt[S::NP][S::PER_LANE];
-      load_rows<D, KT>(a, seq, jn, lane, nxt);
-      encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
-                                     s_dir, s_rho);
-#pragma unroll
-      for (int h = 0; h < S::NP; ++h)
-#pragma unroll
-        for (int k = 0; k < S::PER_LANE; ++k) raw[h][k] = nxt[h][k];
-    }
+    encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
+                                   s_dir, s_rho);
+    if constexpr (!QJL) break;
   }
 }
 
@@ -815,11 +794,11 @@ inline hipError_t launch_encode256_t(const EncodeArgs& a, bool joint, int64_t n_
 template <int D, int B, int KT, bool QJL, bool JR>
 inline hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
-  constexpr int EW = enc_waves<QJL>();
+  constexpr int EW = enc_waves<QJL, B>();
   const int64_t per = (int64_t)EW * kTile;
   int64_t gx = (a.n_new + per - 1) / per;
-  // With QJL each block first stages the matrix in LDS: a grid of about two
-  // blocks per compute unit then loops over the tiles.
+  // With QJL each block first stages the matrix in LDS and then loops over
+  // the tiles: a grid of about 512 blocks (one resident per compute unit).
   if (QJL) gx = std::min<int64_t>(gx, std::max<int64_t>(1, (512 + n_seq - 1) / n_seq));
   const dim3 grid((unsigned)gx, (unsigned)n_seq);
   hipLaunchKernelGGL((k_encode<D, B, KT, QJL, JR>), grid, dim3(64 * EW), 0, s, a);
@@ -916,10 +895,10 @@ inline int enc_copy_recs(const char* kernel, LdsCopyRec* out, int n, int max) {
 template <int B>
 inline int enc_copy_recs_b(LdsCopyRec* out, int n, int max) {
 #define OCTO_REC_D(D)                                                                            \
-  n = enc_copy_recs<D, B, false, false, 64 * enc_waves<false>()>("k_encode", out, n, max);       \
-  n = enc_copy_recs<D, B, false, true, 64 * enc_waves<false>()>("k_encode (joint)", out, n, max); \
-  n = enc_copy_recs<D, B, true, false, 64 * enc_waves<true>()>("k_encode (qjl)", out, n, max);    \
-  n = enc_copy_recs<D, B, true, true, 64 * enc_waves<true>()>("k_encode (qjl, joint)", out, n, max); \
+  n = enc_copy_recs<D, B, false, false, 64 * enc_waves<false, B>()>("k_encode", out, n, max);       \
+  n = enc_copy_recs<D, B, false, true, 64 * enc_waves<false, B>()>("k_encode (joint)", out, n, max); \
+  n = enc_copy_recs<D, B, true, false, 64 * enc_waves<true, B>()>("k_encode (qjl)", out, n, max);    \
+  n = enc_copy_recs<D, B, true, true, 64 * enc_waves<true, B>()>("k_encode (qjl, joint)", out, n, max); \
   n = enc_copy_recs<D, B, false, false, 256>("k_encode_one", out, n, max);
   OCTO_REC_D(64)
   OCTO_REC_D(128)
