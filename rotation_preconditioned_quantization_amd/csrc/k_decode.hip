@@ -115,11 +115,13 @@ struct SQShared {
   static constexpr int NENT = kCombined ? (1 << C::BT) : C::NDIR;
   static constexpr int NCOPY = !REP ? 1 : (8192 / NENT < 16 ? 8192 / NENT : 16);
   static constexpr int QD = ((3 * C::T + 15) / 16) * 16;   // whole 16-dim groups (QRegs)
+  // the nibble table first: its per-lookup offsets then fit the 16-bit
+  // offset field of ds_read (no address add per lookup)
+  float4 lut[QJL ? (D / 4) * 16 : 1];
   float4 tab[NENT * NCOPY];
   float rho[C::LR];
   float q[4][QD];
   float qp[QJL ? 4 : 1][QJL ? D : 1];
-  float4 lut[QJL ? (D / 4) * 16 : 1];
 };
 
 // The copy of a single-query kernel's code table into LDS by NTH threads.
@@ -403,9 +405,9 @@ __device__ __forceinline__ floatx4 tile_logits(const SQShared<D, B, QJL, REP>& s
   }
   floatx4 r = (acc[0] + acc[3]) + (acc[1] + acc[4]) + (acc[2] + acc[5]);
   if constexpr (QJL) {
-    float4 corr = make_float4(0.f, 0.f, 0.f, 0.f);
+    float4 corr = sh.lut[k.sw[0] & 15u];   // nibble 0 (no adds to zero)
 #pragma unroll
-    for (int m = 0; m < D / 4; ++m) {
+    for (int m = 1; m < D / 4; ++m) {
       const uint32_t nib = (k.sw[m >> 3] >> (4 * (m & 7))) & 15u;
       const float4 e = sh.lut[(m << 4) + nib];
       corr.x += e.x; corr.y += e.y; corr.z += e.z; corr.w += e.w;
