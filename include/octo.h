@@ -171,6 +171,20 @@ typedef struct {
 } octo_lds_copy;
 octo_status octo_debug_lds_copy(int index, octo_lds_copy* out);
 
+/* Check aid for the encoder's nearest-centroid lookup ([YL] 三元组分解 step 4,
+ * the midpoint rule): out[i] = the index the encoder kernels take for value
+ * x[i] of xi (table OCTO_TABLE_QX) or eta (OCTO_TABLE_QE), by the kernels'
+ * own formula (one fma, its bits less a magic constant, one bucket entry,
+ * one compare) evaluated on the host over the codebook's table; it should
+ * equal #{k : x[i] > m_k} over the component's fp32 midpoints m_k.  x, out:
+ * host arrays of n entries.  Any codebook built with kernels (device or
+ * host-only).  OCTO_ERR_INVALID_ARG for another table, a NULL array, or an
+ * x whose bucket lies outside the table (the kernels are given values in
+ * [-1, 1] up to rounding); OCTO_ERR_UNSUPPORTED for a codebook without
+ * encoder tables. */
+octo_status octo_debug_bucket_index(const octo_codebook* cb, int table, const float* x, int64_t n,
+                                    uint32_t* out);
+
 /* Bytes of the packed stream for n_seq sequences of capacity cap (cap % 64 == 0). */
 size_t octo_packed_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap);
 size_t octo_qjl_bits_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap);
@@ -183,7 +197,9 @@ size_t octo_qjl_bits_bytes(const octo_codebook* cb, int64_t n_seq, int64_t cap);
  *   and with a QJL codebook also qjl_bits and qjl_norm (fp16 [n_seq][cap]);
  *   pass NULL for both to skip QJL.  Requires pos0 + n_new <= cap, cap % 64 == 0.
  * Rounding is scalar nearest-centroid (midpoint rule, ties to the lower
- * index).  Other positions of the cache are not touched. */
+ * index).  Other positions of the cache are not touched.  Keys must be
+ * finite: a key holding inf or NaN gets unspecified words and gamma (the
+ * call still completes and touches no other key). */
 octo_status octo_encode(const octo_codebook* cb, const void* keys, octo_dtype kdt,
                         int64_t n_seq, int64_t n_new, int64_t seq_stride, int64_t key_stride,
                         int64_t pos0, int64_t cap, void* packed, float* gamma,

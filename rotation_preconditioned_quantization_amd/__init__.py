@@ -79,6 +79,7 @@ _SIGS = {
     "octo_debug_copy": (_I, [_P, _P, _SZ, _P]),
     "octo_codebook_table_entries": (_I64, [_P, _I]),
     "octo_debug_lds_copy": (_I, [_I, _P]),
+    "octo_debug_bucket_index": (_I, [_P, _I, _P, _I64, _P]),
     "octo_status_str": (ctypes.c_char_p, [_I]),
     "octo_last_error": (ctypes.c_char_p, []),
 }
@@ -421,6 +422,18 @@ def octo_debug_lds_copies():
         out.append({f: getattr(rec, f) for f, _ in octo_lds_copy._fields_})
         out[-1]["kernel"] = rec.kernel.decode()
         i += 1
+    return out
+
+
+def octo_debug_bucket_index(cb: Codebook, table: int, x):
+    """The encoder kernels' nearest-centroid index of each value of x for xi
+    (table TABLES.index("qx")) or eta ("qe"), by their own lookup formula on
+    the host (octo_debug_bucket_index); numpy float32 in, uint32 out."""
+    import numpy as np
+    xs = np.ascontiguousarray(x, dtype=np.float32)
+    out = np.zeros(xs.shape, dtype=np.uint32)
+    _check(lib().octo_debug_bucket_index(cb.handle, table, xs.ctypes.data, xs.size, out.ctypes.data),
+           "octo_debug_bucket_index")
     return out
 
 

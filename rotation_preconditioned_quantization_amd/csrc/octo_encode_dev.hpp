@@ -10,12 +10,12 @@
 
 namespace octo {
 
-// #{k : x > m_k} from a one-midpoint-per-bucket table in LDS (see Bucket1),
-// for x in [-1, 1] up to rounding: the bucket position is then above -1, so
-// truncation toward zero gives bucket 0 at the bottom, and the guard entries
-// cover the top.
+// #{k : x > m_k} from a centred one-midpoint-per-bucket table in LDS (see
+// Bucket1), for x in [-1, 1] up to rounding: the fma rounds the bucket
+// position to an integer in [0, nb] inside its own mantissa, so the bucket
+// is its bits less kBucketMagicBits (one address add, no conversion).
 __device__ __forceinline__ uint32_t quant1(float x, const uint2* t, float scale, float bias) {
-  const uint2 e = t[(int)__builtin_fmaf(x, scale, bias)];
+  const uint2 e = t[__float_as_uint(__builtin_fmaf(x, scale, bias)) - kBucketMagicBits];
   return e.x + (x > __uint_as_float(e.y) ? 1u : 0u);
 }
 

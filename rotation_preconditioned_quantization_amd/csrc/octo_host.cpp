@@ -133,16 +133,27 @@ std::vector<double> antisymmetrize(const std::vector<double>& c) {
 }
 
 // One-midpoint-per-bucket table (see Bucket1) for the value range [lo, hi)
-// cut into nb buckets; the first bucket extends to -inf, the last to +inf.
-// Tries several bucket counts; false if none keeps <= 1 midpoint in every
-// bucket widened by the rounding margin of the device's bucket formula.
+// cut into nb buckets of width w; the first bucket extends to -inf, the last
+// to +inf.  Tries several bucket counts; false if none keeps <= 1 midpoint
+// in every bucket widened by the rounding margin of the device's bucket
+// formula.
+//   plain: bucket b covers [lo + b w, lo + (b + 1) w), b < nb, found by
+//     truncating x scale + bias; two guard buckets follow.
+//   centred: bucket b covers [lo + (b - 1/2) w, lo + (b + 1/2) w), b <= nb,
+//     found by rounding: with bias = -lo scale + kBucketMagic (lo scale an
+//     integer), fmaf(x, scale, bias) holds kBucketMagic + round(x scale -
+//     lo scale) exactly, so its bits minus kBucketMagicBits are the bucket
+//     (one rounding of the exact value; a tie lands in either neighbour,
+//     both of whose widened ranges hold x); one guard bucket follows.
+// Either way the table has nb + 2 entries.
 struct HostB1 {
   std::vector<uint32_t> t;  // 2 words per bucket: base, float bits of the midpoint
   float scale = 0, bias = 0;
   int nb = 0;
+  bool centred = false;
 };
 
-bool build_bucket1(const std::vector<double>& mids, double lo, double hi, HostB1* q) {
+bool build_bucket1(const std::vector<double>& mids, double lo, double hi, bool centred, HostB1* q) {
   const int nmid = (int)mids.size();
   std::vector<float> mf(nmid);
   for (int k = 0; k < nmid; ++k) mf[k] = (float)mids[k];
@@ -150,11 +161,13 @@ bool build_bucket1(const std::vector<double>& mids, double lo, double hi, HostB1
   for (int nb : {256, 128, 64}) {
     if (nb > kMaxLut) continue;
     const double w = (hi - lo) / nb;
-    std::vector<uint32_t> t(2 * (size_t)nb);
+    const int nbk = centred ? nb + 1 : nb;   // buckets before the guards
+    const double off = centred ? -0.5 : 0.0;
+    std::vector<uint32_t> t(2 * (size_t)nbk);
     bool ok = true;
-    for (int b = 0; b < nb && ok; ++b) {
-      const double L = b == 0 ? -INFINITY : lo + b * w - eps;
-      const double U = b == nb - 1 ? INFINITY : lo + (b + 1) * w + eps;
+    for (int b = 0; b < nbk && ok; ++b) {
+      const double L = b == 0 ? -INFINITY : lo + (b + off) * w - eps;
+      const double U = b == nbk - 1 ? INFINITY : lo + (b + 1 + off) * w + eps;
       int below = 0, inside = 0;
       float m_in = INFINITY;
       for (int k = 0; k < nmid; ++k) {
@@ -168,13 +181,21 @@ bool build_bucket1(const std::vector<double>& mids, double lo, double hi, HostB1
       t[2 * b + 1] = bits;
     }
     if (!ok) continue;
-    // two guard buckets repeating the last one: a value a rounding step above
-    // hi lands in bucket nb without a clamp
-    for (int g = 0; g < 2; ++g) { t.push_back(t[2 * (nb - 1)]); t.push_back(t[2 * (nb - 1) + 1]); }
+    // guard buckets repeating the last one (a value a rounding step above hi
+    // lands in one without a clamp), up to nb + 2 entries
+    while ((int)t.size() < 2 * (nb + 2)) { t.push_back(t[2 * (nbk - 1)]); t.push_back(t[2 * (nbk - 1) + 1]); }
+    const double scale = nb / (hi - lo);
+    if (centred) {
+      const double bias = -lo * scale;
+      if (bias != std::floor(bias) || std::fabs(bias) >= 1 << 20) continue;
+      q->bias = (float)(bias + kBucketMagic);
+    } else {
+      q->bias = (float)(-lo * scale);
+    }
     q->t = t;
-    q->scale = (float)(nb / (hi - lo));
-    q->bias = (float)(-lo * (nb / (hi - lo)));
+    q->scale = (float)scale;
     q->nb = nb;
+    q->centred = centred;
     return true;
   }
   return false;
@@ -202,6 +223,7 @@ struct octo_codebook {
   void* dev = nullptr;
   DevTables tables{};
   int64_t table_entries[TAB_COUNT] = {0, 0, 0, 0, 0, 0, 0};  // entries per table (octo_table)
+  HostB1 qx, qe;           // host copies of the xi / eta bucket tables (octo_debug_bucket_index)
   float qjl_kappa = 0.f;   // QJL estimator constant of S
 };
 
@@ -223,13 +245,13 @@ octo_status make_host_tables(octo_codebook* cb, HostTables& h) {
   HostB1& qx = h.qx;
   HostB1& qe = h.qe;
   HostB1& qr2 = h.qr2;
-  if (!build_bucket1(midpoints(cb->c_xi), -1.0, 1.0, &qx) ||
-      !build_bucket1(midpoints(cb->c_eta), -1.0, 1.0, &qe))
+  if (!build_bucket1(midpoints(cb->c_xi), -1.0, 1.0, true, &qx) ||
+      !build_bucket1(midpoints(cb->c_eta), -1.0, 1.0, true, &qe))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the xi/eta midpoints");
   std::vector<double> m2 = midpoints(cb->c_rho);
   for (double& m : m2) m = m * m;
   const double hi = m2.empty() ? 1.0 : std::min(1.0, 1.25 * m2.back() + 1e-3);
-  if (!build_bucket1(m2, 0.0, hi, &qr2))
+  if (!build_bucket1(m2, 0.0, hi, false, &qr2))
     return fail(OCTO_ERR_UNSUPPORTED, "no bucket table fits the rho midpoints");
   h.rho_mid2 = m2;
 
@@ -640,6 +662,10 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     // one only their sizes are kept (octo_codebook_table_entries)
     HostTables h;
     octo_status st = make_host_tables(cb, h);
+    if (st == OCTO_OK) {
+      cb->qx = h.qx;
+      cb->qe = h.qe;
+    }
     if (st == OCTO_OK && cb->device >= 0) st = upload_tables(cb, h);
     if (st != OCTO_OK && cb->device >= 0) {
       delete cb;
@@ -698,6 +724,29 @@ octo_status octo_codebook_export(const octo_codebook* cb, double* c_xi, double* 
 int64_t octo_codebook_table_entries(const octo_codebook* cb, int table) {
   if (!cb || table < 0 || table >= TAB_COUNT) return -1;
   return cb->table_entries[table];
+}
+
+octo_status octo_debug_bucket_index(const octo_codebook* cb, int table, const float* x, int64_t n,
+                                    uint32_t* out) {
+  if (!cb || (n > 0 && (!x || !out))) return fail(OCTO_ERR_INVALID_ARG, "NULL argument");
+  if (table != TAB_QX && table != TAB_QE)
+    return fail(OCTO_ERR_INVALID_ARG, "table must be OCTO_TABLE_QX or OCTO_TABLE_QE");
+  const HostB1& q = table == TAB_QX ? cb->qx : cb->qe;
+  if (q.t.empty()) return fail(OCTO_ERR_UNSUPPORTED, "codebook has no encoder tables");
+  const int64_t entries = (int64_t)q.t.size() / 2;
+  for (int64_t i = 0; i < n; ++i) {
+    // the device formula: one fma, its bits less the magic, one compare
+    uint32_t bits;
+    const float f = std::fmaf(x[i], q.scale, q.bias);
+    std::memcpy(&bits, &f, 4);
+    const int64_t b = (int64_t)bits - (int64_t)kBucketMagicBits;
+    if (b < 0 || b >= entries)
+      return fail(OCTO_ERR_INVALID_ARG, "x[" + std::to_string(i) + "] lies outside the table's range");
+    float mid;
+    std::memcpy(&mid, &q.t[2 * b + 1], 4);
+    out[i] = q.t[2 * b] + (x[i] > mid ? 1u : 0u);
+  }
+  return OCTO_OK;
 }
 
 octo_status octo_debug_lds_copy(int index, octo_lds_copy* out) {

@@ -17,19 +17,28 @@ constexpr int kMaxDevices = 64;
 
 // Nearest-centroid lookup for one scalar component (encoder): the index
 // #{k : x > m_k} of the midpoint rule.  The value range is cut into nb equal
-// buckets, b = (int) clamp(fma(x, scale, bias), 0, nb - 1); every bucket,
-// widened by the rounding of that formula, holds at most one midpoint, so the
-// index is t[b].x + (x > t[b].y as float): t[b].x counts the midpoints below
-// the bucket, t[b].y is the one inside it (+inf if none).  The host checks
-// the one-midpoint property when it builds the table.  Two guard entries
-// t[nb], t[nb + 1] repeat t[nb - 1], so values that can exceed the range only
-// by rounding (xi, eta in [-1, 1]) need no upper clamp; the float-to-unsigned
-// conversion already saturates below at 0.
+// buckets; every bucket, widened by the rounding of the formula that finds
+// it, holds at most one midpoint, so the index is t[b].x + (x > t[b].y as
+// float): t[b].x counts the midpoints below the bucket, t[b].y is the one
+// inside it (+inf if none).  The host checks the one-midpoint property when
+// it builds the table.  Two layouts, both of nb + 2 entries:
+//   xi, eta (centred on the integers): bucket b = bits of fmaf(x, scale,
+//     bias) - kBucketMagicBits, where bias carries kBucketMagic, so the fma
+//     itself rounds x scale + (bias - kBucketMagic) to the integer b in
+//     [0, nb] for x in [-1, 1] up to rounding; one guard entry t[nb + 1];
+//   rho^2 (from 0): b = (int) min(x scale, nb - 1) (the float-to-unsigned
+//     conversion saturates below at 0), two guard entries.
 struct Bucket1 {
   const uint2* t;     // nb + 2 entries
   float scale, bias;
   int nb;
 };
+
+// 1.5 * 2^23: floats in [2^23, 2^24) are spaced 1 apart, so adding this to a
+// value of magnitude below 2^22 rounds the value to an integer, which the
+// sum's low mantissa bits then hold (offset by kBucketMagicBits).
+constexpr float kBucketMagic = 12582912.0f;
+constexpr uint32_t kBucketMagicBits = 0x4B400000u;
 
 struct DevTables {
   Bucket1 qx, qe, qr2;      // xi, eta over [-1, 1]; rho^2 (squared midpoints) over [0, inf)
