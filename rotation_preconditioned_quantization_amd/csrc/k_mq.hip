@@ -10,7 +10,9 @@
 //      largest gamma scaled into [1/2, 1)): wave w takes the 64 keys of half
 //      w / PARTS (one per lane) and the dim range w % PARTS of each, i.e. only
 //      the triplets that touch those dims;
-//   2. the bf16 V tile is stored transposed in LDS as fp16;
+//   2. the bf16 V tile is stored in LDS as fp16 key rows (64-byte segments
+//      XOR-swizzled by row), and the P.V operands come out transposed from
+//      ds_read_b64_tr_b16;
 //   3. each wave computes S^T = K^ Q'^T for its 32 queries with
 //      v_mfma_f32_32x32x16_f16 (fp32 accumulate), runs the online softmax in
 //      the accumulator registers (the half's 2^e folded into the one scale
@@ -42,18 +44,22 @@ template <int D>
 struct MQShape {
   static constexpr int KT = 128;                  // keys per tile
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
-  // V^T row pitch in bytes (fp16): 66 dwords keep the 8-byte P.V operand
-  // reads of 32 consecutive rows on distinct banks and halve the bank
-  // collisions of the transposing writes against a 68-dword pitch
-  static constexpr int VP = KT * 2 + 8;
+  static constexpr int VR = D * 2;                // V row bytes (fp16, unpadded)
   static constexpr int SW = D == 64 ? 4 : 0;      // staging-only waves
   static constexpr int NW = kMQCompute + SW;      // waves per workgroup
   static constexpr int NSW = SW ? SW : kMQCompute;  // waves that stage
   static constexpr int PARTS = NSW / 2;           // staging waves per 64-key half
   static constexpr int DQ = D / PARTS;            // dims rebuilt per lane
   static constexpr int NTH_S = 64 * NSW;          // staging threads
-  static constexpr int KPT = KT * D / (8 * NTH_S);  // keys per thread of the V transpose
+  static constexpr int KPT = KT * D / (8 * NTH_S);  // V rows staged per thread
+  static constexpr int KGS = NTH_S / (D / 8);       // key stride between them
 };
+
+// 64-byte segment swizzle of V row r in LDS: segment s is stored at s ^
+// vswz(r).  The 4 rows one half-wave's transposing read touches (r = 4m ..
+// 4m + 3) then cover all 64 banks, as do the 16-byte staging writes.
+template <int D>
+__device__ __forceinline__ int vswz(int r) { return D == 64 ? (r >> 1) & 1 : r & 3; }
 
 // Registers carrying one tile's global data from its loads (issued during
 // the previous tile's matrix work) to its LDS staging.
@@ -61,7 +67,7 @@ template <int D, int B>
 struct MQStage {
   uint32_t words[Codec<D, B>::W];   // the lane's key
   float gamma;                      // its norm
-  uint4 v[MQShape<D>::KPT];         // KPT V rows, 8 dims each
+  uint4 v[MQShape<D>::KPT];         // V rows kg + KGS i, 8 dims each
 };
 
 // Loads of tile t by staging thread stid (rows past n_keys read the last
@@ -82,7 +88,7 @@ __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t,
   const uint4* vseq = (const uint4*)a.v + seq * a.cap * (D / 8) + c;
 #pragma unroll
   for (int i = 0; i < S::KPT; ++i) {
-    int64_t kv = t * S::KT + kg * S::KPT + i;
+    int64_t kv = t * S::KT + kg + S::KGS * i;
     kv = kv < a.n_keys ? kv : a.n_keys - 1;
     st.v[i] = vseq[kv * (D / 8)];
   }
@@ -99,6 +105,15 @@ __device__ __forceinline__ float pair32_max(float x) {
 __device__ __forceinline__ float pair32_sum(float x) {
   const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Transposing LDS read of 4 fp16 (ds_read_b64_tr_b16; the lane layout is
+// described where the P.V operands are read).
+typedef __attribute__((__vector_size__(4 * sizeof(__fp16)))) __fp16 fp16x4_tr;
+__device__ __forceinline__ half4 read_tr16(const unsigned char* p) {
+  typedef __attribute__((address_space(3))) fp16x4_tr lds_fp16x4;
+  return __builtin_bit_cast(half4, __builtin_amdgcn_ds_read_tr16_b64_v4f16(
+                                       (lds_fp16x4*)(const_cast<unsigned char*>(p))));
 }
 
 // bf16 pair -> f16 pair (V of the multi-query path must lie in fp16 range).
@@ -144,13 +159,13 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
   using C = Codec<D, B>;
   using S = MQShape<D>;
   constexpr int T = C::T;
-  constexpr int KT = S::KT, KP = S::KP, VP = S::VP, NTH = 64 * S::NW;
+  constexpr int KT = S::KT, KP = S::KP, VR = S::VR, NTH = 64 * S::NW;
   constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
   constexpr int NMB = D / 32;  // 32-row blocks of O^T
 
   // two sets of tile buffers: tile t + 1 is staged while tile t is computed
   __shared__ __align__(16) unsigned char s_k[2][KT * KP];
-  __shared__ __align__(16) unsigned char s_vt[2][D * VP];
+  __shared__ __align__(16) unsigned char s_v[2][KT * VR];
   __shared__ int s_e[2][KT / 64];   // the exponent e of each 64-key half
   __shared__ float4 s_dir[C::NDIR];
   __shared__ float s_rho[C::LR];
@@ -212,7 +227,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
 
   // Stage one tile from the registers of its loads into LDS buffer set bs:
   //   keys rebuilt by wave w for key half w / 4 and dim quarter w % 4;
-  //   V transposed to [dim][key] fp16, this thread's KPT keys x 8 dims.
+  //   V rows as fp16, this thread's 8 dims of keys kg + KGS i.
   MQStage<D, B> st;
   auto stage = [&](int64_t k0, int bs) {
     {
@@ -240,25 +255,15 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
       }
     }
     const int c = stid % (D / 8), kg = stid / (D / 8);
-    uint32_t hv[KPT][4];   // f16 pairs (dims 2e, 2e+1) per key
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
-      const bool ok = k0 + kg * KPT + i < a.n_keys;
+      const int key = kg + S::KGS * i;
+      const bool ok = k0 + key < a.n_keys;
       const uint32_t src[4] = {st.v[i].x, st.v[i].y, st.v[i].z, st.v[i].w};
+      uint32_t hv[4];   // f16 pairs (dims 2e, 2e+1)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) hv[i][e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
-    }
-#pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const uint32_t sel = (dd & 1) ? 0x07060302u : 0x05040100u;
-      uint32_t col[KPT / 2];
-#pragma unroll
-      for (int i = 0; i < KPT / 2; ++i)
-        col[i] = __builtin_amdgcn_perm(hv[2 * i + 1][dd >> 1], hv[2 * i][dd >> 1], sel);
-      unsigned char* dst = s_vt[bs] + (8 * c + dd) * VP + kg * KPT * 2;
-      if constexpr (KPT == 2) *(uint32_t*)dst = col[0];
-      else if constexpr (KPT == 4) *(uint2*)dst = make_uint2(col[0], col[1]);
-      else *(uint4*)dst = make_uint4(col[0], col[1], col[2], col[3]);
+      for (int e = 0; e < 4; ++e) hv[e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
+      *(uint4*)(s_v[bs] + key * VR + ((16 * c) ^ (vswz<D>(key) << 6))) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
   };
 
@@ -269,6 +274,21 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
     mq_load<D, B>(a, seq, t_begin + 1 < t_end ? t_begin + 1 : t_begin, stid, st);
   }
   __syncthreads();
+
+  // P.V operands by transposing reads (ds_read_b64_tr_b16: in each group of
+  // 16 lanes, lane i receives element i % 4 of the 8 bytes that lanes
+  // i / 4 + 4 k, k = 0..3, name).  Lane j of a group names V row 4 g + j / 4
+  // of the chunk's 16-key half, dims 32 mb + 16 (ln / 16) + 4 (j % 4) ..
+  // + 3, so lane (ln, g) receives dim 32 mb + ln of keys 4 g + 0..3, the
+  // order P^T's registers hold them in (and keys + 8 from the row 8 below).
+  int voff[NMB];
+  {
+    const int jt = lane & 15;
+#pragma unroll
+    for (int mb = 0; mb < NMB; ++mb)
+      voff[mb] = (4 * g + (jt >> 2)) * VR +
+                 ((64 * mb + 32 * (ln >> 4) + 8 * (jt & 3)) ^ (vswz<D>(jt >> 2) << 6));
+  }
 
   for (int64_t t = t_begin; t < t_end; ++t) {
     const int64_t k0 = t * KT;
@@ -281,7 +301,7 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
       mq_load<D, B>(a, seq, t + 2 < t_end ? t + 2 : t + 1, stid, st);
     }
     const unsigned char* sk = s_k[cb];
-    const unsigned char* svt = s_vt[cb];
+    const unsigned char* svt = s_v[cb];
     if (wave_q) {
     // 3. 64 keys (one half) at a time: S^T, online softmax, O^T += V^T P^T.
     // The accumulators hold s' = q'.(gamma 2^-e u'^) 2^qsh, so the score in
@@ -363,9 +383,9 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
           const int kbase = ch * 64 + sb * 32 + 16 * half + 4 * g;
 #pragma unroll
           for (int mb = 0; mb < NMB; ++mb) {
-            const unsigned char* vrow = svt + (32 * mb + ln) * VP;
-            const half4 lo = *(const half4*)(vrow + kbase * 2);
-            const half4 hi = *(const half4*)(vrow + (kbase + 8) * 2);
+            const unsigned char* vp = svt + (kbase - 4 * g) * VR + voff[mb];
+            const half4 lo = read_tr16(vp);
+            const half4 hi = read_tr16(vp + 8 * VR);
             const half8 vf = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
             o[mb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(vf, pf[sb][half], o[mb], 0, 0, 0);
           }
