@@ -143,6 +143,33 @@ __device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][
   }
 }
 
+// The three bucket tables (nb + 2 <= kMaxLut + 2 entries each) into LDS
+// by NTH threads: every thread requests all of its entries before it stores
+// any, so the block waits one memory round trip for them, not one per table
+// and per round of a copy loop.
+template <int NTH>
+__device__ __forceinline__ void copy_bucket_tables(const DevTables& t, uint2* s_qx, uint2* s_qe,
+                                                   uint2* s_qr, int tid) {
+  constexpr int R = (kMaxLut + 2 + NTH - 1) / NTH;
+  const Bucket1* q[3] = {&t.qx, &t.qe, &t.qr2};
+  uint2* dst[3] = {s_qx, s_qe, s_qr};
+  uint2 v[3][R];
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = tid + NTH * r;
+      v[k][r] = i < q[k]->nb + 2 ? q[k]->t[i] : make_uint2(0u, 0u);
+    }
+#pragma unroll
+  for (int k = 0; k < 3; ++k)
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int i = tid + NTH * r;
+      if (i < q[k]->nb + 2) dst[k][i] = v[k][r];
+    }
+}
+
 // Waves (64-key tiles in flight) per encoder block: 4, or 8 with QJL below
 // 5 bits, where one block per CU holds the LDS copy of S and two waves per
 // SIMD then overlap one wave's projection on the matrix cores with the
@@ -495,9 +522,7 @@ __attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : 2))) void k_encode(Encode
   const int64_t seq = blockIdx.y;
 
   // the block's waves share the quantiser tables (and the QJL matrix)
-  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 64 * EW) s_qx[i] = a.t.qx.t[i];
-  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 64 * EW) s_qe[i] = a.t.qe.t[i];
-  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 64 * EW) s_qr[i] = a.t.qr2.t[i];
+  copy_bucket_tables<64 * EW>(a.t, s_qx, s_qe, s_qr, threadIdx.x);
   if constexpr (QJL) {
     constexpr int CPRS = SLds<D>::CPRS;
     for (int c = threadIdx.x; c < SLds<D>::CHUNKS; c += 64 * EW)
@@ -536,9 +561,7 @@ __global__ __launch_bounds__(256) void k_encode_one(EncodeArgs a) {
   __shared__ uint32_t s_w[4][W];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
-  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
-  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  copy_bucket_tables<256>(a.t, s_qx, s_qe, s_qr, threadIdx.x);
   __syncthreads();
   const int64_t k = (int64_t)blockIdx.x * 4 + wave;  // keys flattened over (seq, new key)
   if (k >= a.n_new * a.seq_count) return;
@@ -627,9 +650,7 @@ void k_encode256(EncodeArgs a) {
   __shared__ float s_rho[JR ? C::LR : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
-  for (int i = threadIdx.x; i < a.t.qx.nb + 2; i += 256) s_qx[i] = a.t.qx.t[i];
-  for (int i = threadIdx.x; i < a.t.qe.nb + 2; i += 256) s_qe[i] = a.t.qe.t[i];
-  for (int i = threadIdx.x; i < a.t.qr2.nb + 2; i += 256) s_qr[i] = a.t.qr2.t[i];
+  copy_bucket_tables<256>(a.t, s_qx, s_qe, s_qr, threadIdx.x);
   if constexpr (JR) {
     for (int i = threadIdx.x; i < C::NDIR; i += 256) s_dir[i] = a.t.dirtab[i];
     if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];

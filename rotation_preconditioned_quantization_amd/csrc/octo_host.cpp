@@ -134,9 +134,10 @@ std::vector<double> antisymmetrize(const std::vector<double>& c) {
 
 // One-midpoint-per-bucket table (see Bucket1) for the value range [lo, hi)
 // cut into nb buckets of width w; the first bucket extends to -inf, the last
-// to +inf.  Tries several bucket counts; false if none keeps <= 1 midpoint
-// in every bucket widened by the rounding margin of the device's bucket
-// formula.
+// to +inf.  Takes the smallest bucket count (16 ... 256) that keeps <= 1
+// midpoint in every bucket widened by the rounding margin of the device's
+// bucket formula (a small table is copied into each encoder block's LDS
+// sooner); false if none does.
 //   plain: bucket b covers [lo + b w, lo + (b + 1) w), b < nb, found by
 //     truncating x scale + bias; two guard buckets follow.
 //   centred: bucket b covers [lo + (b - 1/2) w, lo + (b + 1/2) w), b <= nb,
@@ -158,7 +159,7 @@ bool build_bucket1(const std::vector<double>& mids, double lo, double hi, bool c
   std::vector<float> mf(nmid);
   for (int k = 0; k < nmid; ++k) mf[k] = (float)mids[k];
   const double eps = 1e-6 * (hi - lo);
-  for (int nb : {256, 128, 64}) {
+  for (int nb : {16, 32, 64, 128, 256}) {
     if (nb > kMaxLut) continue;
     const double w = (hi - lo) / nb;
     const int nbk = centred ? nb + 1 : nb;   // buckets before the guards

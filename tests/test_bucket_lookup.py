@@ -28,8 +28,9 @@ def _probe_values(m32):
     pts = [np.linspace(-1.0, 1.0, 20001, dtype=np.float32), m32,
            np.nextafter(m32, f32(np.inf)), np.nextafter(m32, f32(-np.inf))]
     # bucket edges of a centred table of nb buckets over [-1, 1] (the
-    # builder tries 256, 128 and 64), and their neighbours
-    for n in (256, 128, 64):
+    # builder takes the smallest of 16 ... 256 that works), and their
+    # neighbours
+    for n in (16, 32, 64, 128, 256):
         e = (-1.0 + (np.arange(n + 1) + 0.5) * (2.0 / n)).astype(np.float32)
         pts += [e, np.nextafter(e, f32(np.inf)), np.nextafter(e, f32(-np.inf))]
     ends = np.array([-1.0, 1.0, -1.0 - 2.0 ** -22, 1.0 + 2.0 ** -22, 0.0, -0.0], dtype=np.float32)
