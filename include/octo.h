@@ -63,9 +63,7 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
  *             for a host-only codebook).  At d = 256 there is no QJL variant
  *             (a QJL codebook is refused with OCTO_ERR_UNSUPPORTED) and no
  *             multi-query path; the encoder gives each key two lanes there.
- *   b         bit budget per coordinate; kernels exist for 1 .. 5 (the
- *             multi-query path and the fp32-key QJL encoder not at d = 128,
- *             b = 5).
+ *   b         bit budget per coordinate; kernels exist for 1 .. 5.
  *   seed      seeds the WHT sign vector and the QJL projection.
  *   cb_seed   seeds the Monte-Carlo samples the Lloyd-Max tables are fit to.
  *   b_xi, b_eta, b_rho  bits per component; any value < 0 selects the pages'

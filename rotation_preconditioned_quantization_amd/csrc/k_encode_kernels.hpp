@@ -32,14 +32,16 @@ namespace octo {
 // coalesced 16-byte loads (consecutive lanes read consecutive chunks).  The
 // WHT sign flips are applied here, on the raw chunk bits: every lane always
 // handles the same chunk column, so one 16-byte mask per lane does it.
-template <int D, int KT>
+// NRW rows per phase: 16, or 8 where the block's LDS is short.
+template <int D, int KT, int NRW = 16>
 struct Stage {
   static constexpr int ES = DtSize<KT>::v;
   static constexpr int ROWB = D * ES;       // bytes per key row
   static constexpr int CPR = ROWB / 16;     // 16-byte chunks per row
   static constexpr int PITCH = ROWB + 16;   // padded pitch: conflict-free row reads
   static constexpr int VPC = 16 / ES;       // values per chunk
-  static constexpr int NR = 16;             // rows staged per phase
+  static constexpr int NR = NRW;            // rows staged per phase
+  static_assert(NR * CPR % 64 == 0 && kTile % NR == 0, "whole chunks per lane and phases per tile");
   static constexpr int NP = kTile / NR;     // phases
   static constexpr int PER_LANE = NR * CPR / 64;
 };
@@ -72,10 +74,10 @@ constexpr int kBufferDescWord3 = 0x00020000;
 // of them.  That pays in the QJL encoder, whose waves walk several tiles;
 // in the one-tile-per-wave encoder the cheaper issue measured 2-3 % slower
 // (the tile's loads then leave in one burst, all waves in step).
-template <int D, int KT, bool FAST>
+template <int D, int KT, bool FAST, int NRW = 16>
 __device__ __forceinline__ void load_rows(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
-                                          uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE]) {
-  using S = Stage<D, KT>;
+                                          uint4 (&raw)[Stage<D, KT, NRW>::NP][Stage<D, KT, NRW>::PER_LANE]) {
+  using S = Stage<D, KT, NRW>;
   const unsigned char* kbase = (const unsigned char*)a.keys + (seq * a.seq_stride) * S::ES;
   const int col = lane % S::CPR;
   const int64_t rs = a.key_stride * S::ES;  // bytes between key rows
@@ -113,11 +115,11 @@ __device__ __forceinline__ void load_rows(const EncodeArgs& a, int64_t seq, int6
 
 // Hand every lane its own key row (sign-flipped, raw bits) through the
 // wave's LDS buffer of NR rows, one phase at a time.
-template <int D, int KT>
-__device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE],
+template <int D, int KT, int NRW = 16>
+__device__ __forceinline__ void stage_rows(const uint4 (&raw)[Stage<D, KT, NRW>::NP][Stage<D, KT, NRW>::PER_LANE],
                                            int lane, unsigned char* s_keys, const uint4& smask,
-                                           uint4 (&rowbits)[Stage<D, KT>::CPR]) {
-  using S = Stage<D, KT>;
+                                           uint4 (&rowbits)[Stage<D, KT, NRW>::CPR]) {
+  using S = Stage<D, KT, NRW>;
   const int col = lane % S::CPR;
   const int my_phase = lane / S::NR;
   const unsigned char* row = s_keys + (lane % S::NR) * S::PITCH;
@@ -177,6 +179,12 @@ __device__ __forceinline__ void copy_bucket_tables(const DevTables& t, uint2* s_
 // for 8 waves' staging buffers).
 template <bool QJL, int B>
 constexpr int enc_waves() { return QJL && B < 5 ? 8 : 4; }
+
+// Key rows staged per phase: 8 for fp32 keys with QJL at d = 128, b = 5,
+// where the f16 QJL matrix (68 KiB) and the 4096-entry direction table
+// (64 KiB) leave 26 KiB of LDS for the four waves' staging buffers; else 16.
+template <int D, int B, int KT, bool QJL>
+constexpr int enc_stage_rows() { return QJL && B >= 5 && KT == DT_F32 && D == 128 ? 8 : 16; }
 
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
@@ -324,20 +332,20 @@ __device__ __forceinline__ uint32_t joint_code(float x, float y, float z, uint32
 
 // Encode the 64-key tile at j0 from its raw rows (load_rows): one key per
 // lane, entirely in registers.
-template <int D, int B, int KT, bool QJL, bool JR>
+template <int D, int B, int KT, bool QJL, bool JR, int NRW = 16>
 __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, int64_t j0, int lane,
-                                            const uint4 (&raw)[Stage<D, KT>::NP][Stage<D, KT>::PER_LANE],
+                                            const uint4 (&raw)[Stage<D, KT, NRW>::NP][Stage<D, KT, NRW>::PER_LANE],
                                             unsigned char* s_keys, const uint4& smask,
                                             const uint2* s_qx, const uint2* s_qe, const uint2* s_qr,
                                             const unsigned char* s_S, const float4* s_dir,
                                             const float* s_rho) {
   using C = Codec<D, B>;
-  using S = Stage<D, KT>;
+  using S = Stage<D, KT, NRW>;
   constexpr int T = C::T, W = C::W;
   float v[D];
   {
     uint4 rowbits[S::CPR];
-    stage_rows<D, KT>(raw, lane, s_keys, smask, rowbits);
+    stage_rows<D, KT, NRW>(raw, lane, s_keys, smask, rowbits);
     if constexpr (KT == DT_F32) {
 #pragma unroll
       for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
@@ -505,7 +513,8 @@ template <int D, int B, int KT, bool QJL, bool JR>
 __global__ __launch_bounds__((64 * enc_waves<QJL, B>()))
 __attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : 2))) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
-  using S = Stage<D, KT>;
+  constexpr int NRW = enc_stage_rows<D, B, KT, QJL>();
+  using S = Stage<D, KT, NRW>;
   constexpr int EW = enc_waves<QJL, B>();
   __shared__ __align__(16) unsigned char s_keys[EW][S::NR * S::PITCH];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
@@ -540,9 +549,9 @@ __attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : 2))) void k_encode(Encode
   for (int64_t j0 = ((int64_t)blockIdx.x * EW + wave) * kTile; j0 < a.n_new;
        j0 += (int64_t)gridDim.x * EW * kTile) {
     uint4 raw[S::NP][S::PER_LANE];
-    load_rows<D, KT, QJL>(a, seq, j0, lane, raw);
-    encode_tile<D, B, KT, QJL, JR>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr, s_S,
-                                   s_dir, s_rho);
+    load_rows<D, KT, QJL, NRW>(a, seq, j0, lane, raw);
+    encode_tile<D, B, KT, QJL, JR, NRW>(a, seq, j0, lane, raw, s_keys[wave], smask, s_qx, s_qe, s_qr,
+                                        s_S, s_dir, s_rho);
     if constexpr (!QJL) break;
   }
 }
@@ -861,19 +870,11 @@ inline hipError_t launch_encode_t(const EncodeArgs& a, int64_t n_seq, hipStream_
 
 template <int D, int B, int KT>
 inline hipError_t enc_q(bool qjl, bool joint, const EncodeArgs& a, int64_t n_seq, hipStream_t s) {
-  // fp32 keys with QJL at d = 128, b = 5: the staging buffer, the matrix and
-  // the 4096-entry direction table exceed the LDS (the host refuses it)
-  if constexpr (D == 128 && B == 5 && KT == DT_F32) {
-    if (qjl) return hipErrorInvalidValue;
-    return joint ? launch_encode_t<D, B, KT, false, true>(a, n_seq, s)
-                 : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
-  } else {
-    if (joint)
-      return qjl ? launch_encode_t<D, B, KT, true, true>(a, n_seq, s)
-                 : launch_encode_t<D, B, KT, false, true>(a, n_seq, s);
-    return qjl ? launch_encode_t<D, B, KT, true, false>(a, n_seq, s)
-               : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
-  }
+  if (joint)
+    return qjl ? launch_encode_t<D, B, KT, true, true>(a, n_seq, s)
+               : launch_encode_t<D, B, KT, false, true>(a, n_seq, s);
+  return qjl ? launch_encode_t<D, B, KT, true, false>(a, n_seq, s)
+             : launch_encode_t<D, B, KT, false, false>(a, n_seq, s);
 }
 
 template <int D, int B>

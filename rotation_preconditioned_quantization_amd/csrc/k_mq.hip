@@ -39,17 +39,20 @@ constexpr int kMQQueries = 32 * kMQCompute;  // queries per workgroup (32 per ma
 
 // Workgroup shape.  At d = 64 the matrix waves fit three to a SIMD, so four
 // more waves do the staging (key rebuild, V transpose, loads) next to them;
-// at d = 128 the eight matrix waves stage the tiles themselves.
-template <int D>
+// at d = 128 the eight matrix waves stage the tiles themselves.  Tiles hold
+// 128 keys, except at d = 128, b = 5, where the 4096-entry direction table
+// (64 KiB) leaves room in LDS for two buffer sets of 64-key tiles only.
+template <int D, int B>
 struct MQShape {
-  static constexpr int KT = 128;                  // keys per tile
+  static constexpr int KT = D == 128 && B == 5 ? 64 : 128;  // keys per tile
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
   static constexpr int VR = D * 2;                // V row bytes (fp16, unpadded)
   static constexpr int SW = D == 64 ? 4 : 0;      // staging-only waves
   static constexpr int NW = kMQCompute + SW;      // waves per workgroup
   static constexpr int NSW = SW ? SW : kMQCompute;  // waves that stage
-  static constexpr int PARTS = NSW / 2;           // staging waves per 64-key half
+  static constexpr int PARTS = NSW / (KT / 64);   // staging waves per 64-key half
   static constexpr int DQ = D / PARTS;            // dims rebuilt per lane
+  static_assert(DQ % 8 == 0 && PARTS * DQ == D, "whole 16-byte row segments per lane");
   static constexpr int NTH_S = 64 * NSW;          // staging threads
   static constexpr int KPT = KT * D / (8 * NTH_S);  // V rows staged per thread
   static constexpr int KGS = NTH_S / (D / 8);       // key stride between them
@@ -67,7 +70,7 @@ template <int D, int B>
 struct MQStage {
   uint32_t words[Codec<D, B>::W];   // the lane's key
   float gamma;                      // its norm
-  uint4 v[MQShape<D>::KPT];         // V rows kg + KGS i, 8 dims each
+  uint4 v[MQShape<D, B>::KPT];         // V rows kg + KGS i, 8 dims each
 };
 
 // Loads of tile t by staging thread stid (rows past n_keys read the last
@@ -76,7 +79,7 @@ struct MQStage {
 template <int D, int B>
 __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int stid,
                                         MQStage<D, B>& st) {
-  using S = MQShape<D>;
+  using S = MQShape<D, B>;
   constexpr int W = Codec<D, B>::W;
   const int lane = stid & 63, sw = stid >> 6;
   const int64_t tiles64 = a.cap / kTile;
@@ -129,7 +132,7 @@ template <int D, int B, int PART>
 __device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, float gs, const float4* s_dir,
                                            const float* s_rho, unsigned char* krow) {
   using C = Codec<D, B>;
-  constexpr int DQ = MQShape<D>::DQ, LO = PART * DQ, HI = LO + DQ;
+  constexpr int DQ = MQShape<D, B>::DQ, LO = PART * DQ, HI = LO + DQ;
   float u[DQ];
 #pragma unroll
   for (int i = LO / 3; i <= (HI - 1) / 3; ++i) {
@@ -154,10 +157,23 @@ __device__ __forceinline__ void mq_rebuild(const MQStage<D, B>& st, float gs, co
   }
 }
 
+// mq_rebuild of dim part `part` (wave-uniform), one of P .. PARTS - 1.
+template <int D, int B, int P>
+__device__ __forceinline__ void mq_rebuild_from(int part, const MQStage<D, B>& st, float gs,
+                                                const float4* s_dir, const float* s_rho,
+                                                unsigned char* krow) {
+  if constexpr (P == MQShape<D, B>::PARTS - 1) {
+    if (P > 1 || part == P) mq_rebuild<D, B, P>(st, gs, s_dir, s_rho, krow);
+  } else {
+    if (part == P) mq_rebuild<D, B, P>(st, gs, s_dir, s_rho, krow);
+    else mq_rebuild_from<D, B, P + 1>(part, st, gs, s_dir, s_rho, krow);
+  }
+}
+
 template <int D, int B>
-__global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
+__global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) {
   using C = Codec<D, B>;
-  using S = MQShape<D>;
+  using S = MQShape<D, B>;
   constexpr int T = C::T;
   constexpr int KT = S::KT, KP = S::KP, VR = S::VR, NTH = 64 * S::NW;
   constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
@@ -247,11 +263,8 @@ __global__ __launch_bounds__(64 * MQShape<D>::NW) void k_mq_attn(MQArgs a) {
       if (part == 0) {
         mq_rebuild<D, B, 0>(st, gs, s_dir, s_rho, krow);
         if (lane == 0) s_e[bs][sw / S::PARTS] = e;
-      } else if (part == 1) {
-        mq_rebuild<D, B, 1>(st, gs, s_dir, s_rho, krow);
-      } else if constexpr (S::PARTS > 2) {
-        if (part == 2) mq_rebuild<D, B, 2>(st, gs, s_dir, s_rho, krow);
-        else mq_rebuild<D, B, 3>(st, gs, s_dir, s_rho, krow);
+      } else {
+        mq_rebuild_from<D, B, 1>(part, st, gs, s_dir, s_rho, krow);
       }
     }
     const int c = stid % (D / 8), kg = stid / (D / 8);
@@ -414,7 +427,7 @@ template <int D, int B>
 static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
   const dim3 grid((unsigned)a.n_split, (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries),
                   (unsigned)(a.B * a.H));
-  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3(64 * MQShape<D>::NW), 0, s, a);
+  hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3((64 * MQShape<D, B>::NW)), 0, s, a);
   return hipGetLastError();
 }
 
@@ -422,7 +435,7 @@ static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
 template <int D, int B>
 static int mq_copy_recs(LdsCopyRec* out, int n, int max) {
   using C = Codec<D, B>;
-  constexpr int NTH = 64 * MQShape<D>::NW;
+  constexpr int NTH = 64 * MQShape<D, B>::NW;
   using TC = TableCopy<C::NDIR, NTH>;
   if (n < max)
     out[n++] = {"k_mq_attn", D, B, 0, TAB_DIR, C::NDIR, TC::SLOTS, TC::ENTRIES, C::NDIR, NTH, TC::MASKED};
@@ -441,10 +454,13 @@ int lds_copies_mq(LdsCopyRec* out, int max) {
   n = mq_copy_recs<128, 2>(out, n, max);
   n = mq_copy_recs<128, 3>(out, n, max);
   n = mq_copy_recs<128, 4>(out, n, max);
+  n = mq_copy_recs<128, 5>(out, n, max);
   return n;
 }
 
-int mq_tile_keys(int d) { return d == 64 ? MQShape<64>::KT : MQShape<128>::KT; }
+int mq_tile_keys(int d, int b) {
+  return d == 64 ? MQShape<64, 1>::KT : (b == 5 ? MQShape<128, 5>::KT : MQShape<128, 1>::KT);
+}
 int mq_block_queries() { return kMQQueries; }
 
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
@@ -458,8 +474,7 @@ hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
     case 1284: return mq_t<128, 4>(a, s);
     case 645: return mq_t<64, 5>(a, s);
     case 1281: return mq_t<128, 1>(a, s);
-    // d = 128 at b = 5: the 4096-entry direction table and the two tile
-    // buffer sets do not fit the 160 KiB of LDS together (not supported)
+    case 1285: return mq_t<128, 5>(a, s);
   }
   return hipErrorInvalidValue;
 }

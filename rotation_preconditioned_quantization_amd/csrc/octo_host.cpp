@@ -450,8 +450,8 @@ int64_t device_cus() {
 // Multi-query split: the number of splits that minimises the tile steps of
 // the slowest compute unit, ceil(rows * n_split / CUs) * tiles_per_split;
 // among equal costs the fewest splits (least partial traffic).
-Split mq_split(int64_t n_keys, int d, int64_t rows) {
-  const int kt = mq_tile_keys(d);
+Split mq_split(int64_t n_keys, int d, int b, int64_t rows) {
+  const int kt = mq_tile_keys(d, b);
   const int64_t ntile = std::max<int64_t>(1, (n_keys + kt - 1) / kt);
   const int64_t slots = device_cus();
   rows = std::max<int64_t>(1, rows);
@@ -483,7 +483,7 @@ WsLayout ws_layout(const octo_codebook* cb, int mode, int B, int Hq, int Hkv, in
   if (cb->qjl) off += align256(rows * cb->d * sizeof(float));
   w.part = off;
   if (mode == 1 && n_q > 1) {
-    const Split sp = mq_split(n_keys, cb->d, mq_rows(B, Hq, n_q));
+    const Split sp = mq_split(n_keys, cb->d, cb->b, mq_rows(B, Hq, n_q));
     off += align256(rows * (size_t)sp.n_split * (cb->d + 2) * sizeof(float));
   } else if (mode == 1) {
     const int G = Hkv > 0 ? Hq / Hkv : 1;
@@ -814,8 +814,6 @@ static octo_status encode_impl(const octo_codebook* cb, const void* keys, octo_d
   if (qjl_bits && !cb->qjl) return fail(OCTO_ERR_INVALID_ARG, "codebook built without QJL");
   if (qjl_bits && (!aligned(qjl_bits, 16) || !aligned(qjl_norm, 2)))
     return fail(OCTO_ERR_INVALID_ARG, "QJL buffers misaligned");
-  if (qjl_bits && cb->d == 128 && cb->b == 5 && kdt == OCTO_F32)
-    return fail(OCTO_ERR_UNSUPPORTED, "QJL encoder: no kernel for fp32 keys at d = 128, b = 5");
   EncodeArgs a{};
   a.t = cb->tables;
   a.keys = keys;
@@ -1074,15 +1072,13 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
-    if (cb->d == 128 && cb->b == 5)
-      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 128, b = 5");
     if (cb->d == 256)
       return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 256 (one query at a time)");
     if (stages & OCTO_STAGE_ROTATE) {
       st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
       if (st != OCTO_OK) return st;
     }
-    const Split sp = mq_split(n_keys, cb->d, mq_rows(B, Hq, n_q));
+    const Split sp = mq_split(n_keys, cb->d, cb->b, mq_rows(B, Hq, n_q));
     MQArgs m{};
     m.t = cb->tables;
     m.qrot = r.qrot;

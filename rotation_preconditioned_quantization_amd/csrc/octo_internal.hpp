@@ -176,7 +176,7 @@ int lds_copies_encode(LdsCopyRec* out, int max);
 // Device address of the static decode scratch on `device` (the current
 // device), resolved once per device.
 hipError_t static_scratch(int device, void** out);
-int mq_tile_keys(int d);  // keys per tile of the multi-query kernel
+int mq_tile_keys(int d, int b);  // keys per tile of the multi-query kernel
 int mq_block_queries();   // queries per workgroup of the multi-query kernel
 
 }  // namespace octo

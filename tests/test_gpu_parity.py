@@ -348,6 +348,22 @@ def test_logits_qjl_wider_bit_budgets(d, b):
     check_logits(cfg, 1, 1, 2, 200, 256, seed=3 + b, qjl=True, label=f"qjl-d{d}b{b}")
 
 
+@pytest.mark.parametrize("d,b", [(128, 5), (128, 3), (64, 4)])
+def test_logits_qjl_fp32_keys(d, b):
+    """The QJL encoder with fp32 keys (at d = 128, b = 5 its blocks stage 8
+    key rows per phase instead of 16, so that the staging buffers fit the LDS
+    beside the QJL matrix and the 4096-entry direction table); ragged tail."""
+    cfg = WL.CONFIGS[5].scaled(d=d, b=b, kdtype="f32")
+    check_logits(cfg, 2, 1, 2, 333, 384, seed=11 + b, qjl=True, label=f"qjl-f32-d{d}b{b}")
+
+
+def test_mq_d128_b5_multi_split():
+    """d = 128, b = 5 runs the multi-query kernel on 64-key tiles (the
+    4096-entry direction table leaves LDS for no more): a cache long enough
+    for several splits, a ragged last tile and GQA."""
+    check_mq(WL.CONFIGS[4].scaled(d=128, b=5), 2, 1, 300, 5000, 5056, seed=17, label="mq-d128b5-split")
+
+
 # --------------------------------------------------------------- attention --
 def check_attention(cfg, B, Hkv, G, n, cap, seed=0, qjl=False, label="", seqs=None):
     octo = _octo()
@@ -857,7 +873,7 @@ def test_mq_video_recipe_small():
     check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
 
 
-@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1)])
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5)])
 def test_mq_shapes_and_gqa(d, b):
     check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
 
