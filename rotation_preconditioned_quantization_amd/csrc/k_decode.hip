@@ -60,10 +60,16 @@ __global__ __launch_bounds__(64) void k_rotate(RotateArgs a) {
       x[k] = (l & hh) ? (o - x[k]) : (x[k] + o);
     }
   }
-  if constexpr (NV == 2) {
-    const float a0 = x[0], a1 = x[1];
-    x[0] = a0 + a1;
-    x[1] = a0 - a1;
+  // strides 64, 128: between the values a lane holds
+#pragma unroll
+  for (int hr = 1; hr < NV; hr <<= 1) {
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      if (k & hr) continue;
+      const float a0 = x[k], a1 = x[k + hr];
+      x[k] = a0 + a1;
+      x[k + hr] = a0 - a1;
+    }
   }
   const float mult = a.mult * rsqrtf((float)D);
   float* out = a.qrot + (int64_t)orow * (3 * T);
@@ -910,6 +916,7 @@ hipError_t launch_rotate(int d, const RotateArgs& a, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (d == 64) hipLaunchKernelGGL(k_rotate<64>, dim3(rows), dim3(64), 0, s, a);
   else if (d == 128) hipLaunchKernelGGL(k_rotate<128>, dim3(rows), dim3(64), 0, s, a);
+  else if (d == 256) hipLaunchKernelGGL(k_rotate<256>, dim3(rows), dim3(64), 0, s, a);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }

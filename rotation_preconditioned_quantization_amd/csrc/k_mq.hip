@@ -39,14 +39,20 @@ constexpr int kMQQueries = 32 * kMQCompute;  // queries per workgroup (32 per ma
 
 // Workgroup shape.  At d = 64 the matrix waves fit three to a SIMD, so four
 // more waves do the staging (key rebuild, V transpose, loads) next to them;
-// at d = 128 the eight matrix waves stage the tiles themselves.  Tiles hold
+// at d >= 128 the eight matrix waves stage the tiles themselves.  Tiles hold
 // 128 keys, except at d = 128, b = 5, where the 4096-entry direction table
-// (64 KiB) leaves room in LDS for two buffer sets of 64-key tiles only.
+// (64 KiB) leaves room in LDS for two buffer sets of 64-key tiles only, and
+// at d = 256 (K^ rows of 512 bytes).  At d = 256 the value dims are split
+// over two workgroups (adjacent blocks, value part blockIdx.x % 2): each
+// computes every score of its queries and the output of 128 value dims, so
+// a matrix wave holds 64 accumulator registers of O^T, not 128.
 template <int D, int B>
 struct MQShape {
-  static constexpr int KT = D == 128 && B == 5 ? 64 : 128;  // keys per tile
+  static constexpr int KT = D == 256 || (D == 128 && B == 5) ? 64 : 128;  // keys per tile
+  static constexpr int DV = D > 128 ? 128 : D;    // value dims per workgroup
+  static constexpr int NVP = D / DV;              // value parts
   static constexpr int KP = D * 2 + 16;           // K^ row pitch in bytes (fp16)
-  static constexpr int VR = D * 2;                // V row bytes (fp16, unpadded)
+  static constexpr int VR = DV * 2;               // V row bytes (fp16, unpadded)
   static constexpr int SW = D == 64 ? 4 : 0;      // staging-only waves
   static constexpr int NW = kMQCompute + SW;      // waves per workgroup
   static constexpr int NSW = SW ? SW : kMQCompute;  // waves that stage
@@ -54,15 +60,15 @@ struct MQShape {
   static constexpr int DQ = D / PARTS;            // dims rebuilt per lane
   static_assert(DQ % 8 == 0 && PARTS * DQ == D, "whole 16-byte row segments per lane");
   static constexpr int NTH_S = 64 * NSW;          // staging threads
-  static constexpr int KPT = KT * D / (8 * NTH_S);  // V rows staged per thread
-  static constexpr int KGS = NTH_S / (D / 8);       // key stride between them
+  static constexpr int KPT = KT * DV / (8 * NTH_S);  // V rows staged per thread
+  static constexpr int KGS = NTH_S / (DV / 8);       // key stride between them
 };
 
 // 64-byte segment swizzle of V row r in LDS: segment s is stored at s ^
 // vswz(r).  The 4 rows one half-wave's transposing read touches (r = 4m ..
 // 4m + 3) then cover all 64 banks, as do the 16-byte staging writes.
-template <int D>
-__device__ __forceinline__ int vswz(int r) { return D == 64 ? (r >> 1) & 1 : r & 3; }
+template <int DV>
+__device__ __forceinline__ int vswz(int r) { return DV == 64 ? (r >> 1) & 1 : r & 3; }
 
 // Registers carrying one tile's global data from its loads (issued during
 // the previous tile's matrix work) to its LDS staging.
@@ -77,7 +83,7 @@ struct MQStage {
 // key; they are masked later).  The waves of a key half all load the half's
 // words (the same lines).
 template <int D, int B>
-__device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int stid,
+__device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t, int stid, int vp,
                                         MQStage<D, B>& st) {
   using S = MQShape<D, B>;
   constexpr int W = Codec<D, B>::W;
@@ -87,8 +93,8 @@ __device__ __forceinline__ void mq_load(const MQArgs& a, int64_t seq, int64_t t,
   key = key < a.n_keys ? key : a.n_keys - 1;
   TileWords<W>::load(a.packed + (seq * tiles64 + (key >> 6)) * W * kTile, (int)(key & 63), st.words);
   st.gamma = a.gamma[seq * a.cap + key];
-  const int c = stid % (D / 8), kg = stid / (D / 8);
-  const uint4* vseq = (const uint4*)a.v + seq * a.cap * (D / 8) + c;
+  const int c = stid % (S::DV / 8), kg = stid / (S::DV / 8);
+  const uint4* vseq = (const uint4*)a.v + seq * a.cap * (D / 8) + vp * (S::DV / 8) + c;
 #pragma unroll
   for (int i = 0; i < S::KPT; ++i) {
     int64_t kv = t * S::KT + kg + S::KGS * i;
@@ -177,7 +183,7 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
   constexpr int T = C::T;
   constexpr int KT = S::KT, KP = S::KP, VR = S::VR, NTH = 64 * S::NW;
   constexpr int NKS = D / 16;  // MFMA K-steps over the head dim
-  constexpr int NMB = D / 32;  // 32-row blocks of O^T
+  constexpr int NMB = S::DV / 32;  // 32-row blocks of O^T
 
   // two sets of tile buffers: tile t + 1 is staged while tile t is computed
   __shared__ __align__(16) unsigned char s_k[2][KT * KP];
@@ -237,7 +243,8 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
   float m_run = -INFINITY, l_run = 0.f;
 
   const int64_t ntile = (a.n_keys + KT - 1) / KT;
-  const int64_t t_begin = (int64_t)blockIdx.x * a.tiles_per_split;
+  const int split = blockIdx.x / S::NVP, vp = blockIdx.x % S::NVP;   // (uniform)
+  const int64_t t_begin = (int64_t)split * a.tiles_per_split;
   const int64_t t_end = t_begin + a.tiles_per_split < ntile ? t_begin + a.tiles_per_split : ntile;
   constexpr int KPT = S::KPT;
 
@@ -267,7 +274,7 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
         mq_rebuild_from<D, B, 1>(part, st, gs, s_dir, s_rho, krow);
       }
     }
-    const int c = stid % (D / 8), kg = stid / (D / 8);
+    const int c = stid % (S::DV / 8), kg = stid / (S::DV / 8);
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int key = kg + S::KGS * i;
@@ -276,15 +283,15 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
       uint32_t hv[4];   // f16 pairs (dims 2e, 2e+1)
 #pragma unroll
       for (int e = 0; e < 4; ++e) hv[e] = ok ? bf16x2_to_f16x2(src[e]) : 0u;
-      *(uint4*)(s_v[bs] + key * VR + ((16 * c) ^ (vswz<D>(key) << 6))) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
+      *(uint4*)(s_v[bs] + key * VR + ((16 * c) ^ (vswz<S::DV>(key) << 6))) = make_uint4(hv[0], hv[1], hv[2], hv[3]);
     }
   };
 
-  if (stager) mq_load<D, B>(a, seq, t_begin < ntile ? t_begin : 0, stid, st);
+  if (stager) mq_load<D, B>(a, seq, t_begin < ntile ? t_begin : 0, stid, vp, st);
   __syncthreads();  // s_dir / s_rho
   if (stager && t_begin < t_end) {
     stage(t_begin * KT, 0);
-    mq_load<D, B>(a, seq, t_begin + 1 < t_end ? t_begin + 1 : t_begin, stid, st);
+    mq_load<D, B>(a, seq, t_begin + 1 < t_end ? t_begin + 1 : t_begin, stid, vp, st);
   }
   __syncthreads();
 
@@ -300,7 +307,7 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
       voff[mb] = (4 * g + (jt >> 2)) * VR +
-                 ((64 * mb + 32 * (ln >> 4) + 8 * (jt & 3)) ^ (vswz<D>(jt >> 2) << 6));
+                 ((64 * mb + 32 * (ln >> 4) + 8 * (jt & 3)) ^ (vswz<S::DV>(jt >> 2) << 6));
   }
 
   for (int64_t t = t_begin; t < t_end; ++t) {
@@ -311,7 +318,7 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
     // request the tile after it
     if (stager && t + 1 < t_end) {
       stage(k0 + KT, cb ^ 1);
-      mq_load<D, B>(a, seq, t + 2 < t_end ? t + 2 : t + 1, stid, st);
+      mq_load<D, B>(a, seq, t + 2 < t_end ? t + 2 : t + 1, stid, vp, st);
     }
     const unsigned char* sk = s_k[cb];
     const unsigned char* svt = s_v[cb];
@@ -411,22 +418,22 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
 
   l_run = pair32_sum(l_run);
   if (qvalid) {
-    float* dst = a.part + (((int64_t)bh * a.n_q + q) * a.n_split + blockIdx.x) * (D + 2);
-    if (g == 0) {
+    float* dst = a.part + (((int64_t)bh * a.n_q + q) * a.n_split + split) * (D + 2);
+    if (g == 0 && vp == 0) {
       dst[0] = m_run;
       dst[1] = l_run;
     }
 #pragma unroll
     for (int mb = 0; mb < NMB; ++mb)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) dst[2 + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = o[mb][r];
+      for (int r = 0; r < 16; ++r) dst[2 + vp * S::DV + 32 * mb + 8 * (r >> 2) + 4 * g + (r & 3)] = o[mb][r];
   }
 }
 
 template <int D, int B>
 static hipError_t mq_t(const MQArgs& a, hipStream_t s) {
-  const dim3 grid((unsigned)a.n_split, (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries),
-                  (unsigned)(a.B * a.H));
+  const dim3 grid((unsigned)(a.n_split * MQShape<D, B>::NVP),
+                  (unsigned)((a.n_q + kMQQueries - 1) / kMQQueries), (unsigned)(a.B * a.H));
   hipLaunchKernelGGL((k_mq_attn<D, B>), grid, dim3((64 * MQShape<D, B>::NW)), 0, s, a);
   return hipGetLastError();
 }
@@ -455,12 +462,19 @@ int lds_copies_mq(LdsCopyRec* out, int max) {
   n = mq_copy_recs<128, 3>(out, n, max);
   n = mq_copy_recs<128, 4>(out, n, max);
   n = mq_copy_recs<128, 5>(out, n, max);
+  n = mq_copy_recs<256, 1>(out, n, max);
+  n = mq_copy_recs<256, 2>(out, n, max);
+  n = mq_copy_recs<256, 3>(out, n, max);
+  n = mq_copy_recs<256, 4>(out, n, max);
   return n;
 }
 
 int mq_tile_keys(int d, int b) {
-  return d == 64 ? MQShape<64, 1>::KT : (b == 5 ? MQShape<128, 5>::KT : MQShape<128, 1>::KT);
+  if (d == 64) return MQShape<64, 1>::KT;
+  if (d == 256) return MQShape<256, 1>::KT;
+  return b == 5 ? MQShape<128, 5>::KT : MQShape<128, 1>::KT;
 }
+int mq_value_parts(int d) { return d == 256 ? MQShape<256, 1>::NVP : 1; }
 int mq_block_queries() { return kMQQueries; }
 
 hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
@@ -475,6 +489,12 @@ hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
     case 645: return mq_t<64, 5>(a, s);
     case 1281: return mq_t<128, 1>(a, s);
     case 1285: return mq_t<128, 5>(a, s);
+    case 2561: return mq_t<256, 1>(a, s);
+    case 2562: return mq_t<256, 2>(a, s);
+    case 2563: return mq_t<256, 3>(a, s);
+    case 2564: return mq_t<256, 4>(a, s);
+    // d = 256 at b = 5: the 4096-entry direction table (64 KiB) and the two
+    // buffer sets of 64-key tiles (98 KiB) exceed the LDS (refused)
   }
   return hipErrorInvalidValue;
 }

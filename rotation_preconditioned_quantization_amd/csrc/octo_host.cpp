@@ -454,7 +454,7 @@ Split mq_split(int64_t n_keys, int d, int b, int64_t rows) {
   const int kt = mq_tile_keys(d, b);
   const int64_t ntile = std::max<int64_t>(1, (n_keys + kt - 1) / kt);
   const int64_t slots = device_cus();
-  rows = std::max<int64_t>(1, rows);
+  rows = std::max<int64_t>(1, rows) * mq_value_parts(d);   // workgroups per split
   int64_t best_ns = 1, best_cost = INT64_MAX;
   for (int64_t ns = 1; ns <= std::min<int64_t>(ntile, kMaxSplit); ++ns) {
     const int64_t tps = (ntile + ns - 1) / ns;
@@ -1072,8 +1072,8 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
-    if (cb->d == 256)
-      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 256 (one query at a time)");
+    if (cb->d == 256 && cb->b == 5)
+      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 256, b = 5 (LDS)");
     if (stages & OCTO_STAGE_ROTATE) {
       st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
       if (st != OCTO_OK) return st;

@@ -177,6 +177,7 @@ int lds_copies_encode(LdsCopyRec* out, int max);
 // device), resolved once per device.
 hipError_t static_scratch(int device, void** out);
 int mq_tile_keys(int d, int b);  // keys per tile of the multi-query kernel
+int mq_value_parts(int d);       // workgroups sharing one (query block, split): value dim parts
 int mq_block_queries();   // queries per workgroup of the multi-query kernel
 
 }  // namespace octo

@@ -357,6 +357,14 @@ def test_logits_qjl_fp32_keys(d, b):
     check_logits(cfg, 2, 1, 2, 333, 384, seed=11 + b, qjl=True, label=f"qjl-f32-d{d}b{b}")
 
 
+@pytest.mark.parametrize("b", [2, 3])
+def test_mq_d256_multi_split(b):
+    """d = 256: the value dims split over two adjacent workgroups, each
+    forming every score of its queries; 64-key tiles, several splits, a
+    ragged last tile, GQA and a partial query block."""
+    check_mq(WL.CONFIGS[4].scaled(d=256, b=b), 4, 2, 300, 3000, 3008, seed=23 + b, label=f"mq-d256b{b}-split")
+
+
 def test_mq_d128_b5_multi_split():
     """d = 128, b = 5 runs the multi-query kernel on 64-key tiles (the
     4096-entry direction table leaves LDS for no more): a cache long enough
@@ -680,12 +688,13 @@ def test_decode_step_append_d256():
 
 
 def test_d256_unsupported_paths_are_refused():
-    """QJL codebooks and the multi-query path have no d = 256 kernel."""
+    """QJL codebooks have no d = 256 kernel, nor the multi-query path at
+    d = 256, b = 5 (its direction table and tiles exceed the LDS)."""
     octo = _octo()
     with pytest.raises(octo.OctoError) as e:
         octo.Codebook(256, 3, qjl=True, device=0)
     assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
-    g = gcb(256, 3)
+    g = gcb(256, 5)
     cache = octo.Cache(g, 1, 128)
     keys = torch.randn((1, 100, 256), device="cuda", dtype=torch.bfloat16)
     octo.octo_encode(g, keys, cache)
@@ -873,7 +882,7 @@ def test_mq_video_recipe_small():
     check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
 
 
-@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5)])
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5), (256, 1), (256, 4)])
 def test_mq_shapes_and_gqa(d, b):
     check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
 
