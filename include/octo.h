@@ -60,10 +60,8 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
  * ([AR] 位元分配: it depends only on d and the bit budget; [AB]: deterministic
  * given a seed).
  *   d         head dim: 64, 128 and 256 have kernels (any power of two 4..1024
- *             for a host-only codebook).  At d = 256 there is no QJL variant
- *             (a QJL codebook is refused with OCTO_ERR_UNSUPPORTED) and no
- *             multi-query path at b = 5; the encoder gives each key two lanes
- *             there.
+ *             for a host-only codebook).  At d = 256 there is no multi-query
+ *             path at b = 5; the encoder gives each key two lanes there.
  *   b         bit budget per coordinate; kernels exist for 1 .. 5.
  *   seed      seeds the WHT sign vector and the QJL projection.
  *   cb_seed   seeds the Monte-Carlo samples the Lloyd-Max tables are fit to.

@@ -939,15 +939,13 @@ static hipError_t attn_t(const DecodeArgs& a, int64_t n_seq, hipStream_t s) {
   return hipGetLastError();
 }
 
-// d = 256: no QJL kernels
 #define OCTO_DISPATCH_DBQ(FN, ...)                                                              \
-  if (d == 256 && qjl) return hipErrorInvalidValue;                                             \
   switch (d * 10 + b) {                                                                         \
-    case 2561: return FN<256, 1, false>(__VA_ARGS__);                                           \
-    case 2562: return FN<256, 2, false>(__VA_ARGS__);                                           \
-    case 2563: return FN<256, 3, false>(__VA_ARGS__);                                           \
-    case 2564: return FN<256, 4, false>(__VA_ARGS__);                                           \
-    case 2565: return FN<256, 5, false>(__VA_ARGS__);                                           \
+    case 2561: return qjl ? FN<256, 1, true>(__VA_ARGS__) : FN<256, 1, false>(__VA_ARGS__);     \
+    case 2562: return qjl ? FN<256, 2, true>(__VA_ARGS__) : FN<256, 2, false>(__VA_ARGS__);     \
+    case 2563: return qjl ? FN<256, 3, true>(__VA_ARGS__) : FN<256, 3, false>(__VA_ARGS__);     \
+    case 2564: return qjl ? FN<256, 4, true>(__VA_ARGS__) : FN<256, 4, false>(__VA_ARGS__);     \
+    case 2565: return qjl ? FN<256, 5, true>(__VA_ARGS__) : FN<256, 5, false>(__VA_ARGS__);     \
     case 641: return qjl ? FN<64, 1, true>(__VA_ARGS__) : FN<64, 1, false>(__VA_ARGS__);        \
     case 642: return qjl ? FN<64, 2, true>(__VA_ARGS__) : FN<64, 2, false>(__VA_ARGS__);        \
     case 643: return qjl ? FN<64, 3, true>(__VA_ARGS__) : FN<64, 3, false>(__VA_ARGS__);        \
@@ -994,6 +992,7 @@ int lds_copies_decode(LdsCopyRec* out, int max) {
   OCTO_REC_B(128, false)
   OCTO_REC_B(128, true)
   OCTO_REC_B(256, false)
+  OCTO_REC_B(256, true)
 #undef OCTO_REC_B
   return n;
 }

@@ -640,8 +640,68 @@ __device__ __forceinline__ void load_half_rows(const EncodeArgs& a, int64_t seq,
   }
 }
 
-template <int B, int KT, bool JR>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(JR || KT == DT_F32 ? 2 : 3)))
+// QJL signs of the wave's 32 keys at d = 256 (two lanes per key: lane l < 32
+// holds dims 0..127 of key l's residual r', lane l + 32 dims 128..255) on
+// the matrix cores, P = R' S^T, P[key][j] = <S_j, r'_key>, bit j of the key's
+// sign words = (P >= 0) ([YL] 可选的残差修正; sgn(0) = +1).  The same three-term
+// f16 split as qjl_signs; the contraction index is ordered so that every lane
+// supplies its own dims: step kb of v_mfma_f32_32x32x16_f16 takes dims
+// 128 g + 8 kb .. + 7 from lane (key, g) for the A operand and from S row
+// j = 32 nb + l % 32 for the B operand, read straight from the f16 planes in
+// global memory (S of d = 256 does not fit the LDS; 256 KiB, L2-resident).
+// Output register r of lane (l % 32, g) is key 8 (r / 4) + 4 g + r % 4 and
+// projection 32 nb + l % 32; the ballots give lane k (k < 32) key k's words.
+__device__ __forceinline__ void qjl_signs256(const float (&v)[128], const uint4* S16, int lane,
+                                             uint32_t (&sw)[8]) {
+  constexpr int D = 256;
+  half8 ah[16], al[16];
+#pragma unroll
+  for (int kb = 0; kb < 16; ++kb) {
+    uint32_t ph[4], pl[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const float x0 = v[8 * kb + 2 * p] * 4096.f, x1 = v[8 * kb + 2 * p + 1] * 4096.f;
+      const __half2 h = __float22half2_rn(make_float2(x0, x1));
+      const float2 hf = __half22float2(h);
+      const __half2 l = __float22half2_rn(make_float2(x0 - hf.x, x1 - hf.y));
+      ph[p] = __builtin_bit_cast(uint32_t, h);
+      pl[p] = __builtin_bit_cast(uint32_t, l);
+    }
+    ah[kb] = __builtin_bit_cast(half8, make_uint4(ph[0], ph[1], ph[2], ph[3]));
+    al[kb] = __builtin_bit_cast(half8, make_uint4(pl[0], pl[1], pl[2], pl[3]));
+  }
+  const int ln = lane & 31, g = lane >> 5;
+  // 16-byte units: row j of a plane is 32 units, the lo plane follows the hi
+#pragma unroll 1
+  for (int nb = 0; nb < D / 32; ++nb) {
+    const uint4* row = S16 + (32 * nb + ln) * (D / 8) + 16 * g;
+    floatx16 c;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) c[r] = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 16; ++kb) {
+      const half8 bh = __builtin_bit_cast(half8, row[kb]);
+      const half8 bl = __builtin_bit_cast(half8, row[D * D / 8 + kb]);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], bh, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(ah[kb], bl, c, 0, 0, 0);
+      c = __builtin_amdgcn_mfma_f32_32x32x16_f16(al[kb], bh, c, 0, 0, 0);
+    }
+    int w = 0;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+      const uint64_t m = __ballot(c[r] >= 0.f);
+      const int key = 8 * (r >> 2) + (r & 3);
+      w = octo_writelane((int)(uint32_t)m, key, w);
+      w = octo_writelane((int)(uint32_t)(m >> 32), key + 4, w);
+    }
+    // (nb is not unrolled: a lane-indexed select keeps sw in registers)
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sw[k] = nb == k ? (uint32_t)w : sw[k];
+  }
+}
+
+template <int B, int KT, bool JR, bool QJL>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(QJL || JR || KT == DT_F32 ? 2 : 3)))
 void k_encode256(EncodeArgs a) {
   constexpr int D = 256;
   using C = Codec<D, B>;
@@ -654,13 +714,14 @@ void k_encode256(EncodeArgs a) {
   __shared__ __align__(16) unsigned char s_keys[4][S::NR * S::PITCH];
   __shared__ uint2 s_qx[kMaxLut + 2], s_qe[kMaxLut + 2], s_qr[kMaxLut + 2];
   __shared__ uint32_t s_w[4][32][W | 1];                   // odd pitch: conflict-free rows
-  // unit directions and rho centroids (joint rounding)
-  __shared__ float4 s_dir[JR ? C::NDIR : 1];
-  __shared__ float s_rho[JR ? C::LR : 1];
+  // unit directions and rho centroids (joint rounding, QJL residual)
+  constexpr bool TABS = JR || QJL;
+  __shared__ float4 s_dir[TABS ? C::NDIR : 1];
+  __shared__ float s_rho[TABS ? C::LR : 1];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int64_t seq = blockIdx.y;
   copy_bucket_tables<256>(a.t, s_qx, s_qe, s_qr, threadIdx.x);
-  if constexpr (JR) {
+  if constexpr (TABS) {
     for (int i = threadIdx.x; i < C::NDIR; i += 256) s_dir[i] = a.t.dirtab[i];
     if (threadIdx.x < C::LR) s_rho[threadIdx.x] = a.t.rho_tab[threadIdx.x];
   }
@@ -809,6 +870,49 @@ void k_encode256(EncodeArgs a) {
   }
   const float gamma = __builtin_ldexpf(__builtin_sqrtf(tot * (1.0f / D)), sexp);
 
+  // QJL: the rotated unit-direction residual r' = u' - u'^ over the lane's
+  // 128 dims, its norm over the pair, and the signs of S r'.  The first
+  // lane's element j lies in its triplet j / 3 (component j % 3); the second
+  // lane's element j >= 1 in its triplet (j - 1) / 3, and its element 0 (the
+  // key's element 128) in the first lane's triplet 42.
+  uint32_t sbits[QJL ? 8 : 1];
+  float nu = 0.f;
+  if constexpr (QJL) {
+    const float inv_norm = tot > 0.f ? __builtin_amdgcn_rsqf(tot) : 0.f;
+    const uint32_t c42 = pair_xchg(field_at<WL>(wl, 42 * C::BT, C::BT), lane);
+    float cur[3], prev[3];
+    {
+      const float4 n = s_dir[c42 & C::DIR_MASK];
+      const float rh = s_rho[c42 >> (C::BX + C::BE)];
+      cur[0] = rh * n.x; cur[1] = rh * n.y; cur[2] = rh * n.z;
+    }
+    float nu2 = 0.f;
+#pragma unroll
+    for (int j = 0; j < 128; ++j) {
+      const int c = j % 3;
+      if (c == 0) {
+#pragma unroll
+        for (int k = 0; k < 3; ++k) prev[k] = cur[k];
+        const uint32_t code = field_at<WL>(wl, (j / 3) * C::BT, C::BT);
+        const float4 n = s_dir[code & C::DIR_MASK];
+        const float rh = s_rho[code >> (C::BX + C::BE)];
+        cur[0] = rh * n.x; cur[1] = rh * n.y; cur[2] = rh * n.z;
+      }
+      const float sub = hi ? (c == 0 ? prev[2] : cur[c - 1]) : cur[c];
+      const float r = __builtin_fmaf(v[j], inv_norm, -sub);
+      v[j] = r;
+      nu2 = __builtin_fmaf(r, r, nu2);
+    }
+    nu2 += pair_xchg(nu2, lane);
+    // formed here: left to itself the compiler may sink the sum past the
+    // projection and keep all 128 residuals live through it
+    asm volatile("" : "+v"(nu2));
+    nu = __builtin_sqrtf(nu2);
+#pragma unroll
+    for (int k = 0; k < 8; ++k) sbits[k] = 0u;
+    qjl_signs256(v, a.t.S16, lane, sbits);
+  }
+
   // Assemble the key's word stream in LDS: the first lane's words hold bits
   // 0 .. OFF-1; the second lane's, shifted to bit OFF, are ORed in after.
   const int key = lane % 32;
@@ -842,15 +946,28 @@ void k_encode256(EncodeArgs a) {
     TileWords<W>::store(a.packed + (seq * (a.cap / kTile) + (pos >> 6)) * W * kTile, (int)(pos & 63),
                         words);
     a.gamma[seq * a.cap + pos] = gamma;
+    if constexpr (QJL) {
+      TileWords<D / 32>::store(a.qjl_bits + (seq * (a.cap / kTile) + (pos >> 6)) * (D / 32) * kTile,
+                               (int)(pos & 63), sbits);
+      a.qjl_norm[seq * a.cap + pos] = __half_as_ushort(__float2half_rn(nu));
+    }
   }
 }
 
 template <int B, int KT>
-inline hipError_t launch_encode256_t(const EncodeArgs& a, bool joint, int64_t n_seq, hipStream_t s) {
+inline hipError_t launch_encode256_t(const EncodeArgs& a, bool joint, bool qjl, int64_t n_seq,
+                                     hipStream_t s) {
   if (a.t.qx.nb > kMaxLut || a.t.qe.nb > kMaxLut || a.t.qr2.nb > kMaxLut) return hipErrorInvalidValue;
+  if (qjl && (a.t.S16 == nullptr || a.qjl_bits == nullptr || a.qjl_norm == nullptr))
+    return hipErrorInvalidValue;
   const dim3 grid((unsigned)((a.n_new + 127) / 128), (unsigned)n_seq);
-  if (joint) hipLaunchKernelGGL((k_encode256<B, KT, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_encode256<B, KT, false>), grid, dim3(256), 0, s, a);
+  if (qjl) {
+    if (joint) hipLaunchKernelGGL((k_encode256<B, KT, true, true>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_encode256<B, KT, false, true>), grid, dim3(256), 0, s, a);
+  } else {
+    if (joint) hipLaunchKernelGGL((k_encode256<B, KT, true, false>), grid, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL((k_encode256<B, KT, false, false>), grid, dim3(256), 0, s, a);
+  }
   return hipGetLastError();
 }
 
@@ -906,13 +1023,12 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
     if (d == 256) { OCTO_ENC_ONE(256) }
     return hipErrorInvalidValue;
   }
-  // d = 256: two lanes per key (scalar or joint rounding, no QJL)
+  // d = 256: two lanes per key (scalar or joint rounding, with or without QJL)
   if (d == 256) {
-    if (qjl) return hipErrorInvalidValue;
     switch (kdt) {
-      case DT_F32: return launch_encode256_t<B, DT_F32>(a, joint, n_seq, s);
-      case DT_BF16: return launch_encode256_t<B, DT_BF16>(a, joint, n_seq, s);
-      case DT_F16: return launch_encode256_t<B, DT_F16>(a, joint, n_seq, s);
+      case DT_F32: return launch_encode256_t<B, DT_F32>(a, joint, qjl, n_seq, s);
+      case DT_BF16: return launch_encode256_t<B, DT_BF16>(a, joint, qjl, n_seq, s);
+      case DT_F16: return launch_encode256_t<B, DT_F16>(a, joint, qjl, n_seq, s);
     }
     return hipErrorInvalidValue;
   }
@@ -926,8 +1042,9 @@ hipError_t launch_encode_b(int d, int kdt, bool qjl, bool joint, const EncodeArg
 // the quantiser tables (loops bounded at run time by the table's nb + 2
 // entries, which the launchers check against the kMaxLut + 2 LDS entries),
 // and, where the variant holds them, the unit directions and rho centroids
-// (QJL residual, joint rounding) and the f16 QJL matrix.
-template <int D, int B, bool QJL, bool JR, int NTH>
+// (QJL residual, joint rounding) and the f16 QJL matrix (SLDS: held in LDS;
+// the d = 256 encoder reads it from global memory).
+template <int D, int B, bool QJL, bool JR, int NTH, bool SLDS = QJL>
 inline int enc_copy_recs(const char* kernel, LdsCopyRec* out, int n, int max) {
   using C = Codec<D, B>;
   for (int tab : {TAB_QX, TAB_QE, TAB_QR2})
@@ -938,7 +1055,7 @@ inline int enc_copy_recs(const char* kernel, LdsCopyRec* out, int n, int max) {
       out[n++] = {kernel, D, B, QJL, TAB_DIR, C::NDIR, TC::SLOTS, TC::ENTRIES, C::NDIR, NTH, TC::MASKED};
     if (n < max) out[n++] = {kernel, D, B, QJL, TAB_RHO, C::LR, C::LR, C::LR, C::LR, NTH, C::LR % NTH != 0};
   }
-  if (QJL) {
+  if (SLDS) {
     using SL = SLds<D>;
     if (n < max)
       out[n++] = {kernel, D, B, QJL, TAB_S16, SL::BYTES / 16, SL::SLOT_END, SL::CHUNKS, SL::CHUNKS, NTH,
@@ -960,6 +1077,8 @@ inline int enc_copy_recs_b(LdsCopyRec* out, int n, int max) {
 #undef OCTO_REC_D
   n = enc_copy_recs<256, B, false, false, 256>("k_encode256", out, n, max);
   n = enc_copy_recs<256, B, false, true, 256>("k_encode256 (joint)", out, n, max);
+  n = enc_copy_recs<256, B, true, false, 256, false>("k_encode256 (qjl)", out, n, max);
+  n = enc_copy_recs<256, B, true, true, 256, false>("k_encode256 (qjl, joint)", out, n, max);
   n = enc_copy_recs<256, B, false, false, 256>("k_encode_one", out, n, max);
   return n;
 }

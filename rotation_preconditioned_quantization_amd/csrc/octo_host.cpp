@@ -529,8 +529,6 @@ octo_status octo_codebook_build(const octo_params* p, octo_codebook** out) {
     return fail(OCTO_ERR_UNSUPPORTED,
                 "kernels exist for d in {64,128,256}, b in 1..5 and the (b+1,b+1,b-1) allocation; "
                 "build with device = -1 for host-only tables");
-  if (p->device >= 0 && p->qjl && d > 128)
-    return fail(OCTO_ERR_UNSUPPORTED, "QJL kernels exist for d in {64,128}");
   octo_codebook* cb = new (std::nothrow) octo_codebook();
   if (!cb) return fail(OCTO_ERR_NOMEM, "host allocation failed");
   cb->d = d;

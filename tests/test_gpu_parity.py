@@ -127,27 +127,28 @@ def test_encode_joint_rounding(d, b, kdt):
     assert mse(codes.reshape(-1, cb.T, 3)) < mse(scal.codes)
 
 
-def test_encode_joint_rounding_with_qjl():
+@pytest.mark.parametrize("d,b", [(128, 3), (256, 3)])
+def test_encode_joint_rounding_with_qjl(d, b):
     """Joint rounding with the QJL residual: the residual follows the chosen codes."""
     octo = _octo()
-    cfg = WL.CONFIGS[5]
+    cfg = WL.CONFIGS[5].scaled(d=d, b=b)
     keys = WL.make_keys(cfg, "cuda", seed=9, n_seq=2, n=130)
-    g = gcb(128, 3, 0, 0, True)
+    g = gcb(d, b, 0, 0, True)
     cache = octo.Cache(g, 2, 192, qjl=True)
     octo.octo_encode_joint(g, keys, cache)
     torch.cuda.synchronize()
-    cb = ocb(128, 3)
-    kk = f64(keys).reshape(-1, 128)
+    cb = ocb(d, b)
+    kk = f64(keys).reshape(-1, d)
     enc = O.encode(kk, cb, rounding="joint")
     codes = unpack_device_codes(cache.packed.cpu().numpy(), cb, 2, 192, 130)
     n_mis, n_exc, n_unexc, total = compare_joint_codes(codes, enc, cb)
     assert n_unexc == 0 and n_exc <= MAX_EXCUSED_FRACTION * total
     # signs of S r' with r' from the device's own codes
-    S = O.qjl_matrix(128, 0)
+    S = O.qjl_matrix(d, 0)
     uh = O.decode_rotated(codes.reshape(-1, cb.T, 3), cb)
     qe = O.qjl_encode(enc.rotated, uh, S)
-    signs = unpack_device_signs(cache.qjl_bits.cpu().numpy(), 128, 2, 192, 130).reshape(-1, 128)
-    r = enc.rotated - uh
+    signs = unpack_device_signs(cache.qjl_bits.cpu().numpy(), d, 2, 192, 130).reshape(-1, d)
+    r = enc.rotated[:, :d] - uh[:, :d]
     proj = r @ S.T
     bad = (signs != qe.signs) & (np.abs(proj) > 1e-6 * np.linalg.norm(S, axis=1)[None, :]
                                  * np.linalg.norm(r, axis=1)[:, None])
@@ -346,6 +347,23 @@ def test_logits_qjl_d64():
 def test_logits_qjl_wider_bit_budgets(d, b):
     cfg = WL.CONFIGS[5].scaled(d=d, b=b)
     check_logits(cfg, 1, 1, 2, 200, 256, seed=3 + b, qjl=True, label=f"qjl-d{d}b{b}")
+
+
+@pytest.mark.parametrize("b,kdt", [(1, "bf16"), (2, "bf16"), (3, "f32"), (4, "bf16"), (5, "f16")])
+def test_logits_qjl_d256(b, kdt):
+    """OCTOPUS-QJL at d = 256: the two-lane-per-key encoder forms the residual
+    over both halves (the key's element 128 lies in the first lane's last
+    triplet) and the signs of S r' on the matrix cores with S read from
+    global memory; logits against the oracle, ragged tail."""
+    cfg = WL.CONFIGS[5].scaled(d=256, b=b, kdtype=kdt)
+    check_logits(cfg, 1, 2, 2, 333, 384, seed=31 + b, qjl=True, label=f"qjl-d256b{b}{kdt}")
+
+
+def test_attention_qjl_d256():
+    """Single-query attention with the QJL term at d = 256 (the value dims
+    over two blocks, each forming the QJL-corrected logits)."""
+    cfg = WL.CONFIGS[5].scaled(d=256, b=3, keys="gauss")
+    check_attention(cfg, 1, 2, 4, 300, 320, seed=37, qjl=True, label="attn-qjl-d256")
 
 
 @pytest.mark.parametrize("d,b", [(128, 5), (128, 3), (64, 4)])
@@ -688,12 +706,9 @@ def test_decode_step_append_d256():
 
 
 def test_d256_unsupported_paths_are_refused():
-    """QJL codebooks have no d = 256 kernel, nor the multi-query path at
-    d = 256, b = 5 (its direction table and tiles exceed the LDS)."""
+    """The multi-query path has no kernel at d = 256, b = 5 (its direction
+    table and tiles exceed the LDS); the multi-query path has no QJL variant."""
     octo = _octo()
-    with pytest.raises(octo.OctoError) as e:
-        octo.Codebook(256, 3, qjl=True, device=0)
-    assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
     g = gcb(256, 5)
     cache = octo.Cache(g, 1, 128)
     keys = torch.randn((1, 100, 256), device="cuda", dtype=torch.bfloat16)
