@@ -330,6 +330,70 @@ __device__ __forceinline__ uint32_t joint_code(float x, float y, float z, uint32
   return best;
 }
 
+// The lane's key from the tile's raw rows: staged through LDS, then as fp32
+// values (16-bit keys: after WHT strides 1 and 2, taken on the matrix cores
+// straight from the packed elements by h4_apply).
+template <int D, int KT, int NRW>
+__device__ __forceinline__ void tile_values(const uint4 (&raw)[Stage<D, KT, NRW>::NP][Stage<D, KT, NRW>::PER_LANE],
+                                            int lane, unsigned char* s_keys, const uint4& smask,
+                                            float (&v)[D]) {
+  using S = Stage<D, KT, NRW>;
+  uint4 rowbits[S::CPR];
+  stage_rows<D, KT, NRW>(raw, lane, s_keys, smask, rowbits);
+  if constexpr (KT == DT_F32) {
+#pragma unroll
+    for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
+  } else {
+    const uint2 h4 = h4_row<KT>(lane);
+#pragma unroll
+    for (int c = 0; c < S::CPR; ++c) {
+      const wht4_t y0 = h4_apply<KT>(h4, rowbits[c].x, rowbits[c].y);
+      const wht4_t y1 = h4_apply<KT>(h4, rowbits[c].z, rowbits[c].w);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        v[8 * c + k] = y0[k];
+        v[8 * c + 4 + k] = y1[k];
+      }
+    }
+  }
+}
+
+// Keys with entries far from 1 in magnitude are scaled by an exact power of
+// two (changes no ratio) so that no triplet energy under- or overflows: the
+// exponent of the largest value (after strides 1 and 2 for 16-bit keys, of
+// the raw values for fp32 keys) decides, as in every encoder.  Returns it
+// (0: not scaled).
+template <int D>
+__device__ __forceinline__ int prescale_scan(float (&v)[D]) {
+  float amax = 0.f;
+#pragma unroll
+  for (int j = 0; j < D; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
+  int ex = 0;
+  __builtin_frexpf(amax, &ex);
+  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
+  if (__any(sexp != 0)) {
+    const float scale = __builtin_ldexpf(1.0f, -sexp);
+#pragma unroll
+    for (int j = 0; j < D; ++j) v[j] *= scale;
+  }
+  return sexp;
+}
+
+// A range of |y|^2 (y: the key after the whole unnormalised WHT) inside which
+// prescale_scan leaves the key alone.  y's squared norm is F times that of the
+// values prescale_scan looks at (F = D / 4 after strides 1 and 2, D for raw
+// fp32 values), and that lies in [amax^2, D amax^2].  prescale_scan scales
+// when amax >= 2^50 (then |y|^2 >= F 2^100) or 0 < amax < 2^-51 (then
+// |y|^2 < F D 2^-102); with a factor 2 of margin for the rounding of the sum,
+// |y|^2 in [F D 2^-101, F 2^99), or 0, means amax in [2^-51, 2^50) or 0.
+template <int D, int KT>
+struct NormRange {
+  static constexpr float F = KT == DT_F32 ? (float)D : (float)(D / 4);
+  static constexpr float LO = F * (float)D * 0x1p-101f;
+  static constexpr float HI = F * 0x1p99f;
+  __device__ static bool unscaled(float tot) { return tot == 0.f || (tot >= LO && tot < HI); }
+};
+
 // Encode the 64-key tile at j0 from its raw rows (load_rows): one key per
 // lane, entirely in registers.
 template <int D, int B, int KT, bool QJL, bool JR, int NRW = 16>
@@ -342,42 +406,15 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   using C = Codec<D, B>;
   using S = Stage<D, KT, NRW>;
   constexpr int T = C::T, W = C::W;
+  // The plain encoder skips the magnitude scan: it checks |y|^2 after the
+  // transform instead, and only a tile with a key outside NormRange is
+  // formed again with the scan.  A key inside the range is one the scan
+  // leaves alone, so every key gets the same words as in the other encoders.
+  constexpr bool CHECK = !QJL && !JR;
   float v[D];
-  {
-    uint4 rowbits[S::CPR];
-    stage_rows<D, KT, NRW>(raw, lane, s_keys, smask, rowbits);
-    if constexpr (KT == DT_F32) {
-#pragma unroll
-      for (int c = 0; c < S::CPR; ++c) cvt_chunk<KT>(rowbits[c], &v[c * S::VPC]);
-    } else {
-      // strides 1 and 2 on the matrix cores, straight from the packed 16-bit
-      // elements (h4_apply)
-      const uint2 h4 = h4_row<KT>(lane);
-#pragma unroll
-      for (int c = 0; c < S::CPR; ++c) {
-        const wht4_t y0 = h4_apply<KT>(h4, rowbits[c].x, rowbits[c].y);
-        const wht4_t y1 = h4_apply<KT>(h4, rowbits[c].z, rowbits[c].w);
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          v[8 * c + k] = y0[k];
-          v[8 * c + 4 + k] = y1[k];
-        }
-      }
-    }
-  }
-  // Keys with entries far from 1 in magnitude are scaled by an exact power of
-  // two (changes no ratio) so that no triplet energy under- or overflows.
-  float amax = 0.f;
-#pragma unroll
-  for (int j = 0; j < D; ++j) amax = __builtin_fmaxf(amax, __builtin_fabsf(v[j]));
-  int ex = 0;
-  __builtin_frexpf(amax, &ex);
-  const int sexp = (ex > 50 || ex < -50) && amax > 0.f ? ex : 0;
-  if (__any(sexp != 0)) {
-    const float scale = __builtin_ldexpf(1.0f, -sexp);
-#pragma unroll
-    for (int j = 0; j < D; ++j) v[j] *= scale;
-  }
+  tile_values<D, KT, NRW>(raw, lane, s_keys, smask, v);
+  int sexp = 0;
+  if constexpr (!CHECK) sexp = prescale_scan<D>(v);
   if constexpr (KT == DT_F32) wht_regs<D>(v);
   else wht_regs_from<D, 4>(v);
 
@@ -393,7 +430,48 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   const int64_t pos = a.pos0 + j;
   const int64_t tiles = a.cap / kTile;
   float tot = 0.f;
-  if constexpr (!JR) {
+  if constexpr (CHECK) {
+    // Pass 1: triplet energies and |y|^2.
+    float e[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      e[i] = triplet_energy(x, y, z);
+      tot += e[i];
+    }
+    if (__any(!NormRange<D, KT>::unscaled(tot))) {
+      // rare: a key far from unit magnitude; the tile again, with the scan
+      // (the lane index passes through an empty asm, so that the compiler
+      // cannot hoist these loads and their addresses out of the branch)
+      int lane2 = lane;
+      asm volatile("" : "+v"(lane2));
+      uint4 raw2[S::NP][S::PER_LANE];
+      load_rows<D, KT, false, NRW>(a, seq, j0, lane2, raw2);
+      tile_values<D, KT, NRW>(raw2, lane2, s_keys, smask, v);
+      sexp = prescale_scan<D>(v);
+      if constexpr (KT == DT_F32) wht_regs<D>(v);
+      else wht_regs_from<D, 4>(v);
+      tot = 0.f;
+#pragma unroll
+      for (int i = 0; i < T; ++i) {
+        float x, y, z;
+        triplet_of<D>(v, i, x, y, z);
+        e[i] = triplet_energy(x, y, z);
+        tot += e[i];
+      }
+    }
+    // Pass 2: the (xi, eta) indices and the rho index from rho_i^2 =
+    // e_i / |y|^2 against the squared midpoints, each code packed once.
+    const RhoQuant<C::LR> rq(a.t, tot);
+#pragma unroll
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be) |
+                                     (rq.index(e[i], s_qr, sr, mr) << (C::BX + C::BE)));
+    }
+  } else if constexpr (!JR) {
     // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
     float e[T];
 #pragma unroll
