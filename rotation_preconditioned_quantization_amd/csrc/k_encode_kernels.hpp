@@ -431,14 +431,13 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   const int64_t tiles = a.cap / kTile;
   float tot = 0.f;
   if constexpr (CHECK) {
-    // Pass 1: triplet energies and |y|^2.
-    float e[T];
+    // Pass 1: |y|^2 (the energies are formed again in pass 2, as the same
+    // operations: holding all T of them would cost T registers)
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       float x, y, z;
       triplet_of<D>(v, i, x, y, z);
-      e[i] = triplet_energy(x, y, z);
-      tot += e[i];
+      tot += triplet_energy(x, y, z);
     }
     if (__any(!NormRange<D, KT>::unscaled(tot))) {
       // rare: a key far from unit magnitude; the tile again, with the scan
@@ -457,8 +456,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
       for (int i = 0; i < T; ++i) {
         float x, y, z;
         triplet_of<D>(v, i, x, y, z);
-        e[i] = triplet_energy(x, y, z);
-        tot += e[i];
+        tot += triplet_energy(x, y, z);
       }
     }
     // Pass 2: the (xi, eta) indices and the rho index from rho_i^2 =
@@ -469,7 +467,7 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
       float x, y, z;
       triplet_of<D>(v, i, x, y, z);
       pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be) |
-                                     (rq.index(e[i], s_qr, sr, mr) << (C::BX + C::BE)));
+                                     (rq.index(triplet_energy(x, y, z), s_qr, sr, mr) << (C::BX + C::BE)));
     }
   } else if constexpr (!JR) {
     // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
@@ -584,12 +582,15 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
   }
 }
 
-// Two waves per SIMD (the one-key-per-lane state fits 256 registers; left
-// alone the allocator took 257 at b = 1 and halved the occupancy), except
-// with QJL at 5 bits, where the LDS allows one wave per SIMD anyway.
+// Three waves per SIMD for the plain encoder of 16-bit keys (its state fits
+// 168 registers once the triplet energies are formed again in the second
+// pass instead of held); two otherwise (the one-key-per-lane state fits 256
+// registers; left alone the allocator took 257 at b = 1 and halved the
+// occupancy), except with QJL at 5 bits, where the LDS allows one wave per
+// SIMD anyway.
 template <int D, int B, int KT, bool QJL, bool JR>
 __global__ __launch_bounds__((64 * enc_waves<QJL, B>()))
-__attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : 2))) void k_encode(EncodeArgs a) {
+__attribute__((amdgpu_waves_per_eu(QJL && B >= 5 ? 1 : (!QJL && !JR && KT != DT_F32 ? 3 : 2)))) void k_encode(EncodeArgs a) {
   using C = Codec<D, B>;
   constexpr int NRW = enc_stage_rows<D, B, KT, QJL>();
   using S = Stage<D, KT, NRW>;
