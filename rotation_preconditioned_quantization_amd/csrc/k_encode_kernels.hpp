@@ -470,21 +470,23 @@ __device__ __forceinline__ void encode_tile(const EncodeArgs& a, int64_t seq, in
                                      (rq.index(triplet_energy(x, y, z), s_qr, sr, mr) << (C::BX + C::BE)));
     }
   } else if constexpr (!JR) {
-    // Pass 1: triplet energies and the (xi, eta) indices, packed into place.
-    float e[T];
+    // (QJL) Pass 1: |y|^2; pass 2: the codes, each packed once, with the
+    // energies formed again rather than held (T registers fewer through the
+    // residual and its projection).
 #pragma unroll
     for (int i = 0; i < T; ++i) {
       float x, y, z;
       triplet_of<D>(v, i, x, y, z);
-      e[i] = triplet_energy(x, y, z);
-      tot += e[i];
-      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be));
+      tot += triplet_energy(x, y, z);
     }
-    // Pass 2: rho index from rho_i^2 = e_i / |y|^2 against the squared midpoints.
     const RhoQuant<C::LR> rq(a.t, tot);
 #pragma unroll
-    for (int i = 0; i < T; ++i)
-      pack_code<C::BT>(words, i, rq.index(e[i], s_qr, sr, mr) << (C::BX + C::BE));
+    for (int i = 0; i < T; ++i) {
+      float x, y, z;
+      triplet_of<D>(v, i, x, y, z);
+      pack_code<C::BT>(words, i, xi_eta_code<C::BX>(x, y, z, s_qx, sx, bx, s_qe, se, be) |
+                                     (rq.index(triplet_energy(x, y, z), s_qr, sr, mr) << (C::BX + C::BE)));
+    }
   } else {
     // Joint rounding ([YL] 联合取整).  Pass 1: the energy and the scalar
     // (xi, eta) indices, the centre of the search.  Pass 2, per triplet t of
