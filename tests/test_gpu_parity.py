@@ -185,6 +185,39 @@ def test_encode_few_keys_equals_bulk(d, b, kdt):
     encode_and_check(d, b, keys[:, 1:6].contiguous(), cap=128, pos0=1, label=f"few d{d}b{b}{kdt}")
 
 
+@pytest.mark.parametrize("d,kdt", [(128, "bf16"), (64, "bf16"), (128, "f32")])
+def test_encode_magnitude_range_boundaries(d, kdt):
+    """The bulk encoder checks |y|^2 instead of scanning each key's largest
+    value; keys whose largest value sits on either side of the scan's
+    thresholds (2^50 and 2^-51), alone in their tile or mixed with others,
+    must get the same words and gamma as the one-key encoder, which scans
+    every key, and agree with the oracle."""
+    octo = _octo()
+    b = 3
+    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    n = 192
+    keys = WL.make_keys(cfg, "cuda", seed=5 + d, n_seq=3, n=n).float()
+    exps = [44, 46, 47, 48, 49, 50, 51, -47, -48, -49, -50, -51, -52, -53, -55]
+    # sequence 0: whole tiles at one magnitude each; 1: the magnitudes mixed
+    # key by key; 2: every fourth key scaled, the rest unit
+    sc = torch.ones(3, n, device="cuda")
+    for t in range(3):
+        sc[0, 64 * t:64 * (t + 1)] = 2.0 ** exps[(5 * t) % len(exps)]
+    sc[1] = torch.tensor([2.0 ** exps[i % len(exps)] for i in range(n)], device="cuda")
+    sc[2, ::4] = torch.tensor([2.0 ** exps[i % len(exps)] for i in range(n // 4)], device="cuda")
+    keys = (keys * sc[..., None]).to(WL._DT[kdt]).contiguous()
+    g = gcb(d, b)
+    bulk = octo.Cache(g, 3, n)
+    octo.octo_encode(g, keys, bulk)
+    few = octo.Cache(g, 3, n)
+    for p in range(0, n, 16):
+        octo.octo_encode(g, keys[:, p:p + 16].contiguous(), few, pos0=p)
+    torch.cuda.synchronize()
+    assert torch.equal(bulk.packed, few.packed)
+    assert torch.equal(bulk.gamma, few.gamma)
+    encode_and_check(d, b, keys, cap=n, label=f"range d{d}{kdt}")
+
+
 def test_encode_f16_keys():
     cfg = WL.CONFIGS[2].scaled(kdtype="f16", keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=2, n=130)
