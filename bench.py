@@ -239,7 +239,8 @@ def quality_harness(dev, repeats: int = 64, bits=(2, 3, 4)):
     Per bit width: normalised MSE E|k - k^|^2/|k|^2, mean cosine(k, k^),
     inner-product error RMS(<q,k^> - <q,k>)/RMS(<q,k>) without and with the
     1-bit QJL term, and the softmax mass (scale 1/sqrt(d)) on the needle when
-    the query is the needle key (the exact keys' mass beside it).  The
+    the query is the needle key, without and with the QJL term (the exact
+    keys' mass beside it).  The
     needle's query and the softmax scale are readings: the pages do not print
     them."""
     import numpy as np
@@ -253,7 +254,7 @@ def quality_harness(dev, repeats: int = 64, bits=(2, 3, 4)):
     rms = lambda x: float(torch.sqrt(torch.mean(x.double() ** 2)))  # noqa: E731
     for b in bits:
         cb = octo.Codebook(d, b, qjl=True, device=0)
-        acc = {k: [] for k in ("mse", "cos", "ip", "ip_qjl", "needle", "needle_exact")}
+        acc = {k: [] for k in ("mse", "cos", "ip", "ip_qjl", "needle", "needle_qjl", "needle_exact")}
         for r in range(repeats):
             keys, q, nk, nq, pos = WL.make_quality_inputs(dev, seed=r)
             cache = octo.Cache(cb, 1, 1024, qjl=True)
@@ -271,6 +272,8 @@ def quality_harness(dev, repeats: int = 64, bits=(2, 3, 4)):
             octo.octo_encode(cb, nk, ncache)
             nl = octo.octo_decode_logits(cb, nq, ncache, nk.shape[1], 1, use_qjl=False)[0, 0].double()
             acc["needle"].append(float(torch.softmax(nl / math.sqrt(d), 0)[pos]))
+            nlq = octo.octo_decode_logits(cb, nq, ncache, nk.shape[1], 1, use_qjl=True)[0, 0].double()
+            acc["needle_qjl"].append(float(torch.softmax(nlq / math.sqrt(d), 0)[pos]))
             ne = (nq[0, 0].double() @ nk[0].double().T) / math.sqrt(d)
             acc["needle_exact"].append(float(torch.softmax(ne, 0)[pos]))
         cb.close()

@@ -1072,3 +1072,8 @@ def test_quality_harness_reproduces_printed_mse():
     assert q["b4"]["cos"] > 0.99
     # at 4 bits the needle keeps nearly all of the exact keys' softmax mass
     assert abs(q["b4"]["needle"] - q["b4"]["needle_exact"]) < 0.02
+    # at 2 bits the QJL-corrected logits keep the needle's mass near the
+    # printed 0.92 ([YL] 实验结果; 0.929 over 64 repeats), the plain ones lose
+    # some of it (0.875: they shrink every logit towards zero)
+    assert abs(q["b2"]["needle_qjl"] - 0.92) < 0.02, q["b2"]
+    assert q["b2"]["needle"] < q["b2"]["needle_qjl"]
