@@ -36,13 +36,18 @@ def _case(cb, cfg, B, Hkv, G, n_q, n, cap, seed):
     return cache, v, q
 
 
-@pytest.mark.parametrize("path", ["single", "multi"])
+@pytest.mark.parametrize("path", ["single", "multi", "multi-d256"])
 def test_static_scratch_equals_workspace_call(path):
     octo = _octo()
     if path == "single":
         cfg = WL.CONFIGS[3]
         cb = octo.Codebook(128, 2, device=0)
         shapes = [(2, 4, 4, 1, 20000, 20032), (1, 2, 4, 1, 3000, 3008)]   # second call smaller
+    elif path == "multi-d256":
+        # two value-dim workgroups per query block and split
+        cfg = WL.CONFIGS[4].scaled(d=256, b=3)
+        cb = octo.Codebook(256, 3, device=0)
+        shapes = [(1, 2, 1, 300, 3000, 3008), (1, 1, 1, 70, 500, 512)]
     else:
         cfg = WL.CONFIGS[4]
         cb = octo.Codebook(64, 3, device=0)
