@@ -717,8 +717,10 @@ def test_attention_d256(b, G):
     check_attention(cfg, 1, 2, G, 300, 320, seed=b, label=f"attn-d256b{b}g{G}")
 
 
-def test_decode_step_append_d256():
-    """The fused append step at d = 256 equals bulk encode + attention."""
+@pytest.mark.parametrize("qjl", [False, True])
+def test_decode_step_append_d256(qjl):
+    """The append step at d = 256 (fused without QJL; with QJL the two-lane
+    encoder then the attention) equals bulk encode + attention."""
     octo = _octo()
     cfg = WL.CONFIGS[2].scaled(d=256, b=4)
     n, B, Hkv, G = 200, 1, 2, 4
@@ -726,15 +728,18 @@ def test_decode_step_append_d256():
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=n_seq, n=n)
     v = WL.make_values(cfg, "cuda", seed=3, n_seq=n_seq, cap=cap)
     q = WL.make_queries(cfg.scaled(Hq=Hq, n_q=1), "cuda", seed=3, B=B)
-    g = gcb(256, 4)
-    ref_cache = octo.Cache(g, n_seq, cap)
+    g = gcb(256, 4, 0, 0, qjl)
+    ref_cache = octo.Cache(g, n_seq, cap, qjl=qjl)
     octo.octo_encode(g, keys, ref_cache)
     ref = octo.octo_decode_attn(g, q, ref_cache, v, n, Hkv)
-    step = octo.Cache(g, n_seq, cap)
+    step = octo.Cache(g, n_seq, cap, qjl=qjl)
     octo.octo_encode(g, keys[:, : n - 1].contiguous(), step)
     out = octo.octo_decode_attn_append(g, keys[:, n - 1].contiguous(), q, step, v, n, Hkv)
     torch.cuda.synchronize()
     assert torch.equal(step.packed, ref_cache.packed) and torch.equal(step.gamma, ref_cache.gamma)
+    if qjl:
+        assert torch.equal(step.qjl_bits, ref_cache.qjl_bits)
+        assert torch.equal(step.qjl_norm, ref_cache.qjl_norm)
     assert torch.equal(out, ref)
 
 
