@@ -60,8 +60,8 @@ typedef struct octo_codebook octo_codebook; /* opaque, owned by the library */
  * ([AR] 位元分配: it depends only on d and the bit budget; [AB]: deterministic
  * given a seed).
  *   d         head dim: 64, 128 and 256 have kernels (any power of two 4..1024
- *             for a host-only codebook).  At d = 256 there is no multi-query
- *             path at b = 5; the encoder gives each key two lanes there.
+ *             for a host-only codebook).  At d = 256 the encoder gives each
+ *             key two lanes.
  *   b         bit budget per coordinate; kernels exist for 1 .. 5.
  *   seed      seeds the WHT sign vector and the QJL projection.
  *   cb_seed   seeds the Monte-Carlo samples the Lloyd-Max tables are fit to.
@@ -244,7 +244,7 @@ octo_status octo_decode_logits(const octo_codebook* cb, const void* q, octo_dtyp
  * n_keys keys, l the logits above (QJL-corrected when the QJL buffers are
  * given), no mask.  scale <= 0 selects 1/sqrt(d).  n_q == 1 runs the split-K
  * single-query kernels; n_q > 1 runs the multi-query MFMA kernel (refused
- * with OCTO_ERR_UNSUPPORTED for QJL buffers and at d = 256, b = 5).
+ * with OCTO_ERR_UNSUPPORTED for QJL buffers).
  * n_keys == 0 writes zeros.
  * Value range: the single-query kernels use V as stored (any bf16).  The
  * multi-query kernel multiplies in fp16: bf16 values with |v| in fp16's

@@ -189,7 +189,11 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
   __shared__ __align__(16) unsigned char s_k[2][KT * KP];
   __shared__ __align__(16) unsigned char s_v[2][KT * VR];
   __shared__ int s_e[2][KT / 64];   // the exponent e of each 64-key half
-  __shared__ float4 s_dir[C::NDIR];
+  // unit directions in LDS, except at d = 256, b = 5, where the 4096-entry
+  // table (64 KiB) does not fit beside the tiles: the rebuild then reads it
+  // from global memory (L2-resident)
+  constexpr bool DIR_LDS = !(D == 256 && B == 5);
+  __shared__ float4 s_dir[DIR_LDS ? C::NDIR : 1];
   __shared__ float s_rho[C::LR];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -206,7 +210,13 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
   const int stid = S::SW == 0 ? tid : tid - 64 * kMQCompute;  // staging thread index
 
   static_assert(TableCopy<C::NDIR, NTH>::SLOTS <= C::NDIR && C::LR <= NTH, "table copies in bounds");
-  for (int i = tid; i < C::NDIR; i += NTH) s_dir[i] = a.t.dirtab[i];
+  const float4* dirp;
+  if constexpr (DIR_LDS) {
+    for (int i = tid; i < C::NDIR; i += NTH) s_dir[i] = a.t.dirtab[i];
+    dirp = s_dir;
+  } else {
+    dirp = a.t.dirtab;
+  }
   if (tid < C::LR) s_rho[tid] = a.t.rho_tab[tid];
 
   // Q' fragment: B[k = dim][n = query], lane (ln, g) holds dims 16j + 8g + 0..7.
@@ -268,10 +278,10 @@ __global__ __launch_bounds__((64 * MQShape<D, B>::NW)) void k_mq_attn(MQArgs a) 
       e = e < -126 ? -126 : (e > 126 ? 126 : e);
       const float gs = gk * __builtin_ldexpf(1.0f, -e);
       if (part == 0) {
-        mq_rebuild<D, B, 0>(st, gs, s_dir, s_rho, krow);
+        mq_rebuild<D, B, 0>(st, gs, dirp, s_rho, krow);
         if (lane == 0) s_e[bs][sw / S::PARTS] = e;
       } else {
-        mq_rebuild_from<D, B, 1>(part, st, gs, s_dir, s_rho, krow);
+        mq_rebuild_from<D, B, 1>(part, st, gs, dirp, s_rho, krow);
       }
     }
     const int c = stid % (S::DV / 8), kg = stid / (S::DV / 8);
@@ -444,7 +454,7 @@ static int mq_copy_recs(LdsCopyRec* out, int n, int max) {
   using C = Codec<D, B>;
   constexpr int NTH = 64 * MQShape<D, B>::NW;
   using TC = TableCopy<C::NDIR, NTH>;
-  if (n < max)
+  if (n < max && !(D == 256 && B == 5))   // (d = 256, b = 5: no LDS copy of the directions)
     out[n++] = {"k_mq_attn", D, B, 0, TAB_DIR, C::NDIR, TC::SLOTS, TC::ENTRIES, C::NDIR, NTH, TC::MASKED};
   if (n < max) out[n++] = {"k_mq_attn", D, B, 0, TAB_RHO, C::LR, C::LR, C::LR, C::LR, NTH, C::LR % NTH != 0};
   return n;
@@ -466,6 +476,7 @@ int lds_copies_mq(LdsCopyRec* out, int max) {
   n = mq_copy_recs<256, 2>(out, n, max);
   n = mq_copy_recs<256, 3>(out, n, max);
   n = mq_copy_recs<256, 4>(out, n, max);
+  n = mq_copy_recs<256, 5>(out, n, max);
   return n;
 }
 
@@ -493,8 +504,7 @@ hipError_t launch_mq_attn(int d, int b, const MQArgs& a, hipStream_t s) {
     case 2562: return mq_t<256, 2>(a, s);
     case 2563: return mq_t<256, 3>(a, s);
     case 2564: return mq_t<256, 4>(a, s);
-    // d = 256 at b = 5: the 4096-entry direction table (64 KiB) and the two
-    // buffer sets of 64-key tiles (98 KiB) exceed the LDS (refused)
+    case 2565: return mq_t<256, 5>(a, s);
   }
   return hipErrorInvalidValue;
 }

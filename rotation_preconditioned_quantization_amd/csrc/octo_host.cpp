@@ -1070,8 +1070,6 @@ static octo_status decode_attn_impl(const octo_codebook* cb, const void* q, octo
   const int G = Hq / Hkv;
   if (n_q > 1) {
     if (qjl) return fail(OCTO_ERR_UNSUPPORTED, "multi-query path has no QJL variant");
-    if (cb->d == 256 && cb->b == 5)
-      return fail(OCTO_ERR_UNSUPPORTED, "multi-query path: no kernel for d = 256, b = 5 (LDS)");
     if (stages & OCTO_STAGE_ROTATE) {
       st = hip_status(launch_rotate(cb->d, r, s), "rotate launch");
       if (st != OCTO_OK) return st;

@@ -743,16 +743,17 @@ def test_decode_step_append_d256(qjl):
     assert torch.equal(out, ref)
 
 
-def test_d256_unsupported_paths_are_refused():
-    """The multi-query path has no kernel at d = 256, b = 5 (its direction
-    table and tiles exceed the LDS); the multi-query path has no QJL variant."""
+@pytest.mark.parametrize("d", [128, 256])
+def test_multi_query_with_qjl_is_refused(d):
+    """The multi-query path has no QJL variant: a call with the QJL buffers
+    and several query tokens is refused before any launch."""
     octo = _octo()
-    g = gcb(256, 5)
-    cache = octo.Cache(g, 1, 128)
-    keys = torch.randn((1, 100, 256), device="cuda", dtype=torch.bfloat16)
+    g = gcb(d, 3, 0, 0, True)
+    cache = octo.Cache(g, 1, 128, qjl=True)
+    keys = torch.randn((1, 100, d), device="cuda", dtype=torch.bfloat16)
     octo.octo_encode(g, keys, cache)
-    q = torch.randn((1, 2, 8, 256), device="cuda", dtype=torch.bfloat16)
-    v = torch.zeros((1, 128, 256), device="cuda", dtype=torch.bfloat16)
+    q = torch.randn((1, 2, 8, d), device="cuda", dtype=torch.bfloat16)
+    v = torch.zeros((1, 128, d), device="cuda", dtype=torch.bfloat16)
     with pytest.raises(octo.OctoError) as e:
         octo.octo_decode_attn(g, q, cache, v, 100, 1)
     assert e.value.status == octo.OCTO_ERR_UNSUPPORTED
@@ -935,7 +936,8 @@ def test_mq_video_recipe_small():
     check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
 
 
-@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5), (256, 1), (256, 4)])
+@pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5), (256, 1), (256, 4),
+                                 (256, 5)])
 def test_mq_shapes_and_gqa(d, b):
     check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
 
