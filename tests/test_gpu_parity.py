@@ -2,7 +2,7 @@
 
 Every test draws seeded synthetic inputs (workloads), runs the library on
 cuda:0 and compares with the oracle under the rules in tests/parity.py.
-Sizes span several 64-key tiles with ragged tails; the full-size configs
+Sizes span several 64-key tiles with ragged tails; the full-size workloads
 compare sampled sequences.  Marked gpu: needs an MI355X and the built library.
 """
 import functools
@@ -75,10 +75,10 @@ def encode_and_check(d, b, keys, cap, pos0=0, qjl=False, seed=0, label="", cap_f
 
 
 # ----------------------------------------------------------------- encoder --
-def test_encode_toy_full_config1():
-    cfg = WL.CONFIGS[1]
+def test_encode_toy_full():
+    cfg = WL.WORKLOADS["toy"]
     keys = WL.make_keys(cfg, "cuda")
-    cache, codes, enc = encode_and_check(cfg.d, cfg.b, keys, cfg.cap, label="config1")
+    cache, codes, enc = encode_and_check(cfg.d, cfg.b, keys, cfg.cap, label="toy")
     # reconstruction of the device stream
     octo = _octo()
     rec = f64(octo.octo_debug_reconstruct(gcb(cfg.d, cfg.b), cache, cfg.N)).reshape(-1, cfg.d)
@@ -91,7 +91,7 @@ def test_encode_toy_full_config1():
                                  (128, 1), (128, 5), (64, 1), (64, 5)])
 @pytest.mark.parametrize("kdt", ["f32", "bf16"])
 def test_encode_all_shapes_ragged(d, b, kdt):
-    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=d + b, n_seq=3, n=200)
     encode_and_check(d, b, keys, cap=256, label=f"d{d}b{b}{kdt}")
 
@@ -103,7 +103,7 @@ def test_encode_joint_rounding(d, b, kdt):
     """octo_encode_joint against the oracle's joint rounding ([YL] 联合取整),
     ragged tail, with the same gamma as the scalar encoder."""
     octo = _octo()
-    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=40 + d + b, n_seq=3, n=200)
     g = gcb(d, b)
     cache = octo.Cache(g, 3, 256)
@@ -131,7 +131,7 @@ def test_encode_joint_rounding(d, b, kdt):
 def test_encode_joint_rounding_with_qjl(d, b):
     """Joint rounding with the QJL residual: the residual follows the chosen codes."""
     octo = _octo()
-    cfg = WL.CONFIGS[5].scaled(d=d, b=b)
+    cfg = WL.WORKLOADS["qjl"].scaled(d=d, b=b)
     keys = WL.make_keys(cfg, "cuda", seed=9, n_seq=2, n=130)
     g = gcb(d, b, 0, 0, True)
     cache = octo.Cache(g, 2, 192, qjl=True)
@@ -164,7 +164,7 @@ def test_encode_few_keys_equals_bulk(d, b, kdt):
     encoder; it writes the same words and gamma as the bulk encoder, bit for
     bit (same fp32 operations in the same order), including extreme keys."""
     octo = _octo()
-    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=77 + d, n_seq=3, n=100)
     keys[0, 3] = 0
     keys[1, 5] *= 1e-30 if kdt == "f32" else 1e-3
@@ -194,7 +194,7 @@ def test_encode_magnitude_range_boundaries(d, kdt):
     every key, and agree with the oracle."""
     octo = _octo()
     b = 3
-    cfg = WL.CONFIGS[2].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=d, b=b, kdtype=kdt, keys="gauss")
     n = 192
     keys = WL.make_keys(cfg, "cuda", seed=5 + d, n_seq=3, n=n).float()
     exps = [44, 46, 47, 48, 49, 50, 51, -47, -48, -49, -50, -51, -52, -53, -55]
@@ -219,7 +219,7 @@ def test_encode_magnitude_range_boundaries(d, kdt):
 
 
 def test_encode_f16_keys():
-    cfg = WL.CONFIGS[2].scaled(kdtype="f16", keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(kdtype="f16", keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=2, n=130)
     encode_and_check(128, 4, keys, cap=192, label="f16")
 
@@ -228,7 +228,7 @@ def test_encode_online_append_matches_bulk():
     """Encoding in pieces (one token at a time at the end) writes the same
     words as one bulk call ([AB]: online codec)."""
     octo = _octo()
-    cfg = WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["llm_decode"]
     keys = WL.make_keys(cfg, "cuda", seed=11, n_seq=2, n=139)
     g = gcb(128, 4)
     bulk = octo.Cache(g, 2, 192)
@@ -287,7 +287,7 @@ def test_encode_degenerate_keys():
 
 def test_encode_is_deterministic():
     octo = _octo()
-    keys = WL.make_keys(WL.CONFIGS[3], "cuda", seed=2, n_seq=4, n=300)
+    keys = WL.make_keys(WL.WORKLOADS["extreme"], "cuda", seed=2, n_seq=4, n=300)
     g = gcb(128, 2)
     a = octo.Cache(g, 4, 320)
     b = octo.Cache(g, 4, 320)
@@ -349,36 +349,36 @@ def check_qjl_encoder(enc, codes, gsign, gnu, cb, S, label):
     assert ok.all(), f"{label}: residual norms differ by more than one fp16 ulp"
 
 
-def test_logits_toy_full_config1():
-    cfg = WL.CONFIGS[1]
-    check_logits(cfg, 1, 1, 1, cfg.N, cfg.cap, label="config1")
+def test_logits_toy_full():
+    cfg = WL.WORKLOADS["toy"]
+    check_logits(cfg, 1, 1, 1, cfg.N, cfg.cap, label="toy")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 4, 8])
 def test_logits_gqa_ragged(G):
-    cfg = WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["llm_decode"]
     check_logits(cfg, 2, 2, G, 333, 384, seed=G, label=f"gqa{G}")
 
 
 @pytest.mark.parametrize("d,b", [(64, 3), (128, 2), (128, 1), (128, 5), (64, 5), (64, 1), (64, 2), (64, 4)])
 def test_logits_other_shapes(d, b):
-    cfg = WL.CONFIGS[3].scaled(d=d, b=b)
+    cfg = WL.WORKLOADS["extreme"].scaled(d=d, b=b)
     check_logits(cfg, 1, 2, 4, 700, 768, seed=5, label=f"d{d}b{b}")
 
 
-def test_logits_qjl_small_config5_recipe():
-    cfg = WL.CONFIGS[5]
+def test_logits_qjl_small_recipe():
+    cfg = WL.WORKLOADS["qjl"]
     check_logits(cfg, 2, 2, 4, 450, 512, seed=1, qjl=True, label="qjl")
 
 
 def test_logits_qjl_d64():
-    cfg = WL.CONFIGS[5].scaled(d=64)
+    cfg = WL.WORKLOADS["qjl"].scaled(d=64)
     check_logits(cfg, 1, 1, 2, 200, 256, seed=2, qjl=True, label="qjl-d64")
 
 
 @pytest.mark.parametrize("d,b", [(128, 1), (128, 5), (64, 5), (128, 2), (64, 2), (64, 1), (128, 4), (64, 4)])
 def test_logits_qjl_wider_bit_budgets(d, b):
-    cfg = WL.CONFIGS[5].scaled(d=d, b=b)
+    cfg = WL.WORKLOADS["qjl"].scaled(d=d, b=b)
     check_logits(cfg, 1, 1, 2, 200, 256, seed=3 + b, qjl=True, label=f"qjl-d{d}b{b}")
 
 
@@ -388,14 +388,14 @@ def test_logits_qjl_d256(b, kdt):
     over both halves (the key's element 128 lies in the first lane's last
     triplet) and the signs of S r' on the matrix cores with S read from
     global memory; logits against the oracle, ragged tail."""
-    cfg = WL.CONFIGS[5].scaled(d=256, b=b, kdtype=kdt)
+    cfg = WL.WORKLOADS["qjl"].scaled(d=256, b=b, kdtype=kdt)
     check_logits(cfg, 1, 2, 2, 333, 384, seed=31 + b, qjl=True, label=f"qjl-d256b{b}{kdt}")
 
 
 def test_attention_qjl_d256():
     """Single-query attention with the QJL term at d = 256 (the value dims
     over two blocks, each forming the QJL-corrected logits)."""
-    cfg = WL.CONFIGS[5].scaled(d=256, b=3, keys="gauss")
+    cfg = WL.WORKLOADS["qjl"].scaled(d=256, b=3, keys="gauss")
     check_attention(cfg, 1, 2, 4, 300, 320, seed=37, qjl=True, label="attn-qjl-d256")
 
 
@@ -404,7 +404,7 @@ def test_logits_qjl_fp32_keys(d, b):
     """The QJL encoder with fp32 keys (at d = 128, b = 5 its blocks stage 8
     key rows per phase instead of 16, so that the staging buffers fit the LDS
     beside the QJL matrix and the 4096-entry direction table); ragged tail."""
-    cfg = WL.CONFIGS[5].scaled(d=d, b=b, kdtype="f32")
+    cfg = WL.WORKLOADS["qjl"].scaled(d=d, b=b, kdtype="f32")
     check_logits(cfg, 2, 1, 2, 333, 384, seed=11 + b, qjl=True, label=f"qjl-f32-d{d}b{b}")
 
 
@@ -413,14 +413,14 @@ def test_mq_d256_multi_split(b):
     """d = 256: the value dims split over two adjacent workgroups, each
     forming every score of its queries; 64-key tiles, several splits, a
     ragged last tile, GQA and a partial query block."""
-    check_mq(WL.CONFIGS[4].scaled(d=256, b=b), 4, 2, 300, 3000, 3008, seed=23 + b, label=f"mq-d256b{b}-split")
+    check_mq(WL.WORKLOADS["video_block"].scaled(d=256, b=b), 4, 2, 300, 3000, 3008, seed=23 + b, label=f"mq-d256b{b}-split")
 
 
 def test_mq_d128_b5_multi_split():
     """d = 128, b = 5 runs the multi-query kernel on 64-key tiles (the
     4096-entry direction table leaves LDS for no more): a cache long enough
     for several splits, a ragged last tile and GQA."""
-    check_mq(WL.CONFIGS[4].scaled(d=128, b=5), 2, 1, 300, 5000, 5056, seed=17, label="mq-d128b5-split")
+    check_mq(WL.WORKLOADS["video_block"].scaled(d=128, b=5), 2, 1, 300, 5000, 5056, seed=17, label="mq-d128b5-split")
 
 
 # --------------------------------------------------------------- attention --
@@ -469,33 +469,33 @@ def check_attention(cfg, B, Hkv, G, n, cap, seed=0, qjl=False, label="", seqs=No
 
 
 def test_attention_llm_recipe_small():
-    check_attention(WL.CONFIGS[2], 1, 2, 4, 1000, 1024, seed=1, label="llm-small")
+    check_attention(WL.WORKLOADS["llm_decode"], 1, 2, 4, 1000, 1024, seed=1, label="llm-small")
 
 
 def test_attention_extreme_recipe_small():
-    check_attention(WL.CONFIGS[3], 2, 2, 4, 777, 832, seed=2, label="extreme-small")
+    check_attention(WL.WORKLOADS["extreme"], 2, 2, 4, 777, 832, seed=2, label="extreme-small")
 
 
 @pytest.mark.parametrize("G", [1, 2, 3, 8])
 def test_attention_gqa(G):
-    check_attention(WL.CONFIGS[2].scaled(b=3), 1, 2, G, 300, 320, seed=G, label=f"attn-gqa{G}")
+    check_attention(WL.WORKLOADS["llm_decode"].scaled(b=3), 1, 2, G, 300, 320, seed=G, label=f"attn-gqa{G}")
 
 
 @pytest.mark.parametrize("d,b,qjl", [(128, 1, False), (128, 5, False), (64, 5, False), (128, 5, True)])
 def test_attention_wider_bit_budgets(d, b, qjl):
     """b = 1 (rho takes 0 bits: one level) and b = 5 (4096 directions, not the
     combined table) through the single-query attention, with and without QJL."""
-    cfg = (WL.CONFIGS[5] if qjl else WL.CONFIGS[2]).scaled(d=d, b=b, keys="gauss")
+    cfg = (WL.WORKLOADS["qjl"] if qjl else WL.WORKLOADS["llm_decode"]).scaled(d=d, b=b, keys="gauss")
     check_attention(cfg, 1, 2, 4, 300, 320, seed=b + d, qjl=qjl, label=f"attn-d{d}b{b}{'q' if qjl else ''}")
 
 
 def test_attention_d64():
-    check_attention(WL.CONFIGS[3].scaled(d=64, b=3, keys="gauss"), 1, 3, 2, 500, 512, seed=4,
+    check_attention(WL.WORKLOADS["extreme"].scaled(d=64, b=3, keys="gauss"), 1, 3, 2, 500, 512, seed=4,
                     label="attn-d64")
 
 
 def test_attention_with_qjl():
-    check_attention(WL.CONFIGS[5], 1, 2, 4, 400, 448, seed=6, qjl=True, label="attn-qjl")
+    check_attention(WL.WORKLOADS["qjl"], 1, 2, 4, 400, 448, seed=6, qjl=True, label="attn-qjl")
 
 
 @pytest.mark.parametrize("n,qjl", [(1000, False), (65, False), (1, False), (400, True)])
@@ -505,7 +505,7 @@ def test_decode_step_append(n, qjl):
     octo_decode_attn: the same cache bytes and the same output; the output
     also matches the oracle."""
     octo = _octo()
-    cfg = WL.CONFIGS[5] if qjl else WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["qjl"] if qjl else WL.WORKLOADS["llm_decode"]
     B, Hkv, G, cap = 1, 2, 4, ((n + 63) // 64) * 64
     Hq, n_seq, d = Hkv * G, B * Hkv, cfg.d
     keys = WL.make_keys(cfg, "cuda", seed=n, n_seq=n_seq, n=n)
@@ -540,7 +540,7 @@ def test_decode_step_append(n, qjl):
 
 @pytest.mark.parametrize("n", [1, 63, 64, 65])
 def test_attention_tiny_caches(n):
-    check_attention(WL.CONFIGS[2], 1, 1, 4, n, 128, seed=n, label=f"attn-n{n}")
+    check_attention(WL.WORKLOADS["llm_decode"], 1, 1, 4, n, 128, seed=n, label=f"attn-n{n}")
 
 
 def test_attention_empty_cache_writes_zeros():
@@ -604,7 +604,7 @@ def test_decode_stages_equal_one_call(mode):
     """The launches run one by one (rotate, main kernel, combine, as the
     timing harness does) give the same bytes as one call with all stages."""
     octo = _octo()
-    cfg = WL.CONFIGS[4 if mode == "attn_mq" else 2]
+    cfg = WL.WORKLOADS["video_block" if mode == "attn_mq" else "llm_decode"]
     n_q = 40 if mode == "attn_mq" else 1
     g, _, cache, v, q, Hkv = _decode_setup(cfg, 700, 768, seed=3, n_q=n_q)
     if mode == "logits":
@@ -627,7 +627,7 @@ def test_decode_stages_equal_one_call(mode):
 def test_side_stream_equals_default_stream():
     """Every entry point runs on the stream it is given."""
     octo = _octo()
-    cfg = WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["llm_decode"]
     g, keys, cache, v, q, Hkv = _decode_setup(cfg, 500, 512, seed=4)
     ref = octo.octo_decode_attn(g, q, cache, v, 500, Hkv)
     side = torch.cuda.Stream()
@@ -646,7 +646,7 @@ def test_graph_replays_equal_eager(mode):
     """Encode + decode captured in a HIP graph: every replay, with eager work
     and synchronisations between the replays, reproduces the eager bytes."""
     octo = _octo()
-    cfg = WL.CONFIGS[4 if mode == "attn_mq" else 2]
+    cfg = WL.WORKLOADS["video_block" if mode == "attn_mq" else "llm_decode"]
     n_q = 48 if mode == "attn_mq" else 1
     n, cap = 600, 640
     g, keys, cache, v, q, Hkv = _decode_setup(cfg, n, cap, seed=6, n_q=n_q)
@@ -692,13 +692,13 @@ def test_graph_replays_equal_eager(mode):
 # encoder, and the attention kernel splits the value dims over two blocks.
 @pytest.mark.parametrize("b,kdt", [(2, "bf16"), (4, "bf16"), (3, "f32"), (1, "f16"), (5, "bf16")])
 def test_encode_d256(b, kdt):
-    cfg = WL.CONFIGS[2].scaled(d=256, b=b, kdtype=kdt, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=256, b=b, kdtype=kdt, keys="gauss")
     keys = WL.make_keys(cfg, "cuda", seed=256 + b, n_seq=2, n=150)
     encode_and_check(256, b, keys, cap=192, label=f"d256b{b}{kdt}")
 
 
 def test_encode_d256_outliers_and_zero_key():
-    cfg = WL.CONFIGS[2].scaled(d=256, b=4)
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=256, b=4)
     keys = WL.make_keys(cfg, "cuda", seed=9, n_seq=1, n=70)
     keys[0, 5] = 0
     keys[0, 6] *= 1e-3
@@ -707,13 +707,13 @@ def test_encode_d256_outliers_and_zero_key():
 
 @pytest.mark.parametrize("b", [1, 2, 3, 4, 5])
 def test_logits_d256(b):
-    cfg = WL.CONFIGS[3].scaled(d=256, b=b)
+    cfg = WL.WORKLOADS["extreme"].scaled(d=256, b=b)
     check_logits(cfg, 1, 2, 4, 300, 320, seed=7, label=f"logits-d256b{b}")
 
 
 @pytest.mark.parametrize("b,G", [(4, 4), (3, 6), (5, 2), (1, 4)])
 def test_attention_d256(b, G):
-    cfg = WL.CONFIGS[2].scaled(d=256, b=b, keys="gauss")
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=256, b=b, keys="gauss")
     check_attention(cfg, 1, 2, G, 300, 320, seed=b, label=f"attn-d256b{b}g{G}")
 
 
@@ -722,7 +722,7 @@ def test_decode_step_append_d256(qjl):
     """The append step at d = 256 (fused without QJL; with QJL the two-lane
     encoder then the attention) equals bulk encode + attention."""
     octo = _octo()
-    cfg = WL.CONFIGS[2].scaled(d=256, b=4)
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=256, b=4)
     n, B, Hkv, G = 200, 1, 2, 4
     cap, Hq, n_seq = 256, Hkv * G, B * Hkv
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=n_seq, n=n)
@@ -766,7 +766,7 @@ def test_max_sequences_per_launch():
     sequences against the oracle."""
     octo = _octo()
     d, b, n_seq, n, cap = 64, 1, 65535, 3, 64
-    cfg = WL.CONFIGS[4].scaled(b=b)
+    cfg = WL.WORKLOADS["video_block"].scaled(b=b)
     keys = WL.make_keys(cfg, "cuda", seed=8, n_seq=n_seq, n=n)
     g = gcb(d, b)
     cache = octo.Cache(g, n_seq, cap)
@@ -800,7 +800,7 @@ def test_cache_past_4_gib_of_codes():
     d, b, G = 128, 4, 4
     cap, n_new = 1 << 26, 200
     pos0 = cap - n_new
-    cfg = WL.CONFIGS[2]
+    cfg = WL.WORKLOADS["llm_decode"]
     g = gcb(d, b)
     cache = octo.Cache(g, 1, cap)
     keys = WL.make_keys(cfg, "cuda", seed=5, n_seq=1, n=n_new)
@@ -837,30 +837,30 @@ def test_cache_past_4_gib_of_codes():
 
 
 # ---------------------------------------------------------- full-size runs --
-def test_full_config2_attention():
-    cfg = WL.CONFIGS[2]
-    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config2-full",
+def test_full_llm_decode_attention():
+    cfg = WL.WORKLOADS["llm_decode"]
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="llm_decode-full",
                     seqs=[0, 5])
 
 
-def test_full_config2_shape_at_d256_sampled():
+def test_full_llm_decode_shape_at_d256_sampled():
     """The LLM-decode shape (8 KV heads x 32768 keys, GQA 4) at d = 256, in
     the launch configuration bench.py --head-dim 256 times; two sequences
     checked against the oracle in full."""
-    cfg = WL.CONFIGS[2].scaled(d=256)
-    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config2-d256-full",
+    cfg = WL.WORKLOADS["llm_decode"].scaled(d=256)
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="llm_decode-d256-full",
                     seqs=[2, 7])
 
 
-def test_full_config3_attention_sampled():
-    cfg = WL.CONFIGS[3]
-    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="config3-full",
+def test_full_extreme_attention_sampled():
+    cfg = WL.WORKLOADS["extreme"]
+    check_attention(cfg, cfg.B, cfg.Hkv, cfg.G, cfg.N, cfg.cap, seed=0, label="extreme-full",
                     seqs=[3, 30])
 
 
-def test_full_config5_qjl_logits_sampled():
+def test_full_qjl_logits_sampled():
     octo = _octo()
-    cfg = WL.CONFIGS[5]
+    cfg = WL.WORKLOADS["qjl"]
     d, b = cfg.d, cfg.b
     keys = WL.make_keys(cfg, "cuda")
     g = gcb(d, b, 0, 0, True)
@@ -878,11 +878,11 @@ def test_full_config5_qjl_logits_sampled():
         enc = O.encode(kk, cb)
         packed = cache.packed.view(cfg.n_seq, -1)[s].cpu().numpy()
         codes = unpack_device_codes(packed, cb, 1, cfg.cap, cfg.N)
-        assert_codes_match(codes, enc, cb, f"config5 seq{s}")
+        assert_codes_match(codes, enc, cb, f"qjl seq{s}")
         gsign = unpack_device_signs(cache.qjl_bits.view(cfg.n_seq, -1)[s].cpu().numpy(), d, 1,
                                     cfg.cap, cfg.N)
         gnu = cache.qjl_norm.view(cfg.n_seq, -1)[s].cpu().numpy().view(np.float16)[: cfg.N]
-        check_qjl_encoder(enc, codes, gsign, gnu[None], cb, S, f"config5 seq{s}")
+        check_qjl_encoder(enc, codes, gsign, gnu[None], cb, S, f"qjl seq{s}")
         uh = O.decode_rotated(codes[0], cb)
         gam = cache.gamma.view(cfg.n_seq, -1)[s, : cfg.N].cpu().numpy()
         qe = O.QJLEncoded(gsign[0], gnu, None, None)
@@ -891,7 +891,7 @@ def test_full_config5_qjl_logits_sampled():
             ref = O.qjl_logits(qq[bb, h], uh, gam, qe, S, cb)
             err = logit_err(f64(lg[bb, h]), ref, np.linalg.norm(qq[bb, h]), gam, d)
             assert err <= 1e-3, (s, h, err)
-    say("[config5-full] sampled sequences ok")
+    say("[qjl-full] sampled sequences ok")
 
 
 # ------------------------------------------------------- multi-query (MFMA) --
@@ -933,18 +933,18 @@ def check_mq(cfg, Hq, Hkv, n_q, n, cap, seed=0, label="", heads=None, chunk=None
 
 
 def test_mq_video_recipe_small():
-    check_mq(WL.CONFIGS[4], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
+    check_mq(WL.WORKLOADS["video_block"], 2, 2, 200, 1000, 1024, seed=1, label="mq-small")
 
 
 @pytest.mark.parametrize("d,b", [(64, 2), (64, 4), (128, 3), (64, 5), (128, 1), (128, 5), (256, 1), (256, 4),
                                  (256, 5)])
 def test_mq_shapes_and_gqa(d, b):
-    check_mq(WL.CONFIGS[4].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
+    check_mq(WL.WORKLOADS["video_block"].scaled(d=d, b=b), 4, 2, 130, 700, 768, seed=d + b, label=f"mq-d{d}b{b}")
 
 
 @pytest.mark.parametrize("n_q,n", [(2, 1), (2, 255), (129, 257)])
 def test_mq_edges(n_q, n):
-    check_mq(WL.CONFIGS[4], 1, 1, n_q, n, 320, seed=n, label=f"mq-edge{n_q}x{n}")
+    check_mq(WL.WORKLOADS["video_block"], 1, 1, n_q, n, 320, seed=n, label=f"mq-edge{n_q}x{n}")
 
 
 def _mq_with_values(vfix, vref, kfix=None):
@@ -952,7 +952,7 @@ def _mq_with_values(vfix, vref, kfix=None):
     vfix(v) (and the keys by kfix(keys)); the oracle attends over vref(v)
     (float64 of the bf16 values)."""
     octo = _octo()
-    cfg = WL.CONFIGS[4]
+    cfg = WL.WORKLOADS["video_block"]
     d, b, n, cap, n_q = cfg.d, cfg.b, 500, 512, 40
     keys = WL.make_keys(cfg, "cuda", seed=21, n_seq=1, n=n)
     if kfix is not None:
@@ -1017,9 +1017,9 @@ def test_mq_key_norms_spread_within_a_tile():
     assert err <= 2e-3
 
 
-def test_full_config4_video_block_sampled():
-    cfg = WL.CONFIGS[4]
-    check_mq(cfg, cfg.Hq, cfg.Hkv, cfg.n_q, cfg.N, cfg.cap, seed=0, label="config4-full",
+def test_full_video_block_sampled():
+    cfg = WL.WORKLOADS["video_block"]
+    check_mq(cfg, cfg.Hq, cfg.Hkv, cfg.n_q, cfg.N, cfg.cap, seed=0, label="video_block-full",
              heads=[0, 17], chunk=cfg.chunk)
 
 
@@ -1032,7 +1032,7 @@ def test_qjl_seed_averaged_bias():
     error against the exact logit: QJL within 3 standard errors of 0, plain
     OCTOPUS clearly negative."""
     octo = _octo()
-    cfg = WL.CONFIGS[5].scaled(B=1, Hq=4, Hkv=1, N=2048)
+    cfg = WL.WORKLOADS["qjl"].scaled(B=1, Hq=4, Hkv=1, N=2048)
     keys = WL.make_keys(cfg, "cuda", seed=3, n_seq=1, n=cfg.N)
     q = WL.make_queries(cfg, "cuda", seed=3)[:, :, 0].contiguous()
     exact = f64(q[0]) @ f64(keys[0]).T

@@ -40,16 +40,16 @@ def _case(cb, cfg, B, Hkv, G, n_q, n, cap, seed):
 def test_static_scratch_equals_workspace_call(path):
     octo = _octo()
     if path == "single":
-        cfg = WL.CONFIGS[3]
+        cfg = WL.WORKLOADS["extreme"]
         cb = octo.Codebook(128, 2, device=0)
         shapes = [(2, 4, 4, 1, 20000, 20032), (1, 2, 4, 1, 3000, 3008)]   # second call smaller
     elif path == "multi-d256":
         # two value-dim workgroups per query block and split
-        cfg = WL.CONFIGS[4].scaled(d=256, b=3)
+        cfg = WL.WORKLOADS["video_block"].scaled(d=256, b=3)
         cb = octo.Codebook(256, 3, device=0)
         shapes = [(1, 2, 1, 300, 3000, 3008), (1, 1, 1, 70, 500, 512)]
     else:
-        cfg = WL.CONFIGS[4]
+        cfg = WL.WORKLOADS["video_block"]
         cb = octo.Codebook(64, 3, device=0)
         shapes = [(1, 4, 1, 300, 9000, 9024), (1, 2, 1, 70, 1000, 1024)]
     out_static = None

@@ -68,6 +68,8 @@ CONFIGS = {
               chunk=16384),
     5: Config(5, "qjl", 128, 3, 8, 32, 8, 65536, "bf16", "bf16", 1, "logits", "gauss", qjl=True),
 }
+# the same workloads by name
+WORKLOADS = {c.name: c for c in CONFIGS.values()}
 
 _DT = {"f32": torch.float32, "bf16": torch.bfloat16, "f16": torch.float16}
 
